@@ -1,0 +1,146 @@
+"""fp64 CPU oracle of the KDA operator -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never does, and
+this package never imports the product library: the two share no code.
+
+Three independent forms of the same operator (the "Kimi Linear" page,
+sections "Background: from the delta rule to gated DeltaNet", "Kimi Delta
+Attention", "Why channel-wise gating matters" and "The constrained DPLR form
+and the chunkwise algorithm"):
+
+* ``recurrent``   -- plain C, fp64, token by token (kda_oracle.c); the oracle.
+* ``forms.brute`` -- explicit dk x dk transition matrices and the
+  "query dotted with keys weighted by a cumulative product of transitions"
+  expansion; numpy fp64, tiny sizes only.
+* ``forms.chunkwise`` -- the chunked WY/UT form, fp64, written from the
+  algebra of the recurrence; used to pin the recurrent form.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_BUILD = os.path.join(_HERE, "_build")
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIBS: dict = {}
+
+
+def lib_path(mutant: int = 0) -> str:
+    name = "libkda_oracle.so" if mutant == 0 else f"libkda_oracle_m{mutant}.so"
+    return os.path.join(_BUILD, name)
+
+
+def build(mutant: int = 0, force: bool = True) -> str:
+    """Compile the C oracle with gcc (no GPU code involved)."""
+    os.makedirs(_BUILD, exist_ok=True)
+    out = lib_path(mutant)
+    if force or not os.path.exists(out):
+        tmp = out + f".tmp{os.getpid()}"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+               f"-DKDA_ORACLE_MUTANT={mutant}", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _lib(mutant: int = 0):
+    if mutant in _LIBS:
+        return _LIBS[mutant]
+    path = lib_path(mutant)
+    if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+        build(mutant)
+    lib = ctypes.CDLL(path)
+    f = lib.kda_oracle_forward
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    _LIBS[mutant] = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, threads=None,
+              mutant: int = 0):
+    """fp64 token-by-token KDA forward.
+
+    Inputs (numpy): q, k [T, H, dk] and v [T, H, dv] as float32 or uint16
+    (bf16 bits); log_alpha float32 [T, H, dk]; beta float32 [T, H];
+    init_state [N, H, dk, dv] (widened to fp64) or None; cu_seqlens int [N+1] or None
+    (one sequence).  A leading batch axis [B, T, H, d] is accepted when
+    cu_seqlens is None and is treated as B sequences of length T.
+
+    Returns (out fp64 with the shape of v, final_state fp64 [N, H, dk, dv]).
+    """
+    vshape = v.shape
+    if q.ndim == 4:
+        assert cu_seqlens is None
+        B, T = q.shape[:2]
+        q, k, v = (x.reshape((B * T,) + x.shape[2:]) for x in (q, k, v))
+        log_alpha = log_alpha.reshape((B * T,) + log_alpha.shape[2:])
+        beta = beta.reshape(B * T, -1)
+        cu_seqlens = np.arange(B + 1, dtype=np.int64) * T
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], np.int64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    assert int(cu[-1]) == T, "cu_seqlens must cover every token"
+    bf16 = q.dtype == np.uint16
+    want = np.uint16 if bf16 else np.float32
+    q, k, v = (np.ascontiguousarray(x, dtype=want) for x in (q, k, v))
+    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    be = np.ascontiguousarray(beta, dtype=np.float32).reshape(T, H)
+    init = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float64)
+    if init is not None:
+        assert init.shape == (N, H, dk, dv)
+    out = np.zeros((T, H, dv), np.float64)
+    fin = np.zeros((N, H, dk, dv), np.float64)
+    nt = threads or max(1, min(64, os.cpu_count() or 1))
+    rc = _lib(mutant).kda_oracle_forward(N, cu.ctypes.data, H, dk, dv, int(bf16), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(la), _ptr(be), _ptr(init), _ptr(out),
+                                         _ptr(fin), nt)
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_forward failed ({rc})")
+    return out.reshape(vshape), fin
+
+
+def decode_steps(state, steps, threads=None, mutant: int = 0):
+    """Consecutive one-token updates of N independent sequences.
+
+    ``state`` [N, H, dk, dv] (any float dtype); ``steps`` a list of dicts with
+    q, k [N, H, dk], v [N, H, dv], beta [N, H], log_alpha [N, H, dk].  Each
+    step is the recurrence over N one-token sequences starting from the
+    current state, which is carried in fp64 between steps.  Returns (list of
+    fp64 outputs [N, H, dv], fp64 final state).
+    """
+    S = np.asarray(state, np.float64)
+    cu = np.arange(S.shape[0] + 1, dtype=np.int64)
+    outs = []
+    for st in steps:
+        o, S = recurrent(st["q"], st["k"], st["v"], st["log_alpha"], st["beta"], S, cu,
+                         threads, mutant)
+        outs.append(o)
+    return outs, S
+
+
+def metrics(x, ref):
+    """max|x - ref| / RMS(ref) plus the absolute max and RMS errors."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(x - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    mx = float(err.max()) if err.size else 0.0
+    return {"max_over_rms": mx / rms if rms > 0 else (0.0 if mx == 0 else float("inf")),
+            "max_abs": mx, "rms_err": float(np.sqrt(np.mean(err * err))) if err.size else 0.0,
+            "rms_ref": rms}

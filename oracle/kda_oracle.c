@@ -1,0 +1,235 @@
+/*
+ * kda_oracle.c -- fp64 token-by-token reference of the KDA operator.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library includes, links
+ * or calls this file; only tests, the smoke check and the CPU-baseline leg of
+ * the benchmark load it.  It shares no code with the HIP path.
+ *
+ * What it computes ("Kimi Linear" page, sections "Background: from the delta
+ * rule to gated DeltaNet", "Kimi Delta Attention" and "The constrained DPLR
+ * form and the chunkwise algorithm"):  the gated delta rule whose scalar
+ * forget gate is replaced by a diagonal (per key channel) gate,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = S_t^T q_t,            alpha_t = exp(log_alpha_t)  (elementwise),
+ *
+ * i.e. the DPLR transition Diag(alpha) - a b^T with a = beta k (the
+ * learning-rate-scaled key) and b = alpha (.) k (the key modulated by the
+ * gate).  Each step, literally in the order the page describes the delta rule:
+ *   1. decay:      S <- Diag(alpha_t) S          (rows of S are key channels)
+ *   2. read:       p = S^T k_t                   (what the memory predicts)
+ *   3. correct:    u = beta_t (v_t - p)
+ *   4. write:      S <- S + k_t u^T
+ *   5. output:     o_t = S^T q_t                 (reads the updated state)
+ *
+ * Layout: tokens packed as [T_total, H, d] (row-major, d fastest); sequence s
+ * is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.  State [N, H, dk, dv], dv
+ * fastest.  q/k/v are fp32 or bf16 (uint16 bit patterns); bf16 values are
+ * widened exactly, so the oracle sees the same real numbers the GPU reads.
+ *
+ * Threads: one (sequence, head) unit at a time per thread, pthreads.
+ *
+ * KDA_ORACLE_MUTANT (compile-time, tests only): plants one deliberate mistake
+ * so the pin tests can show they catch it.  0 (default) is the correct oracle;
+ * 1 decay after the write, 2 output before the write, 3 wrong sign of the
+ * prediction, 4 transposed state in the output, 5 beta dropped, 6 gate used
+ * without exp, 7 initial state ignored.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef KDA_ORACLE_MUTANT
+#define KDA_ORACLE_MUTANT 0
+#endif
+
+typedef struct {
+    int64_t num_seqs;
+    const int64_t* cu;
+    int heads, dk, dv;
+    int in_bf16;
+    const void *q, *k, *v;
+    const float *log_alpha, *beta;
+    const double* init;
+    double *out, *final_state;
+    int64_t next_unit;
+    pthread_mutex_t lock;
+} job_t;
+
+static double load_in(const void* p, int bf16, int64_t i) {
+    if (bf16) {
+        uint32_t u = ((uint32_t)((const uint16_t*)p)[i]) << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)p)[i];
+}
+
+static void run_unit(job_t* J, int64_t unit, double* S, double* kv, double* qv, double* vv,
+                     double* av, double* u) {
+    const int H = J->heads, dk = J->dk, dv = J->dv;
+    const int64_t s = unit / H, h = unit % H;
+    const int64_t t0 = J->cu[s], t1 = J->cu[s + 1];
+
+    for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+#if KDA_ORACLE_MUTANT == 7
+        S[i] = 0.0; /* mutant: initial state ignored */
+#else
+        S[i] = J->init ? J->init[(s * H + h) * (int64_t)dk * dv + i] : 0.0;
+#endif
+
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t th = t * H + h;
+        for (int c = 0; c < dk; ++c) {
+            kv[c] = load_in(J->k, J->in_bf16, th * dk + c);
+            qv[c] = load_in(J->q, J->in_bf16, th * dk + c);
+#if KDA_ORACLE_MUTANT == 6
+            av[c] = (double)J->log_alpha[th * dk + c]; /* mutant: gate used without exp */
+#else
+            av[c] = exp((double)J->log_alpha[th * dk + c]);
+#endif
+        }
+        for (int j = 0; j < dv; ++j) vv[j] = load_in(J->v, J->in_bf16, th * dv + j);
+#if KDA_ORACLE_MUTANT == 5
+        const double b = 1.0; /* mutant: beta dropped */
+#else
+        const double b = (double)J->beta[th];
+#endif
+
+#if KDA_ORACLE_MUTANT != 1
+        /* 1. decay the key-channel rows */
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) S[c * dv + j] *= av[c];
+#endif
+        /* 2-3. read the prediction for k_t and form the correction */
+        for (int j = 0; j < dv; ++j) u[j] = 0.0;
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) u[j] += S[c * dv + j] * kv[c];
+        for (int j = 0; j < dv; ++j) {
+#if KDA_ORACLE_MUTANT == 3
+            u[j] = b * (vv[j] + u[j]); /* mutant: wrong sign of the prediction */
+#else
+            u[j] = b * (vv[j] - u[j]);
+#endif
+        }
+#if KDA_ORACLE_MUTANT == 2
+        /* mutant: output taken from the state before the write */
+        for (int j = 0; j < dv; ++j) {
+            double o = 0.0;
+            for (int c = 0; c < dk; ++c) o += S[c * dv + j] * qv[c];
+            J->out[th * dv + j] = o;
+        }
+#endif
+        /* 4. write the correction */
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) S[c * dv + j] += kv[c] * u[j];
+#if KDA_ORACLE_MUTANT == 1
+        /* mutant: decay applied after the delta write instead of before */
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) S[c * dv + j] *= av[c];
+#endif
+#if KDA_ORACLE_MUTANT != 2
+        /* 5. output from the updated state */
+        for (int j = 0; j < dv; ++j) {
+            double o = 0.0;
+#if KDA_ORACLE_MUTANT == 4
+            /* mutant: transposed state (only meaningful for dk == dv) */
+            for (int c = 0; c < dk; ++c) o += S[j * dv + c] * qv[c];
+#else
+            for (int c = 0; c < dk; ++c) o += S[c * dv + j] * qv[c];
+#endif
+            J->out[th * dv + j] = o;
+        }
+#endif
+    }
+    if (J->final_state) {
+        double* F = J->final_state + (s * H + h) * (int64_t)dk * dv;
+        memcpy(F, S, sizeof(double) * (size_t)dk * dv);
+    }
+}
+
+static void* worker(void* arg) {
+    job_t* J = (job_t*)arg;
+    const int dk = J->dk, dv = J->dv;
+    const int dm = dk > dv ? dk : dv;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+    double* buf = (double*)malloc(sizeof(double) * (size_t)5 * dm);
+    if (!S || !buf) {
+        free(S);
+        free(buf);
+        return (void*)1;
+    }
+    const int64_t units = J->num_seqs * J->heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t unit = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (unit >= units) break;
+        run_unit(J, unit, S, buf, buf + dm, buf + 2 * dm, buf + 3 * dm, buf + 4 * dm);
+    }
+    free(S);
+    free(buf);
+    return NULL;
+}
+
+/*
+ * kda_oracle_forward: run every (sequence, head) unit.
+ *   cu_seqlens  int64 [num_seqs+1], non-decreasing, cu[0] = 0
+ *   q, k        [T_total, heads, dk]  (fp32, or bf16 bits if in_bf16)
+ *   v           [T_total, heads, dv]
+ *   log_alpha   fp32 [T_total, heads, dk];  beta fp32 [T_total, heads]
+ *   init_state  fp64 [num_seqs, heads, dk, dv] or NULL (zero)
+ *   out         fp64 [T_total, heads, dv];  final_state fp64 [num_seqs, heads, dk, dv] or NULL
+ * Returns 0 on success, nonzero on bad arguments or allocation failure.
+ */
+int kda_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, int dk, int dv,
+                       int in_bf16, const void* q, const void* k, const void* v,
+                       const float* log_alpha, const float* beta, const double* init_state,
+                       double* out, double* final_state, int nthreads) {
+    if (num_seqs < 0 || heads <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
+    if (cu_seqlens[0] != 0) return 1;
+    for (int64_t s = 0; s < num_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return 1;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !log_alpha || !beta || !out)) return 1;
+    job_t J;
+    J.num_seqs = num_seqs;
+    J.cu = cu_seqlens;
+    J.heads = heads;
+    J.dk = dk;
+    J.dv = dv;
+    J.in_bf16 = in_bf16;
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.log_alpha = log_alpha;
+    J.beta = beta;
+    J.init = init_state;
+    J.out = out;
+    J.final_state = final_state;
+    J.next_unit = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int rc = 0, started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &J) != 0) break;
+        ++started;
+    }
+    if (started == 0) {
+        void* r = worker(&J);
+        rc = r != NULL;
+    }
+    for (int i = 0; i < started; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r) rc = 2;
+    }
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}
+
+int kda_oracle_mutant(void) { return KDA_ORACLE_MUTANT; }
