@@ -1,0 +1,133 @@
+"""MI355X (gfx950) Kimi Delta Attention operator: chunked prefill and recurrent decode.
+
+A thin binding over ``libkda.so`` (see ``include/kda.h``).  Every step of the
+computation runs in the library's HIP kernels; this module only checks
+shapes, allocates outputs and workspace through PyTorch, and passes device
+pointers and the current HIP stream across the C ABI.  If the library has
+not been built the calls raise; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+from . import _lib
+from ._lib import KdaError, lib, status_string  # noqa: F401
+
+__all__ = ["chunk_fwd", "decode_step", "workspace_size", "KdaError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt):
+    torch = _torch()
+    if dt == torch.float32:
+        return _lib.DTYPE_F32
+    if dt == torch.bfloat16:
+        return _lib.DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}; use torch.float32 or torch.bfloat16")
+
+
+def _stream_handle(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def workspace_size(batch, seqlen, heads, dk, dv, in_dtype, out_dtype=None, num_seqs=0, max_seqlen=0):
+    """Bytes of device workspace ``chunk_fwd`` needs (varlen iff num_seqs > 0)."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    shape = _lib.Shape(batch, seqlen, num_seqs, max_seqlen, heads, dk, dv, _dtype_code(in_dtype),
+                       _dtype_code(out_dtype))
+    return int(lib().kda_chunk_fwd_workspace_size(shape))
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out=None,
+              out_dtype=None, final_state=True, max_seqlen=None, workspace=None):
+    """Chunked KDA prefill.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16), log_alpha [B,T,H,dk] fp32,
+    beta [B,T,H] fp32; init_state [N,H,dk,dv] fp32 or None; cu_seqlens int32
+    [N+1] (GPU) or None.  ``final_state`` may be True (allocate), False/None
+    (skip) or a tensor to write into (may be ``init_state`` itself).
+    Returns (out, final_state or None).
+    """
+    torch = _torch()
+    _check_dev(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_dev(k, "k", q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (B, T, H, dv))
+    _check_dev(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    _check_dev(beta, "beta", torch.float32, (B, T, H))
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if B != 1:
+            raise ValueError("varlen inputs must have batch 1")
+        N = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = T  # safe upper bound without a device sync
+    else:
+        N = B
+    if init_state is not None:
+        _check_dev(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    out_dtype = q.dtype if out_dtype is None and out is None else (out.dtype if out is not None else out_dtype)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _check_dev(out, "out", out_dtype, (B, T, H, dv))
+    if final_state is True:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
+                       _dtype_code(q.dtype), _dtype_code(out_dtype))
+    L = lib()
+    need = int(L.kda_chunk_fwd_workspace_size(shape))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_dev(workspace, "workspace", torch.uint8)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = L.kda_chunk_fwd(shape, ptr(q), ptr(k), ptr(v), ptr(log_alpha), ptr(beta), ptr(init_state),
+                         ptr(cu_seqlens), ptr(out), ptr(final_state), ptr(workspace), workspace.numel(),
+                         _stream_handle(q.device))
+    _lib.check(st, "kda_chunk_fwd")
+    return out, final_state
+
+
+def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
+    """One recurrent KDA step for N sequences; updates ``state`` [N,H,dk,dv] in place.
+
+    q, k [N,H,dk], v [N,H,dv] (fp32 or bf16), log_alpha [N,H,dk] fp32,
+    beta [N,H] fp32.  Returns out [N,H,dv].
+    """
+    torch = _torch()
+    _check_dev(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_dev(k, "k", q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (N, H, dv))
+    _check_dev(log_alpha, "log_alpha", torch.float32, (N, H, dk))
+    _check_dev(beta, "beta", torch.float32, (N, H))
+    _check_dev(state, "state", torch.float32, (N, H, dk, dv))
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    _check_dev(out, "out", None, (N, H, dv))
+    st = lib().kda_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), q.data_ptr(),
+                               k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
+                               state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
+    _lib.check(st, "kda_decode_step")
+    return out

@@ -1,0 +1,191 @@
+// kda_api.hip -- the extern "C" boundary of libkda: argument validation,
+// workspace sizing and kernel launches.  See include/kda.h for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+#include "kda_internal.h"
+
+namespace {
+
+constexpr int CHUNK = 64;
+// Per-window record budget: records written by the chunk-local pass should
+// still sit in the 256 MB last-level (MALL) cache when the state pass reads them.
+constexpr size_t RECORD_BUDGET = size_t(128) << 20;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || an == 0 || bn == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bn && y < x + an;
+}
+
+size_t dsize(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+
+struct Plan {
+    int64_t N, tokens, max_len, max_chunks;
+    int d;
+    size_t rec, state_bytes;
+};
+
+kda_status_t plan_chunk(const kda_shape_t* s, Plan& p) {
+    if (!s) return KDA_ERR_INVALID_ARG;
+    if (s->heads <= 0 || s->batch <= 0 || s->seqlen < 0 || s->dk <= 0 || s->dv <= 0 || s->max_seqlen < 0)
+        return KDA_ERR_INVALID_ARG;
+    if ((s->in_dtype != KDA_DTYPE_F32 && s->in_dtype != KDA_DTYPE_BF16) ||
+        (s->out_dtype != KDA_DTYPE_F32 && s->out_dtype != KDA_DTYPE_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (s->dk != s->dv || (s->dk != 64 && s->dk != 128)) return KDA_ERR_UNSUPPORTED;
+    p.d = s->dk;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status_t st) {
+    switch (st) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) {
+    kda_status_t st = plan_chunk(s, p);
+    if (st != KDA_OK) return st;
+    if (varlen) {
+        if (s->batch != 1 || s->num_seqs < 0) return KDA_ERR_INVALID_ARG;
+        p.N = s->num_seqs;
+        p.tokens = s->seqlen;
+        p.max_len = s->max_seqlen > 0 ? s->max_seqlen : s->seqlen;
+    } else {
+        p.N = s->batch;
+        p.tokens = (int64_t)s->batch * s->seqlen;
+        p.max_len = s->seqlen;
+    }
+    if (p.N * (int64_t)s->heads > INT32_MAX / 16) return KDA_ERR_UNSUPPORTED;
+    p.max_chunks = (p.max_len + CHUNK - 1) / CHUNK;
+    p.rec = kda::chunk_record_bytes(p.d, s->in_dtype == KDA_DTYPE_BF16);
+    p.state_bytes = align256((size_t)p.N * s->heads * p.d * p.d * sizeof(float));
+    return KDA_OK;
+}
+
+size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
+    Plan p;
+    if (!s || chunk_plan_full(s, s->num_seqs > 0, p) != KDA_OK) return 0;
+    const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
+    if (per_chunk == 0) return p.state_bytes + 256;
+    int64_t wc = (int64_t)(RECORD_BUDGET / per_chunk);
+    if (wc < 1) wc = 1;
+    if (wc > p.max_chunks) wc = p.max_chunks > 0 ? p.max_chunks : 1;
+    return p.state_bytes + (size_t)wc * per_chunk;
+}
+
+kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Plan p;
+    kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p);
+    if (st != KDA_OK) return st;
+    const int H = s->heads, d = p.d;
+    const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
+    const size_t tok_bytes = (size_t)p.tokens * H * d;
+    const size_t state_elems = (size_t)p.N * H * d * d;
+    if (p.tokens > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !out) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(out))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    if ((init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERR_INVALID_ARG;
+    if (init_state && final_state && init_state != final_state &&
+        overlaps(init_state, state_elems * 4, final_state, state_elems * 4))
+        return KDA_ERR_INVALID_ARG;
+    const size_t out_bytes = tok_bytes * out_b;
+    if (overlaps(out, out_bytes, q, tok_bytes * in_b) || overlaps(out, out_bytes, k, tok_bytes * in_b) ||
+        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, log_alpha, tok_bytes * 4) ||
+        overlaps(out, out_bytes, beta, (size_t)p.tokens * H * 4) ||
+        overlaps(out, out_bytes, init_state, state_elems * 4) ||
+        overlaps(out, out_bytes, final_state, state_elems * 4))
+        return KDA_ERR_INVALID_ARG;
+    if (final_state && (overlaps(final_state, state_elems * 4, q, tok_bytes * in_b) ||
+                        overlaps(final_state, state_elems * 4, k, tok_bytes * in_b) ||
+                        overlaps(final_state, state_elems * 4, v, tok_bytes * in_b)))
+        return KDA_ERR_INVALID_ARG;
+
+    const size_t per_chunk = (size_t)p.N * H * p.rec;
+    if (p.N == 0) return KDA_OK;  // nothing to compute
+    if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
+        return KDA_ERR_WORKSPACE;
+    int64_t wc = (int64_t)((workspace_bytes - p.state_bytes) / per_chunk);
+    if (wc > p.max_chunks) wc = p.max_chunks;
+    if (wc < 1) wc = 1;
+    if (wc > INT32_MAX / 2) wc = INT32_MAX / 2;
+    const int64_t nwin64 = p.max_chunks > 0 ? (p.max_chunks + wc - 1) / wc : 1;
+    if (nwin64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::ChunkArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.la = log_alpha;
+    a.beta = beta;
+    a.cu = cu_seqlens;
+    a.T = s->seqlen;
+    a.H = H;
+    a.N = (int)p.N;
+    a.Wc = (int)wc;
+    a.win = 0;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.state_buf = final_state ? final_state : reinterpret_cast<float*>(ws);
+    a.rec = ws + p.state_bytes;
+    a.rec_bytes = p.rec;
+    a.init = init_state;
+    a.out = out;
+    const int bv = kda::chunk_value_slice(d, p.N * H);
+    hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, bv, a,
+                                       (int)nwin64, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                             kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, float* state_inout, void* out,
+                             void* stream) {
+    if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if ((in_dtype != KDA_DTYPE_F32 && in_dtype != KDA_DTYPE_BF16) ||
+        (out_dtype != KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (batch == 0) return KDA_OK;
+    const int64_t units = (int64_t)batch * heads;
+    if (units > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !log_alpha || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(state_inout) || !aligned16(out)) return KDA_ERR_INVALID_ARG;
+    const size_t vec = (size_t)units * dk;
+    const size_t in_b = dsize(in_dtype), out_b = dsize(out_dtype);
+    const size_t st_bytes = (size_t)units * dk * dv * 4, out_bytes = vec * out_b;
+    if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps(out, out_bytes, q, vec * in_b) ||
+        overlaps(out, out_bytes, k, vec * in_b) || overlaps(out, out_bytes, v, vec * in_b) ||
+        overlaps(out, out_bytes, log_alpha, vec * 4) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
+        overlaps(state_inout, st_bytes, q, vec * in_b) || overlaps(state_inout, st_bytes, k, vec * in_b) ||
+        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, log_alpha, vec * 4) ||
+        overlaps(state_inout, st_bytes, beta, (size_t)units * 4))
+        return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::decode_dispatch((int)units, dk, in_dtype == KDA_DTYPE_BF16, out_dtype == KDA_DTYPE_BF16, q,
+                                        k, v, log_alpha, beta, state_inout, out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

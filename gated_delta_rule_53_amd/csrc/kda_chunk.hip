@@ -1,0 +1,586 @@
+// kda_chunk.hip -- chunked KDA prefill on gfx950.
+//
+// The chunked algorithm ("Kimi Linear" page, "The constrained DPLR form and
+// the chunkwise algorithm"): split each sequence into 64-token chunks, fold the
+// per-token corrections of a chunk into a WY form through the UT transform
+// (I + A)^-1, run recurrently between chunks and in parallel inside each.
+// Because KDA ties both low-rank vectors of its DPLR transition to the key,
+// the per-channel gate factors out of every product as a diagonal scaling of
+// keys and queries; that is what lets all products below run on matrix cores.
+//
+// Notation for one (sequence, head) and one chunk of n <= 64 tokens, rows r
+// and columns i indexing tokens, c key channels, j value channels;
+// G_r = sum_{t<=r} log_alpha_t (chunk-local, per channel):
+//   Atil[r,i] = beta_r sum_c k_rc k_ic e^{G_rc - G_ic}      (i < r)
+//   P[r,i]    =        sum_c q_rc k_ic e^{G_rc - G_ic}      (i <= r)
+//   T         = (I + Atil)^-1
+//   W  = T diag(beta) (K e^G),    Ut = T diag(beta) V
+//   Qg = Q e^G,   Kh = K e^{G_last - G},   gamma = e^{G_last}
+// and between chunks, with the fp32 state S (dk x dv):
+//   U = Ut - W S;   O = Qg S + P U;   S <- Diag(gamma) S + Kh^T U.
+//
+// Two kernels per window of chunks:
+//   chunk_local_kernel  one workgroup per (chunk, head): all of the above that
+//                       does not depend on S, written to a per-chunk record;
+//   chunk_inter_kernel  one workgroup per (sequence, head, slice of BV value
+//                       columns): walks the chunks in order carrying S.
+// The value columns of S never interact (each column is its own recurrence),
+// which is what makes the slice split exact.
+//
+// Numerics.  Gate products are formed as products of alpha = e^{log_alpha}
+// taken over index ranges, never as differences of cumulative sums, so no
+// factor overflows: off-diagonal 16x16 sub-blocks use the first row of the
+// row block as anchor (both factors <= 1), diagonal sub-blocks use their
+// ninth row (factors bounded by eight tokens of decay).  Matrix-core operands
+// are fp16 for bf16 inputs and fp32 for fp32 inputs; accumulation, the UT
+// inverse and the state are fp32.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+__device__ __forceinline__ void seq_bounds(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
+    if (a.cu) {
+        t0 = a.cu[s];
+        L = (int64_t)a.cu[s + 1] - t0;
+    } else {
+        t0 = (int64_t)s * a.T;
+        L = a.T;
+    }
+}
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Per-chunk record layout (bytes); OT is the matrix-core operand type.
+template <int D, typename OT>
+struct Rec {
+    static constexpr size_t W = 0;                                        // OT [64][D]
+    static constexpr size_t QG = align256(W + CH * D * sizeof(OT));       // OT [64][D]
+    static constexpr size_t KHT = align256(QG + CH * D * sizeof(OT));     // OT [D][64]
+    static constexpr size_t P = align256(KHT + CH * D * sizeof(OT));      // OT [64][64]
+    static constexpr size_t UT = align256(P + CH * CH * sizeof(OT));      // f32 [64][D]
+    static constexpr size_t GAM = align256(UT + CH * D * sizeof(float));  // f32 [D]
+    static constexpr size_t BYTES = align256(GAM + D * sizeof(float));
+};
+
+template <typename OT>
+struct Pad {
+    static constexpr int v = sizeof(OT) == 2 ? 8 : 4;  // keeps 16-byte row alignment, breaks bank strides
+};
+
+// fp32 tile product with B given row-major (B[k][j] at B + k*ldb + j).
+__device__ __forceinline__ void mma_tile_f32_rowB(floatx4& acc, const float* A, int lda, const float* B, int ldb,
+                                                  int K, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[i * lda + k0 + g], B[(k0 + g) * ldb + i], acc, 0, 0, 0);
+}
+
+template <typename OT>
+__device__ __forceinline__ void store16(OT* dst, const float* x);
+template <>
+__device__ __forceinline__ void store16<_Float16>(_Float16* dst, const float* x) {
+    half8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (_Float16)x[e];
+        b[e] = (_Float16)x[8 + e];
+    }
+    reinterpret_cast<half8*>(dst)[0] = a;
+    reinterpret_cast<half8*>(dst)[1] = b;
+}
+template <>
+__device__ __forceinline__ void store16<float>(float* dst, const float* x) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        reinterpret_cast<float4*>(dst)[e] = make_float4(x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]);
+}
+
+template <typename OT>
+__device__ __forceinline__ void store4(OT* dst, floatx4 x);
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* dst, floatx4 x) {
+    half4 h;
+    h[0] = (_Float16)x[0];
+    h[1] = (_Float16)x[1];
+    h[2] = (_Float16)x[2];
+    h[3] = (_Float16)x[3];
+    *reinterpret_cast<half4*>(dst) = h;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, floatx4 x) {
+    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// ---------------------------------------------------------------------------
+// chunk-local kernel
+// ---------------------------------------------------------------------------
+template <int D, typename OT>
+struct LocalCfg {
+    static constexpr int NT = 4 * D;  // one thread per (channel, 16-row block)
+    static constexpr int NW = NT / 64;
+    static constexpr int PD = Pad<OT>::v;
+    static constexpr int DP = D + PD;   // pitch of [row][channel] operand rows
+    static constexpr int KP = CH + PD;  // pitch of [channel][token] rows
+    static constexpr int AP = CH + 4;   // pitch of fp32 [64][64]
+    static constexpr int YP = 17;
+    static constexpr size_t SZ_OP = 192 * DP * sizeof(OT);
+    static constexpr size_t SZ_KT = (size_t)D * KP * sizeof(OT);
+    static constexpr size_t SZ_F = (size_t)CH * AP * sizeof(float);
+    static constexpr size_t OFF_OP = 0;
+    static constexpr size_t OFF_KGT = 0;                   // aliases the operand region after use
+    static constexpr size_t OFF_VBT = SZ_KT;
+    static constexpr size_t OFF_Y = 2 * SZ_KT;
+    static constexpr size_t OFF_A = align256(SZ_OP);      // Atil fp32, later T as OT [64][KP]
+    static constexpr size_t OFF_T = OFF_A + SZ_F;          // T fp32
+    static constexpr size_t OFF_X = OFF_T + SZ_F;          // block products and block-start gates
+    static constexpr size_t SMEM = OFF_X + 2 * 4 * D * sizeof(float);
+    static_assert(OFF_Y + NW * 16 * YP * sizeof(float) <= SZ_OP, "scratch must fit the operand region");
+};
+
+template <int D, typename IT, typename OT>
+__global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
+    using C = LocalCfg<D, OT>;
+    using R = Rec<D, OT>;
+    __shared__ __align__(16) unsigned char smem[C::SMEM];
+    OT* sOp = reinterpret_cast<OT*>(smem + C::OFF_OP);
+    OT* sKgT = reinterpret_cast<OT*>(smem + C::OFF_KGT);
+    OT* sVbT = reinterpret_cast<OT*>(smem + C::OFF_VBT);
+    float* sY = reinterpret_cast<float*>(smem + C::OFF_Y);
+    float* sAt = reinterpret_cast<float*>(smem + C::OFF_A);
+    OT* sTh = reinterpret_cast<OT*>(smem + C::OFF_A);
+    float* sT = reinterpret_cast<float*>(smem + C::OFF_T);
+    float* sBP = reinterpret_cast<float*>(smem + C::OFF_X);
+    float* sA0 = sBP + 4 * D;
+
+    const int s = blockIdx.x / a.Wc, jl = blockIdx.x % a.Wc, h = blockIdx.y;
+    int64_t tb, L;
+    seq_bounds(a, s, tb, L);
+    const int64_t c0 = (int64_t)(a.win * a.Wc + jl) * CH;
+    if (c0 >= L) return;  // whole workgroup: no chunk here
+    const int n = (int)min<int64_t>(CH, L - c0);
+    const int64_t tok0 = tb + c0;
+    const int H = a.H;
+
+    unsigned char* rec = a.rec + ((size_t)(s * a.Wc + jl) * H + h) * a.rec_bytes;
+    OT* rW = reinterpret_cast<OT*>(rec + R::W);
+    OT* rQg = reinterpret_cast<OT*>(rec + R::QG);
+    OT* rKhT = reinterpret_cast<OT*>(rec + R::KHT);
+    OT* rP = reinterpret_cast<OT*>(rec + R::P);
+    float* rUt = reinterpret_cast<float*>(rec + R::UT);
+    float* rG = reinterpret_cast<float*>(rec + R::GAM);
+
+    const IT* q = static_cast<const IT*>(a.q);
+    const IT* k = static_cast<const IT*>(a.k);
+    const IT* v = static_cast<const IT*>(a.v);
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int gq = lane >> 4, li = lane & 15;
+    const int c = t % D, b = t / D;  // this thread's channel and 16-row block
+    const int rb0 = 16 * b;
+
+    // ---- per-thread gate products over its 16 rows of channel c ----
+    float kk[16], qq[16], bb[16], al[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = rb0 + i;
+        const bool ok = r < n;
+        const size_t tokh = (size_t)(tok0 + r) * H + h;
+        const size_t off = tokh * D + c;
+        kk[i] = ok ? to_f32(k[off]) : 0.f;
+        qq[i] = ok ? to_f32(q[off]) : 0.f;
+        al[i] = ok ? fast_exp(a.la[off]) : 1.f;
+        bb[i] = ok ? a.beta[tokh] : 0.f;
+    }
+    // Lf[i] = prod_{j=1..i} alpha_j : e^{G_i - G_0} within the block
+    float Lf[16];
+    Lf[0] = 1.f;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) Lf[i] = Lf[i - 1] * al[i];
+    // Rb[i] = prod_{j=i+1..15} alpha_j : e^{G_15 - G_i}
+    float Rb[16];
+    Rb[15] = 1.f;
+#pragma unroll
+    for (int i = 14; i >= 0; --i) Rb[i] = Rb[i + 1] * al[i + 1];
+    // diagonal sub-block factors around the anchor row 8 of the block
+    float Dl[16], Dr[16];
+    {
+        float M = 1.f;
+        Dl[8] = 1.f;
+        Dr[8] = 1.f;
+#pragma unroll
+        for (int i = 9; i < 16; ++i) {
+            M *= al[i];
+            Dl[i] = M;  // e^{G_i - G_8}
+            Dr[i] = 1.f / M;
+        }
+        float Bk = 1.f;
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+            Bk *= al[i + 1];
+            Dr[i] = Bk;  // e^{G_8 - G_i}
+            Dl[i] = 1.f / Bk;
+        }
+    }
+    sBP[b * D + c] = al[0] * Lf[15];  // product over the whole block
+    sA0[b * D + c] = al[0];           // gate of the block's first row
+    // strictly-upper blocks of P are zero in the record
+    for (int idx = t; idx < CH * CH; idx += C::NT) {
+        const int r = idx / CH, i = idx % CH;
+        if ((i >> 4) > (r >> 4)) rP[idx] = from_f32<OT>(0.f);
+    }
+    __syncthreads();
+
+    float PB[4], A0[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        PB[e] = sBP[e * D + c];
+        A0[e] = sA0[e * D + c];
+    }
+    float E = 1.f, Sfx = 1.f;  // products over the blocks before / after this one
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (e < b) E *= PB[e];
+        if (e > b) Sfx *= PB[e];
+    }
+    const float gamma = ((PB[0] * PB[1]) * PB[2]) * PB[3];
+    if (b == 0) rG[c] = gamma;
+
+    // Qg (row-major) and Kh^T (channel-major) go straight to the record
+    float F[16];
+    {
+        float kh[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            F[i] = E * (al[0] * Lf[i]);  // e^{G_{rb0+i}}
+            rQg[(rb0 + i) * D + c] = from_f32<OT>(qq[i] * F[i]);
+            kh[i] = kk[i] * (Rb[i] * Sfx);  // k e^{G_last - G}
+        }
+        store16<OT>(rKhT + (size_t)c * CH + rb0, kh);
+    }
+
+    // ---- phase A: off-diagonal 16x16 sub-blocks of Atil and P ----
+    // rows 0..47: beta k e^{G_r - G_a} of blocks 1..3 (a = first row of the block)
+    // rows 48..95: q e^{G_r - G_a} of blocks 1..3
+    // rows 96..191: for each (row block rb, column block cb < rb): k e^{G_a(rb) - G_i}
+    if (b >= 1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sOp[(16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Lf[i]);
+            sOp[(48 + 16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(qq[i] * Lf[i]);
+        }
+    }
+#pragma unroll
+    for (int rb = 1; rb < 4; ++rb) {
+        if (rb > b) {
+            float X = A0[rb];  // e^{G_a(rb) - G_end(b)}
+#pragma unroll
+            for (int e = 1; e < 3; ++e)
+                if (e > b && e < rb) X *= PB[e];
+            const int slot = rb * (rb - 1) / 2 + b;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sOp[(96 + 16 * slot + i) * C::DP + c] = from_f32<OT>(kk[i] * Rb[i] * X);
+        }
+    }
+    __syncthreads();
+    for (int p = wave; p < 12; p += C::NW) {
+        const int sl = p % 6;
+        const int rb = sl == 0 ? 1 : (sl < 3 ? 2 : 3);
+        const int cb = sl - rb * (rb - 1) / 2;
+        floatx4 acc = zero4();
+        const OT* A = sOp + ((p < 6 ? 0 : 48) + 16 * (rb - 1)) * C::DP;
+        mma_tile<OT>(acc, A, C::DP, sOp + (96 + 16 * sl) * C::DP, C::DP, D, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
+            if (p < 6)
+                sAt[row * C::AP + col] = acc[r];
+            else
+                rP[row * CH + col] = from_f32<OT>(acc[r]);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase B: diagonal sub-blocks ----
+    // rows 0..63: beta k e^{G_r - G_m}; 64..127: q e^{G_r - G_m}; 128..191: k e^{G_m - G_i}
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        sOp[(rb0 + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Dl[i]);
+        sOp[(64 + rb0 + i) * C::DP + c] = from_f32<OT>(qq[i] * Dl[i]);
+        sOp[(128 + rb0 + i) * C::DP + c] = from_f32<OT>(kk[i] * Dr[i]);
+    }
+    __syncthreads();
+    for (int p = wave; p < 8; p += C::NW) {
+        const int db = p & 3;
+        floatx4 acc = zero4();
+        const OT* A = sOp + ((p < 4 ? 0 : 64) + 16 * db) * C::DP;
+        mma_tile<OT>(acc, A, C::DP, sOp + (128 + 16 * db) * C::DP, C::DP, D, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lr = 4 * gq + r;
+            const int row = 16 * db + lr, col = 16 * db + li;
+            if (p < 4)
+                sAt[row * C::AP + col] = acc[r];
+            else
+                rP[row * CH + col] = from_f32<OT>(lr >= li ? acc[r] : 0.f);
+        }
+    }
+    __syncthreads();
+
+    // ---- W / Ut right-hand sides (channel-major), T diagonal blocks ----
+    {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = bb[i] * kk[i] * F[i];
+        store16<OT>(sKgT + (size_t)c * C::KP + rb0, x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = rb0 + i;
+            x[i] = r < n ? bb[i] * to_f32(v[((size_t)(tok0 + r) * H + h) * D + c]) : 0.f;
+        }
+        store16<OT>(sVbT + (size_t)c * C::KP + rb0, x);
+    }
+    // off-diagonal blocks of T start at zero
+    for (int idx = t; idx < CH * CH; idx += C::NT) {
+        const int r = idx / CH, i = idx % CH;
+        if ((r >> 4) != (i >> 4)) sT[r * C::AP + i] = 0.f;
+    }
+    if (t < 64) {
+        // column j of the inverse of the unit lower-triangular block (I + Atil_bb)
+        const int db = t >> 4, j = t & 15;
+        const float* Ab = sAt + (16 * db) * C::AP + 16 * db;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc += Ab[r * C::AP + i] * x[i];
+            x[r] = r < j ? 0.f : (r == j ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * db + r) * C::AP + 16 * db + j] = x[r];
+    }
+    __syncthreads();
+    // block forward substitution: T_{rb,cb} = -T_{rb,rb} sum_{cb<=j<rb} Atil_{rb,j} T_{j,cb}
+#pragma unroll
+    for (int rb = 1; rb < 4; ++rb) {
+        const int cb = wave;
+        float* Yw = sY + wave * 16 * C::YP;
+        if (cb < rb) {
+            floatx4 acc = zero4();
+            for (int j = cb; j < rb; ++j)
+                mma_tile_f32_rowB(acc, sAt + (16 * rb) * C::AP + 16 * j, C::AP, sT + (16 * j) * C::AP + 16 * cb,
+                                  C::AP, 16, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Yw[(4 * gq + r) * C::YP + li] = acc[r];
+        }
+        __syncthreads();
+        if (cb < rb) {
+            floatx4 acc = zero4();
+            mma_tile_f32_rowB(acc, sT + (16 * rb) * C::AP + 16 * rb, C::AP, Yw, C::YP, 16, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sT[(16 * rb + 4 * gq + r) * C::AP + 16 * cb + li] = -acc[r];
+        }
+        __syncthreads();
+    }
+    // T as a matrix-core operand (aliases Atil, which is no longer needed)
+    for (int idx = t; idx < CH * CH; idx += C::NT) {
+        const int r = idx / CH, i = idx % CH;
+        sTh[r * C::KP + i] = from_f32<OT>(sT[r * C::AP + i]);
+    }
+    __syncthreads();
+
+    // ---- W = T (beta K e^G), Ut = T (beta V) ----
+    constexpr int NTC = D / 16;
+    for (int p = wave; p < 8 * NTC; p += C::NW) {
+        const bool isU = p >= 4 * NTC;
+        const int rem = p % (4 * NTC);
+        const int rb = rem / NTC, ct = rem % NTC;
+        constexpr int KS = Mma<OT>::KSTEP;
+        const int K = ((16 * (rb + 1) + KS - 1) / KS) * KS;
+        floatx4 acc = zero4();
+        mma_tile<OT>(acc, sTh + (16 * rb) * C::KP, C::KP, (isU ? sVbT : sKgT) + (16 * ct) * C::KP, C::KP, K, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * gq + r, col = 16 * ct + li;
+            if (isU)
+                rUt[row * D + col] = acc[r];
+            else
+                rW[row * D + col] = from_f32<OT>(acc[r]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// inter-chunk kernel
+// ---------------------------------------------------------------------------
+template <int D, int BV, typename OT, typename OUT>
+__global__ void __launch_bounds__(256) chunk_inter_kernel(ChunkArgs a) {
+    using R = Rec<D, OT>;
+    constexpr int RT = D / 64;  // 16-row state tiles per wave
+    constexpr int CT = BV / 16; // 16-column tiles
+    constexpr int PD = Pad<OT>::v;
+    constexpr int SP = D + PD;
+    constexpr int UP = CH + PD;
+    __shared__ __align__(16) OT sS[BV * SP];
+    __shared__ __align__(16) OT sU[BV * UP];
+
+    const int H = a.H;
+    const int NH = a.N * H;
+    const int u = blockIdx.x % NH, z = blockIdx.x / NH;
+    const int s = u / H, h = u % H;
+    int64_t tb, L;
+    seq_bounds(a, s, tb, L);
+    const int nchunks = (int)((L + CH - 1) / CH);
+    const int jb = a.win * a.Wc;
+    const int je = min(nchunks, jb + a.Wc);
+    if (jb >= je && a.win > 0) return;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
+    const int gq = lane >> 4, li = lane & 15;
+    const int col0 = z * BV;
+
+    const float* src = a.win == 0 ? a.init : a.state_buf;
+    floatx4 Sacc[RT][CT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
+                Sacc[rt][ct][r] = src ? src[((size_t)u * D + row) * D + col0 + 16 * ct + li] : 0.f;
+            }
+
+    OUT* out = static_cast<OUT*>(a.out);
+    for (int j = jb; j < je; ++j) {
+        const unsigned char* rec = a.rec + ((size_t)(s * a.Wc + (j - jb)) * H + h) * a.rec_bytes;
+        const OT* rW = reinterpret_cast<const OT*>(rec + R::W);
+        const OT* rQg = reinterpret_cast<const OT*>(rec + R::QG);
+        const OT* rKhT = reinterpret_cast<const OT*>(rec + R::KHT);
+        const OT* rP = reinterpret_cast<const OT*>(rec + R::P);
+        const float* rUt = reinterpret_cast<const float*>(rec + R::UT);
+        const float* rG = reinterpret_cast<const float*>(rec + R::GAM);
+        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
+        const int64_t tok0 = tb + (int64_t)j * CH;
+
+        // S as the B operand: sS[col][channel]
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                store4<OT>(sS + (16 * ct + li) * SP + w * (D / 4) + 16 * rt + 4 * gq, Sacc[rt][ct]);
+        __syncthreads();
+
+        floatx4 accO[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            floatx4 accU = zero4();
+            accO[ct] = zero4();
+            mma_tile<OT>(accU, rW + (16 * w) * D, D, sS + (16 * ct) * SP, SP, D, lane);
+            mma_tile<OT>(accO[ct], rQg + (16 * w) * D, D, sS + (16 * ct) * SP, SP, D, lane);
+            floatx4 Uv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                Uv[r] = rUt[(16 * w + 4 * gq + r) * D + col0 + 16 * ct + li] - accU[r];
+            store4<OT>(sU + (16 * ct + li) * UP + 16 * w + 4 * gq, Uv);
+        }
+        __syncthreads();
+
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            mma_tile<OT>(accO[ct], rP + (16 * w) * CH, CH, sU + (16 * ct) * UP, UP, CH, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * w + 4 * gq + r;
+                if (row < n) out[((size_t)(tok0 + row) * H + h) * D + col0 + 16 * ct + li] = from_f32<OUT>(accO[ct][r]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int rowb = w * (D / 4) + 16 * rt;
+            float gm[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gm[r] = rG[rowb + 4 * gq + r];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[rt][ct][r] *= gm[r];
+                mma_tile<OT>(Sacc[rt][ct], rKhT + (size_t)rowb * CH, CH, sU + (16 * ct) * UP, UP, CH, lane);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
+                a.state_buf[((size_t)u * D + row) * D + col0 + 16 * ct + li] = Sacc[rt][ct][r];
+            }
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch
+// ---------------------------------------------------------------------------
+size_t chunk_record_bytes(int d, bool in_bf16) {
+    if (d == 128) return in_bf16 ? Rec<128, _Float16>::BYTES : Rec<128, float>::BYTES;
+    return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
+}
+
+int chunk_value_slice(int d, int64_t units) {
+    if (units <= 64) return 16;
+    if (units <= 256 || d == 64) return 32;
+    return 64;
+}
+
+template <int D, typename IT, typename OT, typename OUT, int BV>
+static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
+    using C = LocalCfg<D, OT>;
+    const int units = base.N * base.H;
+    for (int w = 0; w < nwin; ++w) {
+        ChunkArgs a = base;
+        a.win = w;
+        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.N * base.Wc, base.H), dim3(C::NT), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(256), 0, st, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int D, typename IT, typename OT, typename OUT>
+static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, hipStream_t st) {
+    if (bv == 16) return run_windows<D, IT, OT, OUT, 16>(a, nwin, st);
+    if (bv == 32) return run_windows<D, IT, OT, OUT, 32>(a, nwin, st);
+    return run_windows<D, IT, OT, OUT, 64>(a, nwin, st);
+}
+
+hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
+                          hipStream_t st) {
+#define KDA_RUN(DD, IT, OT, OUT) return run_bv<DD, IT, OT, OUT>(a, nwin, bv, st)
+    if (d == 128) {
+        if (in_bf16) {
+            if (out_bf16) KDA_RUN(128, bf16_t, _Float16, bf16_t);
+            KDA_RUN(128, bf16_t, _Float16, float);
+        }
+        if (out_bf16) KDA_RUN(128, float, float, bf16_t);
+        KDA_RUN(128, float, float, float);
+    }
+    if (in_bf16) {
+        if (out_bf16) KDA_RUN(64, bf16_t, _Float16, bf16_t);
+        KDA_RUN(64, bf16_t, _Float16, float);
+    }
+    if (out_bf16) KDA_RUN(64, float, float, bf16_t);
+    KDA_RUN(64, float, float, float);
+#undef KDA_RUN
+}
+
+}  // namespace kda

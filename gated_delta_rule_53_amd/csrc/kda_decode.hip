@@ -1,0 +1,161 @@
+// kda_decode.hip -- fused one-token KDA update, memory-bound state streaming.
+//
+// Per (sequence, head) the update ("Kimi Linear" page, "Kimi Delta Attention"
+// with the delta-rule read/correct/write of "Background: from the delta rule
+// to gated DeltaNet") is evaluated column by column of the dk x dv state:
+//     S'_{cj} = alpha_c S_{cj}                       (decay, alpha = exp(log_alpha))
+//     p_j     = sum_c k_c S'_{cj}                    (prediction)
+//     u_j     = beta (v_j - p_j)                     (correction)
+//     S_{cj}  = S'_{cj} + k_c u_j                    (write)
+//     o_j     = sum_c q_c S_{cj} = sum_c q_c S'_{cj} + (q . k) u_j
+// so the state is read once and written once.  One 256-thread workgroup per
+// (sequence, head); thread t owns columns 4*(t % CG) .. +3 and a run of RPT
+// rows, loading the state as float4 (a wave covers whole 512-byte rows, fully
+// coalesced).  The three dot products over c are reduced with a cross-lane
+// shuffle inside the wave and through LDS across the four waves, in a fixed
+// order, so results are deterministic.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int D, typename IT, typename OUT>
+__global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
+                                                     const IT* __restrict__ v,
+                                                     const float* __restrict__ log_alpha,
+                                                     const float* __restrict__ beta, float* __restrict__ state,
+                                                     OUT* __restrict__ out) {
+    constexpr int CG = D / 4;       // float4 column groups
+    constexpr int RG = 256 / CG;    // row groups
+    constexpr int RPT = D / RG;     // rows per thread
+    constexpr int GPW = 64 / CG;    // row groups per wave
+    static_assert(CG * RG == 256 && RPT * RG == D && GPW >= 1, "decode tiling");
+
+    const int unit = blockIdx.x;  // sequence * heads + head
+    const int t = threadIdx.x;
+    const int jg = t % CG, rg = t / CG;
+    const int lane = t & 63, wave = t >> 6;
+
+    float* S_base = state + (size_t)unit * D * D;
+    float4 S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        S[i] = *reinterpret_cast<const float4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg);
+
+    __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
+    __shared__ float s_red[4][CG][9];
+    const size_t vec = (size_t)unit * D;
+    if (t < D) {
+        s_alpha[t] = fast_exp(log_alpha[vec + t]);
+        s_k[t] = to_f32(k[vec + t]);
+        s_q[t] = to_f32(q[vec + t]);
+        s_v[t] = to_f32(v[vec + t]);
+    }
+    const float b = beta[unit];
+    __syncthreads();
+
+    // decay, then partial dot products over this thread's rows
+    float p[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = rg * RPT + i;
+        const float a = s_alpha[c], kc = s_k[c], qc = s_q[c];
+        S[i].x *= a;
+        S[i].y *= a;
+        S[i].z *= a;
+        S[i].w *= a;
+        p[0] += kc * S[i].x;
+        p[1] += kc * S[i].y;
+        p[2] += kc * S[i].z;
+        p[3] += kc * S[i].w;
+        r[0] += qc * S[i].x;
+        r[1] += qc * S[i].y;
+        r[2] += qc * S[i].z;
+        r[3] += qc * S[i].w;
+        qk += qc * kc;
+    }
+    // reduce over the row groups inside the wave (lanes with the same column group)
+#pragma unroll
+    for (int off = CG; off < 64; off *= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] += __shfl_xor(p[e], off);
+            r[e] += __shfl_xor(r[e], off);
+        }
+        qk += __shfl_xor(qk, off);
+    }
+    if (lane < CG) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s_red[wave][jg][e] = p[e];
+            s_red[wave][jg][4 + e] = r[e];
+        }
+        s_red[wave][jg][8] = qk;
+    }
+    __syncthreads();
+    float pp[4], rr[4], qq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pp[e] = 0.f;
+        rr[e] = 0.f;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pp[e] += s_red[w][jg][e];
+            rr[e] += s_red[w][jg][4 + e];
+        }
+        qq += s_red[w][jg][8];
+    }
+    float u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = b * (s_v[4 * jg + e] - pp[e]);
+
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float kc = s_k[rg * RPT + i];
+        float4 n;
+        n.x = S[i].x + kc * u[0];
+        n.y = S[i].y + kc * u[1];
+        n.z = S[i].z + kc * u[2];
+        n.w = S[i].w + kc * u[3];
+        *reinterpret_cast<float4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg) = n;
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[vec + 4 * jg + e] = from_f32<OUT>(rr[e] + qq * u[e]);
+    }
+}
+
+template <int D, typename IT, typename OUT>
+hipError_t launch_decode(int units, const void* q, const void* k, const void* v, const float* la,
+                         const float* beta, float* state, void* out, hipStream_t st) {
+    hipLaunchKernelGGL((decode_kernel<D, IT, OUT>), dim3(units), dim3(256), 0, st,
+                       static_cast<const IT*>(q), static_cast<const IT*>(k), static_cast<const IT*>(v), la,
+                       beta, state, static_cast<OUT*>(out));
+    return hipGetLastError();
+}
+
+hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                           const void* v, const float* la, const float* beta, float* state, void* out,
+                           hipStream_t st) {
+#define KDA_DEC(DD, IT, OT) return launch_decode<DD, IT, OT>(units, q, k, v, la, beta, state, out, st)
+    if (d == 128) {
+        if (in_bf16) {
+            if (out_bf16) KDA_DEC(128, bf16_t, bf16_t);
+            KDA_DEC(128, bf16_t, float);
+        }
+        if (out_bf16) KDA_DEC(128, float, bf16_t);
+        KDA_DEC(128, float, float);
+    }
+    if (in_bf16) {
+        if (out_bf16) KDA_DEC(64, bf16_t, bf16_t);
+        KDA_DEC(64, bf16_t, float);
+    }
+    if (out_bf16) KDA_DEC(64, float, bf16_t);
+    KDA_DEC(64, float, float);
+#undef KDA_DEC
+}
+
+}  // namespace kda

@@ -1,0 +1,37 @@
+// kda_internal.h -- declarations shared by the kernel files and the C ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Arguments of one window of the chunked prefill (see kda_chunk.hip).
+struct ChunkArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* la;
+    const float* beta;
+    const int32_t* cu;  // packed sequence offsets, or null for a dense batch
+    int64_t T;          // dense: tokens per sequence
+    int H;
+    int N;       // sequences
+    int Wc;      // chunks per sequence per window
+    int win;     // window index
+    unsigned char* rec;
+    size_t rec_bytes;
+    const float* init;
+    float* state_buf;
+    void* out;
+};
+
+size_t chunk_record_bytes(int d, bool in_bf16);
+int chunk_value_slice(int d, int64_t units);
+hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
+                          hipStream_t st);
+hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                           const void* v, const float* la, const float* beta, float* state, void* out,
+                           hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,127 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator.
+ *
+ * The operator is the gated delta rule with a diagonal, per-key-channel
+ * forget gate ("Kimi Linear" page, sections "Kimi Delta Attention" and
+ * "The constrained DPLR form and the chunkwise algorithm"):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,          alpha_t = exp(log_alpha_t) per key channel,
+ *
+ * with the state S (dk x dv per sequence and head) kept in fp32.  Prefill
+ * evaluates it chunkwise (64-token chunks, WY/UT form inside a chunk,
+ * recurrent between chunks, as the same page section describes); decode
+ * applies one token per sequence.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *    allocates no device memory and keeps no global mutable state.
+ *  - Layouts are row-major and contiguous.  Tokens are [B, T, H, d] (d
+ *    fastest); the recurrent state is [N, H, dk, dv] with dv fastest, rows =
+ *    key channels, and the same layout serves initial, final and decode
+ *    states.  Data pointers must be 16-byte aligned.
+ *  - Supported head dims: dk == dv, and dk in {64, 128}.  q/k/v dtype is
+ *    fp32 or bf16; log_alpha and beta are always fp32; out is fp32 or bf16.
+ *  - Preconditions not checked on the device: log_alpha finite and <= 0
+ *    (the chunked path also needs log_alpha >= -10 per token so that
+ *    within-chunk decay ratios stay inside fp32 range); beta finite;
+ *    cu_seqlens non-decreasing with cu_seqlens[0] = 0 and
+ *    cu_seqlens[N] = total tokens.  With bf16 q/k/v the matrix-core
+ *    operands are staged in fp16, so |v|, state entries and outputs must
+ *    stay below 6.5e4 (larger values give non-finite results, never silent
+ *    garbage); q and k are expected L2-normalised per head as in the KDA
+ *    layer.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
+ *    and runs asynchronously; results are valid once the stream is
+ *    synchronised.  Argument validation is synchronous: on any error no
+ *    work is enqueued and a status other than KDA_OK is returned.  No entry
+ *    point prints, aborts or throws.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer, bad aliasing */
+    KDA_ERR_UNSUPPORTED = 2, /* a shape or dtype outside the supported set */
+    KDA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    KDA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} kda_status_t;
+
+/* Problem description for the chunked prefill.
+ *   batch       dense batch B; must be 1 when cu_seqlens is given
+ *   seqlen      tokens per sequence (dense) or total packed tokens (varlen)
+ *   num_seqs    0 for a dense batch (N = batch); varlen: N = len(cu_seqlens) - 1
+ *               (kda_chunk_fwd treats the call as varlen iff cu_seqlens != NULL;
+ *               the workspace query treats the shape as varlen iff num_seqs > 0)
+ *   max_seqlen  varlen: an upper bound on the longest sequence (host value,
+ *               used to size the launch); 0 means "use seqlen"
+ *   heads, dk, dv, in_dtype (q/k/v), out_dtype (out) */
+typedef struct {
+    int32_t batch;
+    int64_t seqlen;
+    int32_t num_seqs;
+    int64_t max_seqlen;
+    int32_t heads;
+    int32_t dk;
+    int32_t dv;
+    kda_dtype_t in_dtype;
+    kda_dtype_t out_dtype;
+} kda_shape_t;
+
+/* Bytes of scratch device memory kda_chunk_fwd needs for `s` (0 if `s` is
+ * invalid).  Any workspace at least this large works; a larger one lets the
+ * library keep more chunks per launch. */
+size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s);
+
+/* Chunked KDA prefill ("Kimi Linear" page, "The constrained DPLR form and the
+ * chunkwise algorithm": 64-token chunks, WY representation, UT transform,
+ * recurrent between chunks and parallel inside each).
+ *   q, k        [B, T, H, dk]  in_dtype
+ *   v           [B, T, H, dv]  in_dtype
+ *   log_alpha   [B, T, H, dk]  fp32, natural log of the per-channel gate
+ *   beta        [B, T, H]      fp32
+ *   init_state  [N, H, dk, dv] fp32, or NULL for a zero initial state
+ *   cu_seqlens  int32 [N+1] device array of packed sequence offsets, or NULL
+ *               for a dense batch (then N = B, each sequence T tokens)
+ *   out         [B, T, H, dv]  out_dtype; must not alias any input
+ *   final_state [N, H, dk, dv] fp32, or NULL; may equal init_state exactly
+ *               (in-place continuation) but must not partially overlap it
+ *   workspace   device scratch of workspace_bytes >= the size above
+ * Sequences of length 0 return final_state = init_state. */
+kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* out, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* One recurrent decode step for `batch` independent sequences ("Kimi Linear"
+ * page, "Why linear attention exists": decoding is a recurrent update whose
+ * cost does not depend on context length; "Kimi Delta Attention" for the
+ * update itself).  Per (sequence, head), with alpha = exp(log_alpha):
+ *     S <- Diag(alpha) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T q.
+ *   q, k        [batch, H, dk] in_dtype;   v [batch, H, dv] in_dtype
+ *   log_alpha   [batch, H, dk] fp32;       beta [batch, H] fp32
+ *   state_inout [batch, H, dk, dv] fp32, read and overwritten in place
+ *   out         [batch, H, dv] out_dtype; must not alias any other argument */
+kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv,
+                             kda_dtype_t in_dtype, kda_dtype_t out_dtype, const void* q,
+                             const void* k, const void* v, const float* log_alpha,
+                             const float* beta, float* state_inout, void* out, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* kda_status_string(kda_status_t st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */
