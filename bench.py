@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one chunked prefill of a 64K-token, 32-head, d=128 KDA layer
+(bf16 q/k/v, fp32 gates, fp32 state in and out, fp32 output) followed by 100
+consecutive decode steps of 256 sequences x 32 heads (bf16 inputs, fp32
+state updated in place, 512 MiB).  Inputs are synthetic, seeded, resident in
+HBM before timing starts.
+
+Prints one JSON line.  ``value`` is prefill tokens/s; the decode HBM
+bandwidth is in ``decode``.  ``roofline`` describes the dominant kernel of a
+step (the decode kernel: 100 launches per step); ``prefill_roofline`` the
+prefill call.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
+on a bounded sample of the prefill workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
+PAGE_FLOP_PER_TOKEN_HEAD = lambda d, C=64: 6 * d * d + 3 * C * d + C * C  # cost per head, per token
+METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode-step HBM GB/s, 1 MI355X"
+KERNEL_SOURCES = ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_chunk.hip",
+                  "gated_delta_rule_53_amd/csrc/kda_device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(tokens, heads, d, in_b=2, out_b=4, states=1):
+    """Algorithmic HBM bytes: q,k,v + fp32 log_alpha + fp32 beta + out, plus state in/out."""
+    per_th = 3 * d * in_b + 4 * d + 4 + d * out_b
+    return tokens * heads * per_th + 2 * states * heads * d * d * 4
+
+
+def decode_bytes(units, d, in_b=2, out_b=4):
+    """State read + write, plus q,k,v, log_alpha, beta and out, per (sequence, head)."""
+    return units * (2 * d * d * 4 + 3 * d * in_b + 4 * d + 4 + d * out_b)
+
+
+def to_dev(x, torch):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel):
+    """HBM bytes per launch from committed counter summaries, if they match the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_hash") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_tokens, threads):
+    """Time the fp64 oracle on the first ``sample_tokens`` tokens of every head of workload w."""
+    import oracle
+    import synth
+    d = synth.gen_tokens(w.seed, sample_tokens, w.heads, w.dk, w.dv, w.dtype, w.gate_scale)
+    init = synth.gen_states(w.seed, 1, w.heads, w.dk, w.dv, w.init_std) if w.init_std else None
+    oracle.build(force=False)
+    t = time.perf_counter()
+    oracle.recurrent(d["q"], d["k"], d["v"], d["log_alpha"], d["beta"], init, threads=threads)
+    dt = time.perf_counter() - t
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": min(threads, w.heads), "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens x {w.heads} heads of the {w.name} workload "
+                      f"(fp64 token-by-token recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens per head for the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_53_amd as kda
+    import synth
+    from synth import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kda._lib.lib()  # fail loudly if the library is missing
+
+    wp, wd = WORKLOADS[2], WORKLOADS[3]
+    # ---- prefill inputs (64K tokens, 32 heads) ----
+    t0 = time.time()
+    d = synth.make_prefill(wp)
+    log(f"prefill inputs generated in {time.time() - t0:.1f}s")
+    T, H, D = wp.seqlen, wp.heads, wp.dk
+    q, k, v = (to_dev(d[x], torch).unsqueeze(0) for x in ("q", "k", "v"))
+    la = to_dev(d["log_alpha"], torch).unsqueeze(0)
+    be = to_dev(d["beta"], torch).unsqueeze(0)
+    init = to_dev(d["init"], torch)
+    del d
+    out = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+    fin = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+
+    # ---- decode inputs (256 x 32, 100 distinct steps) ----
+    t0 = time.time()
+    state0 = to_dev(synth.make_decode_state(wd), torch)
+    steps = []
+    for s in range(args.decode_steps):
+        st = synth.make_decode_step(wd, s)
+        steps.append(tuple(to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")))
+    log(f"decode inputs generated in {time.time() - t0:.1f}s")
+    state = state0.clone()
+    dout = torch.empty((wd.batch, wd.heads, wd.dv), dtype=torch.float32, device="cuda")
+
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        kda.chunk_fwd(q, k, v, la, be, init, None, out=out, final_state=fin, workspace=ws)
+
+    def decode_all():
+        for (sq, sk, sv, sla, sb) in steps:
+            kda.decode_step(sq, sk, sv, sla, sb, state, out=dout)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode_all()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode_all()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    pre_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+    dec_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+
+    pre_s = float(np.median(pre_ms)) / 1e3
+    tok_s = T / pre_s
+    pbytes = prefill_bytes(T, H, D)
+    pflops = PAGE_FLOP_PER_TOKEN_HEAD(D) * T * H
+    dec_launch_s = float(np.median(dec_ms)) / 1e3 / args.decode_steps
+    units = wd.batch * wd.heads
+    dbytes = decode_bytes(units, D)
+    dec_gbs = dbytes / dec_launch_s / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate/state",
+        "data": "synthetic (seeded; q,k L2-normalised, beta=sigmoid(N), log_alpha=-s*softplus(N))",
+        "config": {"workload": f"{wp.name} + {wd.name}",
+                   "prefill": {"batch": 1, "seq_len": T, "heads": H, "dk": D, "dv": D, "chunk": 64,
+                               "in": "bf16", "out": "fp32", "init_state": "fp32 N(0,0.02^2)"},
+                   "decode": {"batch": wd.batch, "heads": wd.heads, "dk": D, "dv": D,
+                              "steps": args.decode_steps, "in": "bf16", "out": "fp32", "state": "fp32 in place"}},
+        "prefill": {"ms": pre_s * 1e3, "ms_min": float(pre_ms.min()), "tokens_per_s": tok_s,
+                    "hbm_gbs": pbytes / pre_s / 1e9},
+        "decode": {"value": dec_gbs, "unit": "GB/s", "us_per_step": dec_launch_s * 1e6,
+                   "ms_per_100_steps": dec_launch_s * 1e5},
+        "roofline": {"kernel": "decode_kernel<128,bf16,fp32>", "bound": "hbm", "achieved": dec_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic_from_profiles("decode"),
+                     "algorithmic_bytes_per_launch": dbytes, "launch_us": dec_launch_s * 1e6},
+        "prefill_roofline": {"bound": "hbm", "achieved": pbytes / pre_s / 1e9, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes_per_call": pbytes,
+                             "mfma_frac_page_flops": pflops / pre_s / 1e12 / BF16_DENSE_TFLOPS,
+                             "traffic": traffic_from_profiles("prefill")},
+        "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
+                   "(model level, hardware not stated)",
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        res["cpu_baseline"] = cpu_baseline(wp, args.cpu_sample, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -116,45 +116,90 @@ __device__ __forceinline__ void store4<float>(float* dst, floatx4 x) {
 // ---------------------------------------------------------------------------
 // chunk-local kernel
 // ---------------------------------------------------------------------------
+// One workgroup of 4*D threads per (head, chunk); thread t owns key channel
+// c = t % D over the 16 rows of block b = t / D.  Every global load is issued
+// first and every global store comes after the last barrier, so no barrier
+// waits on memory traffic.  LDS regions:
+//   R0  operand rows of the Atil / P sub-block products, later T (fp32) and
+//       the channel-major right-hand sides of W and Ut;
+//   R1  Atil (fp32), later T as a matrix-core operand;
+//   R2  P staged as the record stores it;
+//   R3  per-block gate products and beta.
 template <int D, typename OT>
 struct LocalCfg {
-    static constexpr int NT = 4 * D;  // one thread per (channel, 16-row block)
+    static constexpr int NT = 4 * D;
     static constexpr int NW = NT / 64;
     static constexpr int PD = Pad<OT>::v;
-    static constexpr int DP = D + PD;   // pitch of [row][channel] operand rows
-    static constexpr int KP = CH + PD;  // pitch of [channel][token] rows
-    static constexpr int AP = CH + 4;   // pitch of fp32 [64][64]
+    static constexpr int DP = D + PD;   // pitch of [row][channel] operand rows (OT)
+    static constexpr int DP32 = D + 4;  // pitch of fp32 diagonal-block operand rows
+    static constexpr int KP = CH + PD;  // pitch of [channel][token] rows (OT)
+    static constexpr int AP = CH + 1;   // pitch of fp32 [64][64] matrices
     static constexpr int YP = 17;
+    static constexpr bool F16 = sizeof(OT) == 2;
     static constexpr size_t SZ_OP = 192 * DP * sizeof(OT);
     static constexpr size_t SZ_KT = (size_t)D * KP * sizeof(OT);
     static constexpr size_t SZ_F = (size_t)CH * AP * sizeof(float);
-    static constexpr size_t OFF_OP = 0;
-    static constexpr size_t OFF_KGT = 0;                   // aliases the operand region after use
-    static constexpr size_t OFF_VBT = SZ_KT;
-    static constexpr size_t OFF_Y = 2 * SZ_KT;
-    static constexpr size_t OFF_A = align256(SZ_OP);      // Atil fp32, later T as OT [64][KP]
-    static constexpr size_t OFF_T = OFF_A + SZ_F;          // T fp32
-    static constexpr size_t OFF_X = OFF_T + SZ_F;          // block products and block-start gates
-    static constexpr size_t SMEM = OFF_X + 2 * 4 * D * sizeof(float);
-    static_assert(OFF_Y + NW * 16 * YP * sizeof(float) <= SZ_OP, "scratch must fit the operand region");
+    static constexpr size_t OFF_Y = align256(SZ_F);          // in R0, during the T phase
+    static constexpr size_t OFF_KG = F16 ? 0 : SZ_F;          // in R0, after the T phase
+    static constexpr size_t R1 = align256(SZ_OP);
+    static constexpr size_t R2 = R1 + SZ_F;
+    static constexpr size_t R3 = R2 + (size_t)CH * CH * sizeof(OT);
+    static constexpr size_t SMEM = R3 + 2 * 4 * D * sizeof(float) + CH * sizeof(float);
+    static_assert(OFF_Y + NW * 16 * YP * sizeof(float) <= SZ_OP, "T scratch must fit R0");
+    static_assert(OFF_KG + 2 * SZ_KT <= SZ_OP, "W/Ut right-hand sides must fit R0");
+    static_assert(!F16 || 96 * DP32 * sizeof(float) <= SZ_OP, "fp32 diagonal operands must fit R0");
+    static_assert(!F16 || (size_t)CH * KP * sizeof(OT) <= SZ_F, "T operand must fit R1");
 };
 
+
+// Sixteen rows of one channel held in registers: bf16 inputs stay packed two per
+// register (widened exactly on use), fp32 inputs stay as they are.
+template <typename IT>
+struct Col16;
+template <>
+struct Col16<bf16_t> {
+    uint32_t w[8];
+    __device__ __forceinline__ void set(int i, bf16_t x) {
+        if (i & 1)
+            w[i >> 1] = (w[i >> 1] & 0xFFFFu) | (uint32_t(x.bits) << 16);
+        else
+            w[i >> 1] = (w[i >> 1] & 0xFFFF0000u) | x.bits;
+    }
+    __device__ __forceinline__ float operator[](int i) const {
+        return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+    }
+};
+template <>
+struct Col16<float> {
+    float w[16];
+    __device__ __forceinline__ void set(int i, float x) { w[i] = x; }
+    __device__ __forceinline__ float operator[](int i) const { return w[i]; }
+};
+
+// Largest magnitude an fp16 operand may take before the diagonal sub-blocks
+// switch to fp32 operands.
+constexpr float F16_OPERAND_LIMIT = 6.0e4f;
+
 template <int D, typename IT, typename OT>
-__global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
+__global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
     using C = LocalCfg<D, OT>;
     using R = Rec<D, OT>;
     __shared__ __align__(16) unsigned char smem[C::SMEM];
-    OT* sOp = reinterpret_cast<OT*>(smem + C::OFF_OP);
-    OT* sKgT = reinterpret_cast<OT*>(smem + C::OFF_KGT);
-    OT* sVbT = reinterpret_cast<OT*>(smem + C::OFF_VBT);
+    OT* sOp = reinterpret_cast<OT*>(smem);
+    float* sOp32 = reinterpret_cast<float*>(smem);
+    float* sT = reinterpret_cast<float*>(smem);
     float* sY = reinterpret_cast<float*>(smem + C::OFF_Y);
-    float* sAt = reinterpret_cast<float*>(smem + C::OFF_A);
-    OT* sTh = reinterpret_cast<OT*>(smem + C::OFF_A);
-    float* sT = reinterpret_cast<float*>(smem + C::OFF_T);
-    float* sBP = reinterpret_cast<float*>(smem + C::OFF_X);
+    OT* sKgT = reinterpret_cast<OT*>(smem + C::OFF_KG);
+    OT* sVbT = reinterpret_cast<OT*>(smem + C::OFF_KG + C::SZ_KT);
+    float* sAt = reinterpret_cast<float*>(smem + C::R1);
+    OT* sTh = C::F16 ? reinterpret_cast<OT*>(smem + C::R1) : reinterpret_cast<OT*>(smem);
+    constexpr int THP = C::F16 ? C::KP : C::AP;  // pitch of the T operand
+    OT* sP = reinterpret_cast<OT*>(smem + C::R2);
+    float* sBP = reinterpret_cast<float*>(smem + C::R3);
     float* sA0 = sBP + 4 * D;
+    float* sBeta = sA0 + 4 * D;
 
-    const int s = blockIdx.x / a.Wc, jl = blockIdx.x % a.Wc, h = blockIdx.y;
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc;
     int64_t tb, L;
     seq_bounds(a, s, tb, L);
     const int64_t c0 = (int64_t)(a.win * a.Wc + jl) * CH;
@@ -163,14 +208,6 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
     const int64_t tok0 = tb + c0;
     const int H = a.H;
 
-    unsigned char* rec = a.rec + ((size_t)(s * a.Wc + jl) * H + h) * a.rec_bytes;
-    OT* rW = reinterpret_cast<OT*>(rec + R::W);
-    OT* rQg = reinterpret_cast<OT*>(rec + R::QG);
-    OT* rKhT = reinterpret_cast<OT*>(rec + R::KHT);
-    OT* rP = reinterpret_cast<OT*>(rec + R::P);
-    float* rUt = reinterpret_cast<float*>(rec + R::UT);
-    float* rG = reinterpret_cast<float*>(rec + R::GAM);
-
     const IT* q = static_cast<const IT*>(a.q);
     const IT* k = static_cast<const IT*>(a.k);
     const IT* v = static_cast<const IT*>(a.v);
@@ -178,58 +215,47 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int gq = lane >> 4, li = lane & 15;
-    const int c = t % D, b = t / D;  // this thread's channel and 16-row block
+    const int c = t % D, b = t / D;
     const int rb0 = 16 * b;
 
-    // ---- per-thread gate products over its 16 rows of channel c ----
-    float kk[16], qq[16], bb[16], al[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = rb0 + i;
-        const bool ok = r < n;
-        const size_t tokh = (size_t)(tok0 + r) * H + h;
-        const size_t off = tokh * D + c;
-        kk[i] = ok ? to_f32(k[off]) : 0.f;
-        qq[i] = ok ? to_f32(q[off]) : 0.f;
-        al[i] = ok ? fast_exp(a.la[off]) : 1.f;
-        bb[i] = ok ? a.beta[tokh] : 0.f;
-    }
-    // Lf[i] = prod_{j=1..i} alpha_j : e^{G_i - G_0} within the block
-    float Lf[16];
-    Lf[0] = 1.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) Lf[i] = Lf[i - 1] * al[i];
-    // Rb[i] = prod_{j=i+1..15} alpha_j : e^{G_15 - G_i}
-    float Rb[16];
-    Rb[15] = 1.f;
-#pragma unroll
-    for (int i = 14; i >= 0; --i) Rb[i] = Rb[i + 1] * al[i + 1];
-    // diagonal sub-block factors around the anchor row 8 of the block
-    float Dl[16], Dr[16];
+    // ---- all global loads first (rows past the end read the last valid row, then get zeroed) ----
+    Col16<IT> kk, qq, vv;
+    float al[16];
     {
-        float M = 1.f;
-        Dl[8] = 1.f;
-        Dr[8] = 1.f;
+        float lr[16];
 #pragma unroll
-        for (int i = 9; i < 16; ++i) {
-            M *= al[i];
-            Dl[i] = M;  // e^{G_i - G_8}
-            Dr[i] = 1.f / M;
+        for (int i = 0; i < 16; ++i) {
+            const int r = min(rb0 + i, n - 1);
+            const size_t off = ((size_t)(tok0 + r) * H + h) * D + c;
+            kk.set(i, k[off]);
+            qq.set(i, q[off]);
+            vv.set(i, v[off]);
+            lr[i] = a.la[off];
         }
-        float Bk = 1.f;
+        if (t < CH) sBeta[t] = t < n ? a.beta[(size_t)(tok0 + t) * H + h] : 0.f;
+        const IT zero = from_f32<IT>(0.f);
 #pragma unroll
-        for (int i = 7; i >= 0; --i) {
-            Bk *= al[i + 1];
-            Dr[i] = Bk;  // e^{G_8 - G_i}
-            Dl[i] = 1.f / Bk;
+        for (int i = 0; i < 16; ++i) {
+            const bool ok = rb0 + i < n;
+            if (!ok) {
+                kk.set(i, zero);
+                qq.set(i, zero);
+                vv.set(i, zero);
+            }
+            al[i] = ok ? fast_exp(lr[i]) : 1.f;
         }
     }
-    sBP[b * D + c] = al[0] * Lf[15];  // product over the whole block
-    sA0[b * D + c] = al[0];           // gate of the block's first row
-    // strictly-upper blocks of P are zero in the record
+    {
+        float pb = al[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) pb *= al[i];
+        sBP[b * D + c] = pb;  // product of the block's gates
+        sA0[b * D + c] = al[0];
+    }
+    // strictly-upper blocks of the staged P are zero
     for (int idx = t; idx < CH * CH; idx += C::NT) {
         const int r = idx / CH, i = idx % CH;
-        if ((i >> 4) > (r >> 4)) rP[idx] = from_f32<OT>(0.f);
+        if ((i >> 4) > (r >> 4)) sP[idx] = from_f32<OT>(0.f);
     }
     __syncthreads();
 
@@ -239,49 +265,44 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
         PB[e] = sBP[e * D + c];
         A0[e] = sA0[e * D + c];
     }
-    float E = 1.f, Sfx = 1.f;  // products over the blocks before / after this one
+    float E = 1.f, Sfx = 1.f;  // gate products over the blocks before / after this one
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (e < b) E *= PB[e];
         if (e > b) Sfx *= PB[e];
     }
-    const float gamma = ((PB[0] * PB[1]) * PB[2]) * PB[3];
-    if (b == 0) rG[c] = gamma;
+    const float* bb = sBeta + rb0;  // beta of this block's rows (LDS broadcast reads)
 
-    // Qg (row-major) and Kh^T (channel-major) go straight to the record
-    float F[16];
-    {
-        float kh[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            F[i] = E * (al[0] * Lf[i]);  // e^{G_{rb0+i}}
-            rQg[(rb0 + i) * D + c] = from_f32<OT>(qq[i] * F[i]);
-            kh[i] = kk[i] * (Rb[i] * Sfx);  // k e^{G_last - G}
-        }
-        store16<OT>(rKhT + (size_t)c * CH + rb0, kh);
-    }
-
-    // ---- phase A: off-diagonal 16x16 sub-blocks of Atil and P ----
-    // rows 0..47: beta k e^{G_r - G_a} of blocks 1..3 (a = first row of the block)
-    // rows 48..95: q e^{G_r - G_a} of blocks 1..3
-    // rows 96..191: for each (row block rb, column block cb < rb): k e^{G_a(rb) - G_i}
+    // ---- phase A: off-diagonal sub-blocks of Atil and P ----
+    // rows 0..47  beta k e^{G_r - G_a}, blocks 1..3 (a = first row of the block)
+    // rows 48..95 q e^{G_r - G_a}, blocks 1..3
+    // rows 96..   k e^{G_a(rb) - G_i} for each (row block rb, column block cb < rb)
     if (b >= 1) {
+        float Lf = 1.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            sOp[(16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Lf[i]);
-            sOp[(48 + 16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(qq[i] * Lf[i]);
+            if (i > 0) Lf *= al[i];
+            sOp[(16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Lf);
+            sOp[(48 + 16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(qq[i] * Lf);
         }
     }
+    {
+        float X[4];
 #pragma unroll
-    for (int rb = 1; rb < 4; ++rb) {
-        if (rb > b) {
-            float X = A0[rb];  // e^{G_a(rb) - G_end(b)}
+        for (int rb = 1; rb < 4; ++rb) {
+            X[rb] = A0[rb];  // e^{G_a(rb) - G_end(b)}
 #pragma unroll
             for (int e = 1; e < 3; ++e)
-                if (e > b && e < rb) X *= PB[e];
-            const int slot = rb * (rb - 1) / 2 + b;
+                if (e > b && e < rb) X[rb] *= PB[e];
+        }
+        float Rb = 1.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sOp[(96 + 16 * slot + i) * C::DP + c] = from_f32<OT>(kk[i] * Rb[i] * X);
+        for (int i = 15; i >= 0; --i) {
+            if (i < 15) Rb *= al[i + 1];
+#pragma unroll
+            for (int rb = 1; rb < 4; ++rb)
+                if (rb > b)
+                    sOp[(96 + 16 * (rb * (rb - 1) / 2 + b) + i) * C::DP + c] = from_f32<OT>(kk[i] * Rb * X[rb]);
         }
     }
     __syncthreads();
@@ -290,65 +311,106 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
         const int rb = sl == 0 ? 1 : (sl < 3 ? 2 : 3);
         const int cb = sl - rb * (rb - 1) / 2;
         floatx4 acc = zero4();
-        const OT* A = sOp + ((p < 6 ? 0 : 48) + 16 * (rb - 1)) * C::DP;
-        mma_tile<OT>(acc, A, C::DP, sOp + (96 + 16 * sl) * C::DP, C::DP, D, lane);
+        mma_tile<OT>(acc, sOp + ((p < 6 ? 0 : 48) + 16 * (rb - 1)) * C::DP, C::DP, sOp + (96 + 16 * sl) * C::DP,
+                     C::DP, D, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
             if (p < 6)
                 sAt[row * C::AP + col] = acc[r];
             else
-                rP[row * CH + col] = from_f32<OT>(acc[r]);
+                sP[row * CH + col] = from_f32<OT>(acc[r]);
         }
     }
-    __syncthreads();
 
-    // ---- phase B: diagonal sub-blocks ----
-    // rows 0..63: beta k e^{G_r - G_m}; 64..127: q e^{G_r - G_m}; 128..191: k e^{G_m - G_i}
+    // ---- phase B: diagonal sub-blocks, anchored at row 8 of the block ----
+    // rows 0..63 beta k e^{G_r - G_m}; 64..127 q e^{G_r - G_m}; 128..191 k e^{G_m - G_i}
+    // e^{G_i - G_m} and e^{G_m - G_i} for every row i of the block, visited in a fixed order
+    auto diag_factors = [&](auto&& visit) {
+        float M = 1.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        sOp[(rb0 + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Dl[i]);
-        sOp[(64 + rb0 + i) * C::DP + c] = from_f32<OT>(qq[i] * Dl[i]);
-        sOp[(128 + rb0 + i) * C::DP + c] = from_f32<OT>(kk[i] * Dr[i]);
+        for (int i = 8; i < 16; ++i) {
+            if (i > 8) M *= al[i];
+            visit(i, M, __builtin_amdgcn_rcpf(M));
+        }
+        float Bk = 1.f;
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+            Bk *= al[i + 1];
+            visit(i, __builtin_amdgcn_rcpf(Bk), Bk);
+        }
+    };
+    int wide = 0;
+    if (C::F16) {
+        float mx = 0.f;
+        diag_factors([&](int i, float dl, float dr) {
+            mx = fmaxf(mx, fmaxf(fabsf(bb[i] * kk[i] * dl), fmaxf(fabsf(qq[i] * dl), fabsf(kk[i] * dr))));
+        });
+        wide = __syncthreads_or(!(mx <= F16_OPERAND_LIMIT));
+    } else {
+        __syncthreads();
     }
-    __syncthreads();
-    for (int p = wave; p < 8; p += C::NW) {
-        const int db = p & 3;
-        floatx4 acc = zero4();
-        const OT* A = sOp + ((p < 4 ? 0 : 64) + 16 * db) * C::DP;
-        mma_tile<OT>(acc, A, C::DP, sOp + (128 + 16 * db) * C::DP, C::DP, D, lane);
+    if (!wide) {
+        diag_factors([&](int i, float dl, float dr) {
+            sOp[(rb0 + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * dl);
+            sOp[(64 + rb0 + i) * C::DP + c] = from_f32<OT>(qq[i] * dl);
+            sOp[(128 + rb0 + i) * C::DP + c] = from_f32<OT>(kk[i] * dr);
+        });
+        __syncthreads();
+        for (int p = wave; p < 8; p += C::NW) {
+            const int db = p & 3;
+            floatx4 acc = zero4();
+            mma_tile<OT>(acc, sOp + ((p < 4 ? 0 : 64) + 16 * db) * C::DP, C::DP, sOp + (128 + 16 * db) * C::DP,
+                         C::DP, D, lane);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int lr = 4 * gq + r;
-            const int row = 16 * db + lr, col = 16 * db + li;
-            if (p < 4)
-                sAt[row * C::AP + col] = acc[r];
-            else
-                rP[row * CH + col] = from_f32<OT>(lr >= li ? acc[r] : 0.f);
+            for (int r = 0; r < 4; ++r) {
+                const int lr = 4 * gq + r;
+                const int row = 16 * db + lr, col = 16 * db + li;
+                if (p < 4)
+                    sAt[row * C::AP + col] = acc[r];
+                else
+                    sP[row * CH + col] = from_f32<OT>(lr >= li ? acc[r] : 0.f);
+            }
+        }
+        __syncthreads();
+    } else {
+        // fp16 would overflow: fp32 operands, two block pairs at a time
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if ((b >> 1) == half) {
+                const int rr0 = 16 * (b & 1);
+                diag_factors([&](int i, float dl, float dr) {
+                    sOp32[(rr0 + i) * C::DP32 + c] = bb[i] * kk[i] * dl;
+                    sOp32[(32 + rr0 + i) * C::DP32 + c] = qq[i] * dl;
+                    sOp32[(64 + rr0 + i) * C::DP32 + c] = kk[i] * dr;
+                });
+            }
+            __syncthreads();
+            for (int p = wave; p < 4; p += C::NW) {
+                const int hb = p & 1, db = 2 * half + hb;
+                floatx4 acc = zero4();
+                mma_tile<float>(acc, sOp32 + ((p < 2 ? 0 : 32) + 16 * hb) * C::DP32, C::DP32,
+                                sOp32 + (64 + 16 * hb) * C::DP32, C::DP32, D, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lr = 4 * gq + r;
+                    const int row = 16 * db + lr, col = 16 * db + li;
+                    if (p < 2)
+                        sAt[row * C::AP + col] = acc[r];
+                    else
+                        sP[row * CH + col] = from_f32<OT>(lr >= li ? acc[r] : 0.f);
+                }
+            }
+            __syncthreads();
         }
     }
-    __syncthreads();
 
-    // ---- W / Ut right-hand sides (channel-major), T diagonal blocks ----
-    {
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = bb[i] * kk[i] * F[i];
-        store16<OT>(sKgT + (size_t)c * C::KP + rb0, x);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = rb0 + i;
-            x[i] = r < n ? bb[i] * to_f32(v[((size_t)(tok0 + r) * H + h) * D + c]) : 0.f;
-        }
-        store16<OT>(sVbT + (size_t)c * C::KP + rb0, x);
-    }
-    // off-diagonal blocks of T start at zero
+    // ---- T = (I + Atil)^-1 : diagonal blocks by substitution, then block substitution ----
     for (int idx = t; idx < CH * CH; idx += C::NT) {
         const int r = idx / CH, i = idx % CH;
         if ((r >> 4) != (i >> 4)) sT[r * C::AP + i] = 0.f;
     }
     if (t < 64) {
-        // column j of the inverse of the unit lower-triangular block (I + Atil_bb)
         const int db = t >> 4, j = t & 15;
         const float* Ab = sAt + (16 * db) * C::AP + 16 * db;
         float x[16];
@@ -363,7 +425,6 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
         for (int r = 0; r < 16; ++r) sT[(16 * db + r) * C::AP + 16 * db + j] = x[r];
     }
     __syncthreads();
-    // block forward substitution: T_{rb,cb} = -T_{rb,rb} sum_{cb<=j<rb} Atil_{rb,j} T_{j,cb}
 #pragma unroll
     for (int rb = 1; rb < 4; ++rb) {
         const int cb = wave;
@@ -385,14 +446,38 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
         }
         __syncthreads();
     }
-    // T as a matrix-core operand (aliases Atil, which is no longer needed)
-    for (int idx = t; idx < CH * CH; idx += C::NT) {
-        const int r = idx / CH, i = idx % CH;
-        sTh[r * C::KP + i] = from_f32<OT>(sT[r * C::AP + i]);
+    if (C::F16) {
+        for (int idx = t; idx < CH * CH; idx += C::NT) {
+            const int r = idx / CH, i = idx % CH;
+            sTh[r * THP + i] = from_f32<OT>(sT[r * C::AP + i]);
+        }
+        __syncthreads();
+    }
+
+    // ---- right-hand sides of W and Ut, channel-major ----
+    {
+        float x[16];
+        float F = E;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            F *= al[i];  // e^{G_{rb0+i}}
+            x[i] = bb[i] * kk[i] * F;
+        }
+        store16<OT>(sKgT + (size_t)c * C::KP + rb0, x);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = bb[i] * vv[i];
+        store16<OT>(sVbT + (size_t)c * C::KP + rb0, x);
     }
     __syncthreads();
 
-    // ---- W = T (beta K e^G), Ut = T (beta V) ----
+    // ---- W = T (beta K e^G), Ut = T (beta V), then every record store ----
+    unsigned char* rec = a.rec + ((size_t)(s * a.Wc + jl) * H + h) * a.rec_bytes;
+    OT* rW = reinterpret_cast<OT*>(rec + R::W);
+    OT* rQg = reinterpret_cast<OT*>(rec + R::QG);
+    OT* rKhT = reinterpret_cast<OT*>(rec + R::KHT);
+    OT* rP = reinterpret_cast<OT*>(rec + R::P);
+    float* rUt = reinterpret_cast<float*>(rec + R::UT);
+    float* rG = reinterpret_cast<float*>(rec + R::GAM);
     constexpr int NTC = D / 16;
     for (int p = wave; p < 8 * NTC; p += C::NW) {
         const bool isU = p >= 4 * NTC;
@@ -401,7 +486,7 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
         constexpr int KS = Mma<OT>::KSTEP;
         const int K = ((16 * (rb + 1) + KS - 1) / KS) * KS;
         floatx4 acc = zero4();
-        mma_tile<OT>(acc, sTh + (16 * rb) * C::KP, C::KP, (isU ? sVbT : sKgT) + (16 * ct) * C::KP, C::KP, K, lane);
+        mma_tile<OT>(acc, sTh + (16 * rb) * THP, THP, (isU ? sVbT : sKgT) + (16 * ct) * C::KP, C::KP, K, lane);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * gq + r, col = 16 * ct + li;
@@ -411,6 +496,26 @@ __global__ void __launch_bounds__(4 * D) chunk_local_kernel(ChunkArgs a) {
                 rW[row * D + col] = from_f32<OT>(acc[r]);
         }
     }
+    {
+        float F = E;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            F *= al[i];
+            rQg[(rb0 + i) * D + c] = from_f32<OT>(qq[i] * F);
+        }
+        float x[16];
+        float Rb = Sfx;  // e^{G_last - G_i}
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            if (i < 15) Rb *= al[i + 1];
+            x[i] = kk[i] * Rb;
+        }
+        store16<OT>(rKhT + (size_t)c * CH + rb0, x);
+        if (b == 0) rG[c] = ((PB[0] * PB[1]) * PB[2]) * PB[3];
+    }
+    constexpr int PER = 16 / sizeof(OT);  // elements per 16-byte store
+    for (int e = t * PER; e < CH * CH; e += C::NT * PER)
+        *reinterpret_cast<float4*>(rP + e) = *reinterpret_cast<const float4*>(sP + e);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,7 +651,7 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
     for (int w = 0; w < nwin; ++w) {
         ChunkArgs a = base;
         a.win = w;
-        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.N * base.Wc, base.H), dim3(C::NT), 0, st, a);
+        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(256), 0, st, a);

@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: exports, status strings, workspace sizing, argument validation.
+
+Every call here fails validation (or has nothing to do) before any HIP call,
+so no kernel is ever launched; the fake device addresses are never touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_53_amd import _lib
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+A = 1 << 20  # a 16-byte-aligned fake device address; never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for st in range(5):
+        s = _lib.status_string(st)
+        assert isinstance(s, str) and s
+    assert _lib.status_string(99) == "unknown status"
+
+
+def _shape(B=1, T=256, N=0, maxT=0, H=2, dk=64, dv=64, i=F32, o=F32):
+    return _lib.Shape(B, T, N, maxT, H, dk, dv, i, o)
+
+
+def test_workspace_size(L):
+    for idx in (0, 1, 2):
+        w = WORKLOADS[idx]
+        s = _shape(1, w.seqlen, 0, 0, w.heads, w.dk, w.dv, BF16 if w.dtype == "bf16" else F32, F32)
+        n = L.kda_chunk_fwd_workspace_size(s)
+        state = w.heads * w.dk * w.dv * 4
+        assert n > state
+        assert n < (1 << 31)
+    # varlen: grows with the number of sequences
+    s1 = _shape(1, 1 << 20, 16, 1 << 17, 32, 128, 128, BF16, F32)
+    s2 = _shape(1, 1 << 20, 1, 1 << 20, 32, 128, 128, BF16, F32)
+    assert L.kda_chunk_fwd_workspace_size(s1) > 0 and L.kda_chunk_fwd_workspace_size(s2) > 0
+    # invalid shapes: 0
+    assert L.kda_chunk_fwd_workspace_size(_shape(dk=96, dv=96)) == 0
+    assert L.kda_chunk_fwd_workspace_size(_shape(dk=64, dv=128)) == 0
+    assert L.kda_chunk_fwd_workspace_size(_shape(H=0)) == 0
+    assert L.kda_chunk_fwd_workspace_size(None) == 0
+
+
+def _fwd(L, s, q=A, k=2 * A, v=3 * A, la=4 * A, b=5 * A, init=None, cu=None, out=6 * A, fin=None,
+         ws=None, wsb=0):
+    return L.kda_chunk_fwd(s, q, k, v, la, b, init, cu, out, fin, ws, wsb, None)
+
+
+def test_chunk_fwd_validation(L):
+    s = _shape()
+    assert L.kda_chunk_fwd(None, A, A, A, A, A, None, None, A, None, A, 1 << 30, None) == INVALID
+    assert _fwd(L, _shape(dk=96, dv=96)) == UNSUPPORTED
+    assert _fwd(L, _shape(dk=64, dv=128)) == UNSUPPORTED
+    assert _fwd(L, _shape(i=7)) == UNSUPPORTED
+    assert _fwd(L, _shape(o=3)) == UNSUPPORTED
+    assert _fwd(L, _shape(H=0)) == INVALID
+    assert _fwd(L, _shape(T=-1)) == INVALID
+    assert _fwd(L, s, q=None) == INVALID
+    assert _fwd(L, s, q=A + 4) == INVALID                       # misaligned
+    assert _fwd(L, s, out=A + 100) == INVALID                   # out overlaps q
+    assert _fwd(L, s, init=7 * A, fin=7 * A + 64) == INVALID    # partial state overlap
+    assert _fwd(L, s, cu=9 * A, ws=10 * A, wsb=1 << 30) == OK       # varlen with zero sequences: no work
+    assert _fwd(L, _shape(B=2), cu=9 * A) == INVALID            # varlen needs batch 1
+    assert _fwd(L, s, ws=None) == WORKSPACE
+    assert _fwd(L, s, ws=10 * A, wsb=1024) == WORKSPACE
+    assert _fwd(L, s, ws=10 * A + 8, wsb=1 << 30) == WORKSPACE  # misaligned workspace
+
+
+def test_decode_validation(L):
+    f = L.kda_decode_step
+    assert f(0, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
+    assert f(-1, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == INVALID
+    assert f(2, 2, 96, 96, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 128, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 64, 5, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 64, F32, F32, None, A, A, A, A, A, A, None) == INVALID
+    st, out = 8 * A, 12 * A
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
+    assert f(2, 2, 64, 64, F32, F32, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state

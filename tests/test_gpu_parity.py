@@ -1,0 +1,248 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Small cases span several 64-token chunks, partial chunks and empty
+sequences; the workload cases run the exact shapes and launch configuration
+the benchmark times.  Every output and final state is compared element by
+element with max|gpu - oracle| / RMS(oracle) <= 1e-4 (fp32 inputs) or 2e-2
+(bf16 inputs); decode, which is fp32 arithmetic throughout, must meet 1e-4.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import WORKLOADS, random_small
+
+from kda_testlib import DECODE_TOL, TOL, assert_close, oracle_chunk, run_chunk, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_53_amd as m
+    m._lib.lib()
+    return m
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,H,D,dtype", [(1, 1, 64, "f32"), (5, 3, 64, "bf16"), (4, 2, 128, "f32"),
+                                         (16, 4, 128, "bf16")])
+def test_decode_small(kda, N, H, D, dtype):
+    st = synth.gen_tokens(11 + N, N, H, D, D, dtype, 0.05)
+    S0 = synth.gen_states(11 + N, N, H, D, D, 0.5)
+    args = [to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")]
+    state = to_dev(S0, torch)
+    outs, ref_outs = [], []
+    S = S0
+    for step in range(3):
+        outs.append(kda.decode_step(*args, state, out_dtype=torch.float32).cpu().numpy())
+        o, S = oracle.decode_steps(S, [st])
+        ref_outs.append(o[0])
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert_close(f"out{i}", outs[i], ref_outs[i], DECODE_TOL)
+    assert_close("state", state.cpu().numpy(), S, DECODE_TOL)
+
+
+def test_decode_workload_100_steps(kda):
+    """256 sequences x 32 heads, 100 distinct steps, state in place; 64 sampled units checked."""
+    w = WORKLOADS[3]
+    S0 = synth.make_decode_state(w)
+    state = to_dev(S0, torch)
+    steps = [synth.make_decode_step(w, s) for s in range(w.steps)]
+    outs = []
+    for st in steps:
+        args = [to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")]
+        outs.append(kda.decode_step(*args, state, out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    seqs = np.sort(rng.choice(w.batch, 8, replace=False))
+    heads = np.sort(rng.choice(w.heads, 8, replace=False))
+    sub = lambda x: x[seqs][:, heads]
+    ref_outs, S_ref = oracle.decode_steps(sub(S0), [{k: sub(v) for k, v in st.items()} for st in steps])
+    got = np.stack([sub(o.cpu().numpy()) for o in outs])
+    assert_close("outputs x100", got, np.stack(ref_outs), DECODE_TOL)
+    assert_close("state", sub(state.cpu().numpy()), S_ref, DECODE_TOL)
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill: small and edge cases
+# ----------------------------------------------------------------------------
+
+CASES = [
+    # (T, H, D, dtype, init, lens)
+    (1, 1, 64, "f32", False, None), (63, 2, 64, "f32", True, None), (64, 1, 128, "f32", True, None),
+    (65, 2, 128, "f32", False, None), (129, 1, 64, "bf16", True, None), (127, 2, 128, "bf16", True, None),
+    (300, 3, 128, "bf16", True, None), (513, 2, 64, "bf16", False, None),
+    (0, 2, 64, "f32", True, [0, 5, 64, 1, 65, 130]), (0, 3, 128, "bf16", True, [1, 0, 64, 200, 63, 129, 0]),
+]
+
+
+@pytest.mark.parametrize("T,H,D,dtype,init,lens", CASES)
+def test_chunk_small(kda, T, H, D, dtype, init, lens):
+    d = random_small(T * 7 + D + H, T, H, D, D, dtype=dtype, init_std=0.02 if init else None, lens=lens)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    if o_ref.size:
+        assert_close("out", o, o_ref, TOL[dtype])
+    assert_close("state", S, S_ref, TOL[dtype])
+    if lens is not None and d["init"] is not None:
+        for s, L in enumerate(lens):
+            if L == 0:  # an empty sequence hands its initial state through unchanged
+                assert np.array_equal(S[s], d["init"][s])
+
+
+def test_chunk_strong_decay(kda):
+    """Gates near the supported edge (log_alpha down to about -10 per token)."""
+    d = random_small(5, 256, 2, 128, 128, dtype="bf16", gate_scale=4.0)
+    assert d["log_alpha"].min() < -8
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
+def test_chunk_workspace_windows(kda):
+    """The smallest workspace (one chunk per window) gives the same bits as the default one."""
+    d = random_small(8, 400, 2, 128, 128, dtype="bf16")
+    o1, S1 = run_chunk(kda, torch, d)
+    # a one-chunk problem with the same sequences and heads needs exactly one record per window
+    need = kda.workspace_size(1, 64, 2, 128, 128, torch.bfloat16, torch.float32)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o2, S2 = run_chunk(kda, torch, d, workspace=ws)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_chunk_deterministic(kda):
+    d = random_small(9, 333, 4, 128, 128, dtype="bf16")
+    o1, S1 = run_chunk(kda, torch, d)
+    o2, S2 = run_chunk(kda, torch, d)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_chunk_bf16_output(kda):
+    d = random_small(10, 200, 2, 128, 128, dtype="bf16")
+    o, S = run_chunk(kda, torch, d, out_dtype=torch.bfloat16)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out(bf16)", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
+# ----------------------------------------------------------------------------
+# state handoff, aliasing, varlen and decode continuation
+# ----------------------------------------------------------------------------
+
+def test_split_handoff_and_alias(kda):
+    """[0, T1) then [T1, T) from the returned state equals [0, T); final may alias init."""
+    T, T1 = 500, 190
+    d = random_small(12, T, 2, 128, 128, dtype="bf16")
+    o_ref, S_ref = oracle_chunk(d)
+    a = {x: d[x][:T1] for x in ("q", "k", "v", "log_alpha", "beta")}
+    a["init"] = d["init"]
+    oa, Sa = run_chunk(kda, torch, a)
+    b = {x: d[x][T1:] for x in ("q", "k", "v", "log_alpha", "beta")}
+    b["init"] = Sa
+    ob, Sb = run_chunk(kda, torch, b)
+    assert_close("out", np.concatenate([oa, ob]), o_ref, TOL["bf16"])
+    assert_close("state", Sb, S_ref, TOL["bf16"])
+    # in-place continuation: final_state is the init_state tensor
+    q, k, v, la, be = (to_dev(b[x], torch).unsqueeze(0) for x in ("q", "k", "v", "log_alpha", "beta"))
+    st = to_dev(Sa, torch)
+    _, fin = kda.chunk_fwd(q, k, v, la, be, st, None, out_dtype=torch.float32, final_state=st)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    assert np.array_equal(st.cpu().numpy(), Sb)
+
+
+def test_varlen_matches_separate_runs(kda):
+    lens = [70, 1, 128, 0, 257]
+    d = random_small(13, 0, 2, 128, 128, dtype="bf16", lens=lens)
+    o, S = run_chunk(kda, torch, d)
+    cu = d["cu_seqlens"]
+    for s in range(len(lens)):
+        t0, t1 = cu[s], cu[s + 1]
+        part = {x: d[x][t0:t1] for x in ("q", "k", "v", "log_alpha", "beta")}
+        part["init"] = d["init"][s:s + 1]
+        if t1 > t0:
+            os_, Ss = run_chunk(kda, torch, part)
+            np.testing.assert_allclose(o[t0:t1], os_, rtol=0, atol=1e-6 * max(1.0, np.abs(os_).max()))
+            np.testing.assert_allclose(S[s], Ss[0], rtol=0, atol=1e-6 * max(1.0, np.abs(Ss).max()))
+
+
+def test_prefill_then_decode(kda):
+    """Decode from the prefill's final state equals prefill over one more token."""
+    T = 200
+    d = random_small(14, T + 1, 4, 128, 128, dtype="bf16")
+    o_ref, S_ref = oracle_chunk(d)
+    a = {x: d[x][:T] for x in ("q", "k", "v", "log_alpha", "beta")}
+    a["init"] = d["init"]
+    _, Sa = run_chunk(kda, torch, a)
+    state = to_dev(Sa, torch)
+    args = [to_dev(d[x][T:T + 1], torch) for x in ("q", "k", "v", "log_alpha", "beta")]
+    o = kda.decode_step(*args, state, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close("decoded token", o.cpu().numpy(), o_ref[T:T + 1], TOL["bf16"])
+    assert_close("state", state.cpu().numpy(), S_ref, TOL["bf16"])
+
+
+def test_pins_on_gpu(kda):
+    """beta = 0 with alpha = 1 leaves the state exactly unchanged; a rewritten key returns its new value."""
+    d = random_small(15, 150, 2, 128, 128, dtype="bf16")
+    d["beta"][:] = 0
+    d["log_alpha"][:] = 0
+    _, S = run_chunk(kda, torch, d)
+    assert np.array_equal(S, d["init"])
+    # overwrite: one-hot key written twice (beta = 1, alpha = 1), then queried
+    D = 128
+    T = 70
+    q = np.zeros((T, 1, D), np.float32)
+    k = np.zeros((T, 1, D), np.float32)
+    v = np.random.default_rng(0).standard_normal((T, 1, D)).astype(np.float32)
+    for t in range(T):
+        k[t, 0, t % D] = 1.0
+    k[66, 0, :] = 0
+    k[66, 0, 3] = 1.0    # key e3 again, in a later chunk
+    q[69, 0, 3] = 1.0    # query e3 at the end
+    one = {"q": q, "k": k, "v": v, "log_alpha": np.zeros((T, 1, D), np.float32),
+           "beta": np.ones((T, 1), np.float32), "init": None}
+    o, _ = run_chunk(kda, torch, one)
+    np.testing.assert_allclose(o[69, 0], v[66, 0], atol=1e-5)
+
+
+# ----------------------------------------------------------------------------
+# the benchmark workloads at full size
+# ----------------------------------------------------------------------------
+
+def test_workload0_f32(kda):
+    w = WORKLOADS[0]
+    d = synth.make_prefill(w)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["f32"])
+    assert_close("state", S, S_ref, TOL["f32"])
+
+
+def test_workload1_bf16(kda):
+    w = WORKLOADS[1]
+    d = synth.make_prefill(w)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
+def test_workload2_long(kda):
+    """64K tokens x 32 heads with a random initial state: every output and state element."""
+    w = WORKLOADS[2]
+    d = synth.make_prefill(w)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
