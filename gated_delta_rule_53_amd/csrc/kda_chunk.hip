@@ -37,6 +37,8 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <stdlib.h>
+
 namespace kda {
 
 __device__ __forceinline__ void seq_bounds(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
@@ -54,13 +56,30 @@ __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~si
 // Per-chunk record layout (bytes); OT is the matrix-core operand type.
 template <int D, typename OT>
 struct Rec {
-    static constexpr size_t W = 0;                                        // OT [64][D]
-    static constexpr size_t QG = align256(W + CH * D * sizeof(OT));       // OT [64][D]
-    static constexpr size_t KHT = align256(QG + CH * D * sizeof(OT));     // OT [D][64]
-    static constexpr size_t P = align256(KHT + CH * D * sizeof(OT));      // OT [64][64]
-    static constexpr size_t UT = align256(P + CH * CH * sizeof(OT));      // f32 [64][D]
-    static constexpr size_t GAM = align256(UT + CH * D * sizeof(float));  // f32 [D]
+    static constexpr size_t W = 0;                                        // OT 64 x D, fragment order
+    static constexpr size_t QG = align256(W + CH * D * sizeof(OT));       // OT 64 x D, fragment order
+    static constexpr size_t KHT = align256(QG + CH * D * sizeof(OT));     // OT D x 64, fragment order
+    static constexpr size_t P = align256(KHT + CH * D * sizeof(OT));      // OT 64 x 64, fragment order
+    static constexpr size_t UT = align256(P + CH * CH * sizeof(OT));      // OT [4 row tiles][D][16 rows]
+    static constexpr size_t GAM = align256(UT + CH * D * sizeof(OT));     // f32 [D]
     static constexpr size_t BYTES = align256(GAM + D * sizeof(float));
+};
+
+// Matrix-core fragment order.  The record keeps every A operand of the state
+// pass as the sequence of 16 x KS fragments one wave loads: fragment (row tile
+// rt, k step kk) is 64 lanes x KE contiguous elements, so each wave load
+// instruction reads one contiguous 1 KB block.  Element (r, c) of a matrix
+// with NC columns (the contraction dimension) lives at idx(r, c, NC).
+template <typename OT>
+struct FragOrder {
+    static constexpr int KE = sizeof(OT) == 2 ? 8 : 1;  // elements per lane per fragment
+    static constexpr int KS = 4 * KE;                   // contraction length of one fragment
+    __host__ __device__ static constexpr int idx(int r, int c, int NC) {
+        return (((r >> 4) * (NC / KS) + c / KS) * 64 + ((c % KS) / KE) * 16 + (r & 15)) * KE + (c % KE);
+    }
+    __host__ __device__ static constexpr int frag(int rt, int kk, int lane, int NC) {
+        return ((rt * (NC / KS) + kk) * 64 + lane) * KE;
+    }
 };
 
 template <typename OT>
@@ -98,6 +117,14 @@ __device__ __forceinline__ void store16<float>(float* dst, const float* x) {
 }
 
 template <typename OT>
+__device__ __forceinline__ void store8(OT* dst, const float* x) {
+    half8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (_Float16)x[e];
+    *reinterpret_cast<half8*>(dst) = a;
+}
+
+template <typename OT>
 __device__ __forceinline__ void store4(OT* dst, floatx4 x);
 template <>
 __device__ __forceinline__ void store4<_Float16>(_Float16* dst, floatx4 x) {
@@ -111,6 +138,21 @@ __device__ __forceinline__ void store4<_Float16>(_Float16* dst, floatx4 x) {
 template <>
 __device__ __forceinline__ void store4<float>(float* dst, floatx4 x) {
     *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+template <typename OT>
+__device__ __forceinline__ floatx4 load4(const OT* src);
+template <>
+__device__ __forceinline__ floatx4 load4<_Float16>(const _Float16* src) {
+    half4 h = *reinterpret_cast<const half4*>(src);
+    floatx4 x = {(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+    return x;
+}
+template <>
+__device__ __forceinline__ floatx4 load4<float>(const float* src) {
+    float4 v = *reinterpret_cast<const float4*>(src);
+    floatx4 x = {v.x, v.y, v.z, v.w};
+    return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -476,7 +518,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     OT* rQg = reinterpret_cast<OT*>(rec + R::QG);
     OT* rKhT = reinterpret_cast<OT*>(rec + R::KHT);
     OT* rP = reinterpret_cast<OT*>(rec + R::P);
-    float* rUt = reinterpret_cast<float*>(rec + R::UT);
+    OT* rUt = reinterpret_cast<OT*>(rec + R::UT);
     float* rG = reinterpret_cast<float*>(rec + R::GAM);
     constexpr int NTC = D / 16;
     for (int p = wave; p < 8 * NTC; p += C::NW) {
@@ -487,13 +529,12 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         const int K = ((16 * (rb + 1) + KS - 1) / KS) * KS;
         floatx4 acc = zero4();
         mma_tile<OT>(acc, sTh + (16 * rb) * THP, THP, (isU ? sVbT : sKgT) + (16 * ct) * C::KP, C::KP, K, lane);
+        if (isU) {
+            store4<OT>(rUt + ((size_t)rb * D + 16 * ct + li) * 16 + 4 * gq, acc);
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * rb + 4 * gq + r, col = 16 * ct + li;
-            if (isU)
-                rUt[row * D + col] = acc[r];
-            else
-                rW[row * D + col] = from_f32<OT>(acc[r]);
+            for (int r = 0; r < 4; ++r)
+                rW[FragOrder<OT>::idx(16 * rb + 4 * gq + r, 16 * ct + li, D)] = from_f32<OT>(acc[r]);
         }
     }
     {
@@ -501,7 +542,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             F *= al[i];
-            rQg[(rb0 + i) * D + c] = from_f32<OT>(qq[i] * F);
+            rQg[FragOrder<OT>::idx(rb0 + i, c, D)] = from_f32<OT>(qq[i] * F);
         }
         float x[16];
         float Rb = Sfx;  // e^{G_last - G_i}
@@ -510,27 +551,77 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
             if (i < 15) Rb *= al[i + 1];
             x[i] = kk[i] * Rb;
         }
-        store16<OT>(rKhT + (size_t)c * CH + rb0, x);
+        if (C::F16) {  // two runs of 8 consecutive tokens are contiguous in fragment order
+            store8<OT>(rKhT + FragOrder<OT>::idx(c, rb0, CH), x);
+            store8<OT>(rKhT + FragOrder<OT>::idx(c, rb0 + 8, CH), x + 8);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) rKhT[FragOrder<OT>::idx(c, rb0 + i, CH)] = from_f32<OT>(x[i]);
+        }
         if (b == 0) rG[c] = ((PB[0] * PB[1]) * PB[2]) * PB[3];
     }
-    constexpr int PER = 16 / sizeof(OT);  // elements per 16-byte store
-    for (int e = t * PER; e < CH * CH; e += C::NT * PER)
-        *reinterpret_cast<float4*>(rP + e) = *reinterpret_cast<const float4*>(sP + e);
+    {
+        using FO = FragOrder<OT>;
+        for (int f = t; f < CH * CH / FO::KE; f += C::NT) {  // one lane slot of one fragment
+            const int l = f & 63, kk = (f >> 6) % (CH / FO::KS), rt = (f >> 6) / (CH / FO::KS);
+            const OT* src = sP + (16 * rt + (l & 15)) * CH + kk * FO::KS + (l >> 4) * FO::KE;
+            OT* dst = rP + (size_t)f * FO::KE;
+            if (FO::KE == 8)
+                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+            else
+                dst[0] = src[0];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // inter-chunk kernel
 // ---------------------------------------------------------------------------
+// One workgroup of 8 waves per (sequence, head, slice of BV value columns).
+// Waves 0..3 carry the state: for chunk j they form U_j = Ut_j - W_j S_j and
+// S_{j+1} = Diag(gamma_j) S_j + Kh_j^T U_j, the only dependent chain.  Waves
+// 4..7 form the outputs O_j = Qg_j S_j + P_j U_j off that chain.  S_j and U_j
+// pass between the two groups through double-buffered fp16 LDS tiles; two
+// barriers per chunk.  Each wave keeps the record fragments it needs for the
+// next RING-1 chunks in registers, loaded while the current chunk computes.
+template <typename OT>
+struct Frag;
+template <>
+struct Frag<_Float16> {
+    using T = half8;
+    __device__ __forceinline__ static T load(const _Float16* p, int g) {
+        return *reinterpret_cast<const half8*>(p + 8 * g);
+    }
+    __device__ __forceinline__ static floatx4 mma(T a, const _Float16* bt, int g, floatx4 acc) {
+        half8 b = *reinterpret_cast<const half8*>(bt + 8 * g);
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+    }
+};
+template <>
+struct Frag<float> {
+    using T = float;
+    __device__ __forceinline__ static T load(const float* p, int g) { return p[g]; }
+    __device__ __forceinline__ static floatx4 mma(T a, const float* bt, int g, floatx4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, bt[g], acc, 0, 0, 0);
+    }
+};
+
 template <int D, int BV, typename OT, typename OUT>
-__global__ void __launch_bounds__(256) chunk_inter_kernel(ChunkArgs a) {
+__global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     using R = Rec<D, OT>;
-    constexpr int RT = D / 64;  // 16-row state tiles per wave
-    constexpr int CT = BV / 16; // 16-column tiles
+    using FR = Frag<OT>;
+    using FT = typename FR::T;
+    constexpr int KS = Mma<OT>::KSTEP;
+    constexpr int NFD = D / KS;   // fragments along a D-long row
+    constexpr int NFT = CH / KS;  // fragments along a 64-long row
+    constexpr int RT = D / 64;    // 16-row state tiles per chain wave
+    constexpr int CT = BV / 16;   // 16-column tiles
     constexpr int PD = Pad<OT>::v;
     constexpr int SP = D + PD;
     constexpr int UP = CH + PD;
-    __shared__ __align__(16) OT sS[BV * SP];
-    __shared__ __align__(16) OT sU[BV * UP];
+    constexpr int RING = sizeof(OT) == 2 ? (BV <= 32 ? 3 : 2) : 1;
+    __shared__ __align__(16) OT sS[2][BV * SP];
+    __shared__ __align__(16) OT sU[2][BV * UP];
 
     const int H = a.H;
     const int NH = a.N * H;
@@ -544,90 +635,172 @@ __global__ void __launch_bounds__(256) chunk_inter_kernel(ChunkArgs a) {
     if (jb >= je && a.win > 0) return;
 
     const int t = threadIdx.x;
-    const int lane = t & 63, w = t >> 6;
+    const int lane = t & 63, wave = t >> 6;
+    const bool chain = wave < 4;
+    const int w = wave & 3;
     const int gq = lane >> 4, li = lane & 15;
     const int col0 = z * BV;
-
-    const float* src = a.win == 0 ? a.init : a.state_buf;
-    floatx4 Sacc[RT][CT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
-                Sacc[rt][ct][r] = src ? src[((size_t)u * D + row) * D + col0 + 16 * ct + li] : 0.f;
-            }
-
     OUT* out = static_cast<OUT*>(a.out);
-    for (int j = jb; j < je; ++j) {
-        const unsigned char* rec = a.rec + ((size_t)(s * a.Wc + (j - jb)) * H + h) * a.rec_bytes;
-        const OT* rW = reinterpret_cast<const OT*>(rec + R::W);
-        const OT* rQg = reinterpret_cast<const OT*>(rec + R::QG);
-        const OT* rKhT = reinterpret_cast<const OT*>(rec + R::KHT);
-        const OT* rP = reinterpret_cast<const OT*>(rec + R::P);
-        const float* rUt = reinterpret_cast<const float*>(rec + R::UT);
-        const float* rG = reinterpret_cast<const float*>(rec + R::GAM);
-        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
-        const int64_t tok0 = tb + (int64_t)j * CH;
 
-        // S as the B operand: sS[col][channel]
+    auto rec_of = [&](int j) {
+        return a.rec + ((size_t)(s * a.Wc + (j - jb)) * H + h) * a.rec_bytes;
+    };
+    // Runs the chunks of this window with a ring of RING register buffers: the
+    // fragments of chunk j + RING - 1 are requested before chunk j is computed.
+    // Prefetches are unconditional (the chunk index is clamped to the window, so
+    // the last record is simply read again); only the steps are conditional and
+    // they issue no global loads, which keeps the load queue accounting exact.
+    auto pipeline = [&](auto* buf, auto&& load, auto&& step) {
+        if (jb >= je) return;
+#pragma unroll
+        for (int p = 0; p + 1 < RING; ++p) load(buf[p], min(jb + p, je - 1));
+        for (int j0 = jb; j0 < je; j0 += RING) {
+#pragma unroll
+            for (int p = 0; p < RING; ++p) {
+                const int j = j0 + p;
+                load(buf[(p + RING - 1) % RING], min(j + RING - 1, je - 1));
+                if (j < je) step(buf[p], j);
+            }
+        }
+    };
+
+    floatx4 Sacc[RT][CT];
+    if (chain) {
+        const float* src = a.win == 0 ? a.init : a.state_buf;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
-                store4<OT>(sS + (16 * ct + li) * SP + w * (D / 4) + 16 * rt + 4 * gq, Sacc[rt][ct]);
-        __syncthreads();
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
+                    Sacc[rt][ct][r] = src ? src[((size_t)u * D + row) * D + col0 + 16 * ct + li] : 0.f;
+                }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                store4<OT>(&sS[0][(16 * ct + li) * SP + w * (D / 4) + 16 * rt + 4 * gq], Sacc[rt][ct]);
 
-        floatx4 accO[CT];
+        // state chain: W, Kh^T, Ut and gamma of one chunk
+        struct ChainBuf {
+            FT W[NFD];
+            FT K[RT][NFT];
+            floatx4 U[CT];
+            floatx4 G[RT];
+        };
+        auto load = [&](ChainBuf& f, int j) {
+            const unsigned char* rec = rec_of(j);
+            using FO = FragOrder<OT>;
+            const OT* rW = reinterpret_cast<const OT*>(rec + R::W);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            floatx4 accU = zero4();
-            accO[ct] = zero4();
-            mma_tile<OT>(accU, rW + (16 * w) * D, D, sS + (16 * ct) * SP, SP, D, lane);
-            mma_tile<OT>(accO[ct], rQg + (16 * w) * D, D, sS + (16 * ct) * SP, SP, D, lane);
-            floatx4 Uv;
+            for (int e = 0; e < NFD; ++e) f.W[e] = FR::load(rW + FO::frag(w, e, lane, D), 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Uv[r] = rUt[(16 * w + 4 * gq + r) * D + col0 + 16 * ct + li] - accU[r];
-            store4<OT>(sU + (16 * ct + li) * UP + 16 * w + 4 * gq, Uv);
-        }
-        __syncthreads();
-
+            for (int rt = 0; rt < RT; ++rt) {
+                const OT* rK = reinterpret_cast<const OT*>(rec + R::KHT);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            mma_tile<OT>(accO[ct], rP + (16 * w) * CH, CH, sU + (16 * ct) * UP, UP, CH, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * gq + r;
-                if (row < n) out[((size_t)(tok0 + row) * H + h) * D + col0 + 16 * ct + li] = from_f32<OUT>(accO[ct][r]);
+                for (int e = 0; e < NFT; ++e) f.K[rt][e] = FR::load(rK + FO::frag(w * RT + rt, e, lane, CH), 0);
+                f.G[rt] = load4<float>(reinterpret_cast<const float*>(rec + R::GAM) + w * (D / 4) + 16 * rt + 4 * gq);
             }
-        }
+            const OT* rUt = reinterpret_cast<const OT*>(rec + R::UT);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int rowb = w * (D / 4) + 16 * rt;
-            float gm[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gm[r] = rG[rowb + 4 * gq + r];
+            for (int ct = 0; ct < CT; ++ct) f.U[ct] = load4<OT>(rUt + ((size_t)w * D + col0 + 16 * ct + li) * 16 + 4 * gq);
+        };
+        auto step = [&](ChainBuf& f, int j) {
+            const int cur = (j - jb) & 1;
+            lds_barrier();  // S_j is in sS[cur]
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
+                floatx4 acc = zero4();
+                const OT* bt = sS[cur] + (16 * ct + li) * SP;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[rt][ct][r] *= gm[r];
-                mma_tile<OT>(Sacc[rt][ct], rKhT + (size_t)rowb * CH, CH, sU + (16 * ct) * UP, UP, CH, lane);
+                for (int e = 0; e < NFD; ++e) acc = FR::mma(f.W[e], bt + e * KS, gq, acc);
+                floatx4 Uv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Uv[r] = f.U[ct][r] - acc[r];
+                store4<OT>(sU[cur] + (16 * ct + li) * UP + 16 * w + 4 * gq, Uv);
             }
-        }
+            lds_barrier();  // U_j is in sU[cur]
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Sacc[rt][ct][r] *= f.G[rt][r];
+                    const OT* bt = sU[cur] + (16 * ct + li) * UP;
+#pragma unroll
+                    for (int e = 0; e < NFT; ++e) Sacc[rt][ct] = FR::mma(f.K[rt][e], bt + e * KS, gq, Sacc[rt][ct]);
+                }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    store4<OT>(sS[cur ^ 1] + (16 * ct + li) * SP + w * (D / 4) + 16 * rt + 4 * gq, Sacc[rt][ct]);
+        };
+        ChainBuf buf[RING];
+        pipeline(buf, load, step);
+    } else {
+        // outputs: Qg and P of one chunk
+        struct OutBuf {
+            FT Q[NFD];
+            FT P[NFT];
+        };
+        auto load = [&](OutBuf& f, int j) {
+            const unsigned char* rec = rec_of(j);
+            using FO = FragOrder<OT>;
+            const OT* rQ = reinterpret_cast<const OT*>(rec + R::QG);
+#pragma unroll
+            for (int e = 0; e < NFD; ++e) f.Q[e] = FR::load(rQ + FO::frag(w, e, lane, D), 0);
+            const OT* rP = reinterpret_cast<const OT*>(rec + R::P);
+#pragma unroll
+            for (int e = 0; e < NFT; ++e) f.P[e] = FR::load(rP + FO::frag(w, e, lane, CH), 0);
+        };
+        auto step = [&](OutBuf& f, int j) {
+            const int cur = (j - jb) & 1;
+            lds_barrier();  // S_j is in sS[cur]
+            floatx4 accO[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                floatx4 acc = zero4();
+                const OT* bt = sS[cur] + (16 * ct + li) * SP;
+#pragma unroll
+                for (int e = 0; e < NFD; ++e) acc = FR::mma(f.Q[e], bt + e * KS, gq, acc);
+                accO[ct] = acc;
+            }
+            lds_barrier();  // U_j is in sU[cur]
+            const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
+            const int64_t tok0 = tb + (int64_t)j * CH;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const OT* bt = sU[cur] + (16 * ct + li) * UP;
+#pragma unroll
+                for (int e = 0; e < NFT; ++e) accO[ct] = FR::mma(f.P[e], bt + e * KS, gq, accO[ct]);
+                OUT* o = out + ((size_t)(tok0 + 16 * w + 4 * gq) * H + h) * D + col0 + 16 * ct + li;
+                if (n == CH) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[(size_t)r * H * D] = from_f32<OUT>(accO[ct][r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * w + 4 * gq + r < n) o[(size_t)r * H * D] = from_f32<OUT>(accO[ct][r]);
+                }
+            }
+        };
+        OutBuf buf[RING];
+        pipeline(buf, load, step);
     }
 
+    if (chain) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
-                a.state_buf[((size_t)u * D + row) * D + col0 + 16 * ct + li] = Sacc[rt][ct][r];
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
+                    a.state_buf[((size_t)u * D + row) * D + col0 + 16 * ct + li] = Sacc[rt][ct][r];
+                }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -638,7 +811,16 @@ size_t chunk_record_bytes(int d, bool in_bf16) {
     return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
 }
 
+// Width of the value-column slice each state workgroup carries.  Narrow slices
+// give more workgroups when there are few (sequence, head) pairs; wide ones
+// read each chunk record fewer times.  KDA_VALUE_SLICE (16, 32 or 64) overrides.
 int chunk_value_slice(int d, int64_t units) {
+    static const int forced = [] {
+        const char* e = getenv("KDA_VALUE_SLICE");
+        const int v = e ? atoi(e) : 0;
+        return (v == 16 || v == 32 || v == 64) ? v : 0;
+    }();
+    if (forced) return forced > d ? d : forced;
     if (units <= 64) return 16;
     if (units <= 256 || d == 64) return 32;
     return 64;
@@ -654,7 +836,7 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
         hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, st, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

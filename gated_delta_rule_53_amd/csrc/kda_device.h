@@ -86,6 +86,15 @@ __device__ __forceinline__ void mma_tile(floatx4& acc, const OT* A, int lda, con
     for (int k0 = 0; k0 < K; k0 += Mma<OT>::KSTEP) Mma<OT>::step(acc, a + k0, b + k0, g);
 }
 
+// Workgroup barrier that orders LDS only: global loads issued before it stay in
+// flight (a plain __syncthreads() also waits for every outstanding global access,
+// which would drain any prefetch).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ floatx4 zero4() {
     floatx4 z = {0.f, 0.f, 0.f, 0.f};
     return z;
