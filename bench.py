@@ -102,6 +102,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens per head for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (tuning runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on sharding)",
@@ -138,7 +139,7 @@ def main():
     t0 = time.time()
     state0 = to_dev(synth.make_decode_state(wd), torch)
     steps = []
-    for s in range(args.decode_steps):
+    for s in range(0 if args.prefill_only else args.decode_steps):
         st = synth.make_decode_step(wd, s)
         steps.append(tuple(to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")))
     log(f"decode inputs generated in {time.time() - t0:.1f}s")
@@ -177,7 +178,7 @@ def main():
     tok_s = T / pre_s
     pbytes = prefill_bytes(T, H, D)
     pflops = PAGE_FLOP_PER_TOKEN_HEAD(D) * T * H
-    dec_launch_s = float(np.median(dec_ms)) / 1e3 / args.decode_steps
+    dec_launch_s = float(np.median(dec_ms)) / 1e3 / max(1, len(steps))
     units = wd.batch * wd.heads
     dbytes = decode_bytes(units, D)
     dec_gbs = dbytes / dec_launch_s / 1e9

@@ -3,6 +3,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <stdlib.h>
+
+#include <mutex>
+
 #include "../../include/kda.h"
 
 #include "kda_internal.h"
@@ -10,9 +14,39 @@
 namespace {
 
 constexpr int CHUNK = 64;
-// Per-window record budget: records written by the chunk-local pass should
-// still sit in the 256 MB last-level (MALL) cache when the state pass reads them.
+// Record budget across the two window buffers: records written by the
+// chunk-local pass should still sit in the 256 MB last-level (MALL) cache when
+// the state pass reads them.
 constexpr size_t RECORD_BUDGET = size_t(128) << 20;
+
+// Per-device overlap resources, created on first use and kept for the life of
+// the process.  The mutex serialises host-side enqueueing of calls on one device.
+struct DeviceResources {
+    std::mutex mu;
+    bool ready = false;
+    kda::Overlap ov;
+};
+constexpr int MAX_DEVICES = 64;
+DeviceResources g_dev[MAX_DEVICES];
+
+DeviceResources* device_resources() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    DeviceResources* r = &g_dev[dev];
+    return r;
+}
+
+void init_overlap(DeviceResources* r) {
+    if (r->ready) return;
+    r->ready = true;
+    kda::Overlap ov;
+    if (hipStreamCreateWithFlags(&ov.side, hipStreamNonBlocking) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&ov.local_done, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ov.inter_done[0], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ov.inter_done[1], hipEventDisableTiming) != hipSuccess)
+        return;  // resources leak on this rare path; the overlap simply stays off
+    r->ov = ov;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -84,10 +118,11 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     if (!s || chunk_plan_full(s, s->num_seqs > 0, p) != KDA_OK) return 0;
     const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
     if (per_chunk == 0) return p.state_bytes + 256;
-    int64_t wc = (int64_t)(RECORD_BUDGET / per_chunk);
+    const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    if ((size_t)all * per_chunk <= RECORD_BUDGET) return p.state_bytes + (size_t)all * per_chunk;
+    int64_t wc = (int64_t)(RECORD_BUDGET / 2 / per_chunk);
     if (wc < 1) wc = 1;
-    if (wc > p.max_chunks) wc = p.max_chunks > 0 ? p.max_chunks : 1;
-    return p.state_bytes + (size_t)wc * per_chunk;
+    return p.state_bytes + 2 * (size_t)wc * per_chunk;  // two windows, or one of twice the size
 }
 
 kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
@@ -128,9 +163,27 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     if (p.N == 0) return KDA_OK;  // nothing to compute
     if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
         return KDA_ERR_WORKSPACE;
-    int64_t wc = (int64_t)((workspace_bytes - p.state_bytes) / per_chunk);
-    if (wc > p.max_chunks) wc = p.max_chunks;
-    if (wc < 1) wc = 1;
+    // KDA_OVERLAP=1 runs the chunk-local pass of the next window concurrently with the
+    // state pass of the current one (two record buffers, an auxiliary stream).  Off by
+    // default: on MI355X the concurrent local pass slows the latency-bound state chain
+    // more than it saves.
+    static const bool overlap_enabled = [] {
+        const char* e = getenv("KDA_OVERLAP");
+        return e && e[0] == '1';
+    }();
+    // one buffer for every chunk if it fits; otherwise windows of chunks
+    const size_t avail = workspace_bytes - p.state_bytes;
+    const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    int64_t wc;
+    bool two = false;
+    if ((size_t)all * per_chunk <= avail) {
+        wc = all;
+    } else if (overlap_enabled && avail >= 2 * per_chunk) {
+        wc = (int64_t)(avail / 2 / per_chunk);
+        two = true;
+    } else {
+        wc = (int64_t)(avail / per_chunk);
+    }
     if (wc > INT32_MAX / 2) wc = INT32_MAX / 2;
     const int64_t nwin64 = p.max_chunks > 0 ? (p.max_chunks + wc - 1) / wc : 1;
     if (nwin64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -154,8 +207,17 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     a.init = init_state;
     a.out = out;
     const int bv = kda::chunk_value_slice(d, p.N * H);
+    kda::Overlap ov;  // defaults: everything on the caller's stream
+    DeviceResources* res = two && nwin64 > 1 ? device_resources() : nullptr;
+    std::unique_lock<std::mutex> lock;
+    if (res) {
+        lock = std::unique_lock<std::mutex>(res->mu);
+        init_overlap(res);
+        ov = res->ov;
+        ov.buffer_bytes = (size_t)wc * per_chunk;
+    }
     hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, bv, a,
-                                       (int)nwin64, static_cast<hipStream_t>(stream));
+                                       (int)nwin64, ov, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

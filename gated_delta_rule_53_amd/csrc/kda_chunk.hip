@@ -528,13 +528,21 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         constexpr int KS = Mma<OT>::KSTEP;
         const int K = ((16 * (rb + 1) + KS - 1) / KS) * KS;
         floatx4 acc = zero4();
-        mma_tile<OT>(acc, sTh + (16 * rb) * THP, THP, (isU ? sVbT : sKgT) + (16 * ct) * C::KP, C::KP, K, lane);
         if (isU) {
+            // Ut tile: lane holds rows 16rb+4gq..+3 of value column 16ct+li
+            mma_tile<OT>(acc, sTh + (16 * rb) * THP, THP, sVbT + (16 * ct) * C::KP, C::KP, K, lane);
             store4<OT>(rUt + ((size_t)rb * D + 16 * ct + li) * 16 + 4 * gq, acc);
         } else {
+            // W^T = (beta K e^G)^T T^T: lane holds channels 16ct+4gq..+3 of row 16rb+li,
+            // which are 4 consecutive elements in fragment order
+            mma_tile<OT>(acc, sKgT + (16 * ct) * C::KP, C::KP, sTh + (16 * rb) * THP, THP, K, lane);
+            if (C::F16) {
+                store4<OT>(rW + FragOrder<OT>::idx(16 * rb + li, 16 * ct + 4 * gq, D), acc);
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rW[FragOrder<OT>::idx(16 * rb + 4 * gq + r, 16 * ct + li, D)] = from_f32<OT>(acc[r]);
+                for (int e = 0; e < 4; ++e)
+                    rW[FragOrder<OT>::idx(16 * rb + li, 16 * ct + 4 * gq + e, D)] = from_f32<OT>(acc[e]);
+            }
         }
     }
     {
@@ -826,33 +834,47 @@ int chunk_value_slice(int d, int64_t units) {
     return 64;
 }
 
+// Window loop.  With one window everything runs on the caller's stream.  With
+// more, the chunk-local pass of window w+1 (caller's stream) overlaps the state
+// pass of window w (the auxiliary stream), the records alternating between two
+// buffers: the local pass of window w+2 waits for the state pass of window w.
 template <int D, typename IT, typename OT, typename OUT, int BV>
-static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
+static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     const int units = base.N * base.H;
+    const bool two = nwin > 1 && ov.side;
     for (int w = 0; w < nwin; ++w) {
         ChunkArgs a = base;
         a.win = w;
+        if (two) a.rec = base.rec + (size_t)(w & 1) * ov.buffer_bytes;
+        hipError_t e;
+        if (two && w >= 2 && (e = hipStreamWaitEvent(st, ov.inter_done[w & 1], 0)) != hipSuccess) return e;
         hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, st, a);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipStream_t is = st;
+        if (two) {
+            if ((e = hipEventRecord(ov.local_done, st)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(ov.side, ov.local_done, 0)) != hipSuccess) return e;
+            is = ov.side;
+        }
+        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, is, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (two && (e = hipEventRecord(ov.inter_done[w & 1], ov.side)) != hipSuccess) return e;
     }
+    if (two) return hipStreamWaitEvent(st, ov.inter_done[(nwin - 1) & 1], 0);
     return hipSuccess;
 }
 
 template <int D, typename IT, typename OT, typename OUT>
-static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, hipStream_t st) {
-    if (bv == 16) return run_windows<D, IT, OT, OUT, 16>(a, nwin, st);
-    if (bv == 32) return run_windows<D, IT, OT, OUT, 32>(a, nwin, st);
-    return run_windows<D, IT, OT, OUT, 64>(a, nwin, st);
+static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, const Overlap& ov, hipStream_t st) {
+    if (bv == 16) return run_windows<D, IT, OT, OUT, 16>(a, nwin, ov, st);
+    if (bv == 32) return run_windows<D, IT, OT, OUT, 32>(a, nwin, ov, st);
+    return run_windows<D, IT, OT, OUT, 64>(a, nwin, ov, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
-                          hipStream_t st) {
-#define KDA_RUN(DD, IT, OT, OUT) return run_bv<DD, IT, OT, OUT>(a, nwin, bv, st)
+                          const Overlap& ov, hipStream_t st) {
+#define KDA_RUN(DD, IT, OT, OUT) return run_bv<DD, IT, OT, OUT>(a, nwin, bv, ov, st)
     if (d == 128) {
         if (in_bf16) {
             if (out_bf16) KDA_RUN(128, bf16_t, _Float16, bf16_t);

@@ -26,10 +26,19 @@ struct ChunkArgs {
     void* out;
 };
 
+// Resources for overlapping the two passes of the chunked prefill: an
+// auxiliary stream and three events, plus the byte size of one record buffer.
+struct Overlap {
+    hipStream_t side = nullptr;  // null: run everything on the caller's stream
+    hipEvent_t local_done = nullptr;
+    hipEvent_t inter_done[2] = {nullptr, nullptr};
+    size_t buffer_bytes = 0;
+};
+
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
-                          hipStream_t st);
+                          const Overlap& ov, hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                            const void* v, const float* la, const float* beta, float* state, void* out,
                            hipStream_t st);

@@ -16,7 +16,13 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer owned by the caller; the library
- *    allocates no device memory and keeps no global mutable state.
+ *    allocates no device memory and, by default, keeps no state between
+ *    calls.  With the environment variable KDA_OVERLAP=1 the prefill overlaps
+ *    its two passes across windows of chunks; it then keeps, per device, one
+ *    auxiliary non-blocking stream and three events (created on first use,
+ *    kept until process exit, enqueueing serialised by a per-device mutex) and
+ *    joins that stream back into `stream` before returning, so callers only
+ *    ever synchronise their own stream.
  *  - Layouts are row-major and contiguous.  Tokens are [B, T, H, d] (d
  *    fastest); the recurrent state is [N, H, dk, dv] with dv fastest, rows =
  *    key channels, and the same layout serves initial, final and decode

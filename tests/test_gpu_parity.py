@@ -118,6 +118,13 @@ def test_chunk_workspace_windows(kda):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     o2, S2 = run_chunk(kda, torch, d, workspace=ws)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    # a workspace of four chunk records: windows of four chunks (with KDA_OVERLAP=1,
+    # two alternating buffers of two chunks each)
+    state = 2 * 128 * 128 * 4
+    per_chunk = need - state
+    ws2 = torch.empty(state + 4 * per_chunk, dtype=torch.uint8, device="cuda")
+    o3, S3 = run_chunk(kda, torch, d, workspace=ws2)
+    assert np.array_equal(o1, o3) and np.array_equal(S1, S3)
 
 
 def test_chunk_deterministic(kda):
