@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=1024, help="tokens per head for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (tuning runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on sharding)",
@@ -118,6 +120,15 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     kda._lib.lib()  # fail loudly if the library is missing
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 10}), flush=True)
+        return
 
     wp, wd = WORKLOADS[2], WORKLOADS[3]
     # ---- prefill inputs (64K tokens, 32 heads) ----

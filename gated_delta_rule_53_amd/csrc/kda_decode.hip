@@ -37,10 +37,12 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
     const int lane = t & 63, wave = t >> 6;
 
     float* S_base = state + (size_t)unit * D * D;
-    float4 S[RPT];
+    // the state is streamed once per step: non-temporal accesses keep it from
+    // displacing other data in L2 and the last-level cache
+    floatx4 S[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-        S[i] = *reinterpret_cast<const float4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg);
+        S[i] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg));
 
     __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
     __shared__ float s_red[4][CG][9];
@@ -60,18 +62,12 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
     for (int i = 0; i < RPT; ++i) {
         const int c = rg * RPT + i;
         const float a = s_alpha[c], kc = s_k[c], qc = s_q[c];
-        S[i].x *= a;
-        S[i].y *= a;
-        S[i].z *= a;
-        S[i].w *= a;
-        p[0] += kc * S[i].x;
-        p[1] += kc * S[i].y;
-        p[2] += kc * S[i].z;
-        p[3] += kc * S[i].w;
-        r[0] += qc * S[i].x;
-        r[1] += qc * S[i].y;
-        r[2] += qc * S[i].z;
-        r[3] += qc * S[i].w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            S[i][e] *= a;
+            p[e] += kc * S[i][e];
+            r[e] += qc * S[i][e];
+        }
         qk += qc * kc;
     }
     // reduce over the row groups inside the wave (lanes with the same column group)
@@ -115,12 +111,10 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const float kc = s_k[rg * RPT + i];
-        float4 n;
-        n.x = S[i].x + kc * u[0];
-        n.y = S[i].y + kc * u[1];
-        n.z = S[i].z + kc * u[2];
-        n.w = S[i].w + kc * u[3];
-        *reinterpret_cast<float4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg) = n;
+        floatx4 n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) n[e] = S[i][e] + kc * u[e];
+        __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg));
     }
     if (rg == 0) {
 #pragma unroll
