@@ -31,8 +31,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
 PAGE_FLOP_PER_TOKEN_HEAD = lambda d, C=64: 6 * d * d + 3 * C * d + C * C  # cost per head, per token
 METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode-step HBM GB/s, 1 MI355X"
-KERNEL_SOURCES = ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_chunk.hip",
-                  "gated_delta_rule_53_amd/csrc/kda_device.h"]
+# sources each traffic measurement depends on (profiles/traffic.json is ignored once they change)
+KERNEL_SOURCES = {
+    "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_device.h"],
+    "prefill": ["gated_delta_rule_53_amd/csrc/kda_chunk.hip", "gated_delta_rule_53_amd/csrc/kda_device.h",
+                "gated_delta_rule_53_amd/csrc/kda_internal.h", "gated_delta_rule_53_amd/csrc/kda_api.hip"],
+}
 
 
 def log(*a):
@@ -57,16 +61,16 @@ def to_dev(x, torch):
     return t.cuda()
 
 
-def kernel_hash():
+def kernel_hash(kernel):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel):
-    """HBM bytes per launch from committed counter summaries, if they match the current source."""
+def traffic_from_profiles(kernel, key):
+    """Calibrated HBM bytes from committed counter summaries, if they match the current source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -74,9 +78,9 @@ def traffic_from_profiles(kernel):
     except (OSError, ValueError):
         return None
     ent = rec.get(kernel)
-    if not ent or ent.get("source_hash") != kernel_hash():
+    if not ent or ent.get("source_hash") != kernel_hash(kernel):
         return None
-    return ent.get("bytes_per_launch")
+    return ent.get(key)
 
 
 def cpu_baseline(w, sample_tokens, threads):
@@ -218,13 +222,13 @@ def main():
                    "ms_per_100_steps": dec_launch_s * 1e5},
         "roofline": {"kernel": "decode_kernel<128,bf16,fp32>", "bound": "hbm", "achieved": dec_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profiles("decode"),
+                     "traffic": traffic_from_profiles("decode", "bytes_per_launch"),
                      "algorithmic_bytes_per_launch": dbytes, "launch_us": dec_launch_s * 1e6},
         "prefill_roofline": {"bound": "hbm", "achieved": pbytes / pre_s / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBS,
                              "algorithmic_bytes_per_call": pbytes,
                              "mfma_frac_page_flops": pflops / pre_s / 1e12 / BF16_DENSE_TFLOPS,
-                             "traffic": traffic_from_profiles("prefill")},
+                             "traffic": traffic_from_profiles("prefill", "bytes_per_call")},
         "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
                    "(model level, hardware not stated)",
     }
