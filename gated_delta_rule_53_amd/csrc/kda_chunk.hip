@@ -117,11 +117,18 @@ __device__ __forceinline__ void store16<float>(float* dst, const float* x) {
 }
 
 template <typename OT>
-__device__ __forceinline__ void store8(OT* dst, const float* x) {
+__device__ __forceinline__ void store8(OT* dst, const float* x);
+template <>
+__device__ __forceinline__ void store8<_Float16>(_Float16* dst, const float* x) {
     half8 a;
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[e] = (_Float16)x[e];
     *reinterpret_cast<half8*>(dst) = a;
+}
+template <>
+__device__ __forceinline__ void store8<float>(float* dst, const float* x) {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(x[0], x[1], x[2], x[3]);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(x[4], x[5], x[6], x[7]);
 }
 
 template <typename OT>
@@ -186,7 +193,8 @@ struct LocalCfg {
     static constexpr size_t R1 = align256(SZ_OP);
     static constexpr size_t R2 = R1 + SZ_F;
     static constexpr size_t R3 = R2 + (size_t)CH * CH * sizeof(OT);
-    static constexpr size_t SMEM = R3 + 2 * 4 * D * sizeof(float) + CH * sizeof(float);
+    static constexpr size_t SMEM = R3 + CH * sizeof(float);
+    static_assert(24 * D * sizeof(float) <= SZ_OP, "half-block products must fit R0");
     static_assert(OFF_Y + NW * 16 * YP * sizeof(float) <= SZ_OP, "T scratch must fit R0");
     static_assert(OFF_KG + 2 * SZ_KT <= SZ_OP, "W/Ut right-hand sides must fit R0");
     static_assert(!F16 || 96 * DP32 * sizeof(float) <= SZ_OP, "fp32 diagonal operands must fit R0");
@@ -194,29 +202,42 @@ struct LocalCfg {
 };
 
 
-// Sixteen rows of one channel held in registers: bf16 inputs stay packed two per
-// register (widened exactly on use), fp32 inputs stay as they are.
+// Eight rows of two adjacent channels held in registers: bf16 inputs keep the
+// two channels of a row packed in one register (widened exactly on use), fp32
+// inputs keep a float2.
 template <typename IT>
-struct Col16;
+struct Pair8;
 template <>
-struct Col16<bf16_t> {
+struct Pair8<bf16_t> {
     uint32_t w[8];
-    __device__ __forceinline__ void set(int i, bf16_t x) {
-        if (i & 1)
-            w[i >> 1] = (w[i >> 1] & 0xFFFFu) | (uint32_t(x.bits) << 16);
-        else
-            w[i >> 1] = (w[i >> 1] & 0xFFFF0000u) | x.bits;
-    }
-    __device__ __forceinline__ float operator[](int i) const {
-        return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
+    __device__ __forceinline__ void load(int i, const bf16_t* p) { w[i] = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ void zero(int i) { w[i] = 0u; }
+    __device__ __forceinline__ float get(int i, int e) const {
+        return __uint_as_float(e ? (w[i] & 0xFFFF0000u) : (w[i] << 16));
     }
 };
 template <>
-struct Col16<float> {
-    float w[16];
-    __device__ __forceinline__ void set(int i, float x) { w[i] = x; }
-    __device__ __forceinline__ float operator[](int i) const { return w[i]; }
+struct Pair8<float> {
+    float2 w[8];
+    __device__ __forceinline__ void load(int i, const float* p) { w[i] = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ void zero(int i) { w[i] = make_float2(0.f, 0.f); }
+    __device__ __forceinline__ float get(int i, int e) const { return e ? w[i].y : w[i].x; }
 };
+
+// Two adjacent operand elements of one row.
+template <typename OT>
+__device__ __forceinline__ void put2(OT* dst, float a, float b);
+template <>
+__device__ __forceinline__ void put2<_Float16>(_Float16* dst, float a, float b) {
+    half2v h;
+    h[0] = (_Float16)a;
+    h[1] = (_Float16)b;
+    *reinterpret_cast<half2v*>(dst) = h;
+}
+template <>
+__device__ __forceinline__ void put2<float>(float* dst, float a, float b) {
+    *reinterpret_cast<float2*>(dst) = make_float2(a, b);
+}
 
 // Largest magnitude an fp16 operand may take before the diagonal sub-blocks
 // switch to fp32 operands.
@@ -226,20 +247,20 @@ template <int D, typename IT, typename OT>
 __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
     using C = LocalCfg<D, OT>;
     using R = Rec<D, OT>;
+    using FO = FragOrder<OT>;
     __shared__ __align__(16) unsigned char smem[C::SMEM];
     OT* sOp = reinterpret_cast<OT*>(smem);
     float* sOp32 = reinterpret_cast<float*>(smem);
     float* sT = reinterpret_cast<float*>(smem);
     float* sY = reinterpret_cast<float*>(smem + C::OFF_Y);
+    float* sX = reinterpret_cast<float*>(smem);  // half-block gate products (aliases R0 before phase A)
     OT* sKgT = reinterpret_cast<OT*>(smem + C::OFF_KG);
     OT* sVbT = reinterpret_cast<OT*>(smem + C::OFF_KG + C::SZ_KT);
     float* sAt = reinterpret_cast<float*>(smem + C::R1);
     OT* sTh = C::F16 ? reinterpret_cast<OT*>(smem + C::R1) : reinterpret_cast<OT*>(smem);
     constexpr int THP = C::F16 ? C::KP : C::AP;  // pitch of the T operand
     OT* sP = reinterpret_cast<OT*>(smem + C::R2);
-    float* sBP = reinterpret_cast<float*>(smem + C::R3);
-    float* sA0 = sBP + 4 * D;
-    float* sBeta = sA0 + 4 * D;
+    float* sBeta = reinterpret_cast<float*>(smem + C::R3);
 
     const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc;
     int64_t tb, L;
@@ -257,42 +278,54 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int gq = lane >> 4, li = lane & 15;
-    const int c = t % D, b = t / D;
-    const int rb0 = 16 * b;
+    // this thread: channels ch, ch+1 over the 8 rows r0..r0+7 of half-block hb
+    constexpr int NP = D / 2;
+    const int cp = t % NP, hb = t / NP;
+    const int ch = 2 * cp;
+    const int b = hb >> 1, hh = hb & 1;  // 16-row block and which half of it
+    const int r0 = 8 * hb;               // first row (within the chunk)
+    const int ib0 = 8 * hh;              // first row within the block
 
-    // ---- all global loads first (rows past the end read the last valid row, then get zeroed) ----
-    Col16<IT> kk, qq, vv;
-    float al[16];
+    // ---- every global load first (rows past the end read the last valid row, then get zeroed) ----
+    Pair8<IT> kk, qq, vv;
+    float al[8][2];
     {
-        float lr[16];
+        float2 lr[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = min(rb0 + i, n - 1);
-            const size_t off = ((size_t)(tok0 + r) * H + h) * D + c;
-            kk.set(i, k[off]);
-            qq.set(i, q[off]);
-            vv.set(i, v[off]);
-            lr[i] = a.la[off];
+        for (int i = 0; i < 8; ++i) {
+            const int r = min(r0 + i, n - 1);
+            const size_t off = ((size_t)(tok0 + r) * H + h) * D + ch;
+            kk.load(i, k + off);
+            qq.load(i, q + off);
+            vv.load(i, v + off);
+            lr[i] = *reinterpret_cast<const float2*>(a.la + off);
         }
         if (t < CH) sBeta[t] = t < n ? a.beta[(size_t)(tok0 + t) * H + h] : 0.f;
-        const IT zero = from_f32<IT>(0.f);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bool ok = rb0 + i < n;
+        for (int i = 0; i < 8; ++i) {
+            const bool ok = r0 + i < n;
             if (!ok) {
-                kk.set(i, zero);
-                qq.set(i, zero);
-                vv.set(i, zero);
+                kk.zero(i);
+                qq.zero(i);
+                vv.zero(i);
             }
-            al[i] = ok ? fast_exp(lr[i]) : 1.f;
+            al[i][0] = ok ? fast_exp(lr[i].x) : 1.f;
+            al[i][1] = ok ? fast_exp(lr[i].y) : 1.f;
         }
     }
+    // half-block products, the half's first gate, and prod_{1..7} (first halves)
     {
-        float pb = al[0];
+        float hp[2], l7[2];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) pb *= al[i];
-        sBP[b * D + c] = pb;  // product of the block's gates
-        sA0[b * D + c] = al[0];
+        for (int e = 0; e < 2; ++e) {
+            l7[e] = al[1][e];
+#pragma unroll
+            for (int i = 2; i < 8; ++i) l7[e] *= al[i][e];
+            hp[e] = al[0][e] * l7[e];
+        }
+        *reinterpret_cast<float2*>(sX + hb * D + ch) = make_float2(hp[0], hp[1]);
+        *reinterpret_cast<float2*>(sX + (8 + hb) * D + ch) = make_float2(al[0][0], al[0][1]);
+        *reinterpret_cast<float2*>(sX + (16 + hb) * D + ch) = make_float2(l7[0], l7[1]);
     }
     // strictly-upper blocks of the staged P are zero
     for (int idx = t; idx < CH * CH; idx += C::NT) {
@@ -301,50 +334,70 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     }
     __syncthreads();
 
-    float PB[4], A0[4];
+    // per-channel products over blocks, half-blocks and anchors
+    float PB[4][2], A0[4][2], E[2], Sfx[2], HPo[2], HP0[2], L7[2], A8[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        PB[e] = sBP[e * D + c];
-        A0[e] = sA0[e * D + c];
-    }
-    float E = 1.f, Sfx = 1.f;  // gate products over the blocks before / after this one
+    for (int e = 0; e < 2; ++e) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        if (e < b) E *= PB[e];
-        if (e > b) Sfx *= PB[e];
+        for (int x = 0; x < 4; ++x) {
+            PB[x][e] = sX[(2 * x) * D + ch + e] * sX[(2 * x + 1) * D + ch + e];
+            A0[x][e] = sX[(8 + 2 * x) * D + ch + e];
+        }
+        E[e] = 1.f;
+        Sfx[e] = 1.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (x < b) E[e] *= PB[x][e];
+            if (x > b) Sfx[e] *= PB[x][e];
+        }
+        HPo[e] = sX[(2 * b + 1 - hh) * D + ch + e];  // the other half of this block
+        HP0[e] = sX[(2 * b) * D + ch + e];           // the first half of this block
+        L7[e] = sX[(16 + 2 * b) * D + ch + e];       // prod_{1..7} of the first half
+        A8[e] = sX[(8 + 2 * b + 1) * D + ch + e];    // gate of the block's row 8
     }
-    const float* bb = sBeta + rb0;  // beta of this block's rows (LDS broadcast reads)
+    const float* bb = sBeta + r0;  // beta of this thread's rows (LDS broadcast reads)
+    __syncthreads();               // sX is overwritten by the operands below
 
     // ---- phase A: off-diagonal sub-blocks of Atil and P ----
     // rows 0..47  beta k e^{G_r - G_a}, blocks 1..3 (a = first row of the block)
     // rows 48..95 q e^{G_r - G_a}, blocks 1..3
     // rows 96..   k e^{G_a(rb) - G_i} for each (row block rb, column block cb < rb)
     if (b >= 1) {
-        float Lf = 1.f;
+        float Lf[2] = {hh ? L7[0] : 1.f, hh ? L7[1] : 1.f};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            if (i > 0) Lf *= al[i];
-            sOp[(16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * Lf);
-            sOp[(48 + 16 * (b - 1) + i) * C::DP + c] = from_f32<OT>(qq[i] * Lf);
+        for (int i = 0; i < 8; ++i) {
+            if (i > 0 || hh) {
+                Lf[0] *= al[i][0];
+                Lf[1] *= al[i][1];
+            }
+            const int row = 16 * (b - 1) + ib0 + i;
+            put2<OT>(sOp + row * C::DP + ch, bb[i] * kk.get(i, 0) * Lf[0], bb[i] * kk.get(i, 1) * Lf[1]);
+            put2<OT>(sOp + (48 + row) * C::DP + ch, qq.get(i, 0) * Lf[0], qq.get(i, 1) * Lf[1]);
         }
     }
     {
-        float X[4];
+        float X[4][2];
 #pragma unroll
-        for (int rb = 1; rb < 4; ++rb) {
-            X[rb] = A0[rb];  // e^{G_a(rb) - G_end(b)}
+        for (int rb = 1; rb < 4; ++rb)
 #pragma unroll
-            for (int e = 1; e < 3; ++e)
-                if (e > b && e < rb) X[rb] *= PB[e];
-        }
-        float Rb = 1.f;
+            for (int e = 0; e < 2; ++e) {
+                X[rb][e] = A0[rb][e];  // e^{G_a(rb) - G_end(b)}
 #pragma unroll
-        for (int i = 15; i >= 0; --i) {
-            if (i < 15) Rb *= al[i + 1];
+                for (int x = 1; x < 3; ++x)
+                    if (x > b && x < rb) X[rb][e] *= PB[x][e];
+            }
+        float Rb[2] = {hh ? 1.f : HPo[0], hh ? 1.f : HPo[1]};  // e^{G_end(b) - G_row}
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+            if (i < 7) {
+                Rb[0] *= al[i + 1][0];
+                Rb[1] *= al[i + 1][1];
+            }
 #pragma unroll
             for (int rb = 1; rb < 4; ++rb)
                 if (rb > b)
-                    sOp[(96 + 16 * (rb * (rb - 1) / 2 + b) + i) * C::DP + c] = from_f32<OT>(kk[i] * Rb * X[rb]);
+                    put2<OT>(sOp + (96 + 16 * (rb * (rb - 1) / 2 + b) + ib0 + i) * C::DP + ch,
+                             kk.get(i, 0) * Rb[0] * X[rb][0], kk.get(i, 1) * Rb[1] * X[rb][1]);
         }
     }
     __syncthreads();
@@ -367,36 +420,49 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 
     // ---- phase B: diagonal sub-blocks, anchored at row 8 of the block ----
     // rows 0..63 beta k e^{G_r - G_m}; 64..127 q e^{G_r - G_m}; 128..191 k e^{G_m - G_i}
-    // e^{G_i - G_m} and e^{G_m - G_i} for every row i of the block, visited in a fixed order
+    // diag_factors visits (i, dl_e, dr_e) for this thread's rows in a fixed order
     auto diag_factors = [&](auto&& visit) {
-        float M = 1.f;
+        float M[2] = {1.f, 1.f}, Bk[2] = {A8[0], A8[1]};
+        if (hh) {
 #pragma unroll
-        for (int i = 8; i < 16; ++i) {
-            if (i > 8) M *= al[i];
-            visit(i, M, __builtin_amdgcn_rcpf(M));
-        }
-        float Bk = 1.f;
+            for (int i = 0; i < 8; ++i) {
+                if (i > 0) {
+                    M[0] *= al[i][0];
+                    M[1] *= al[i][1];
+                }
+                visit(i, M[0], M[1], __builtin_amdgcn_rcpf(M[0]), __builtin_amdgcn_rcpf(M[1]));
+            }
+        } else {
 #pragma unroll
-        for (int i = 7; i >= 0; --i) {
-            Bk *= al[i + 1];
-            visit(i, __builtin_amdgcn_rcpf(Bk), Bk);
+            for (int i = 7; i >= 0; --i) {
+                if (i < 7) {
+                    Bk[0] *= al[i + 1][0];
+                    Bk[1] *= al[i + 1][1];
+                }
+                visit(i, __builtin_amdgcn_rcpf(Bk[0]), __builtin_amdgcn_rcpf(Bk[1]), Bk[0], Bk[1]);
+            }
         }
     };
     int wide = 0;
     if (C::F16) {
         float mx = 0.f;
-        diag_factors([&](int i, float dl, float dr) {
-            mx = fmaxf(mx, fmaxf(fabsf(bb[i] * kk[i] * dl), fmaxf(fabsf(qq[i] * dl), fabsf(kk[i] * dr))));
+        diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
+            const float kb0 = fabsf(kk.get(i, 0)), kb1 = fabsf(kk.get(i, 1));
+            const float sb = fmaxf(1.f, fabsf(bb[i]));
+            mx = fmaxf(mx, fmaxf(fmaxf(kb0, fabsf(qq.get(i, 0))) * sb * dl0, kb0 * dr0));
+            mx = fmaxf(mx, fmaxf(fmaxf(kb1, fabsf(qq.get(i, 1))) * sb * dl1, kb1 * dr1));
         });
         wide = __syncthreads_or(!(mx <= F16_OPERAND_LIMIT));
     } else {
         __syncthreads();
     }
+    const int rowB = 16 * b + ib0;  // first row of this thread in [0, 64)
     if (!wide) {
-        diag_factors([&](int i, float dl, float dr) {
-            sOp[(rb0 + i) * C::DP + c] = from_f32<OT>(bb[i] * kk[i] * dl);
-            sOp[(64 + rb0 + i) * C::DP + c] = from_f32<OT>(qq[i] * dl);
-            sOp[(128 + rb0 + i) * C::DP + c] = from_f32<OT>(kk[i] * dr);
+        diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
+            const float k0 = kk.get(i, 0), k1 = kk.get(i, 1);
+            put2<OT>(sOp + (rowB + i) * C::DP + ch, bb[i] * k0 * dl0, bb[i] * k1 * dl1);
+            put2<OT>(sOp + (64 + rowB + i) * C::DP + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
+            put2<OT>(sOp + (128 + rowB + i) * C::DP + ch, k0 * dr0, k1 * dr1);
         });
         __syncthreads();
         for (int p = wave; p < 8; p += C::NW) {
@@ -416,23 +482,24 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
         __syncthreads();
     } else {
-        // fp16 would overflow: fp32 operands, two block pairs at a time
+        // fp16 would overflow: fp32 operands, two blocks at a time
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if ((b >> 1) == half) {
-                const int rr0 = 16 * (b & 1);
-                diag_factors([&](int i, float dl, float dr) {
-                    sOp32[(rr0 + i) * C::DP32 + c] = bb[i] * kk[i] * dl;
-                    sOp32[(32 + rr0 + i) * C::DP32 + c] = qq[i] * dl;
-                    sOp32[(64 + rr0 + i) * C::DP32 + c] = kk[i] * dr;
+                const int rr0 = 16 * (b & 1) + ib0;
+                diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
+                    const float k0 = kk.get(i, 0), k1 = kk.get(i, 1);
+                    put2<float>(sOp32 + (rr0 + i) * C::DP32 + ch, bb[i] * k0 * dl0, bb[i] * k1 * dl1);
+                    put2<float>(sOp32 + (32 + rr0 + i) * C::DP32 + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
+                    put2<float>(sOp32 + (64 + rr0 + i) * C::DP32 + ch, k0 * dr0, k1 * dr1);
                 });
             }
             __syncthreads();
             for (int p = wave; p < 4; p += C::NW) {
-                const int hb = p & 1, db = 2 * half + hb;
+                const int hbk = p & 1, db = 2 * half + hbk;
                 floatx4 acc = zero4();
-                mma_tile<float>(acc, sOp32 + ((p < 2 ? 0 : 32) + 16 * hb) * C::DP32, C::DP32,
-                                sOp32 + (64 + 16 * hb) * C::DP32, C::DP32, D, lane);
+                mma_tile<float>(acc, sOp32 + ((p < 2 ? 0 : 32) + 16 * hbk) * C::DP32, C::DP32,
+                                sOp32 + (64 + 16 * hbk) * C::DP32, C::DP32, D, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int lr = 4 * gq + r;
@@ -496,19 +563,26 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         __syncthreads();
     }
 
-    // ---- right-hand sides of W and Ut, channel-major ----
+    // ---- right-hand sides of W and Ut, channel-major: 8 tokens of each channel ----
     {
-        float x[16];
-        float F = E;
+        float F[2] = {E[0] * (hh ? HP0[0] : 1.f), E[1] * (hh ? HP0[1] : 1.f)};  // e^{G} of the row before
+        float x0[8], x1[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            F *= al[i];  // e^{G_{rb0+i}}
-            x[i] = bb[i] * kk[i] * F;
+        for (int i = 0; i < 8; ++i) {
+            F[0] *= al[i][0];
+            F[1] *= al[i][1];
+            x0[i] = bb[i] * kk.get(i, 0) * F[0];
+            x1[i] = bb[i] * kk.get(i, 1) * F[1];
         }
-        store16<OT>(sKgT + (size_t)c * C::KP + rb0, x);
+        store8<OT>(sKgT + (size_t)ch * C::KP + r0, x0);
+        store8<OT>(sKgT + (size_t)(ch + 1) * C::KP + r0, x1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = bb[i] * vv[i];
-        store16<OT>(sVbT + (size_t)c * C::KP + rb0, x);
+        for (int i = 0; i < 8; ++i) {
+            x0[i] = bb[i] * vv.get(i, 0);
+            x1[i] = bb[i] * vv.get(i, 1);
+        }
+        store8<OT>(sVbT + (size_t)ch * C::KP + r0, x0);
+        store8<OT>(sVbT + (size_t)(ch + 1) * C::KP + r0, x1);
     }
     __syncthreads();
 
@@ -537,48 +611,62 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
             // which are 4 consecutive elements in fragment order
             mma_tile<OT>(acc, sKgT + (16 * ct) * C::KP, C::KP, sTh + (16 * rb) * THP, THP, K, lane);
             if (C::F16) {
-                store4<OT>(rW + FragOrder<OT>::idx(16 * rb + li, 16 * ct + 4 * gq, D), acc);
+                store4<OT>(rW + FO::idx(16 * rb + li, 16 * ct + 4 * gq, D), acc);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    rW[FragOrder<OT>::idx(16 * rb + li, 16 * ct + 4 * gq + e, D)] = from_f32<OT>(acc[e]);
+                for (int e = 0; e < 4; ++e) rW[FO::idx(16 * rb + li, 16 * ct + 4 * gq + e, D)] = from_f32<OT>(acc[e]);
             }
         }
     }
     {
-        float F = E;
+        // Qg: the two channels of a row are adjacent in fragment order (ch is even)
+        float F[2] = {E[0] * (hh ? HP0[0] : 1.f), E[1] * (hh ? HP0[1] : 1.f)};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            F *= al[i];
-            rQg[FragOrder<OT>::idx(rb0 + i, c, D)] = from_f32<OT>(qq[i] * F);
+        for (int i = 0; i < 8; ++i) {
+            F[0] *= al[i][0];
+            F[1] *= al[i][1];
+            const int idx = FO::idx(r0 + i, ch, D);
+            if (C::F16)
+                put2<OT>(rQg + idx, qq.get(i, 0) * F[0], qq.get(i, 1) * F[1]);
+            else {
+                rQg[idx] = from_f32<OT>(qq.get(i, 0) * F[0]);
+                rQg[FO::idx(r0 + i, ch + 1, D)] = from_f32<OT>(qq.get(i, 1) * F[1]);
+            }
         }
-        float x[16];
-        float Rb = Sfx;  // e^{G_last - G_i}
+        // Kh^T: 8 consecutive tokens of one channel are contiguous in fragment order (fp16)
+        float x0[8], x1[8];
+        float Rb[2] = {Sfx[0] * (hh ? 1.f : HPo[0]), Sfx[1] * (hh ? 1.f : HPo[1])};  // e^{G_last - G_i}
 #pragma unroll
-        for (int i = 15; i >= 0; --i) {
-            if (i < 15) Rb *= al[i + 1];
-            x[i] = kk[i] * Rb;
+        for (int i = 7; i >= 0; --i) {
+            if (i < 7) {
+                Rb[0] *= al[i + 1][0];
+                Rb[1] *= al[i + 1][1];
+            }
+            x0[i] = kk.get(i, 0) * Rb[0];
+            x1[i] = kk.get(i, 1) * Rb[1];
         }
-        if (C::F16) {  // two runs of 8 consecutive tokens are contiguous in fragment order
-            store8<OT>(rKhT + FragOrder<OT>::idx(c, rb0, CH), x);
-            store8<OT>(rKhT + FragOrder<OT>::idx(c, rb0 + 8, CH), x + 8);
+        if (C::F16) {
+            store8<OT>(rKhT + FO::idx(ch, r0, CH), x0);
+            store8<OT>(rKhT + FO::idx(ch + 1, r0, CH), x1);
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) rKhT[FragOrder<OT>::idx(c, rb0 + i, CH)] = from_f32<OT>(x[i]);
+            for (int i = 0; i < 8; ++i) {
+                rKhT[FO::idx(ch, r0 + i, CH)] = from_f32<OT>(x0[i]);
+                rKhT[FO::idx(ch + 1, r0 + i, CH)] = from_f32<OT>(x1[i]);
+            }
         }
-        if (b == 0) rG[c] = ((PB[0] * PB[1]) * PB[2]) * PB[3];
+        if (hb == 0)
+            *reinterpret_cast<float2*>(rG + ch) =
+                make_float2(((PB[0][0] * PB[1][0]) * PB[2][0]) * PB[3][0], ((PB[0][1] * PB[1][1]) * PB[2][1]) * PB[3][1]);
     }
-    {
-        using FO = FragOrder<OT>;
-        for (int f = t; f < CH * CH / FO::KE; f += C::NT) {  // one lane slot of one fragment
-            const int l = f & 63, kk = (f >> 6) % (CH / FO::KS), rt = (f >> 6) / (CH / FO::KS);
-            const OT* src = sP + (16 * rt + (l & 15)) * CH + kk * FO::KS + (l >> 4) * FO::KE;
-            OT* dst = rP + (size_t)f * FO::KE;
-            if (FO::KE == 8)
-                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
-            else
-                dst[0] = src[0];
-        }
+    for (int f = t; f < CH * CH / FO::KE; f += C::NT) {  // P: one lane slot of one fragment per step
+        const int l = f & 63, kk2 = (f >> 6) % (CH / FO::KS), rt = (f >> 6) / (CH / FO::KS);
+        const OT* src = sP + (16 * rt + (l & 15)) * CH + kk2 * FO::KS + (l >> 4) * FO::KE;
+        OT* dst = rP + (size_t)f * FO::KE;
+        if (FO::KE == 8)
+            *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+        else
+            dst[0] = src[0];
     }
 }
 
