@@ -783,7 +783,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
             FT W[NFD];
             FT K[RT][NFT];
             floatx4 U[CT];
-            floatx4 G[RT];
+            float G;  // gamma of state row w*D/4 + lane % (D/4)
         };
         auto load = [&](ChainBuf& f, int j) {
             const unsigned char* rec = rec_of(j);
@@ -796,14 +796,20 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                 const OT* rK = reinterpret_cast<const OT*>(rec + R::KHT);
 #pragma unroll
                 for (int e = 0; e < NFT; ++e) f.K[rt][e] = FR::load(rK + FO::frag(w * RT + rt, e, lane, CH), 0);
-                f.G[rt] = load4<float>(reinterpret_cast<const float*>(rec + R::GAM) + w * (D / 4) + 16 * rt + 4 * gq);
             }
+            // one dword per lane (a 16-byte load per lane would move 16x the bytes gamma has)
+            f.G = reinterpret_cast<const float*>(rec + R::GAM)[w * (D / 4) + lane % (D / 4)];
             const OT* rUt = reinterpret_cast<const OT*>(rec + R::UT);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) f.U[ct] = load4<OT>(rUt + ((size_t)w * D + col0 + 16 * ct + li) * 16 + 4 * gq);
         };
         auto step = [&](ChainBuf& f, int j) {
             const int cur = (j - jb) & 1;
+            float g[RT][4];  // gamma of the four state rows each accumulator lane holds
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) g[rt][r] = __shfl(f.G, 16 * rt + 4 * gq + r);
             lds_barrier();  // S_j is in sS[cur]
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
@@ -822,7 +828,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Sacc[rt][ct][r] *= f.G[rt][r];
+                    for (int r = 0; r < 4; ++r) Sacc[rt][ct][r] *= g[rt][r];
                     const OT* bt = sU[cur] + (16 * ct + li) * UP;
 #pragma unroll
                     for (int e = 0; e < NFT; ++e) Sacc[rt][ct] = FR::mma(f.K[rt][e], bt + e * KS, gq, Sacc[rt][ct]);
@@ -851,9 +857,9 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
             for (int e = 0; e < NFT; ++e) f.P[e] = FR::load(rP + FO::frag(w, e, lane, CH), 0);
         };
+        // called after the first barrier of chunk j (S_j is in sS[cur])
         auto step = [&](OutBuf& f, int j) {
             const int cur = (j - jb) & 1;
-            lds_barrier();  // S_j is in sS[cur]
             floatx4 accO[CT];
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
@@ -882,8 +888,23 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                 }
             }
         };
+        // The output waves issue their record loads right after the first
+        // barrier, while the chain waves compute U_j from LDS and registers, so
+        // the loads do not queue behind the chain's own at the end of the step.
         OutBuf buf[RING];
-        pipeline(buf, load, step);
+        if (jb < je) {
+#pragma unroll
+            for (int p = 0; p + 1 < RING; ++p) load(buf[p], min(jb + p, je - 1));
+            for (int j0 = jb; j0 < je; j0 += RING) {
+#pragma unroll
+                for (int p = 0; p < RING; ++p) {
+                    const int j = j0 + p;
+                    if (j < je) lds_barrier();  // S_j is in sS[cur]
+                    load(buf[(p + RING - 1) % RING], min(j + RING - 1, je - 1));
+                    if (j < je) step(buf[p], j);
+                }
+            }
+        }
     }
 
     if (chain) {
