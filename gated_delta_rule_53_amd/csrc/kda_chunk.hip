@@ -679,7 +679,16 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 // 4..7 form the outputs O_j = Qg_j S_j + P_j U_j off that chain.  S_j and U_j
 // pass between the two groups through double-buffered fp16 LDS tiles; two
 // barriers per chunk.  Each wave keeps the record fragments it needs for the
-// next RING-1 chunks in registers, loaded while the current chunk computes.
+// next RING-1 chunks in registers (a ring of RING buffers).
+//
+// A chunk step moves about 57 KB of record through the CU's vector memory
+// path, which is the step's real cost, so the loads are spread over the two
+// phases of the step: the output waves and the chain's Kh^T loads are issued
+// right after the first barrier (while the chain computes U_j), the chain's
+// W, Ut and gamma loads after its state update.  Prefetches are unconditional
+// (the chunk index is clamped to the window, so past the end the last record
+// is read again) except the chain's Kh^T, which is only needed by steps that
+// run; this keeps the compiler's load-count waits exact.
 template <typename OT>
 struct Frag;
 template <>
@@ -741,25 +750,6 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     auto rec_of = [&](int j) {
         return a.rec + ((size_t)(s * a.Wc + (j - jb)) * H + h) * a.rec_bytes;
     };
-    // Runs the chunks of this window with a ring of RING register buffers: the
-    // fragments of chunk j + RING - 1 are requested before chunk j is computed.
-    // Prefetches are unconditional (the chunk index is clamped to the window, so
-    // the last record is simply read again); only the steps are conditional and
-    // they issue no global loads, which keeps the load queue accounting exact.
-    auto pipeline = [&](auto* buf, auto&& load, auto&& step) {
-        if (jb >= je) return;
-#pragma unroll
-        for (int p = 0; p + 1 < RING; ++p) load(buf[p], min(jb + p, je - 1));
-        for (int j0 = jb; j0 < je; j0 += RING) {
-#pragma unroll
-            for (int p = 0; p < RING; ++p) {
-                const int j = j0 + p;
-                load(buf[(p + RING - 1) % RING], min(j + RING - 1, je - 1));
-                if (j < je) step(buf[p], j);
-            }
-        }
-    };
-
     floatx4 Sacc[RT][CT];
     if (chain) {
         const float* src = a.win == 0 ? a.init : a.state_buf;
@@ -791,19 +781,21 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
             const OT* rW = reinterpret_cast<const OT*>(rec + R::W);
 #pragma unroll
             for (int e = 0; e < NFD; ++e) f.W[e] = FR::load(rW + FO::frag(w, e, lane, D), 0);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                const OT* rK = reinterpret_cast<const OT*>(rec + R::KHT);
-#pragma unroll
-                for (int e = 0; e < NFT; ++e) f.K[rt][e] = FR::load(rK + FO::frag(w * RT + rt, e, lane, CH), 0);
-            }
             // one dword per lane (a 16-byte load per lane would move 16x the bytes gamma has)
             f.G = reinterpret_cast<const float*>(rec + R::GAM)[w * (D / 4) + lane % (D / 4)];
             const OT* rUt = reinterpret_cast<const OT*>(rec + R::UT);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) f.U[ct] = load4<OT>(rUt + ((size_t)w * D + col0 + 16 * ct + li) * 16 + 4 * gq);
         };
-        auto step = [&](ChainBuf& f, int j) {
+        auto loadK = [&](ChainBuf& f, int j) {
+            using FO = FragOrder<OT>;
+            const OT* rK = reinterpret_cast<const OT*>(rec_of(j) + R::KHT);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int e = 0; e < NFT; ++e) f.K[rt][e] = FR::load(rK + FO::frag(w * RT + rt, e, lane, CH), 0);
+        };
+        auto step = [&](ChainBuf& f, ChainBuf& fn, int jn, int j) {
             const int cur = (j - jb) & 1;
             float g[RT][4];  // gamma of the four state rows each accumulator lane holds
 #pragma unroll
@@ -811,6 +803,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) g[rt][r] = __shfl(f.G, 16 * rt + 4 * gq + r);
             lds_barrier();  // S_j is in sS[cur]
+            loadK(fn, jn);  // Kh^T of a later chunk, issued in the phase where the output waves compute
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 floatx4 acc = zero4();
@@ -840,7 +833,21 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                     store4<OT>(sS[cur ^ 1] + (16 * ct + li) * SP + w * (D / 4) + 16 * rt + 4 * gq, Sacc[rt][ct]);
         };
         ChainBuf buf[RING];
-        pipeline(buf, load, step);
+        if (jb < je) {
+#pragma unroll
+            for (int p = 0; p + 1 < RING; ++p) {
+                load(buf[p], min(jb + p, je - 1));
+                loadK(buf[p], min(jb + p, je - 1));
+            }
+            for (int j0 = jb; j0 < je; j0 += RING) {
+#pragma unroll
+                for (int p = 0; p < RING; ++p) {
+                    const int j = j0 + p, jn = min(j + RING - 1, je - 1);
+                    load(buf[(p + RING - 1) % RING], jn);
+                    if (j < je) step(buf[p], buf[(p + RING - 1) % RING], jn, j);
+                }
+            }
+        }
     } else {
         // outputs: Qg and P of one chunk
         struct OutBuf {
