@@ -183,19 +183,16 @@ struct LocalCfg {
     static constexpr int DP32 = D + 4;  // pitch of fp32 diagonal-block operand rows
     static constexpr int KP = CH + PD;  // pitch of [channel][token] rows (OT)
     static constexpr int AP = CH + 1;   // pitch of fp32 [64][64] matrices
-    static constexpr int YP = 17;
     static constexpr bool F16 = sizeof(OT) == 2;
     static constexpr size_t SZ_OP = 192 * DP * sizeof(OT);
     static constexpr size_t SZ_KT = (size_t)D * KP * sizeof(OT);
     static constexpr size_t SZ_F = (size_t)CH * AP * sizeof(float);
-    static constexpr size_t OFF_Y = align256(SZ_F);          // in R0, during the T phase
     static constexpr size_t OFF_KG = F16 ? 0 : SZ_F;          // in R0, after the T phase
     static constexpr size_t R1 = align256(SZ_OP);
     static constexpr size_t R2 = R1 + SZ_F;
     static constexpr size_t R3 = R2 + (size_t)CH * CH * sizeof(OT);
     static constexpr size_t SMEM = R3 + CH * sizeof(float);
     static_assert(24 * D * sizeof(float) <= SZ_OP, "half-block products must fit R0");
-    static_assert(OFF_Y + NW * 16 * YP * sizeof(float) <= SZ_OP, "T scratch must fit R0");
     static_assert(OFF_KG + 2 * SZ_KT <= SZ_OP, "W/Ut right-hand sides must fit R0");
     static_assert(!F16 || 96 * DP32 * sizeof(float) <= SZ_OP, "fp32 diagonal operands must fit R0");
     static_assert(!F16 || (size_t)CH * KP * sizeof(OT) <= SZ_F, "T operand must fit R1");
@@ -252,7 +249,6 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     OT* sOp = reinterpret_cast<OT*>(smem);
     float* sOp32 = reinterpret_cast<float*>(smem);
     float* sT = reinterpret_cast<float*>(smem);
-    float* sY = reinterpret_cast<float*>(smem + C::OFF_Y);
     float* sX = reinterpret_cast<float*>(smem);  // half-block gate products (aliases R0 before phase A)
     OT* sKgT = reinterpret_cast<OT*>(smem + C::OFF_KG);
     OT* sVbT = reinterpret_cast<OT*>(smem + C::OFF_KG + C::SZ_KT);
@@ -514,54 +510,161 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
     }
 
-    // ---- T = (I + Atil)^-1 : diagonal blocks by substitution, then block substitution ----
-    for (int idx = t; idx < CH * CH; idx += C::NT) {
-        const int r = idx / CH, i = idx % CH;
-        if ((r >> 4) != (i >> 4)) sT[r * C::AP + i] = 0.f;
-    }
-    if (t < 64) {
-        const int db = t >> 4, j = t & 15;
-        const float* Ab = sAt + (16 * db) * C::AP + 16 * db;
-        float x[16];
+    // ---- T = (I + Atil)^-1 (fp32) ----
+    // Diagonal 16x16 blocks: wave d < 4 inverts I + A for its strictly lower
+    // block A as (I - A)(I + A^2)(I + A^4)(I + A^8) (A^16 = 0), four levels of
+    // wave-local fp32 tile products.  Its three scratch tiles are off-diagonal
+    // blocks of sT that are written only later.  Off-diagonal blocks by 2x2
+    // block inversion, first of the two 32x32 halves, then of the whole:
+    //   T10 = -T11 A10 T00,  T32 = -T33 A32 T22,
+    //   T_hi,lo = -T_hi (A_hi,lo T_lo)   (hi = blocks 2,3; lo = blocks 0,1).
+    // Upper blocks of sT serve as scratch and read as zero afterwards.
+    {
+        auto blk = [&](float* M, int r, int c) { return M + (16 * r) * C::AP + 16 * c; };
+        auto tload = [&](const float* M) {
+            floatx4 v;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
+            for (int r = 0; r < 4; ++r) v[r] = M[(4 * gq + r) * C::AP + li];
+            return v;
+        };
+        auto tstore = [&](float* M, floatx4 v, float sign) {
 #pragma unroll
-            for (int i = 0; i < r; ++i) acc += Ab[r * C::AP + i] * x[i];
-            x[r] = r < j ? 0.f : (r == j ? 1.f : -acc);
-        }
+            for (int r = 0; r < 4; ++r) M[(4 * gq + r) * C::AP + li] = sign * v[r];
+        };
+        auto prod = [&](floatx4& acc, const float* A, const float* B) {
+            mma_tile_f32_rowB(acc, A, C::AP, B, C::AP, 16, lane);
+        };
+        if (wave < 4) {
+            const int d = wave;
+            // scratch tiles of wave d: (0,1) (0,2) (0,3) | (1,2) (1,3) (2,3) | (2,0) (3,0) (2,1) | (3,1) (3,2) (1,0)
+            constexpr int SR[4][3] = {{0, 0, 0}, {1, 1, 2}, {2, 3, 2}, {3, 3, 1}};
+            constexpr int SC[4][3] = {{1, 2, 3}, {2, 3, 3}, {0, 0, 1}, {1, 2, 0}};
+            float* S0 = blk(sT, SR[d][0], SC[d][0]);
+            float* S1 = blk(sT, SR[d][1], SC[d][1]);
+            float* S2 = blk(sT, SR[d][2], SC[d][2]);
+            const float* Ad = blk(sAt, d, d);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(16 * db + r) * C::AP + 16 * db + j] = x[r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int rb = 1; rb < 4; ++rb) {
-        const int cb = wave;
-        float* Yw = sY + wave * 16 * C::YP;
-        if (cb < rb) {
-            floatx4 acc = zero4();
-            for (int j = cb; j < rb; ++j)
-                mma_tile_f32_rowB(acc, sAt + (16 * rb) * C::AP + 16 * j, C::AP, sT + (16 * j) * C::AP + 16 * cb,
-                                  C::AP, 16, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Yw[(4 * gq + r) * C::YP + li] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * gq + r;
+                const float x = li < row ? Ad[row * C::AP + li] : 0.f;
+                S0[row * C::AP + li] = x;                          // A
+                S1[row * C::AP + li] = (li == row ? 1.f : 0.f) - x;  // I - A
+            }
+            wave_lds_sync();
+            floatx4 m = zero4();
+            prod(m, S0, S0);  // A^2
+            tstore(S2, m, 1.f);
+            wave_lds_sync();
+            m = zero4();
+            prod(m, S2, S2);  // A^4
+            floatx4 x = tload(S1);
+            prod(x, S1, S2);  // (I - A)(I + A^2)
+            wave_lds_sync();
+            tstore(S0, m, 1.f);
+            tstore(S1, x, 1.f);
+            wave_lds_sync();
+            m = zero4();
+            prod(m, S0, S0);  // A^8
+            x = tload(S1);
+            prod(x, S1, S0);  // ... (I + A^4)
+            wave_lds_sync();
+            tstore(S2, m, 1.f);
+            tstore(S1, x, 1.f);
+            wave_lds_sync();
+            x = tload(S1);
+            prod(x, S1, S2);  // ... (I + A^8)
+            tstore(blk(sT, d, d), x, 1.f);
+            if (d == 0 || d == 2) {
+                // A_{d+1,d} T_dd, kept in S0: (0,1) for d = 0, (2,0) for d = 2
+                wave_lds_sync();
+                floatx4 y = zero4();
+                prod(y, blk(sAt, d + 1, d), blk(sT, d, d));
+                tstore(S0, y, 1.f);
+            }
         }
         __syncthreads();
-        if (cb < rb) {
+        for (int task = wave; task < 6; task += C::NW) {
             floatx4 acc = zero4();
-            mma_tile_f32_rowB(acc, sT + (16 * rb) * C::AP + 16 * rb, C::AP, Yw, C::YP, 16, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(16 * rb + 4 * gq + r) * C::AP + 16 * cb + li] = -acc[r];
+            switch (task) {
+                case 0:  // T10 = -T11 (A10 T00)
+                    prod(acc, blk(sT, 1, 1), blk(sT, 0, 1));
+                    tstore(blk(sT, 1, 0), acc, -1.f);
+                    break;
+                case 1:  // T32 = -T33 (A32 T22)
+                    prod(acc, blk(sT, 3, 3), blk(sT, 2, 0));
+                    tstore(blk(sT, 3, 2), acc, -1.f);
+                    break;
+                case 2:  // Y21 = A21 T11
+                    prod(acc, blk(sAt, 2, 1), blk(sT, 1, 1));
+                    tstore(blk(sT, 1, 2), acc, 1.f);
+                    break;
+                case 3:  // Y31 = A31 T11
+                    prod(acc, blk(sAt, 3, 1), blk(sT, 1, 1));
+                    tstore(blk(sT, 1, 3), acc, 1.f);
+                    break;
+                case 4:  // A20 T00 (first term of Y20)
+                    prod(acc, blk(sAt, 2, 0), blk(sT, 0, 0));
+                    tstore(blk(sT, 0, 2), acc, 1.f);
+                    break;
+                default:  // A30 T00 (first term of Y30)
+                    prod(acc, blk(sAt, 3, 0), blk(sT, 0, 0));
+                    tstore(blk(sT, 0, 3), acc, 1.f);
+                    break;
+            }
+        }
+        __syncthreads();
+        for (int task = wave; task < 4; task += C::NW) {
+            floatx4 acc;
+            switch (task) {
+                case 0:  // Y20 = A20 T00 + A21 T10
+                    acc = tload(blk(sT, 0, 2));
+                    prod(acc, blk(sAt, 2, 1), blk(sT, 1, 0));
+                    tstore(blk(sT, 0, 2), acc, 1.f);
+                    break;
+                case 1:  // Y30 = A30 T00 + A31 T10
+                    acc = tload(blk(sT, 0, 3));
+                    prod(acc, blk(sAt, 3, 1), blk(sT, 1, 0));
+                    tstore(blk(sT, 0, 3), acc, 1.f);
+                    break;
+                case 2:  // T21 = -T22 Y21
+                    acc = zero4();
+                    prod(acc, blk(sT, 2, 2), blk(sT, 1, 2));
+                    tstore(blk(sT, 2, 1), acc, -1.f);
+                    break;
+                default:  // T31 = -(T32 Y21 + T33 Y31)
+                    acc = zero4();
+                    prod(acc, blk(sT, 3, 2), blk(sT, 1, 2));
+                    prod(acc, blk(sT, 3, 3), blk(sT, 1, 3));
+                    tstore(blk(sT, 3, 1), acc, -1.f);
+                    break;
+            }
+        }
+        __syncthreads();
+        if (wave < 2) {
+            floatx4 acc = zero4();
+            if (wave == 0) {  // T20 = -T22 Y20
+                prod(acc, blk(sT, 2, 2), blk(sT, 0, 2));
+                tstore(blk(sT, 2, 0), acc, -1.f);
+            } else {  // T30 = -(T32 Y20 + T33 Y30)
+                prod(acc, blk(sT, 3, 2), blk(sT, 0, 2));
+                prod(acc, blk(sT, 3, 3), blk(sT, 0, 3));
+                tstore(blk(sT, 3, 0), acc, -1.f);
+            }
         }
         __syncthreads();
     }
     if (C::F16) {
         for (int idx = t; idx < CH * CH; idx += C::NT) {
             const int r = idx / CH, i = idx % CH;
-            sTh[r * THP + i] = from_f32<OT>(sT[r * C::AP + i]);
+            sTh[r * THP + i] = from_f32<OT>((i >> 4) > (r >> 4) ? 0.f : sT[r * C::AP + i]);
         }
-        __syncthreads();
+    } else {
+        for (int idx = t; idx < CH * CH; idx += C::NT) {
+            const int r = idx / CH, i = idx % CH;
+            if ((i >> 4) > (r >> 4)) sT[r * C::AP + i] = 0.f;
+        }
     }
+    __syncthreads();
 
     // ---- right-hand sides of W and Ut, channel-major: 8 tokens of each channel ----
     {

@@ -95,6 +95,15 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Orders the LDS accesses of one wave's lanes: writes before it are seen by
+// reads after it from any lane of the same wave (LDS executes a wave's
+// operations in order, so only compiler reordering has to be prevented).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 __device__ __forceinline__ floatx4 zero4() {
     floatx4 z = {0.f, 0.f, 0.f, 0.f};
     return z;
