@@ -282,31 +282,40 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     const int r0 = 8 * hb;               // first row (within the chunk)
     const int ib0 = 8 * hh;              // first row within the block
 
-    // ---- every global load first (rows past the end read the last valid row, then get zeroed) ----
+    // ---- every global load first, in order of first use: gates, then k and q,
+    // then v.  The barriers up to the off-diagonal operands order LDS only, so
+    // k, q and v stay in flight while the gate products are formed.  Rows past
+    // the end read the last valid row and are zeroed where first used.
     Pair8<IT> kk, qq, vv;
     float al[8][2];
+    float bval;
     {
         float2 lr[8];
+        size_t off[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = min(r0 + i, n - 1);
-            const size_t off = ((size_t)(tok0 + r) * H + h) * D + ch;
-            kk.load(i, k + off);
-            qq.load(i, q + off);
-            vv.load(i, v + off);
-            lr[i] = *reinterpret_cast<const float2*>(a.la + off);
+            off[i] = ((size_t)(tok0 + min(r0 + i, n - 1)) * H + h) * D + ch;
+            lr[i] = *reinterpret_cast<const float2*>(a.la + off[i]);
         }
-        if (t < CH) sBeta[t] = t < n ? a.beta[(size_t)(tok0 + t) * H + h] : 0.f;
+        // every thread loads a beta (no branch around a load); thread t < 64 stores row t
+        bval = a.beta[(size_t)(tok0 + min(t & (CH - 1), n - 1)) * H + h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kk.load(i, k + off[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qq.load(i, q + off[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vv.load(i, v + off[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const bool ok = r0 + i < n;
-            if (!ok) {
-                kk.zero(i);
-                qq.zero(i);
-                vv.zero(i);
-            }
-            al[i][0] = ok ? fast_exp(lr[i].x) : 1.f;
-            al[i][1] = ok ? fast_exp(lr[i].y) : 1.f;
+            al[i][0] = fast_exp(lr[i].x);
+            al[i][1] = fast_exp(lr[i].y);
+        }
+        // rows past the end decay by nothing (only in a sequence's last chunk; testing
+        // n first keeps the gate loads out of any per-lane branch)
+        if (n < CH) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (r0 + i >= n) al[i][0] = al[i][1] = 1.f;
         }
     }
     // half-block products, the half's first gate, and prod_{1..7} (first halves)
@@ -323,12 +332,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         *reinterpret_cast<float2*>(sX + (8 + hb) * D + ch) = make_float2(al[0][0], al[0][1]);
         *reinterpret_cast<float2*>(sX + (16 + hb) * D + ch) = make_float2(l7[0], l7[1]);
     }
+    if (t < CH) sBeta[t] = t < n ? bval : 0.f;
     // strictly-upper blocks of the staged P are zero
     for (int idx = t; idx < CH * CH; idx += C::NT) {
         const int r = idx / CH, i = idx % CH;
         if ((i >> 4) > (r >> 4)) sP[idx] = from_f32<OT>(0.f);
     }
-    __syncthreads();
+    lds_barrier();
 
     // per-channel products over blocks, half-blocks and anchors
     float PB[4][2], A0[4][2], E[2], Sfx[2], HPo[2], HP0[2], L7[2], A8[2];
@@ -352,7 +362,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         A8[e] = sX[(8 + 2 * b + 1) * D + ch + e];    // gate of the block's row 8
     }
     const float* bb = sBeta + r0;  // beta of this thread's rows (LDS broadcast reads)
-    __syncthreads();               // sX is overwritten by the operands below
+    lds_barrier();                 // sX is overwritten by the operands below
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (r0 + i >= n) {
+            kk.zero(i);
+            qq.zero(i);
+        }
 
     // ---- phase A: off-diagonal sub-blocks of Atil and P ----
     // rows 0..47  beta k e^{G_r - G_a}, blocks 1..3 (a = first row of the block)
@@ -667,6 +683,9 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     __syncthreads();
 
     // ---- right-hand sides of W and Ut, channel-major: 8 tokens of each channel ----
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (r0 + i >= n) vv.zero(i);
     {
         float F[2] = {E[0] * (hh ? HP0[0] : 1.f), E[1] * (hh ? HP0[1] : 1.f)};  // e^{G} of the row before
         float x0[8], x1[8];
