@@ -167,10 +167,8 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     // state pass of the current one (two record buffers, an auxiliary stream).  Off by
     // default: on MI355X the concurrent local pass slows the latency-bound state chain
     // more than it saves.
-    static const bool overlap_enabled = [] {
-        const char* e = getenv("KDA_OVERLAP");
-        return e && e[0] == '1';
-    }();
+    const char* ov_env = getenv("KDA_OVERLAP");  // read per call (cheap next to any launch)
+    const bool overlap_enabled = ov_env && ov_env[0] == '1';
     // one buffer for every chunk if it fits; otherwise windows of chunks
     const size_t avail = workspace_bytes - p.state_bytes;
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;

@@ -1061,11 +1061,9 @@ size_t chunk_record_bytes(int d, bool in_bf16) {
 // give more workgroups when there are few (sequence, head) pairs; wide ones
 // read each chunk record fewer times.  KDA_VALUE_SLICE (16, 32 or 64) overrides.
 int chunk_value_slice(int d, int64_t units) {
-    static const int forced = [] {
-        const char* e = getenv("KDA_VALUE_SLICE");
-        const int v = e ? atoi(e) : 0;
-        return (v == 16 || v == 32 || v == 64) ? v : 0;
-    }();
+    const char* e = getenv("KDA_VALUE_SLICE");  // read per call
+    const int v = e ? atoi(e) : 0;
+    const int forced = (v == 16 || v == 32 || v == 64) ? v : 0;
     if (forced) return forced > d ? d : forced;
     if (units <= 64) return 16;
     if (units <= 256 || d == 64) return 32;

@@ -22,7 +22,11 @@
  *    auxiliary non-blocking stream and three events (created on first use,
  *    kept until process exit, enqueueing serialised by a per-device mutex) and
  *    joins that stream back into `stream` before returning, so callers only
- *    ever synchronise their own stream.
+ *    ever synchronise their own stream.  KDA_VALUE_SLICE=16, 32 or 64
+ *    overrides the number of value columns each state-pass workgroup carries
+ *    (by default 16 for at most 64 (sequence, head) pairs, 32 up to 256, else
+ *    64; 32 for dk = 64).  Both variables are read on every call and change
+ *    scheduling only, never results beyond floating-point summation order.
  *  - Layouts are row-major and contiguous.  Tokens are [B, T, H, d] (d
  *    fastest); the recurrent state is [N, H, dk, dv] with dv fastest, rows =
  *    key channels, and the same layout serves initial, final and decode

@@ -118,13 +118,54 @@ def test_chunk_workspace_windows(kda):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     o2, S2 = run_chunk(kda, torch, d, workspace=ws)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
-    # a workspace of four chunk records: windows of four chunks (with KDA_OVERLAP=1,
-    # two alternating buffers of two chunks each)
+    # a workspace of four chunk records: windows of four chunks
     state = 2 * 128 * 128 * 4
     per_chunk = need - state
     ws2 = torch.empty(state + 4 * per_chunk, dtype=torch.uint8, device="cuda")
     o3, S3 = run_chunk(kda, torch, d, workspace=ws2)
     assert np.array_equal(o1, o3) and np.array_equal(S1, S3)
+
+
+def test_value_slice_widths_same_bits(kda, monkeypatch):
+    """Every state-pass slice width gives the same bits: value columns never interact."""
+    for dtype, D in (("bf16", 128), ("f32", 64)):
+        d = random_small(41 + D, 0, 3, D, D, dtype=dtype, init_std=0.02, lens=[70, 0, 130, 64])
+        ref = None
+        for bv in ("16", "32", "64"):
+            monkeypatch.setenv("KDA_VALUE_SLICE", bv)
+            o, S = run_chunk(kda, torch, d)
+            if ref is None:
+                ref = (o, S)
+            else:
+                assert np.array_equal(o, ref[0]) and np.array_equal(S, ref[1]), (dtype, D, bv)
+        monkeypatch.delenv("KDA_VALUE_SLICE")
+        o_ref, S_ref = oracle_chunk(d)
+        assert_close("out", ref[0], o_ref, TOL[dtype])
+        assert_close("state", ref[1], S_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("nseq,H", [(24, 4), (80, 4)])
+def test_many_units(kda, nseq, H):
+    """Enough (sequence, head) pairs for the wider default slices (32 and 64 columns)."""
+    lens = [int(x) for x in np.random.default_rng(nseq).integers(0, 150, nseq)]
+    d = random_small(nseq, 0, H, 128, 128, dtype="bf16", init_std=0.02, lens=lens)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
+def test_overlap_schedule_same_bits(kda, monkeypatch):
+    """KDA_OVERLAP=1 (two record buffers, second stream) gives the same bits as the default."""
+    d = random_small(8, 400, 2, 128, 128, dtype="bf16", init_std=0.02)
+    o1, S1 = run_chunk(kda, torch, d)
+    need = kda.workspace_size(1, 64, 2, 128, 128, torch.bfloat16, torch.float32)
+    state = 2 * 128 * 128 * 4
+    ws = torch.empty(state + 4 * (need - state), dtype=torch.uint8, device="cuda")  # 2 buffers x 2 chunks
+    monkeypatch.setenv("KDA_OVERLAP", "1")
+    o2, S2 = run_chunk(kda, torch, d, workspace=ws)
+    monkeypatch.delenv("KDA_OVERLAP")
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
 def test_chunk_deterministic(kda):
