@@ -165,15 +165,17 @@ __device__ __forceinline__ floatx4 load4<float>(const float* src) {
 // ---------------------------------------------------------------------------
 // chunk-local kernel
 // ---------------------------------------------------------------------------
-// One workgroup of 4*D threads per (head, chunk); thread t owns key channel
-// c = t % D over the 16 rows of block b = t / D.  Every global load is issued
-// first and every global store comes after the last barrier, so no barrier
-// waits on memory traffic.  LDS regions:
-//   R0  operand rows of the Atil / P sub-block products, later T (fp32) and
-//       the channel-major right-hand sides of W and Ut;
+// One workgroup of 4*D threads per (head, chunk); thread t owns the two
+// adjacent key channels 2*(t % (D/2)) and +1 over the eight rows of half-block
+// t / (D/2) (rows 8*(t/(D/2)) .. +7).  Every global load is issued first and
+// the barriers that precede the first use of k, q and v order LDS only, so
+// those loads stay in flight while the gate products are formed.  LDS regions:
+//   R0  half-block gate products (exchanged once), then the operand rows of
+//       the Atil / P sub-block products, later T (fp32) and the channel-major
+//       right-hand sides of W and Ut;
 //   R1  Atil (fp32), later T as a matrix-core operand;
 //   R2  P staged as the record stores it;
-//   R3  per-block gate products and beta.
+//   R3  beta.
 template <int D, typename OT>
 struct LocalCfg {
     static constexpr int NT = 4 * D;
