@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/kda.h"
 
@@ -93,6 +94,22 @@ const char* kda_status_string(kda_status_t st) {
     return "unknown status";
 }
 
+// KDA_CHECK=1: copy cu_seqlens to the host (synchronising `stream`) and verify
+// the preconditions the kernels rely on: cu[0] = 0, non-decreasing, cu[N] =
+// total tokens, no sequence longer than the max_seqlen the launch is sized for.
+static kda_status_t check_cu_seqlens(const int32_t* cu, const Plan& p, hipStream_t stream) {
+    std::vector<int32_t> h((size_t)p.N + 1);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (h[0] != 0 || h[(size_t)p.N] != p.tokens) return KDA_ERR_INVALID_ARG;
+    for (int64_t i = 0; i < p.N; ++i) {
+        const int64_t len = (int64_t)h[(size_t)i + 1] - h[(size_t)i];
+        if (len < 0 || len > p.max_len) return KDA_ERR_INVALID_ARG;
+    }
+    return KDA_OK;
+}
+
 static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) {
     kda_status_t st = plan_chunk(s, p);
     if (st != KDA_OK) return st;
@@ -161,6 +178,13 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
 
     const size_t per_chunk = (size_t)p.N * H * p.rec;
     if (p.N == 0) return KDA_OK;  // nothing to compute
+    if (cu_seqlens) {
+        const char* chk = getenv("KDA_CHECK");
+        if (chk && chk[0] == '1') {
+            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, static_cast<hipStream_t>(stream));
+            if (cs != KDA_OK) return cs;
+        }
+    }
     if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
         return KDA_ERR_WORKSPACE;
     // KDA_OVERLAP=1 runs the chunk-local pass of the next window concurrently with the

@@ -37,7 +37,11 @@
  *    (the chunked path also needs log_alpha >= -10 per token so that
  *    within-chunk decay ratios stay inside fp32 range); beta finite;
  *    cu_seqlens non-decreasing with cu_seqlens[0] = 0 and
- *    cu_seqlens[N] = total tokens.  With bf16 q/k/v the matrix-core
+ *    cu_seqlens[N] = total tokens, and no sequence longer than max_seqlen.
+ *    With the environment variable KDA_CHECK=1, kda_chunk_fwd copies
+ *    cu_seqlens to the host (synchronising `stream`) and returns
+ *    KDA_ERR_INVALID_ARG when one of the cu_seqlens conditions fails.
+ *    With bf16 q/k/v the matrix-core
  *    operands are staged in fp16, so |v|, state entries and outputs must
  *    stay below 6.5e4 (larger values give non-finite results, never silent
  *    garbage); q and k are expected L2-normalised per head as in the KDA

@@ -168,6 +168,23 @@ def test_overlap_schedule_same_bits(kda, monkeypatch):
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
+def test_check_mode_rejects_bad_cu_seqlens(kda, monkeypatch):
+    """KDA_CHECK=1 verifies cu_seqlens on the host; good inputs give the same bits."""
+    d = random_small(12, 0, 2, 64, 64, dtype="f32", lens=[70, 5, 130])
+    o1, S1 = run_chunk(kda, torch, d)
+    monkeypatch.setenv("KDA_CHECK", "1")
+    o2, S2 = run_chunk(kda, torch, d, max_seqlen=130)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+    with pytest.raises(kda.KdaError, match="invalid argument"):
+        run_chunk(kda, torch, d, max_seqlen=100)          # a sequence longer than max_seqlen
+    bad = dict(d, cu_seqlens=np.array([0, 75, 70, 205]))  # decreasing
+    with pytest.raises(kda.KdaError, match="invalid argument"):
+        run_chunk(kda, torch, bad, max_seqlen=200)
+    bad = dict(d, cu_seqlens=np.array([0, 70, 75, 200]))  # does not end at the token count
+    with pytest.raises(kda.KdaError, match="invalid argument"):
+        run_chunk(kda, torch, bad, max_seqlen=200)
+
+
 def test_chunk_deterministic(kda):
     d = random_small(9, 333, 4, 128, 128, dtype="bf16")
     o1, S1 = run_chunk(kda, torch, d)
