@@ -105,3 +105,11 @@ def test_decode_validation(L):
     assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
     assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
     assert f(2, 2, 64, 64, F32, F32, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """Without libkda.so the binding raises: there is no CPU or PyTorch fallback."""
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libkda.so"))
+    with pytest.raises(ImportError, match="no fallback"):
+        _lib.lib()
