@@ -217,7 +217,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp16 MFMA operands, fp32 accumulate/state",
+        "dtype": "bf16",
+        "precision": "bf16 q/k/v in; fp16 matrix-core operands; fp32 gates, accumulation, state and output",
         "data": "synthetic (seeded; q,k L2-normalised, beta=sigmoid(N), log_alpha=-s*softplus(N))",
         "config": {"workload": f"{wp.name} + {wd.name}",
                    "prefill": {"batch": 1, "seq_len": T, "heads": H, "dk": D, "dv": D, "chunk": 64,
