@@ -44,15 +44,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_bytes(tokens, heads, d, in_b=2, out_b=4, states=1):
+def prefill_bytes(tokens, heads, d, in_b=2, out_b=4, states=1, gate_per_head=False):
     """Algorithmic HBM bytes: q,k,v + fp32 log_alpha + fp32 beta + out, plus state in/out."""
-    per_th = 3 * d * in_b + 4 * d + 4 + d * out_b
+    per_th = 3 * d * in_b + 4 * (1 if gate_per_head else d) + 4 + d * out_b
     return tokens * heads * per_th + 2 * states * heads * d * d * 4
 
 
-def decode_bytes(units, d, in_b=2, out_b=4):
+def decode_bytes(units, d, in_b=2, out_b=4, gate_per_head=False):
     """State read + write, plus q,k,v, log_alpha, beta and out, per (sequence, head)."""
-    return units * (2 * d * d * 4 + 3 * d * in_b + 4 * d + 4 + d * out_b)
+    return units * (2 * d * d * 4 + 3 * d * in_b + 4 * (1 if gate_per_head else d) + 4 + d * out_b)
 
 
 def to_dev(x, torch):
@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=65536, help="tokens per head for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (tuning runs)")
+    ap.add_argument("--gate", choices=("channel", "head"), default="channel",
+                    help="channel: KDA (log_alpha [.., H, dk]); head: one gate per head (Gated DeltaNet)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -141,7 +143,8 @@ def main():
     wp, wd = WORKLOADS[2], WORKLOADS[3]
     # ---- prefill inputs (64K tokens, 32 heads) ----
     t0 = time.time()
-    d = synth.make_prefill(wp)
+    gph = args.gate == "head"
+    d = synth.make_prefill(wp, gate=args.gate)
     log(f"prefill inputs generated in {time.time() - t0:.1f}s")
     T, H, D = wp.seqlen, wp.heads, wp.dk
     q, k, v = (to_dev(d[x], torch).unsqueeze(0) for x in ("q", "k", "v"))
@@ -160,7 +163,7 @@ def main():
     state0 = to_dev(synth.make_decode_state(wd), torch)
     steps = []
     for s in range(0 if args.prefill_only else args.decode_steps):
-        st = synth.make_decode_step(wd, s)
+        st = synth.make_decode_step(wd, s, gate=args.gate)
         steps.append(tuple(to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")))
     log(f"decode inputs generated in {time.time() - t0:.1f}s")
     state = state0.clone()
@@ -199,11 +202,11 @@ def main():
 
     pre_s = float(np.median(pre_ms)) / 1e3
     tok_s = T / pre_s
-    pbytes = prefill_bytes(T, H, D)
+    pbytes = prefill_bytes(T, H, D, gate_per_head=gph)
     pflops = PAGE_FLOP_PER_TOKEN_HEAD(D) * T * H
     dec_launch_s = float(np.median(dec_ms)) / 1e3 / max(1, len(steps))
     units = wd.batch * wd.heads
-    dbytes = decode_bytes(units, D)
+    dbytes = decode_bytes(units, D, gate_per_head=gph)
     dec_gbs = dbytes / dec_launch_s / 1e9
 
     res = {
@@ -220,7 +223,8 @@ def main():
         "dtype": "bf16",
         "precision": "bf16 q/k/v in; fp16 matrix-core operands; fp32 gates, accumulation, state and output",
         "data": "synthetic (seeded; q,k L2-normalised, beta=sigmoid(N), log_alpha=-s*softplus(N))",
-        "config": {"workload": f"{wp.name} + {wd.name}",
+        "config": {"workload": f"{wp.name} + {wd.name}" + ("" if not gph else " (one gate per head)"),
+                   "gate": "per key channel (KDA)" if not gph else "per head (Gated DeltaNet)",
                    "prefill": {"batch": 1, "seq_len": T, "heads": H, "dk": D, "dv": D, "chunk": 64,
                                "in": "bf16", "out": "fp32", "init_state": "fp32 N(0,0.02^2)"},
                    "decode": {"batch": wd.batch, "heads": wd.heads, "dk": D, "dv": D,
@@ -231,13 +235,13 @@ def main():
                    "ms_per_100_steps": dec_launch_s * 1e5},
         "roofline": {"kernel": "decode_kernel<128,bf16,fp32>", "bound": "hbm", "achieved": dec_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": dec_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic_from_profiles("decode", "bytes_per_launch"),
+                     "traffic": None if gph else traffic_from_profiles("decode", "bytes_per_launch"),
                      "algorithmic_bytes_per_launch": dbytes, "launch_us": dec_launch_s * 1e6},
         "prefill_roofline": {"bound": "hbm", "achieved": pbytes / pre_s / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s", "frac": pbytes / pre_s / 1e9 / HBM_PEAK_GBS,
                              "algorithmic_bytes_per_call": pbytes,
                              "mfma_frac_page_flops": pflops / pre_s / 1e12 / BF16_DENSE_TFLOPS,
-                             "traffic": traffic_from_profiles("prefill", "bytes_per_call")},
+                             "traffic": None if gph else traffic_from_profiles("prefill", "bytes_per_call")},
         "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
                    "(model level, hardware not stated)",
     }

@@ -58,8 +58,9 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
               out_dtype=None, final_state=True, max_seqlen=None, workspace=None):
     """Chunked KDA prefill.
 
-    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16), log_alpha [B,T,H,dk] fp32,
-    beta [B,T,H] fp32; init_state [N,H,dk,dv] fp32 or None; cu_seqlens int32
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16), log_alpha [B,T,H,dk] fp32
+    (or [B,T,H]: one gate per head shared by the key channels, the scalar gate
+    of Gated DeltaNet), beta [B,T,H] fp32; init_state [N,H,dk,dv] fp32 or None; cu_seqlens int32
     [N+1] (GPU) or None.  ``final_state`` may be True (allocate), False/None
     (skip) or a tensor to write into (may be ``init_state`` itself).
     Returns (out, final_state or None).
@@ -70,7 +71,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
     dv = v.shape[-1]
     _check_dev(k, "k", q.dtype, q.shape)
     _check_dev(v, "v", q.dtype, (B, T, H, dv))
-    _check_dev(log_alpha, "log_alpha", torch.float32, (B, T, H, dk))
+    gate_per_head = log_alpha.dim() == 3
+    _check_dev(log_alpha, "log_alpha", torch.float32, (B, T, H) if gate_per_head else (B, T, H, dk))
     _check_dev(beta, "beta", torch.float32, (B, T, H))
     if cu_seqlens is not None:
         _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
@@ -94,7 +96,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
     if final_state is not None:
         _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
     shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
-                       _dtype_code(q.dtype), _dtype_code(out_dtype))
+                       _dtype_code(q.dtype), _dtype_code(out_dtype), int(gate_per_head))
     L = lib()
     need = int(L.kda_chunk_fwd_workspace_size(shape))
     if workspace is None:
@@ -111,8 +113,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
 def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
     """One recurrent KDA step for N sequences; updates ``state`` [N,H,dk,dv] in place.
 
-    q, k [N,H,dk], v [N,H,dv] (fp32 or bf16), log_alpha [N,H,dk] fp32,
-    beta [N,H] fp32.  Returns out [N,H,dv].
+    q, k [N,H,dk], v [N,H,dv] (fp32 or bf16), log_alpha [N,H,dk] fp32 (or [N,H]:
+    one gate per head), beta [N,H] fp32.  Returns out [N,H,dv].
     """
     torch = _torch()
     _check_dev(q, "q")
@@ -120,13 +122,15 @@ def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
     dv = v.shape[-1]
     _check_dev(k, "k", q.dtype, q.shape)
     _check_dev(v, "v", q.dtype, (N, H, dv))
-    _check_dev(log_alpha, "log_alpha", torch.float32, (N, H, dk))
+    gate_per_head = log_alpha.dim() == 2
+    _check_dev(log_alpha, "log_alpha", torch.float32, (N, H) if gate_per_head else (N, H, dk))
     _check_dev(beta, "beta", torch.float32, (N, H))
     _check_dev(state, "state", torch.float32, (N, H, dk, dv))
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
     _check_dev(out, "out", None, (N, H, dv))
-    st = lib().kda_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), q.data_ptr(),
+    st = lib().kda_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), int(gate_per_head),
+                               q.data_ptr(),
                                k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                                state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
     _lib.check(st, "kda_decode_step")

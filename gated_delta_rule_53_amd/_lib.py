@@ -25,7 +25,8 @@ class Shape(ctypes.Structure):
     """kda_shape_t"""
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
                 ("max_seqlen", ctypes.c_int64), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
-                ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+                ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("gate_per_head", ctypes.c_int32)]
 
 
 _LIB = None
@@ -46,7 +47,8 @@ def lib():
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_decode_step.restype = ctypes.c_int
-    L.kda_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, i32,
+                                  vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [ctypes.c_int]
     _LIB = L

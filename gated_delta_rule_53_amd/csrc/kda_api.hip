@@ -75,6 +75,7 @@ kda_status_t plan_chunk(const kda_shape_t* s, Plan& p) {
         (s->out_dtype != KDA_DTYPE_F32 && s->out_dtype != KDA_DTYPE_BF16))
         return KDA_ERR_UNSUPPORTED;
     if (s->dk != s->dv || (s->dk != 64 && s->dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (s->gate_per_head != 0 && s->gate_per_head != 1) return KDA_ERR_INVALID_ARG;
     p.d = s->dk;
     return KDA_OK;
 }
@@ -152,6 +153,7 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     const int H = s->heads, d = p.d;
     const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
     const size_t tok_bytes = (size_t)p.tokens * H * d;
+    const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok_bytes) * 4;
     const size_t state_elems = (size_t)p.N * H * d * d;
     if (p.tokens > 0) {
         if (!q || !k || !v || !log_alpha || !beta || !out) return KDA_ERR_INVALID_ARG;
@@ -166,7 +168,7 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
         return KDA_ERR_INVALID_ARG;
     const size_t out_bytes = tok_bytes * out_b;
     if (overlaps(out, out_bytes, q, tok_bytes * in_b) || overlaps(out, out_bytes, k, tok_bytes * in_b) ||
-        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, log_alpha, tok_bytes * 4) ||
+        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, log_alpha, la_bytes) ||
         overlaps(out, out_bytes, beta, (size_t)p.tokens * H * 4) ||
         overlaps(out, out_bytes, init_state, state_elems * 4) ||
         overlaps(out, out_bytes, final_state, state_elems * 4))
@@ -215,6 +217,7 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     a.k = k;
     a.v = v;
     a.la = log_alpha;
+    a.gate_per_head = s->gate_per_head;
     a.beta = beta;
     a.cu = cu_seqlens;
     a.T = s->seqlen;
@@ -244,10 +247,11 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
 }
 
 kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
-                             kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
-                             const float* log_alpha, const float* beta, float* state_inout, void* out,
-                             void* stream) {
+                             kda_dtype_t out_dtype, int32_t gate_per_head, const void* q, const void* k,
+                             const void* v, const float* log_alpha, const float* beta, float* state_inout,
+                             void* out, void* stream) {
     if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    if (gate_per_head != 0 && gate_per_head != 1) return KDA_ERR_INVALID_ARG;
     if ((in_dtype != KDA_DTYPE_F32 && in_dtype != KDA_DTYPE_BF16) ||
         (out_dtype != KDA_DTYPE_F32 && out_dtype != KDA_DTYPE_BF16))
         return KDA_ERR_UNSUPPORTED;
@@ -260,15 +264,17 @@ kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t d
     const size_t vec = (size_t)units * dk;
     const size_t in_b = dsize(in_dtype), out_b = dsize(out_dtype);
     const size_t st_bytes = (size_t)units * dk * dv * 4, out_bytes = vec * out_b;
+    const size_t la_bytes = (gate_per_head ? (size_t)units : vec) * 4;
     if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps(out, out_bytes, q, vec * in_b) ||
         overlaps(out, out_bytes, k, vec * in_b) || overlaps(out, out_bytes, v, vec * in_b) ||
-        overlaps(out, out_bytes, log_alpha, vec * 4) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
+        overlaps(out, out_bytes, log_alpha, la_bytes) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
         overlaps(state_inout, st_bytes, q, vec * in_b) || overlaps(state_inout, st_bytes, k, vec * in_b) ||
-        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, log_alpha, vec * 4) ||
+        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, log_alpha, la_bytes) ||
         overlaps(state_inout, st_bytes, beta, (size_t)units * 4))
         return KDA_ERR_INVALID_ARG;
-    hipError_t e = kda::decode_dispatch((int)units, dk, in_dtype == KDA_DTYPE_BF16, out_dtype == KDA_DTYPE_BF16, q,
-                                        k, v, log_alpha, beta, state_inout, out, static_cast<hipStream_t>(stream));
+    hipError_t e = kda::decode_dispatch((int)units, dk, in_dtype == KDA_DTYPE_BF16, out_dtype == KDA_DTYPE_BF16,
+                                        gate_per_head != 0, q, k, v, log_alpha, beta, state_inout, out,
+                                        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -294,10 +294,20 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     {
         float2 lr[8];
         size_t off[8];
+        if (a.gate_per_head) {  // one gate per (token, head), shared by every key channel
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            off[i] = ((size_t)(tok0 + min(r0 + i, n - 1)) * H + h) * D + ch;
-            lr[i] = *reinterpret_cast<const float2*>(a.la + off[i]);
+            for (int i = 0; i < 8; ++i) {
+                const size_t th = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
+                off[i] = th * D + ch;
+                const float g = a.la[th];
+                lr[i] = make_float2(g, g);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                off[i] = ((size_t)(tok0 + min(r0 + i, n - 1)) * H + h) * D + ch;
+                lr[i] = *reinterpret_cast<const float2*>(a.la + off[i]);
+            }
         }
         // every thread loads a beta (no branch around a load); thread t < 64 stores row t
         bval = a.beta[(size_t)(tok0 + min(t & (CH - 1), n - 1)) * H + h];

@@ -24,7 +24,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
                                                      const IT* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
                                                      const float* __restrict__ beta, float* __restrict__ state,
-                                                     OUT* __restrict__ out) {
+                                                     OUT* __restrict__ out, int gate_per_head) {
     constexpr int CG = D / 4;       // float4 column groups
     constexpr int RG = 256 / CG;    // row groups
     constexpr int RPT = D / RG;     // rows per thread
@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
     __shared__ float s_red[4][CG][9];
     const size_t vec = (size_t)unit * D;
     if (t < D) {
-        s_alpha[t] = fast_exp(log_alpha[vec + t]);
+        s_alpha[t] = fast_exp(gate_per_head ? log_alpha[unit] : log_alpha[vec + t]);
         s_k[t] = to_f32(k[vec + t]);
         s_q[t] = to_f32(q[vec + t]);
         s_v[t] = to_f32(v[vec + t]);
@@ -123,18 +123,19 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
 }
 
 template <int D, typename IT, typename OUT>
-hipError_t launch_decode(int units, const void* q, const void* k, const void* v, const float* la,
+hipError_t launch_decode(int units, bool gph, const void* q, const void* k, const void* v, const float* la,
                          const float* beta, float* state, void* out, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<D, IT, OUT>), dim3(units), dim3(256), 0, st,
                        static_cast<const IT*>(q), static_cast<const IT*>(k), static_cast<const IT*>(v), la,
-                       beta, state, static_cast<OUT*>(out));
+                       beta, state, static_cast<OUT*>(out), gph ? 1 : 0);
     return hipGetLastError();
 }
 
-hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
-                           const void* v, const float* la, const float* beta, float* state, void* out,
-                           hipStream_t st) {
-#define KDA_DEC(DD, IT, OT) return launch_decode<DD, IT, OT>(units, q, k, v, la, beta, state, out, st)
+hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
+                           const void* k, const void* v, const float* la, const float* beta, float* state,
+                           void* out, hipStream_t st) {
+#define KDA_DEC(DD, IT, OT) \
+    return launch_decode<DD, IT, OT>(units, gate_per_head, q, k, v, la, beta, state, out, st)
     if (d == 128) {
         if (in_bf16) {
             if (out_bf16) KDA_DEC(128, bf16_t, bf16_t);

@@ -16,6 +16,7 @@ struct ChunkArgs {
     const int32_t* cu;  // packed sequence offsets, or null for a dense batch
     int64_t T;          // dense: tokens per sequence
     int H;
+    int gate_per_head;  // log_alpha is [tokens, H] (one gate per head) instead of [tokens, H, D]
     int N;       // sequences
     int Wc;      // chunks per sequence per window
     int win;     // window index
@@ -39,8 +40,8 @@ size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
                           const Overlap& ov, hipStream_t st);
-hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
-                           const void* v, const float* la, const float* beta, float* state, void* out,
-                           hipStream_t st);
+hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
+                           const void* k, const void* v, const float* la, const float* beta, float* state,
+                           void* out, hipStream_t st);
 
 }  // namespace kda

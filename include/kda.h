@@ -80,7 +80,12 @@ typedef enum {
  *               the workspace query treats the shape as varlen iff num_seqs > 0)
  *   max_seqlen  varlen: an upper bound on the longest sequence (host value,
  *               used to size the launch); 0 means "use seqlen"
- *   heads, dk, dv, in_dtype (q/k/v), out_dtype (out) */
+ *   heads, dk, dv, in_dtype (q/k/v), out_dtype (out)
+ *   gate_per_head  0: log_alpha holds one gate per key channel, [.., H, dk]
+ *               (KDA); 1: one gate per head shared by all key channels,
+ *               [.., H] (the scalar forget gate of Gated DeltaNet, "Kimi
+ *               Linear" page, "Background: from the delta rule to gated
+ *               DeltaNet") */
 typedef struct {
     int32_t batch;
     int64_t seqlen;
@@ -91,6 +96,7 @@ typedef struct {
     int32_t dv;
     kda_dtype_t in_dtype;
     kda_dtype_t out_dtype;
+    int32_t gate_per_head;
 } kda_shape_t;
 
 /* Bytes of scratch device memory kda_chunk_fwd needs for `s` (0 if `s` is
@@ -104,6 +110,7 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s);
  *   q, k        [B, T, H, dk]  in_dtype
  *   v           [B, T, H, dv]  in_dtype
  *   log_alpha   [B, T, H, dk]  fp32, natural log of the per-channel gate
+ *               ([B, T, H] when s->gate_per_head = 1)
  *   beta        [B, T, H]      fp32
  *   init_state  [N, H, dk, dv] fp32, or NULL for a zero initial state
  *   cu_seqlens  int32 [N+1] device array of packed sequence offsets, or NULL
@@ -124,11 +131,13 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
  * update itself).  Per (sequence, head), with alpha = exp(log_alpha):
  *     S <- Diag(alpha) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T q.
  *   q, k        [batch, H, dk] in_dtype;   v [batch, H, dv] in_dtype
- *   log_alpha   [batch, H, dk] fp32;       beta [batch, H] fp32
+ *   log_alpha   [batch, H, dk] fp32 ([batch, H] when gate_per_head = 1,
+ *               one gate shared by the key channels); beta [batch, H] fp32
  *   state_inout [batch, H, dk, dv] fp32, read and overwritten in place
  *   out         [batch, H, dv] out_dtype; must not alias any other argument */
 kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv,
-                             kda_dtype_t in_dtype, kda_dtype_t out_dtype, const void* q,
+                             kda_dtype_t in_dtype, kda_dtype_t out_dtype, int32_t gate_per_head,
+                             const void* q,
                              const void* k, const void* v, const float* log_alpha,
                              const float* beta, float* state_inout, void* out, void* stream);
 

@@ -74,7 +74,9 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     """fp64 token-by-token KDA forward.
 
     Inputs (numpy): q, k [T, H, dk] and v [T, H, dv] as float32 or uint16
-    (bf16 bits); log_alpha float32 [T, H, dk]; beta float32 [T, H];
+    (bf16 bits); log_alpha float32 [T, H, dk], or [T, H] for one gate per head
+    shared by every key channel (the scalar gate of Gated DeltaNet: it is the
+    same recurrence with the gate broadcast over dk); beta float32 [T, H];
     init_state [N, H, dk, dv] (widened to fp64) or None; cu_seqlens int [N+1] or None
     (one sequence).  A leading batch axis [B, T, H, d] is accepted when
     cu_seqlens is None and is treated as B sequences of length T.
@@ -100,6 +102,8 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     want = np.uint16 if bf16 else np.float32
     q, k, v = (np.ascontiguousarray(x, dtype=want) for x in (q, k, v))
     la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    if la.ndim == 2:
+        la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], (T, H, dk)))
     be = np.ascontiguousarray(beta, dtype=np.float32).reshape(T, H)
     init = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float64)
     if init is not None:
@@ -119,7 +123,7 @@ def decode_steps(state, steps, threads=None, mutant: int = 0):
     """Consecutive one-token updates of N independent sequences.
 
     ``state`` [N, H, dk, dv] (any float dtype); ``steps`` a list of dicts with
-    q, k [N, H, dk], v [N, H, dv], beta [N, H], log_alpha [N, H, dk].  Each
+    q, k [N, H, dk], v [N, H, dv], beta [N, H], log_alpha [N, H, dk] or [N, H].  Each
     step is the recurrence over N one-token sequences starting from the
     current state, which is carried in fp64 between steps.  Returns (list of
     fp64 outputs [N, H, dv], fp64 final state).

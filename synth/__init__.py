@@ -39,7 +39,7 @@ import numpy as np
 BLOCK = 16384  # tokens per independently seeded block
 
 # tensor ids used in the spawn keys
-_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "log_alpha": 4, "init": 5, "lengths": 6}
+_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "log_alpha": 4, "init": 5, "lengths": 6, "log_alpha_head": 7}
 
 
 @dataclass(frozen=True)
@@ -148,11 +148,13 @@ def _unit_rows(dtype):
 
 
 def gen_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_scale: float,
-               heads=None, threads=None) -> dict:
+               heads=None, threads=None, gate: str = "channel") -> dict:
     """Token inputs for T packed tokens: q, k [T,Hs,dk], v [T,Hs,dv], beta [T,Hs], log_alpha [T,Hs,dk].
 
     ``heads`` selects a subset of heads (Hs = len(heads)); values are identical
-    to the same heads of the full draw.
+    to the same heads of the full draw.  ``gate="head"`` draws one gate per
+    (token, head) instead, log_alpha [T,Hs] (the scalar gate of Gated
+    DeltaNet), from its own stream with the same distribution.
     """
     heads = list(range(H)) if heads is None else list(heads)
     Hs = len(heads)
@@ -164,8 +166,9 @@ def gen_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_sca
         "k": np.empty((T, Hs, dk), qk_dt),
         "v": np.empty((T, Hs, dv), qk_dt),
         "beta": np.empty((T, Hs), np.float32),
-        "log_alpha": np.empty((T, Hs, dk), np.float32),
+        "log_alpha": np.empty((T, Hs, dk) if gate == "channel" else (T, Hs), np.float32),
     }
+    assert gate in ("channel", "head"), gate
     _fill_blocks(seed, "q", T, heads, dk, lambda r, n: unit(r, n, dk), out["q"], threads)
     _fill_blocks(seed, "k", T, heads, dk, lambda r, n: unit(r, n, dk), out["k"], threads)
 
@@ -180,10 +183,13 @@ def gen_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_sca
     _fill_blocks(seed, "beta", T, heads, None, bfn, out["beta"], threads)
 
     def afn(r, n):
-        z = r.standard_normal((n, dk))
+        z = r.standard_normal((n, dk) if gate == "channel" else n)
         sp = np.logaddexp(0.0, z)  # softplus
         return (-gate_scale * sp).astype(np.float32)
-    _fill_blocks(seed, "log_alpha", T, heads, dk, afn, out["log_alpha"], threads)
+    if gate == "channel":
+        _fill_blocks(seed, "log_alpha", T, heads, dk, afn, out["log_alpha"], threads)
+    else:
+        _fill_blocks(seed, "log_alpha_head", T, heads, None, afn, out["log_alpha"], threads)
     return out
 
 
@@ -227,7 +233,7 @@ def cu_from_lengths(lens) -> np.ndarray:
 # whole workloads
 # ----------------------------------------------------------------------------
 
-def make_prefill(w: Workload, heads=None, threads=None) -> dict:
+def make_prefill(w: Workload, heads=None, threads=None, gate: str = "channel") -> dict:
     """Inputs for a "prefill" or "varlen" workload in packed token layout [T_total, H, d].
 
     Returns q, k, v, beta, log_alpha, cu_seqlens (int64 [N+1]) and init (or None).
@@ -241,14 +247,14 @@ def make_prefill(w: Workload, heads=None, threads=None) -> dict:
         raise ValueError(w.kind)
     cu = cu_from_lengths(lens)
     T = int(cu[-1])
-    d = gen_tokens(w.seed, T, w.heads, w.dk, w.dv, w.dtype, w.gate_scale, heads=heads, threads=threads)
+    d = gen_tokens(w.seed, T, w.heads, w.dk, w.dv, w.dtype, w.gate_scale, heads=heads, threads=threads, gate=gate)
     d["cu_seqlens"] = cu
     d["init"] = None if w.init_std is None else gen_states(
         w.seed, len(lens), w.heads, w.dk, w.dv, w.init_std, heads=heads)
     return d
 
 
-def make_decode_step(w: Workload, step: int, heads=None) -> dict:
+def make_decode_step(w: Workload, step: int, heads=None, gate: str = "channel") -> dict:
     """Inputs of one decode step: q, k [N,H,dk], v [N,H,dv], beta [N,H], log_alpha [N,H,dk].
 
     Step s draws token index s of each of the N sequences, laid out as a packed
@@ -257,7 +263,7 @@ def make_decode_step(w: Workload, step: int, heads=None) -> dict:
     assert w.kind == "decode"
     # each step is its own seed family so steps can be regenerated alone
     d = gen_tokens(w.seed * 1000003 + 7919 * (step + 1), w.batch, w.heads, w.dk, w.dv, w.dtype,
-                   w.gate_scale, heads=heads)
+                   w.gate_scale, heads=heads, gate=gate)
     return d
 
 
@@ -267,11 +273,11 @@ def make_decode_state(w: Workload, heads=None) -> np.ndarray:
 
 def random_small(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "f32",
                  gate_scale: float = 0.05, init_std: float | None = 0.02, batch: int = 1,
-                 lens=None) -> dict:
+                 lens=None, gate: str = "channel") -> dict:
     """Small ad-hoc workload (tests): same recipe, arbitrary shape; ``lens`` gives varlen."""
     lens = np.full(batch, T, np.int64) if lens is None else np.asarray(lens, np.int64)
     cu = cu_from_lengths(lens)
-    d = gen_tokens(seed, int(cu[-1]), H, dk, dv, dtype, gate_scale, threads=1)
+    d = gen_tokens(seed, int(cu[-1]), H, dk, dv, dtype, gate_scale, threads=1, gate=gate)
     d["cu_seqlens"] = cu
     d["init"] = None if init_std is None else gen_states(seed, len(lens), H, dk, dv, init_std)
     return d

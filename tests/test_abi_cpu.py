@@ -45,8 +45,8 @@ def test_status_strings(L):
     assert _lib.status_string(99) == "unknown status"
 
 
-def _shape(B=1, T=256, N=0, maxT=0, H=2, dk=64, dv=64, i=F32, o=F32):
-    return _lib.Shape(B, T, N, maxT, H, dk, dv, i, o)
+def _shape(B=1, T=256, N=0, maxT=0, H=2, dk=64, dv=64, i=F32, o=F32, gph=0):
+    return _lib.Shape(B, T, N, maxT, H, dk, dv, i, o, gph)
 
 
 def test_workspace_size(L):
@@ -91,20 +91,26 @@ def test_chunk_fwd_validation(L):
     assert _fwd(L, s, ws=None) == WORKSPACE
     assert _fwd(L, s, ws=10 * A, wsb=1024) == WORKSPACE
     assert _fwd(L, s, ws=10 * A + 8, wsb=1 << 30) == WORKSPACE  # misaligned workspace
+    assert _fwd(L, _shape(gph=2)) == INVALID                    # gate layout flag is 0 or 1
+    # out right after log_alpha: overlaps a per-channel gate [T,H,dk] but not a per-head one [T,H]
+    la_head = 256 * 2 * 4
+    assert _fwd(L, s, la=4 * A, out=4 * A + la_head) == INVALID
+    assert _fwd(L, _shape(gph=1), la=4 * A, out=4 * A + la_head) == WORKSPACE  # passes validation
 
 
 def test_decode_validation(L):
     f = L.kda_decode_step
-    assert f(0, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
-    assert f(-1, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == INVALID
-    assert f(2, 2, 96, 96, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 128, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 64, 5, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 64, F32, F32, None, A, A, A, A, A, A, None) == INVALID
+    assert f(0, 2, 64, 64, F32, F32, 0, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
+    assert f(-1, 2, 64, 64, F32, F32, 0, A, A, A, A, A, A, A, None) == INVALID
+    assert f(2, 2, 96, 96, F32, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 128, F32, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 64, 5, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 64, F32, F32, 0, None, A, A, A, A, A, A, None) == INVALID
     st, out = 8 * A, 12 * A
-    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
-    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
-    assert f(2, 2, 64, 64, F32, F32, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state
+    assert f(2, 2, 64, 64, F32, F32, 0, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
+    assert f(2, 2, 64, 64, F32, F32, 0, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
+    assert f(2, 2, 64, 64, F32, F32, 0, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state
+    assert f(2, 2, 64, 64, F32, F32, 3, A, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # bad gate flag
 
 
 def test_missing_library_fails_loudly(monkeypatch):

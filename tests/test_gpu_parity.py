@@ -329,3 +329,40 @@ def test_workload4_varlen_1m(kda):
     o_ref, S_ref = oracle_chunk(d)
     assert_close("out", o, o_ref, TOL["bf16"])
     assert_close("state", S, S_ref, TOL["bf16"])
+
+
+# ----------------------------------------------------------------------------
+# scalar (per-head) gate: the Gated DeltaNet special case on the same kernels
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,D,dtype,lens", [(300, 3, 128, "bf16", None), (130, 2, 64, "f32", None),
+                                             (0, 3, 128, "bf16", [1, 0, 64, 200, 63, 129]),
+                                             (0, 2, 64, "f32", [0, 5, 64, 65, 130])])
+def test_scalar_gate_chunk(kda, T, H, D, dtype, lens):
+    d = random_small(T * 3 + D + 17, T, H, D, D, dtype=dtype, lens=lens, gate="head")
+    assert d["log_alpha"].ndim == 2
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL[dtype])
+    assert_close("state", S, S_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("N,H,D,dtype", [(5, 3, 64, "f32"), (16, 4, 128, "bf16")])
+def test_scalar_gate_decode(kda, N, H, D, dtype):
+    st = synth.gen_tokens(23 + N, N, H, D, D, dtype, 0.05, gate="head")
+    S0 = synth.gen_states(23 + N, N, H, D, D, 0.5)
+    args = [to_dev(st[x], torch) for x in ("q", "k", "v", "log_alpha", "beta")]
+    state = to_dev(S0, torch)
+    out = kda.decode_step(*args, state, out_dtype=torch.float32).cpu().numpy()
+    o, S = oracle.decode_steps(S0, [st])
+    assert_close("out", out, o[0], DECODE_TOL)
+    assert_close("state", state.cpu().numpy(), S, DECODE_TOL)
+
+
+def test_scalar_gate_prefill_workload(kda):
+    """The 4K-token, 32-head bf16 prefill with one gate per (token, head)."""
+    d = synth.make_prefill(WORKLOADS[1], gate="head")
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])

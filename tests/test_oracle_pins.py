@@ -248,6 +248,17 @@ def test_p7_shared_gate_is_gated_delta_rule(oracle_lib):
     assert _close(o, og, 1e-13) and _close(S, Sg, 1e-13)
 
 
+def test_p7_per_head_gate_input(oracle_lib):
+    """A [T, H] gate (one per head) is the scalar-gate gated delta rule, coded independently."""
+    q, k, v, la, b, S0 = _rand(15, 50, 7, 4, gate=0.4)
+    g = la[:, 0].copy()
+    init = np.asarray(S0, np.float64)[None, None]
+    ex = lambda x: x[:, None, ...]
+    o, S = oracle.recurrent(ex(q), ex(k), ex(v), g[:, None], b[:, None], init, None, threads=1)
+    og, Sg = _gated_delta_scalar(*_f64(q, k, v), np.exp(g.astype(np.float64)), b.astype(np.float64), S0)
+    assert _close(o[:, 0], og, 1e-13) and _close(S[0, 0], Sg, 1e-13)
+
+
 def test_p8_overwrite_repeated_key(oracle_lib):
     # one-hot keys, dyadic values: exact
     r = np.random.default_rng(15)

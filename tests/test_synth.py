@@ -65,3 +65,18 @@ def test_workload_table():
     assert WORKLOADS[4].kind == "varlen" and WORKLOADS[4].num_seqs == 16
     d = synth.make_prefill(WORKLOADS[0])
     assert d["q"].shape == (256, 2, 64) and d["q"].dtype == np.float32 and d["init"] is None
+
+
+def test_per_head_gate_draw():
+    """gate="head" draws log_alpha [T, H] from its own stream with the KDA gate's distribution."""
+    import synth
+    d = synth.gen_tokens(3, 5000, 3, 16, 16, "f32", 0.05, threads=1, gate="head")
+    la = d["log_alpha"]
+    assert la.shape == (5000, 3) and la.dtype == np.float32
+    assert (la <= 0).all() and np.isfinite(la).all()
+    # -0.05 * softplus(N(0,1)) has mean -0.05 * 0.8066 (E softplus(Z) for Z ~ N(0,1))
+    assert abs(la.mean() / -0.05 - 0.8066) < 0.02
+    # q, k, v and beta are the same draws as with per-channel gates
+    d2 = synth.gen_tokens(3, 5000, 3, 16, 16, "f32", 0.05, threads=1)
+    for x in ("q", "k", "v", "beta"):
+        assert np.array_equal(d[x], d2[x])
