@@ -111,6 +111,11 @@ static kda_status_t check_cu_seqlens(const int32_t* cu, const Plan& p, hipStream
     return KDA_OK;
 }
 
+// Bytes of one per-segment state array [units, G, d, d] fp32 (256-aligned).
+static size_t segment_bytes(const Plan& p, int heads, int G) {
+    return align256((size_t)p.N * heads * G * p.d * p.d * sizeof(float));
+}
+
 static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) {
     kda_status_t st = plan_chunk(s, p);
     if (st != KDA_OK) return st;
@@ -137,6 +142,11 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
     if (per_chunk == 0) return p.state_bytes + 256;
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    const int64_t units = p.N * s->heads;
+    int sc = 0;
+    const int G = kda::chunk_segments(p.d, kda::chunk_value_slice(p.d, units), units, p.max_chunks, sc);
+    if (G > 0)  // sequence-parallel state pass: every record plus three per-segment state blocks
+        return p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G);
     if ((size_t)all * per_chunk <= RECORD_BUDGET) return p.state_bytes + (size_t)all * per_chunk;
     int64_t wc = (int64_t)(RECORD_BUDGET / 2 / per_chunk);
     if (wc < 1) wc = 1;
@@ -195,12 +205,19 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     // more than it saves.
     const char* ov_env = getenv("KDA_OVERLAP");  // read per call (cheap next to any launch)
     const bool overlap_enabled = ov_env && ov_env[0] == '1';
-    // one buffer for every chunk if it fits; otherwise windows of chunks
+    // Few (sequence, head) pairs and a workspace for every record: the
+    // sequence-parallel state pass.  Otherwise one buffer for every chunk if it
+    // fits, else windows of chunks.
     const size_t avail = workspace_bytes - p.state_bytes;
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    const int bv = kda::chunk_value_slice(d, p.N * H);
+    int sc = 0;
+    int G = overlap_enabled ? 0 : kda::chunk_segments(d, bv, p.N * H, p.max_chunks, sc);
+    const size_t segb = G > 0 ? segment_bytes(p, H, G) : 0;
+    if (G > 0 && avail < (size_t)all * per_chunk + 3 * segb) G = 0;  // workspace too small: windows
     int64_t wc;
     bool two = false;
-    if ((size_t)all * per_chunk <= avail) {
+    if ((size_t)all * per_chunk <= avail || G > 0) {
         wc = all;
     } else if (overlap_enabled && avail >= 2 * per_chunk) {
         wc = (int64_t)(avail / 2 / per_chunk);
@@ -231,7 +248,14 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     a.rec_bytes = p.rec;
     a.init = init_state;
     a.out = out;
-    const int bv = kda::chunk_value_slice(d, p.N * H);
+    if (G > 0) {
+        a.G = G;
+        a.Sc = sc;
+        unsigned char* sb = a.rec + (size_t)all * per_chunk;
+        a.seg_B = reinterpret_cast<float*>(sb);
+        a.seg_M = reinterpret_cast<float*>(sb + segb);
+        a.seg_init = reinterpret_cast<float*>(sb + 2 * segb);
+    }
     kda::Overlap ov;  // defaults: everything on the caller's stream
     DeviceResources* res = two && nwin64 > 1 ? device_resources() : nullptr;
     std::unique_lock<std::mutex> lock;

@@ -39,6 +39,8 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace kda {
 
 __device__ __forceinline__ void seq_bounds(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
@@ -845,7 +847,16 @@ struct Frag<float> {
     }
 };
 
-template <int D, int BV, typename OT, typename OUT>
+// MODE 0: one window of chunks, state carried in state_buf between windows.
+// MODE 1 (sequence-parallel, first pass): workgroup (unit, slice, segment g)
+//   runs segment g's chunks from a zero state and writes the end state to
+//   seg_B; slices D/BV .. 2D/BV-1 instead carry the dk columns of the
+//   segment's transition product, starting from the identity with Ut = 0
+//   (each column obeys S <- (Diag(gamma) - Kh^T W) S), written to seg_M.  No
+//   outputs.
+// MODE 2 (second pass): each segment from its true initial state (seg_init),
+//   forming the outputs; the final state is written by the combine kernel.
+template <int D, int BV, typename OT, typename OUT, int MODE = 0>
 __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     using R = Rec<D, OT>;
     using FR = Frag<OT>;
@@ -862,31 +873,44 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     __shared__ __align__(16) OT sS[2][BV * SP];
     __shared__ __align__(16) OT sU[2][BV * UP];
 
+    constexpr int ZS = D / BV;                   // slices of the value columns
+    constexpr int Z = MODE == 1 ? 2 * ZS : ZS;  // the first segment pass also carries the transition product
     const int H = a.H;
     const int NH = a.N * H;
-    const int u = blockIdx.x % NH, z = blockIdx.x / NH;
+    const int u = blockIdx.x % NH, z = (blockIdx.x / NH) % Z;
+    const int seg = MODE == 0 ? 0 : (int)(blockIdx.x / NH) / Z;
+    const bool mslice = MODE == 1 && z >= ZS;   // a slice of the transition product
     const int s = u / H, h = u % H;
     int64_t tb, L;
     seq_bounds(a, s, tb, L);
     const int nchunks = (int)((L + CH - 1) / CH);
-    const int jb = a.win * a.Wc;
-    const int je = min(nchunks, jb + a.Wc);
-    if (jb >= je && a.win > 0) return;
+    const int jb = MODE == 0 ? a.win * a.Wc : seg * a.Sc;
+    const int je = min(nchunks, MODE == 0 ? jb + a.Wc : jb + a.Sc);
+    if (MODE == 0 ? (jb >= je && a.win > 0) : jb >= je) return;
+    const int jrec0 = MODE == 0 ? jb : 0;        // first chunk held by the record buffer
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const bool chain = wave < 4;
     const int w = wave & 3;
     const int gq = lane >> 4, li = lane & 15;
-    const int col0 = z * BV;
+    const int col0 = (mslice ? z - ZS : z) * BV;
     OUT* out = static_cast<OUT*>(a.out);
 
     auto rec_of = [&](int j) {
-        return a.rec + ((size_t)(s * a.Wc + (j - jb)) * H + h) * a.rec_bytes;
+        return a.rec + ((size_t)(s * a.Wc + (j - jrec0)) * H + h) * a.rec_bytes;
     };
     floatx4 Sacc[RT][CT];
     if (chain) {
-        const float* src = a.win == 0 ? a.init : a.state_buf;
+        const float* src;
+        if (MODE == 0) {
+            src = a.win == 0 ? a.init : a.state_buf;
+            if (src) src += (size_t)u * D * D;
+        } else if (MODE == 1) {
+            src = nullptr;  // zero state, or the identity for the transition product
+        } else {
+            src = a.seg_init + ((size_t)u * a.G + seg) * D * D;
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -894,7 +918,8 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
-                    Sacc[rt][ct][r] = src ? src[((size_t)u * D + row) * D + col0 + 16 * ct + li] : 0.f;
+                    const int col = col0 + 16 * ct + li;
+                    Sacc[rt][ct][r] = src ? src[(size_t)row * D + col] : (mslice && row == col ? 1.f : 0.f);
                 }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -918,8 +943,14 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
             // one dword per lane (a 16-byte load per lane would move 16x the bytes gamma has)
             f.G = reinterpret_cast<const float*>(rec + R::GAM)[w * (D / 4) + lane % (D / 4)];
             const OT* rUt = reinterpret_cast<const OT*>(rec + R::UT);
+            // the transition product sees Ut = 0 (scaled, so the load stays unconditional)
+            const float umask = mslice ? 0.f : 1.f;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) f.U[ct] = load4<OT>(rUt + ((size_t)w * D + col0 + 16 * ct + li) * 16 + 4 * gq);
+            for (int ct = 0; ct < CT; ++ct) {
+                f.U[ct] = load4<OT>(rUt + ((size_t)w * D + col0 + 16 * ct + li) * 16 + 4 * gq);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) f.U[ct][r] *= umask;
+            }
         };
         auto loadK = [&](ChainBuf& f, int j) {
             using FO = FragOrder<OT>;
@@ -981,6 +1012,11 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                     if (j < je) step(buf[p], buf[(p + RING - 1) % RING], jn, j);
                 }
             }
+        }
+    } else if constexpr (MODE == 1) {
+        for (int j = jb; j < je; ++j) {  // no outputs in this pass; keep the barrier count
+            lds_barrier();
+            lds_barrier();
         }
     } else {
         // outputs: Qg and P of one chunk
@@ -1048,7 +1084,9 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
         }
     }
 
-    if (chain) {
+    if (chain && MODE != 2) {
+        float* dst = MODE == 0 ? a.state_buf + (size_t)u * D * D
+                               : (mslice ? a.seg_M : a.seg_B) + ((size_t)u * a.G + seg) * D * D;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1056,9 +1094,53 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = w * (D / 4) + 16 * rt + 4 * gq + r;
-                    a.state_buf[((size_t)u * D + row) * D + col0 + 16 * ct + li] = Sacc[rt][ct][r];
+                    dst[(size_t)row * D + col0 + 16 * ct + li] = Sacc[rt][ct][r];
                 }
     }
+}
+
+// Sequence-parallel state pass, combine step: one workgroup per (unit, 16
+// value columns).  S_0 is the initial state (or 0); for each segment g,
+// seg_init[g] = S_g and, if the segment holds chunks, S_{g+1} = M_g S_g + B_g
+// (fp32).  The final state S_G goes to state_buf.
+template <int D>
+__global__ void __launch_bounds__(256) chunk_segment_combine_kernel(ChunkArgs a) {
+    constexpr int TPR = 256 / D;    // threads per state row
+    constexpr int CPT = 16 / TPR;   // columns per thread
+    __shared__ float sS[D][16];
+    const int u = blockIdx.x, c0 = 16 * blockIdx.y;
+    const int t = threadIdx.x, row = t / TPR, cb = (t % TPR) * CPT;
+    int64_t tb, L;
+    seq_bounds(a, u / a.H, tb, L);
+    const int nchunks = (int)((L + CH - 1) / CH);
+    float x[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) x[c] = a.init ? a.init[((size_t)u * D + row) * D + c0 + cb + c] : 0.f;
+    for (int g = 0; g < a.G; ++g) {
+        const size_t blk = ((size_t)u * a.G + g) * D * D;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            a.seg_init[blk + (size_t)row * D + c0 + cb + c] = x[c];
+            sS[row][cb + c] = x[c];
+        }
+        __syncthreads();
+        if (g * a.Sc < nchunks) {  // uniform
+            float y[CPT];
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) y[c] = a.seg_B[blk + (size_t)row * D + c0 + cb + c];
+            const float* Mr = a.seg_M + blk + (size_t)row * D;
+            for (int k = 0; k < D; ++k) {
+                const float m = Mr[k];
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) y[c] += m * sS[k][cb + c];
+            }
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) x[c] = y[c];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) a.state_buf[((size_t)u * D + row) * D + c0 + cb + c] = x[c];
 }
 
 // ---------------------------------------------------------------------------
@@ -1068,6 +1150,9 @@ size_t chunk_record_bytes(int d, bool in_bf16) {
     if (d == 128) return in_bf16 ? Rec<128, _Float16>::BYTES : Rec<128, float>::BYTES;
     return in_bf16 ? Rec<64, _Float16>::BYTES : Rec<64, float>::BYTES;
 }
+
+// Value-column slice of the sequence-parallel state pass.
+constexpr int SEGMENT_BV = 16;
 
 // Width of the value-column slice each state workgroup carries.  Narrow slices
 // give more workgroups when there are few (sequence, head) pairs; wide ones
@@ -1113,8 +1198,49 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
     return hipSuccess;
 }
 
+// Sequence-parallel state pass: all records in one buffer (a.win = 0, a.Wc =
+// every chunk), a.G segments of a.Sc chunks per sequence.
+template <int D, typename IT, typename OT, typename OUT>
+static hipError_t run_segments(const ChunkArgs& a, hipStream_t st) {
+    using C = LocalCfg<D, OT>;
+    constexpr int BV = SEGMENT_BV;
+    const int NH = a.N * a.H;
+    hipError_t e;
+    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 1>), dim3(NH * 2 * (D / BV) * a.G), dim3(512), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_segment_combine_kernel<D>), dim3(NH, D / 16), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 2>), dim3(NH * (D / BV) * a.G), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks_per_segment) {
+    chunks_per_segment = 0;
+    if (bv != SEGMENT_BV || max_chunks < 2) return 0;
+    const char* e = getenv("KDA_SEGMENTS");  // read per call: "0" turns the sequence-parallel pass off
+    int64_t G;
+    if (e && e[0] >= '0' && e[0] <= '9') {
+        G = atoi(e);
+    } else {
+        // Measured on MI355X at 64K tokens: with at most 32 state-pass workgroups
+        // (4 heads of one sequence) the split pays, best at 128-256 workgroups in
+        // the second pass and no more than 16 segments; at 64 it no longer does.
+        const int64_t wgs = units * (d / bv);  // state-pass workgroups of the windowed schedule
+        if (wgs > 32 || max_chunks < 32) return 0;
+        G = std::min<int64_t>(std::min<int64_t>(16, 256 / wgs), max_chunks / 16);
+    }
+    G = std::min<int64_t>(G, max_chunks);
+    if (G < 2) return 0;
+    const int64_t sc = (max_chunks + G - 1) / G;
+    chunks_per_segment = (int)sc;
+    return (int)((max_chunks + sc - 1) / sc);
+}
+
 template <int D, typename IT, typename OT, typename OUT>
 static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, const Overlap& ov, hipStream_t st) {
+    if (a.G > 0) return run_segments<D, IT, OT, OUT>(a, st);
     if (bv == 16) return run_windows<D, IT, OT, OUT, 16>(a, nwin, ov, st);
     if (bv == 32) return run_windows<D, IT, OT, OUT, 32>(a, nwin, ov, st);
     return run_windows<D, IT, OT, OUT, 64>(a, nwin, ov, st);

@@ -25,6 +25,13 @@ struct ChunkArgs {
     const float* init;
     float* state_buf;
     void* out;
+    // sequence-parallel state pass: G segments of Sc chunks per sequence, all
+    // records in one buffer; per (unit, segment) [D, D] fp32 blocks
+    int G = 0;
+    int Sc = 0;
+    float* seg_B = nullptr;           // end state of each segment from a zero state
+    float* seg_M = nullptr;           // transition product of each segment
+    float* seg_init = nullptr;        // true initial state of each segment
 };
 
 // Resources for overlapping the two passes of the chunked prefill: an
@@ -38,6 +45,9 @@ struct Overlap {
 
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);
+// Segments per sequence for the sequence-parallel state pass (0: windows), and
+// the chunks per segment.  KDA_SEGMENTS=0 turns it off, KDA_SEGMENTS=n asks for n.
+int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks_per_segment);
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
                           const Overlap& ov, hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,

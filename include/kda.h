@@ -25,8 +25,16 @@
  *    ever synchronise their own stream.  KDA_VALUE_SLICE=16, 32 or 64
  *    overrides the number of value columns each state-pass workgroup carries
  *    (by default 16 for at most 64 (sequence, head) pairs, 32 up to 256, else
- *    64; 32 for dk = 64).  Both variables are read on every call and change
- *    scheduling only, never results beyond floating-point summation order.
+ *    64; 32 for dk = 64).  With at most 32 state-pass workgroups (for
+ *    example four heads of one sequence) and sequences of at least 32 chunks
+ *    the prefill runs its state pass sequence-parallel: each sequence is
+ *    split into segments that run concurrently from a zero state while also
+ *    forming their transition product, a small scan gives every segment its
+ *    true initial state, and the segments then form the outputs in parallel;
+ *    the workspace size then covers every chunk record.  KDA_SEGMENTS=0 turns
+ *    this off and KDA_SEGMENTS=n asks for n segments.  These variables are
+ *    read on every call and change scheduling only; results differ at most by
+ *    floating-point summation order.
  *  - Layouts are row-major and contiguous.  Tokens are [B, T, H, d] (d
  *    fastest); the recurrent state is [N, H, dk, dv] with dv fastest, rows =
  *    key channels, and the same layout serves initial, final and decode

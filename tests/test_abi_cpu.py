@@ -119,3 +119,15 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libkda.so"))
     with pytest.raises(ImportError, match="no fallback"):
         _lib.lib()
+
+
+def test_workspace_size_sequence_parallel(L, monkeypatch):
+    """Few (sequence, head) pairs: the workspace holds every record plus three per-segment state arrays."""
+    s = _shape(1, 65536, 0, 0, 2, 128, 128, BF16, F32)
+    state, rec = 2 * 128 * 128 * 4, 74240
+    records = 1024 * 2 * rec
+    n = L.kda_chunk_fwd_workspace_size(s)
+    assert n >= state + records + 3 * 2 * 16 * 128 * 128 * 4  # 16 segments
+    monkeypatch.setenv("KDA_SEGMENTS", "0")                   # windows only
+    n0 = L.kda_chunk_fwd_workspace_size(s)
+    assert state < n0 < n and n0 <= state + (128 << 20)

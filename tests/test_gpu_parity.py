@@ -366,3 +366,32 @@ def test_scalar_gate_prefill_workload(kda):
     o_ref, S_ref = oracle_chunk(d)
     assert_close("out", o, o_ref, TOL["bf16"])
     assert_close("state", S, S_ref, TOL["bf16"])
+
+
+# ----------------------------------------------------------------------------
+# sequence-parallel state pass (few sequence-head pairs)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D,G", [("bf16", 128, "2"), ("bf16", 128, "5"), ("f32", 64, "3"),
+                                       ("f32", 128, "4")])
+def test_segments_forced(kda, monkeypatch, dtype, D, G):
+    """KDA_SEGMENTS=G splits every sequence into G segments; ragged lengths leave some empty."""
+    d = random_small(60 + D + int(G), 0, 2, D, D, dtype=dtype, init_std=0.02, lens=[0, 70, 300, 640, 129])
+    monkeypatch.setenv("KDA_SEGMENTS", G)
+    o, S = run_chunk(kda, torch, d, max_seqlen=640)
+    monkeypatch.setenv("KDA_SEGMENTS", "0")
+    o_w, S_w = run_chunk(kda, torch, d, max_seqlen=640)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL[dtype])
+    assert_close("state", S, S_ref, TOL[dtype])
+    assert_close("out vs windows", o, o_w, TOL[dtype])
+
+
+@pytest.mark.parametrize("gate", ["channel", "head"])
+def test_segments_natural(kda, gate):
+    """Two heads x 4,096 tokens: few enough pairs that the sequence-parallel pass is chosen."""
+    d = random_small(77, 4096, 2, 128, 128, dtype="bf16", init_std=0.02, gate=gate, gate_scale=0.01)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
