@@ -99,26 +99,6 @@ __device__ __forceinline__ void mma_tile_f32_rowB(floatx4& acc, const float* A, 
 }
 
 template <typename OT>
-__device__ __forceinline__ void store16(OT* dst, const float* x);
-template <>
-__device__ __forceinline__ void store16<_Float16>(_Float16* dst, const float* x) {
-    half8 a, b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (_Float16)x[e];
-        b[e] = (_Float16)x[8 + e];
-    }
-    reinterpret_cast<half8*>(dst)[0] = a;
-    reinterpret_cast<half8*>(dst)[1] = b;
-}
-template <>
-__device__ __forceinline__ void store16<float>(float* dst, const float* x) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        reinterpret_cast<float4*>(dst)[e] = make_float4(x[4 * e], x[4 * e + 1], x[4 * e + 2], x[4 * e + 3]);
-}
-
-template <typename OT>
 __device__ __forceinline__ void store8(OT* dst, const float* x);
 template <>
 __device__ __forceinline__ void store8<_Float16>(_Float16* dst, const float* x) {
