@@ -191,7 +191,9 @@ struct Pair8;
 template <>
 struct Pair8<bf16_t> {
     uint32_t w[8];
-    __device__ __forceinline__ void load(int i, const bf16_t* p) { w[i] = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ void load(int i, const bf16_t* p) {
+        w[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
     __device__ __forceinline__ void zero(int i) { w[i] = 0u; }
     __device__ __forceinline__ float get(int i, int e) const {
         return __uint_as_float(e ? (w[i] & 0xFFFF0000u) : (w[i] << 16));
@@ -200,7 +202,10 @@ struct Pair8<bf16_t> {
 template <>
 struct Pair8<float> {
     float2 w[8];
-    __device__ __forceinline__ void load(int i, const float* p) { w[i] = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ void load(int i, const float* p) {
+        const float* f = reinterpret_cast<const float*>(p);
+        w[i] = make_float2(__builtin_nontemporal_load(f), __builtin_nontemporal_load(f + 1));
+    }
     __device__ __forceinline__ void zero(int i) { w[i] = make_float2(0.f, 0.f); }
     __device__ __forceinline__ float get(int i, int e) const { return e ? w[i].y : w[i].x; }
 };
@@ -288,7 +293,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 off[i] = ((size_t)(tok0 + min(r0 + i, n - 1)) * H + h) * D + ch;
-                lr[i] = *reinterpret_cast<const float2*>(a.la + off[i]);
+                lr[i] = make_float2(__builtin_nontemporal_load(a.la + off[i]), __builtin_nontemporal_load(a.la + off[i] + 1));
             }
         }
         // every thread loads a beta (no branch around a load); thread t < 64 stores row t
@@ -805,6 +810,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 // (the chunk index is clamped to the window, so past the end the last record
 // is read again) except the chain's Kh^T, which is only needed by steps that
 // run; this keeps the compiler's load-count waits exact.
+// Outputs are written once and read by nobody here: non-temporal stores keep
+// them from displacing the chunk records in the caches.
+__device__ __forceinline__ void store_out(float* p, float x) { __builtin_nontemporal_store(x, p); }
+__device__ __forceinline__ void store_out(bf16_t* p, float x) {
+    __builtin_nontemporal_store(f32_to_bf16(x).bits, reinterpret_cast<uint16_t*>(p));
+}
+
 template <typename OT>
 struct Frag;
 template <>
@@ -1037,11 +1049,11 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                 OUT* o = out + ((size_t)(tok0 + 16 * w + 4 * gq) * H + h) * D + col0 + 16 * ct + li;
                 if (n == CH) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[(size_t)r * H * D] = from_f32<OUT>(accO[ct][r]);
+                    for (int r = 0; r < 4; ++r) store_out(o + (size_t)r * H * D, accO[ct][r]);
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (16 * w + 4 * gq + r < n) o[(size_t)r * H * D] = from_f32<OUT>(accO[ct][r]);
+                        if (16 * w + 4 * gq + r < n) store_out(o + (size_t)r * H * D, accO[ct][r]);
                 }
             }
         };

@@ -395,3 +395,17 @@ def test_segments_natural(kda, gate):
     o_ref, S_ref = oracle_chunk(d)
     assert_close("out", o, o_ref, TOL["bf16"])
     assert_close("state", S, S_ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("B,T,H,D,dtype", [(3, 200, 2, 128, "bf16"), (2, 129, 3, 64, "f32")])
+def test_dense_batch(kda, B, T, H, D, dtype):
+    """A dense batch [B, T, H, d] without cu_seqlens: B independent sequences of T tokens."""
+    d = random_small(90 + B + T, T, H, D, D, dtype=dtype, init_std=0.02, batch=B)
+    q, k, v, la = (to_dev(d[x].reshape((B, T) + d[x].shape[1:]), torch) for x in ("q", "k", "v", "log_alpha"))
+    b = to_dev(d["beta"].reshape(B, T, H), torch)
+    init = to_dev(d["init"], torch)
+    out, fin = kda.chunk_fwd(q, k, v, la, b, init, None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", out.cpu().numpy().reshape(B * T, H, D), o_ref, TOL[dtype])
+    assert_close("state", fin.cpu().numpy(), S_ref, TOL[dtype])
