@@ -17,8 +17,10 @@ namespace {
 constexpr int CHUNK = 64;
 // Record budget across the two window buffers: records written by the
 // chunk-local pass should still sit in the 256 MB last-level (MALL) cache when
-// the state pass reads them.
-constexpr size_t RECORD_BUDGET = size_t(128) << 20;
+// the state pass reads them.  The chunk-local pass streams its inputs and
+// outputs with non-temporal accesses, so records of up to about 230 MB stay
+// resident; past that the state pass starts missing.
+constexpr size_t RECORD_BUDGET = size_t(220) << 20;
 
 // Per-device overlap resources, created on first use and kept for the life of
 // the process.  The mutex serialises host-side enqueueing of calls on one device.
@@ -148,8 +150,9 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     if (G > 0)  // sequence-parallel state pass: every record plus three per-segment state blocks
         return p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G);
     if ((size_t)all * per_chunk <= RECORD_BUDGET) return p.state_bytes + (size_t)all * per_chunk;
-    int64_t wc = (int64_t)(RECORD_BUDGET / 2 / per_chunk);
-    if (wc < 1) wc = 1;
+    const int64_t wc = (int64_t)(RECORD_BUDGET / 2 / per_chunk);
+    if (wc < 1)  // one chunk index of every unit already fills half the budget: single-index windows
+        return p.state_bytes + per_chunk;
     return p.state_bytes + 2 * (size_t)wc * per_chunk;  // two windows, or one of twice the size
 }
 

@@ -130,4 +130,19 @@ def test_workspace_size_sequence_parallel(L, monkeypatch):
     assert n >= state + records + 3 * 2 * 16 * 128 * 128 * 4  # 16 segments
     monkeypatch.setenv("KDA_SEGMENTS", "0")                   # windows only
     n0 = L.kda_chunk_fwd_workspace_size(s)
-    assert state < n0 < n and n0 <= state + (128 << 20)
+    assert state < n0 < n and n0 <= state + (220 << 20)
+
+
+def test_workspace_size_windows(L):
+    """Record windows stay within the 220 MiB record budget; one chunk index of every unit is the floor."""
+    rec = 74240
+    # one 65,536-token sequence, 32 heads: 96-chunk windows (2 x 48 chunk indices)
+    s = _shape(1, 65536, 0, 0, 32, 128, 128, BF16, F32)
+    state = 32 * 128 * 128 * 4
+    n = L.kda_chunk_fwd_workspace_size(s)
+    assert n == state + 96 * 32 * rec and n - state <= (220 << 20)
+    # 64 sequences of 1,024 tokens: one chunk index of every (sequence, head) pair is 152 MB,
+    # so windows hold that single index
+    s = _shape(1, 65536, 64, 1024, 32, 128, 128, BF16, F32)
+    state = 64 * 32 * 128 * 128 * 4
+    assert L.kda_chunk_fwd_workspace_size(s) == state + 64 * 32 * rec
