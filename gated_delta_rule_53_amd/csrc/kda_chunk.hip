@@ -225,9 +225,14 @@ __device__ __forceinline__ void put2<float>(float* dst, float a, float b) {
     *reinterpret_cast<float2*>(dst) = make_float2(a, b);
 }
 
-// Largest magnitude an fp16 operand may take before the diagonal sub-blocks
-// switch to fp32 operands.
+// The diagonal sub-blocks split e^{G_r - G_i} into a row factor and a column
+// factor about an anchor row; they switch to fp32 operands when an fp16 operand
+// could overflow, or when a factor exceeds F16_FACTOR_LIMIT: its partner factor is
+// then below 1/256, the partner operand may be an fp16 subnormal, and that
+// operand's absolute rounding error times the large factor would no longer be
+// negligible next to the entry being formed (it stays below 2^-17 of |k_r k_i|).
 constexpr float F16_OPERAND_LIMIT = 6.0e4f;
+constexpr float F16_FACTOR_LIMIT = 256.f;
 
 template <int D, typename IT, typename OT>
 __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
@@ -261,11 +266,14 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     const IT* v = static_cast<const IT*>(a.v);
 
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
+    // the wave index is uniform: held in a scalar register, loop bounds and tile
+    // indices derived from it stay off the vector ALU
+    const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int gq = lane >> 4, li = lane & 15;
     // this thread: channels ch, ch+1 over the 8 rows r0..r0+7 of half-block hb
+    // (one half-block per wave when D = 128)
     constexpr int NP = D / 2;
-    const int cp = t % NP, hb = t / NP;
+    const int cp = t % NP, hb = NP == 64 ? wave : t / NP;
     const int ch = 2 * cp;
     const int b = hb >> 1, hh = hb & 1;  // 16-row block and which half of it
     const int r0 = 8 * hb;               // first row (within the chunk)
@@ -318,8 +326,9 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
     }
     // half-block products, the half's first gate, and prod_{1..7} (first halves)
+    float l7[2];  // this thread's prod_{1..7}, kept for the diagonal-block anchors
     {
-        float hp[2], l7[2];
+        float hp[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             l7[e] = al[1][e];
@@ -332,10 +341,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         *reinterpret_cast<float2*>(sX + (16 + hb) * D + ch) = make_float2(l7[0], l7[1]);
     }
     if (t < CH) sBeta[t] = t < n ? bval : 0.f;
-    // strictly-upper blocks of the staged P are zero
-    for (int idx = t; idx < CH * CH; idx += C::NT) {
-        const int r = idx / CH, i = idx % CH;
-        if ((i >> 4) > (r >> 4)) sP[idx] = from_f32<OT>(0.f);
+    // strictly-upper blocks of the staged P are zero (16 bytes per store)
+    {
+        constexpr int PER = 16 / sizeof(OT);
+        for (int idx = t; idx < CH * CH / PER; idx += C::NT) {
+            const int r = idx / (CH / PER), i = (idx % (CH / PER)) * PER;
+            if ((i >> 4) > (r >> 4)) *reinterpret_cast<float4*>(sP + r * CH + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
     lds_barrier();
 
@@ -431,49 +443,80 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
 
     // ---- phase B: diagonal sub-blocks, anchored at row 8 of the block ----
     // rows 0..63 beta k e^{G_r - G_m}; 64..127 q e^{G_r - G_m}; 128..191 k e^{G_m - G_i}
-    // diag_factors visits (i, dl_e, dr_e) for this thread's rows in a fixed order
-    auto diag_factors = [&](auto&& visit) {
-        float M[2] = {1.f, 1.f}, Bk[2] = {A8[0], A8[1]};
-        if (hh) {
+    // With M_i = prod_{1..i} of this thread's gates (rows 8..15 of the block) or
+    // B_i = a_8 prod_{i+1..7} (rows 0..7), the row factor dl_i is M_i or 1 / B_i and
+    // the column factor dr_i is 1 / M_i or B_i.  Both follow from one reciprocal per
+    // channel: dl_i = dl_{i-1} a_i forward from dl_0 = 1 or 1 / (a_8 prod_{1..7}),
+    // dr_i = dr_{i+1} a_{i+1} backward from dr_7 = 1 / prod_{1..7} or a_8.
+    float DL0[2], DR7[2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (i > 0) {
-                    M[0] *= al[i][0];
-                    M[1] *= al[i][1];
-                }
-                visit(i, M[0], M[1], __builtin_amdgcn_rcpf(M[0]), __builtin_amdgcn_rcpf(M[1]));
-            }
-        } else {
+    for (int e = 0; e < 2; ++e) {
+        const float r = __builtin_amdgcn_rcpf(hh ? l7[e] : A8[e] * l7[e]);
+        DL0[e] = hh ? 1.f : r;
+        DR7[e] = hh ? r : A8[e];
+    }
+    auto dl_rows = [&](auto&& visit) {  // visit(i, dl_e0, dl_e1), i ascending
+        float f[2] = {DL0[0], DL0[1]};
 #pragma unroll
-            for (int i = 7; i >= 0; --i) {
-                if (i < 7) {
-                    Bk[0] *= al[i + 1][0];
-                    Bk[1] *= al[i + 1][1];
-                }
-                visit(i, __builtin_amdgcn_rcpf(Bk[0]), __builtin_amdgcn_rcpf(Bk[1]), Bk[0], Bk[1]);
+        for (int i = 0; i < 8; ++i) {
+            if (i > 0) {
+                f[0] *= al[i][0];
+                f[1] *= al[i][1];
             }
+            visit(i, f[0], f[1]);
+        }
+    };
+    auto dr_rows = [&](auto&& visit) {  // visit(i, dr_e0, dr_e1), i descending
+        float f[2] = {DR7[0], DR7[1]};
+#pragma unroll
+        for (int i = 7; i >= 0; --i) {
+            if (i < 7) {
+                f[0] *= al[i + 1][0];
+                f[1] *= al[i + 1][1];
+            }
+            visit(i, f[0], f[1]);
         }
     };
     int wide = 0;
     if (C::F16) {
-        float mx = 0.f;
-        diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
-            const float kb0 = fabsf(kk.get(i, 0)), kb1 = fabsf(kk.get(i, 1));
-            const float sb = fmaxf(1.f, fabsf(bb[i]));
-            mx = fmaxf(mx, fmaxf(fmaxf(kb0, fabsf(qq.get(i, 0))) * sb * dl0, kb0 * dr0));
-            mx = fmaxf(mx, fmaxf(fmaxf(kb1, fabsf(qq.get(i, 1))) * sb * dl1, kb1 * dr1));
+        // bound on every diagonal operand of this thread: the largest |k|, |q| and
+        // |beta| over its rows times the largest row and column factors
+        float km[2] = {0.f, 0.f}, qm[2] = {0.f, 0.f}, sb = 1.f, dlm[2] = {0.f, 0.f}, drm[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                km[e] = fmaxf(km[e], fabsf(kk.get(i, e)));
+                qm[e] = fmaxf(qm[e], fabsf(qq.get(i, e)));
+            }
+            sb = fmaxf(sb, fabsf(bb[i]));
+        }
+        dl_rows([&](int, float f0, float f1) {
+            dlm[0] = fmaxf(dlm[0], f0);
+            dlm[1] = fmaxf(dlm[1], f1);
         });
-        wide = __syncthreads_or(!(mx <= F16_OPERAND_LIMIT));
+        dr_rows([&](int, float f0, float f1) {
+            drm[0] = fmaxf(drm[0], f0);
+            drm[1] = fmaxf(drm[1], f1);
+        });
+        float mx = 0.f, fx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            mx = fmaxf(mx, fmaxf(fmaxf(km[e], qm[e]) * sb * dlm[e], km[e] * drm[e]));
+            fx = fmaxf(fx, fmaxf(dlm[e], drm[e]));
+        }
+        wide = __syncthreads_or(!(mx <= F16_OPERAND_LIMIT) || !(fx <= F16_FACTOR_LIMIT));
     } else {
         __syncthreads();
     }
     const int rowB = 16 * b + ib0;  // first row of this thread in [0, 64)
     if (!wide) {
-        diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
-            const float k0 = kk.get(i, 0), k1 = kk.get(i, 1);
-            put2<OT>(sOp + (rowB + i) * C::DP + ch, bb[i] * k0 * dl0, bb[i] * k1 * dl1);
+        dl_rows([&](int i, float dl0, float dl1) {
+            put2<OT>(sOp + (rowB + i) * C::DP + ch, bb[i] * kk.get(i, 0) * dl0, bb[i] * kk.get(i, 1) * dl1);
             put2<OT>(sOp + (64 + rowB + i) * C::DP + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
-            put2<OT>(sOp + (128 + rowB + i) * C::DP + ch, k0 * dr0, k1 * dr1);
+        });
+        dr_rows([&](int i, float dr0, float dr1) {
+            put2<OT>(sOp + (128 + rowB + i) * C::DP + ch, kk.get(i, 0) * dr0, kk.get(i, 1) * dr1);
         });
         __syncthreads();
         for (int p = wave; p < 8; p += C::NW) {
@@ -498,11 +541,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         for (int half = 0; half < 2; ++half) {
             if ((b >> 1) == half) {
                 const int rr0 = 16 * (b & 1) + ib0;
-                diag_factors([&](int i, float dl0, float dl1, float dr0, float dr1) {
-                    const float k0 = kk.get(i, 0), k1 = kk.get(i, 1);
-                    put2<float>(sOp32 + (rr0 + i) * C::DP32 + ch, bb[i] * k0 * dl0, bb[i] * k1 * dl1);
+                dl_rows([&](int i, float dl0, float dl1) {
+                    put2<float>(sOp32 + (rr0 + i) * C::DP32 + ch, bb[i] * kk.get(i, 0) * dl0,
+                                bb[i] * kk.get(i, 1) * dl1);
                     put2<float>(sOp32 + (32 + rr0 + i) * C::DP32 + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
-                    put2<float>(sOp32 + (64 + rr0 + i) * C::DP32 + ch, k0 * dr0, k1 * dr1);
+                });
+                dr_rows([&](int i, float dr0, float dr1) {
+                    put2<float>(sOp32 + (64 + rr0 + i) * C::DP32 + ch, kk.get(i, 0) * dr0, kk.get(i, 1) * dr1);
                 });
             }
             __syncthreads();
@@ -669,9 +714,14 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         __syncthreads();
     }
     if (C::F16) {
-        for (int idx = t; idx < CH * CH; idx += C::NT) {
-            const int r = idx / CH, i = idx % CH;
-            sTh[r * THP + i] = from_f32<OT>((i >> 4) > (r >> 4) ? 0.f : sT[r * C::AP + i]);
+        // eight consecutive columns of one row per step (16-byte stores)
+        for (int idx = t; idx < CH * CH / 8; idx += C::NT) {
+            const int r = idx / 8, i = (idx % 8) * 8;
+            float x[8];
+            const bool upper = (i >> 4) > (r >> 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = upper ? 0.f : sT[r * C::AP + i + e];
+            store8<OT>(sTh + r * THP + i, x);
         }
     } else {
         for (int idx = t; idx < CH * CH; idx += C::NT) {

@@ -109,6 +109,20 @@ def test_chunk_strong_decay(kda):
     assert_close("state", S, S_ref, TOL["bf16"])
 
 
+@pytest.mark.parametrize("la", [-10.0, -1.5, -1.2, -0.8, -0.6, -0.05])
+def test_chunk_diagonal_operand_range(kda, la):
+    """Uniform gates across the range of the diagonal-block factors (up to e^{8|la|} over
+    eight rows): from -0.8 on they exceed what fp16 operands carry accurately (at -1.2
+    and -1.5 the small partner operands fall into the fp16 subnormals) and every
+    workgroup takes fp32 diagonal operands; at -0.6 and -0.05 fp16 operands suffice."""
+    d = random_small(21, 200, 2, 128, 128, dtype="bf16", lens=[137, 63])
+    d["log_alpha"] = np.full_like(d["log_alpha"], la)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
 def test_chunk_workspace_windows(kda):
     """The smallest workspace (one chunk per window) gives the same bits as the default one."""
     d = random_small(8, 400, 2, 128, 128, dtype="bf16")
