@@ -74,7 +74,8 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     """fp64 token-by-token KDA forward.
 
     Inputs (numpy): q, k [T, H, dk] and v [T, H, dv] as float32 or uint16
-    (bf16 bits); log_alpha float32 [T, H, dk], or [T, H] for one gate per head
+    (bf16 bits), or float64 (then log_alpha and beta are taken in fp64 too);
+    log_alpha float32 [T, H, dk], or [T, H] for one gate per head
     shared by every key channel (the scalar gate of Gated DeltaNet: it is the
     same recurrence with the gate broadcast over dk); beta float32 [T, H];
     init_state [N, H, dk, dv] (widened to fp64) or None; cu_seqlens int [N+1] or None
@@ -99,19 +100,22 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     N = len(cu) - 1
     assert int(cu[-1]) == T, "cu_seqlens must cover every token"
     bf16 = q.dtype == np.uint16
-    want = np.uint16 if bf16 else np.float32
+    f64 = q.dtype == np.float64  # every per-token input then enters in fp64
+    kind = 2 if f64 else int(bf16)
+    want = np.float64 if f64 else (np.uint16 if bf16 else np.float32)
+    fwant = np.float64 if f64 else np.float32
     q, k, v = (np.ascontiguousarray(x, dtype=want) for x in (q, k, v))
-    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    la = np.ascontiguousarray(log_alpha, dtype=fwant)
     if la.ndim == 2:
         la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], (T, H, dk)))
-    be = np.ascontiguousarray(beta, dtype=np.float32).reshape(T, H)
+    be = np.ascontiguousarray(beta, dtype=fwant).reshape(T, H)
     init = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float64)
     if init is not None:
         assert init.shape == (N, H, dk, dv)
     out = np.zeros((T, H, dv), np.float64)
     fin = np.zeros((N, H, dk, dv), np.float64)
     nt = threads or max(1, min(64, os.cpu_count() or 1))
-    rc = _lib(mutant).kda_oracle_forward(N, cu.ctypes.data, H, dk, dv, int(bf16), _ptr(q), _ptr(k),
+    rc = _lib(mutant).kda_oracle_forward(N, cu.ctypes.data, H, dk, dv, kind, _ptr(q), _ptr(k),
                                          _ptr(v), _ptr(la), _ptr(be), _ptr(init), _ptr(out),
                                          _ptr(fin), nt)
     if rc != 0:

@@ -26,6 +26,8 @@
  * is tokens cu_seqlens[s] .. cu_seqlens[s+1]-1.  State [N, H, dk, dv], dv
  * fastest.  q/k/v are fp32 or bf16 (uint16 bit patterns); bf16 values are
  * widened exactly, so the oracle sees the same real numbers the GPU reads.
+ * A third input kind takes every per-token input (q, k, v, log_alpha, beta)
+ * as fp64, for callers that form them in fp64 first.
  *
  * Threads: one (sequence, head) unit at a time per thread, pthreads.
  *
@@ -51,7 +53,7 @@ typedef struct {
     int heads, dk, dv;
     int in_bf16;
     const void *q, *k, *v;
-    const float *log_alpha, *beta;
+    const void *log_alpha, *beta; /* fp32, or fp64 when in_bf16 == 2 */
     const double* init;
     double *out, *final_state;
     int64_t next_unit;
@@ -59,6 +61,7 @@ typedef struct {
 } job_t;
 
 static double load_in(const void* p, int bf16, int64_t i) {
+    if (bf16 == 2) return ((const double*)p)[i];
     if (bf16) {
         uint32_t u = ((uint32_t)((const uint16_t*)p)[i]) << 16;
         float f;
@@ -66,6 +69,10 @@ static double load_in(const void* p, int bf16, int64_t i) {
         return (double)f;
     }
     return (double)((const float*)p)[i];
+}
+
+static double load_gate(const job_t* J, int64_t i) {
+    return J->in_bf16 == 2 ? ((const double*)J->log_alpha)[i] : (double)((const float*)J->log_alpha)[i];
 }
 
 static void run_unit(job_t* J, int64_t unit, double* S, double* kv, double* qv, double* vv,
@@ -87,16 +94,16 @@ static void run_unit(job_t* J, int64_t unit, double* S, double* kv, double* qv, 
             kv[c] = load_in(J->k, J->in_bf16, th * dk + c);
             qv[c] = load_in(J->q, J->in_bf16, th * dk + c);
 #if KDA_ORACLE_MUTANT == 6
-            av[c] = (double)J->log_alpha[th * dk + c]; /* mutant: gate used without exp */
+            av[c] = load_gate(J, th * dk + c); /* mutant: gate used without exp */
 #else
-            av[c] = exp((double)J->log_alpha[th * dk + c]);
+            av[c] = exp(load_gate(J, th * dk + c));
 #endif
         }
         for (int j = 0; j < dv; ++j) vv[j] = load_in(J->v, J->in_bf16, th * dv + j);
 #if KDA_ORACLE_MUTANT == 5
         const double b = 1.0; /* mutant: beta dropped */
 #else
-        const double b = (double)J->beta[th];
+        const double b = J->in_bf16 == 2 ? ((const double*)J->beta)[th] : (double)((const float*)J->beta)[th];
 #endif
 
 #if KDA_ORACLE_MUTANT != 1
@@ -178,16 +185,16 @@ static void* worker(void* arg) {
 /*
  * kda_oracle_forward: run every (sequence, head) unit.
  *   cu_seqlens  int64 [num_seqs+1], non-decreasing, cu[0] = 0
- *   q, k        [T_total, heads, dk]  (fp32, or bf16 bits if in_bf16)
+ *   q, k        [T_total, heads, dk]  (fp32; bf16 bits if in_bf16 == 1; fp64 if 2)
  *   v           [T_total, heads, dv]
- *   log_alpha   fp32 [T_total, heads, dk];  beta fp32 [T_total, heads]
+ *   log_alpha   [T_total, heads, dk];  beta [T_total, heads]  (fp32; fp64 if in_bf16 == 2)
  *   init_state  fp64 [num_seqs, heads, dk, dv] or NULL (zero)
  *   out         fp64 [T_total, heads, dv];  final_state fp64 [num_seqs, heads, dk, dv] or NULL
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
 int kda_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, int dk, int dv,
                        int in_bf16, const void* q, const void* k, const void* v,
-                       const float* log_alpha, const float* beta, const double* init_state,
+                       const void* log_alpha, const void* beta, const double* init_state,
                        double* out, double* final_state, int nthreads) {
     if (num_seqs < 0 || heads <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens) return 1;
     if (cu_seqlens[0] != 0) return 1;
