@@ -11,7 +11,7 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "decode_step", "workspace_size", "KdaError"]
+__all__ = ["chunk_fwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size", "KdaError"]
 
 
 def _torch():
@@ -134,4 +134,105 @@ def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
                                k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
                                state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
     _lib.check(st, "kda_decode_step")
+    return out
+
+
+def _layer(gate, out_gate, norm_weight, qk_l2norm, l2_eps, rms_eps, dv):
+    torch = _torch()
+    if gate.dtype != torch.bfloat16:
+        raise TypeError("gate must be bf16 (the gate pre-activation)")
+    if out_gate is not None and out_gate.dtype != torch.bfloat16:
+        raise TypeError("out_gate must be bf16")
+    if norm_weight is not None:
+        _check_dev(norm_weight, "norm_weight", torch.float32, (dv,))
+    ptr = lambda t: None if t is None else t.data_ptr()
+    return _lib.Layer(int(bool(qk_l2norm)), float(l2_eps), ptr(gate), ptr(out_gate), ptr(norm_weight),
+                      float(rms_eps))
+
+
+def layer_fwd(q, k, v, gate, beta, init_state=None, cu_seqlens=None, *, out_gate=None, norm_weight=None,
+              qk_l2norm=True, l2_eps=1e-6, rms_eps=1e-6, out=None, out_dtype=None, final_state=True,
+              max_seqlen=None, workspace=None):
+    """Chunked prefill of the KDA layer: q/k L2 normalisation, log alpha = -softplus(gate),
+    the recurrence, then y = RMSNorm(o) * norm_weight * sigmoid(out_gate) (skipped when
+    out_gate is None).
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16); gate bf16 [B,T,H,dk] (or [B,T,H]: one
+    gate per head); beta [B,T,H] fp32; out_gate bf16 [B,T,H,dv] or None; norm_weight
+    fp32 [dv] or None (ones).  Other arguments as ``chunk_fwd``.  Returns (y, final_state).
+    """
+    torch = _torch()
+    _check_dev(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_dev(k, "k", q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (B, T, H, dv))
+    gate_per_head = gate.dim() == 3
+    _check_dev(gate, "gate", torch.bfloat16, (B, T, H) if gate_per_head else (B, T, H, dk))
+    _check_dev(beta, "beta", torch.float32, (B, T, H))
+    if out_gate is not None:
+        _check_dev(out_gate, "out_gate", torch.bfloat16, (B, T, H, dv))
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if B != 1:
+            raise ValueError("varlen inputs must have batch 1")
+        N = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = T
+    else:
+        N = B
+    if init_state is not None:
+        _check_dev(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    out_dtype = q.dtype if out_dtype is None and out is None else (out.dtype if out is not None else out_dtype)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=out_dtype, device=q.device)
+    _check_dev(out, "out", out_dtype, (B, T, H, dv))
+    if final_state is True:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
+                       _dtype_code(q.dtype), _dtype_code(out_dtype), int(gate_per_head))
+    layer = _layer(gate, out_gate, norm_weight, qk_l2norm, l2_eps, rms_eps, dv)
+    L = lib()
+    need = int(L.kda_chunk_fwd_workspace_size(shape))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_dev(workspace, "workspace", torch.uint8)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = L.kda_layer_fwd(shape, layer, ptr(q), ptr(k), ptr(v), ptr(beta), ptr(init_state), ptr(cu_seqlens),
+                         ptr(out), ptr(final_state), ptr(workspace), workspace.numel(), _stream_handle(q.device))
+    _lib.check(st, "kda_layer_fwd")
+    return out, final_state
+
+
+def layer_decode_step(q, k, v, gate, beta, state, *, out_gate=None, norm_weight=None, qk_l2norm=True,
+                      l2_eps=1e-6, rms_eps=1e-6, out=None, out_dtype=None):
+    """One decode step of the KDA layer (see ``layer_fwd``); updates ``state`` in place.
+
+    q, k [N,H,dk], v [N,H,dv]; gate bf16 [N,H,dk] or [N,H]; beta [N,H] fp32; out_gate
+    bf16 [N,H,dv] or None.  Returns y [N,H,dv].
+    """
+    torch = _torch()
+    _check_dev(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_dev(k, "k", q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (N, H, dv))
+    gate_per_head = gate.dim() == 2
+    _check_dev(gate, "gate", torch.bfloat16, (N, H) if gate_per_head else (N, H, dk))
+    _check_dev(beta, "beta", torch.float32, (N, H))
+    _check_dev(state, "state", torch.float32, (N, H, dk, dv))
+    if out_gate is not None:
+        _check_dev(out_gate, "out_gate", torch.bfloat16, (N, H, dv))
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    _check_dev(out, "out", None, (N, H, dv))
+    layer = _layer(gate, out_gate, norm_weight, qk_l2norm, l2_eps, rms_eps, dv)
+    st = lib().kda_layer_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype),
+                                     int(gate_per_head), layer, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     beta.data_ptr(), state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
+    _lib.check(st, "kda_layer_decode_step")
     return out

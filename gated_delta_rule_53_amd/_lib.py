@@ -12,7 +12,8 @@ DTYPE_BF16 = 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step", "kda_status_string")
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step", "kda_layer_fwd",
+           "kda_layer_decode_step", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -27,6 +28,12 @@ class Shape(ctypes.Structure):
                 ("max_seqlen", ctypes.c_int64), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
                 ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("gate_per_head", ctypes.c_int32)]
+
+
+class Layer(ctypes.Structure):
+    """kda_layer_t"""
+    _fields_ = [("qk_l2norm", ctypes.c_int32), ("l2_eps", ctypes.c_float), ("gate", ctypes.c_void_p),
+                ("out_gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p), ("rms_eps", ctypes.c_float)]
 
 
 _LIB = None
@@ -49,6 +56,12 @@ def lib():
     L.kda_decode_step.restype = ctypes.c_int
     L.kda_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, i32,
                                   vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_layer_fwd.restype = ctypes.c_int
+    L.kda_layer_fwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                sz, vp]
+    L.kda_layer_decode_step.restype = ctypes.c_int
+    L.kda_layer_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, i32,
+                                        ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [ctypes.c_int]
     _LIB = L

@@ -156,21 +156,33 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     return p.state_bytes + 2 * (size_t)wc * per_chunk;  // two windows, or one of twice the size
 }
 
-kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
-                           const float* log_alpha, const float* beta, const float* init_state,
-                           const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// The prefill behind kda_chunk_fwd (gate: fp32 log_alpha, layer null) and
+// kda_layer_fwd (gate: the layer's bf16 pre-activation).
+static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
+                                   const void* v, const float* log_alpha, const float* beta,
+                                   const float* init_state, const int32_t* cu_seqlens, void* out,
+                                   float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     Plan p;
     kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p);
     if (st != KDA_OK) return st;
     const int H = s->heads, d = p.d;
     const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
     const size_t tok_bytes = (size_t)p.tokens * H * d;
-    const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok_bytes) * 4;
+    const void* gate = layer ? layer->gate : static_cast<const void*>(log_alpha);
+    const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok_bytes) * (layer ? 2 : 4);
+    const size_t og_bytes = layer && layer->out_gate ? tok_bytes * 2 : 0;
+    if (layer) {
+        if ((layer->qk_l2norm != 0 && layer->qk_l2norm != 1) || !(layer->l2_eps >= 0.f) ||
+            !(layer->rms_eps >= 0.f) || !(layer->l2_eps < 3.0e38f) || !(layer->rms_eps < 3.0e38f))
+            return KDA_ERR_INVALID_ARG;
+        if ((layer->out_gate && !aligned16(layer->out_gate)) ||
+            (layer->norm_weight && !aligned16(layer->norm_weight)))
+            return KDA_ERR_INVALID_ARG;
+    }
     const size_t state_elems = (size_t)p.N * H * d * d;
     if (p.tokens > 0) {
-        if (!q || !k || !v || !log_alpha || !beta || !out) return KDA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_alpha) || !aligned16(out))
+        if (!q || !k || !v || !gate || !beta || !out) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out))
             return KDA_ERR_INVALID_ARG;
     }
     if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
@@ -181,7 +193,9 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
         return KDA_ERR_INVALID_ARG;
     const size_t out_bytes = tok_bytes * out_b;
     if (overlaps(out, out_bytes, q, tok_bytes * in_b) || overlaps(out, out_bytes, k, tok_bytes * in_b) ||
-        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, log_alpha, la_bytes) ||
+        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, gate, la_bytes) ||
+        (layer && overlaps(out, out_bytes, layer->out_gate, og_bytes)) ||
+        (layer && overlaps(out, out_bytes, layer->norm_weight, (size_t)d * 4)) ||
         overlaps(out, out_bytes, beta, (size_t)p.tokens * H * 4) ||
         overlaps(out, out_bytes, init_state, state_elems * 4) ||
         overlaps(out, out_bytes, final_state, state_elems * 4))
@@ -238,6 +252,13 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
     a.v = v;
     a.la = log_alpha;
     a.gate_per_head = s->gate_per_head;
+    if (layer) {
+        a.gate = static_cast<const uint16_t*>(layer->gate);
+        a.l2_eps = layer->l2_eps;
+        a.out_gate = static_cast<const uint16_t*>(layer->out_gate);
+        a.norm_weight = layer->norm_weight;
+        a.rms_eps = layer->rms_eps;
+    }
     a.beta = beta;
     a.cu = cu_seqlens;
     a.T = s->seqlen;
@@ -268,15 +289,33 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
         ov = res->ov;
         ov.buffer_bytes = (size_t)wc * per_chunk;
     }
-    hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, bv, a,
-                                       (int)nwin64, ov, static_cast<hipStream_t>(stream));
+    hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16,
+                                       layer && layer->qk_l2norm, bv, a, (int)nwin64, ov,
+                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
-                             kda_dtype_t out_dtype, int32_t gate_per_head, const void* q, const void* k,
-                             const void* v, const float* log_alpha, const float* beta, float* state_inout,
-                             void* out, void* stream) {
+kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return chunk_fwd_impl(s, nullptr, q, k, v, log_alpha, beta, init_state, cu_seqlens, out, final_state,
+                          workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
+                           const void* v, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!layer) return KDA_ERR_INVALID_ARG;
+    return chunk_fwd_impl(s, layer, q, k, v, nullptr, beta, init_state, cu_seqlens, out, final_state, workspace,
+                          workspace_bytes, stream);
+}
+
+static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
+                                const void* q, const void* k, const void* v, const float* log_alpha,
+                                const float* beta, float* state_inout, void* out, void* stream) {
     if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (gate_per_head != 0 && gate_per_head != 1) return KDA_ERR_INVALID_ARG;
     if ((in_dtype != KDA_DTYPE_F32 && in_dtype != KDA_DTYPE_BF16) ||
@@ -286,23 +325,58 @@ kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t d
     if (batch == 0) return KDA_OK;
     const int64_t units = (int64_t)batch * heads;
     if (units > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !log_alpha || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    const void* gate = layer ? layer->gate : static_cast<const void*>(log_alpha);
+    if (!q || !k || !v || !gate || !beta || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    if (layer && ((layer->qk_l2norm != 0 && layer->qk_l2norm != 1) || !(layer->l2_eps >= 0.f) ||
+                  !(layer->rms_eps >= 0.f) || !(layer->l2_eps < 3.0e38f) || !(layer->rms_eps < 3.0e38f)))
+        return KDA_ERR_INVALID_ARG;
     if (!aligned16(state_inout) || !aligned16(out)) return KDA_ERR_INVALID_ARG;
     const size_t vec = (size_t)units * dk;
     const size_t in_b = dsize(in_dtype), out_b = dsize(out_dtype);
     const size_t st_bytes = (size_t)units * dk * dv * 4, out_bytes = vec * out_b;
-    const size_t la_bytes = (gate_per_head ? (size_t)units : vec) * 4;
+    const size_t la_bytes = (gate_per_head ? (size_t)units : vec) * (layer ? 2 : 4);
+    const size_t og_bytes = layer && layer->out_gate ? vec * 2 : 0;
     if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps(out, out_bytes, q, vec * in_b) ||
         overlaps(out, out_bytes, k, vec * in_b) || overlaps(out, out_bytes, v, vec * in_b) ||
-        overlaps(out, out_bytes, log_alpha, la_bytes) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
+        overlaps(out, out_bytes, gate, la_bytes) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
         overlaps(state_inout, st_bytes, q, vec * in_b) || overlaps(state_inout, st_bytes, k, vec * in_b) ||
-        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, log_alpha, la_bytes) ||
-        overlaps(state_inout, st_bytes, beta, (size_t)units * 4))
+        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, gate, la_bytes) ||
+        overlaps(state_inout, st_bytes, beta, (size_t)units * 4) ||
+        (layer && (overlaps(out, out_bytes, layer->out_gate, og_bytes) ||
+                   overlaps(out, out_bytes, layer->norm_weight, (size_t)dv * 4) ||
+                   overlaps(state_inout, st_bytes, layer->out_gate, og_bytes) ||
+                   overlaps(state_inout, st_bytes, layer->norm_weight, (size_t)dv * 4))))
         return KDA_ERR_INVALID_ARG;
+    kda::DecodeLayer L;
+    if (layer) {
+        L.gate = static_cast<const uint16_t*>(layer->gate);
+        L.qk_norm = layer->qk_l2norm;
+        L.l2_eps = layer->l2_eps;
+        L.out_gate = static_cast<const uint16_t*>(layer->out_gate);
+        L.norm_weight = layer->norm_weight;
+        L.rms_eps = layer->rms_eps;
+    }
     hipError_t e = kda::decode_dispatch((int)units, dk, in_dtype == KDA_DTYPE_BF16, out_dtype == KDA_DTYPE_BF16,
-                                        gate_per_head != 0, q, k, v, log_alpha, beta, state_inout, out,
+                                        gate_per_head != 0, q, k, v, log_alpha, beta, state_inout, out, L,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                             kda_dtype_t out_dtype, int32_t gate_per_head, const void* q, const void* k,
+                             const void* v, const float* log_alpha, const float* beta, float* state_inout,
+                             void* out, void* stream) {
+    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, gate_per_head, nullptr, q, k, v, log_alpha, beta,
+                       state_inout, out, stream);
+}
+
+kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                   kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
+                                   const void* q, const void* k, const void* v, const float* beta,
+                                   float* state_inout, void* out, void* stream) {
+    if (!layer) return KDA_ERR_INVALID_ARG;
+    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, gate_per_head, layer, q, k, v, nullptr, beta,
+                       state_inout, out, stream);
 }
 
 }  // extern "C"

@@ -40,6 +40,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace kda {
 
@@ -208,7 +209,51 @@ struct Pair8<float> {
     }
     __device__ __forceinline__ void zero(int i) { w[i] = make_float2(0.f, 0.f); }
     __device__ __forceinline__ float get(int i, int e) const { return e ? w[i].y : w[i].x; }
+    __device__ __forceinline__ void set(int i, float a, float b) { w[i] = make_float2(a, b); }
 };
+// L2-normalised bf16 rows: the two channels of a row packed as fp16 (|x| <= 1)
+template <>
+struct Pair8<_Float16> {
+    uint32_t w[8];
+    __device__ __forceinline__ void zero(int i) { w[i] = 0u; }
+    __device__ __forceinline__ float get(int i, int e) const { return (float)__builtin_bit_cast(half2v, w[i])[e]; }
+    __device__ __forceinline__ void set(int i, float a, float b) {
+        half2v h;
+        h[0] = (_Float16)a;
+        h[1] = (_Float16)b;
+        w[i] = __builtin_bit_cast(uint32_t, h);
+    }
+};
+
+// Register type of q and k rows: the input pairs, or fp16 pairs once bf16 rows are normalised.
+template <typename IT, bool QKN>
+struct QKReg {
+    using type = Pair8<IT>;
+};
+template <>
+struct QKReg<bf16_t, true> {
+    using type = Pair8<_Float16>;
+};
+
+// q and k of a thread's eight rows divided by their L2 norms over the key
+// channels (the NP lanes that hold a row share its sum of squares).
+template <int NP, typename IT, typename QT>
+__device__ __forceinline__ void l2norm_rows(const Pair8<IT>& kr, const Pair8<IT>& qr, Pair8<QT>& kk, Pair8<QT>& qq,
+                                            float eps) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float k0 = kr.get(i, 0), k1 = kr.get(i, 1), q0 = qr.get(i, 0), q1 = qr.get(i, 1);
+        float sk = k0 * k0 + k1 * k1, sq = q0 * q0 + q1 * q1;
+#pragma unroll
+        for (int off = 1; off < NP; off *= 2) {
+            sk += __shfl_xor(sk, off);
+            sq += __shfl_xor(sq, off);
+        }
+        const float rk = __builtin_amdgcn_rsqf(sk + eps), rq = __builtin_amdgcn_rsqf(sq + eps);
+        kk.set(i, k0 * rk, k1 * rk);
+        qq.set(i, q0 * rq, q1 * rq);
+    }
+}
 
 // Two adjacent operand elements of one row.
 template <typename OT>
@@ -234,7 +279,7 @@ __device__ __forceinline__ void put2<float>(float* dst, float a, float b) {
 constexpr float F16_OPERAND_LIMIT = 6.0e4f;
 constexpr float F16_FACTOR_LIMIT = 256.f;
 
-template <int D, typename IT, typename OT>
+template <int D, typename IT, typename OT, bool QKN>
 __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
     using C = LocalCfg<D, OT>;
     using R = Rec<D, OT>;
@@ -283,13 +328,26 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     // then v.  The barriers up to the off-diagonal operands order LDS only, so
     // k, q and v stay in flight while the gate products are formed.  Rows past
     // the end read the last valid row and are zeroed where first used.
-    Pair8<IT> kk, qq, vv;
+    Pair8<IT> kraw, qraw, vv;
     float al[8][2];
     float bval;
     {
         float2 lr[8];
         size_t off[8];
-        if (a.gate_per_head) {  // one gate per (token, head), shared by every key channel
+        if (a.gate) {  // bf16 gate pre-activation g of the layer: alpha = sigmoid(-g)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const size_t th = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
+                off[i] = th * D + ch;
+                if (a.gate_per_head) {
+                    const float g = bf16_bits_to_f32(a.gate[th]);
+                    lr[i] = make_float2(g, g);
+                } else {
+                    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.gate + off[i]));
+                    lr[i] = make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
+                }
+            }
+        } else if (a.gate_per_head) {  // one gate per (token, head), shared by every key channel
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const size_t th = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
@@ -307,15 +365,23 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         // every thread loads a beta (no branch around a load); thread t < 64 stores row t
         bval = a.beta[(size_t)(tok0 + min(t & (CH - 1), n - 1)) * H + h];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kk.load(i, k + off[i]);
+        for (int i = 0; i < 8; ++i) kraw.load(i, k + off[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qq.load(i, q + off[i]);
+        for (int i = 0; i < 8; ++i) qraw.load(i, q + off[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) vv.load(i, v + off[i]);
+        if (a.gate) {  // 1 / (1 + e^g)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            al[i][0] = fast_exp(lr[i].x);
-            al[i][1] = fast_exp(lr[i].y);
+            for (int i = 0; i < 8; ++i) {
+                al[i][0] = __builtin_amdgcn_rcpf(1.f + fast_exp(lr[i].x));
+                al[i][1] = __builtin_amdgcn_rcpf(1.f + fast_exp(lr[i].y));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                al[i][0] = fast_exp(lr[i].x);
+                al[i][1] = fast_exp(lr[i].y);
+            }
         }
         // rows past the end decay by nothing (only in a sequence's last chunk; testing
         // n first keeps the gate loads out of any per-lane branch)
@@ -374,6 +440,13 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     }
     const float* bb = sBeta + r0;  // beta of this thread's rows (LDS broadcast reads)
     lds_barrier();                 // sX is overwritten by the operands below
+    typename QKReg<IT, QKN>::type kk, qq;
+    if constexpr (QKN) {
+        l2norm_rows<NP>(kraw, qraw, kk, qq, a.l2_eps);
+    } else {
+        kk = kraw;
+        qq = qraw;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
         if (r0 + i >= n) {
@@ -866,6 +939,8 @@ __device__ __forceinline__ void store_out(float* p, float x) { __builtin_nontemp
 __device__ __forceinline__ void store_out(bf16_t* p, float x) {
     __builtin_nontemporal_store(f32_to_bf16(x).bits, reinterpret_cast<uint16_t*>(p));
 }
+// fp16 o for the layer epilogue, which reads it back right away: a plain store
+__device__ __forceinline__ void store_out(_Float16* p, float x) { *p = (_Float16)x; }
 
 template <typename OT>
 struct Frag;
@@ -1186,6 +1261,85 @@ __global__ void __launch_bounds__(256) chunk_segment_combine_kernel(ChunkArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// layer epilogue
+// ---------------------------------------------------------------------------
+// Head-wise RMSNorm and sigmoid output gate ("Kimi Delta Attention" section):
+// y = o / sqrt(mean_j o_j^2 + eps) * w * sigmoid(z) per (token, head), in place
+// in `out` over the chunks of one window.  o is what the state pass wrote (OI:
+// fp16 when y is bf16, else fp32); the mean needs a row's dv values, which the
+// state pass spreads over its value-slice workgroups, hence a pass of its own.
+// One workgroup per (head, chunk); LPR lanes hold a row, eight values each.
+template <int D, typename OI>
+__global__ void __launch_bounds__(256) layer_epilogue_kernel(ChunkArgs a) {
+    using OF = typename std::conditional<std::is_same<OI, float>::value, float, bf16_t>::type;
+    constexpr int LPR = D / 8, RPP = 256 / LPR;
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc;
+    int64_t tb, L;
+    seq_bounds(a, s, tb, L);
+    const int64_t c0 = (int64_t)(a.win * a.Wc + jl) * CH;
+    if (c0 >= L) return;
+    const int n = (int)min<int64_t>(CH, L - c0);
+    const int t = threadIdx.x, lr = t / LPR, j0 = 8 * (t % LPR);
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = a.norm_weight ? a.norm_weight[j0 + e] : 1.f;
+    for (int r = lr; r < n; r += RPP) {  // r is uniform over the LPR lanes of a row
+        const size_t base = ((size_t)(tb + c0 + r) * a.H + h) * D + j0;
+        float o[8], y[8];
+        if constexpr (std::is_same<OI, float>::value) {
+            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + base);
+            const float4 x0 = src[0], x1 = src[1];
+            o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
+            o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+        } else {
+            const half8 x = *reinterpret_cast<const half8*>(static_cast<const _Float16*>(a.out) + base);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = (float)x[e];
+        }
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 zb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.out_gate + base));
+        const uint32_t zw[4] = {zb[0], zb[1], zb[2], zb[3]};
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
+#pragma unroll
+        for (int off = 1; off < LPR; off *= 2) ss += __shfl_xor(ss, off);
+        const float rs = __builtin_amdgcn_rsqf(ss * (1.f / D) + a.rms_eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t zw2 = zw[e >> 1];
+            const float z = __uint_as_float((e & 1) ? (zw2 & 0xFFFF0000u) : (zw2 << 16));
+            y[e] = o[e] * rs * w[e] * __builtin_amdgcn_rcpf(1.f + fast_exp(-z));
+        }
+        OF* dst = static_cast<OF*>(a.out) + base;
+        if constexpr (std::is_same<OF, float>::value) {
+            const floatx4 y0 = {y[0], y[1], y[2], y[3]}, y1 = {y[4], y[5], y[6], y[7]};
+            __builtin_nontemporal_store(y0, reinterpret_cast<floatx4*>(dst));
+            __builtin_nontemporal_store(y1, reinterpret_cast<floatx4*>(dst) + 1);
+        } else {
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                pk[e] = uint32_t(f32_to_bf16(y[2 * e]).bits) | (uint32_t(f32_to_bf16(y[2 * e + 1]).bits) << 16);
+            typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+            const u32x4s pv = {pk[0], pk[1], pk[2], pk[3]};
+            __builtin_nontemporal_store(pv, reinterpret_cast<u32x4s*>(dst));
+        }
+    }
+}
+
+template <int D, typename OUT>
+static hipError_t launch_epilogue(const ChunkArgs& a, hipStream_t st) {
+    if constexpr (std::is_same<OUT, bf16_t>::value) {
+        return hipErrorInvalidValue;  // the state pass writes fp16 or fp32 when an epilogue follows
+    } else {
+        if (!a.out_gate) return hipSuccess;
+        hipLaunchKernelGGL((layer_epilogue_kernel<D, OUT>), dim3(a.H, a.N * a.Wc), dim3(256), 0, st, a);
+        return hipGetLastError();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host-side dispatch
 // ---------------------------------------------------------------------------
 size_t chunk_record_bytes(int d, bool in_bf16) {
@@ -1213,7 +1367,7 @@ int chunk_value_slice(int d, int64_t units) {
 // more, the chunk-local pass of window w+1 (caller's stream) overlaps the state
 // pass of window w (the auxiliary stream), the records alternating between two
 // buffers: the local pass of window w+2 waits for the state pass of window w.
-template <int D, typename IT, typename OT, typename OUT, int BV>
+template <int D, typename IT, typename OT, typename OUT, bool QKN, int BV>
 static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     const int units = base.N * base.H;
@@ -1224,7 +1378,7 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
         if (two) a.rec = base.rec + (size_t)(w & 1) * ov.buffer_bytes;
         hipError_t e;
         if (two && w >= 2 && (e = hipStreamWaitEvent(st, ov.inter_done[w & 1], 0)) != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
+        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipStream_t is = st;
         if (two) {
@@ -1234,6 +1388,7 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
         }
         hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, is, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.out_gate && (e = launch_epilogue<D, OUT>(a, is)) != hipSuccess) return e;
         if (two && (e = hipEventRecord(ov.inter_done[w & 1], ov.side)) != hipSuccess) return e;
     }
     if (two) return hipStreamWaitEvent(st, ov.inter_done[(nwin - 1) & 1], 0);
@@ -1242,20 +1397,21 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
 
 // Sequence-parallel state pass: all records in one buffer (a.win = 0, a.Wc =
 // every chunk), a.G segments of a.Sc chunks per sequence.
-template <int D, typename IT, typename OT, typename OUT>
+template <int D, typename IT, typename OT, typename OUT, bool QKN>
 static hipError_t run_segments(const ChunkArgs& a, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     constexpr int BV = SEGMENT_BV;
     const int NH = a.N * a.H;
     hipError_t e;
-    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
+    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 1>), dim3(NH * 2 * (D / BV) * a.G), dim3(512), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_segment_combine_kernel<D>), dim3(NH, D / 16), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 2>), dim3(NH * (D / BV) * a.G), dim3(512), 0, st, a);
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return a.out_gate ? launch_epilogue<D, OUT>(a, st) : hipSuccess;
 }
 
 int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks_per_segment) {
@@ -1280,32 +1436,38 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
     return (int)((max_chunks + sc - 1) / sc);
 }
 
-template <int D, typename IT, typename OT, typename OUT>
+template <int D, typename IT, typename OT, typename OUT, bool QKN>
 static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, const Overlap& ov, hipStream_t st) {
-    if (a.G > 0) return run_segments<D, IT, OT, OUT>(a, st);
-    if (bv == 16) return run_windows<D, IT, OT, OUT, 16>(a, nwin, ov, st);
-    if (bv == 32) return run_windows<D, IT, OT, OUT, 32>(a, nwin, ov, st);
-    return run_windows<D, IT, OT, OUT, 64>(a, nwin, ov, st);
+    if (a.G > 0) return run_segments<D, IT, OT, OUT, QKN>(a, st);
+    if (bv == 16) return run_windows<D, IT, OT, OUT, QKN, 16>(a, nwin, ov, st);
+    if (bv == 32) return run_windows<D, IT, OT, OUT, QKN, 32>(a, nwin, ov, st);
+    return run_windows<D, IT, OT, OUT, QKN, 64>(a, nwin, ov, st);
 }
 
-hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
+// Output type of the state pass: the result's type, or fp16 in place of bf16
+// when the layer epilogue follows (it reads o back and writes bf16 over it).
+template <int D, typename IT, typename OT, bool QKN>
+static hipError_t run_out(const ChunkArgs& a, bool out_bf16, int nwin, int bv, const Overlap& ov, hipStream_t st) {
+    if (!out_bf16) return run_bv<D, IT, OT, float, QKN>(a, nwin, bv, ov, st);
+    if (a.out_gate) return run_bv<D, IT, OT, _Float16, QKN>(a, nwin, bv, ov, st);
+    return run_bv<D, IT, OT, bf16_t, QKN>(a, nwin, bv, ov, st);
+}
+
+template <int D, typename IT, typename OT>
+static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int nwin, int bv, const Overlap& ov,
+                           hipStream_t st) {
+    if (qk_norm) return run_out<D, IT, OT, true>(a, out_bf16, nwin, bv, ov, st);
+    return run_out<D, IT, OT, false>(a, out_bf16, nwin, bv, ov, st);
+}
+
+hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
                           const Overlap& ov, hipStream_t st) {
-#define KDA_RUN(DD, IT, OT, OUT) return run_bv<DD, IT, OT, OUT>(a, nwin, bv, ov, st)
     if (d == 128) {
-        if (in_bf16) {
-            if (out_bf16) KDA_RUN(128, bf16_t, _Float16, bf16_t);
-            KDA_RUN(128, bf16_t, _Float16, float);
-        }
-        if (out_bf16) KDA_RUN(128, float, float, bf16_t);
-        KDA_RUN(128, float, float, float);
+        if (in_bf16) return run_norm<128, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, ov, st);
+        return run_norm<128, float, float>(a, out_bf16, qk_norm, nwin, bv, ov, st);
     }
-    if (in_bf16) {
-        if (out_bf16) KDA_RUN(64, bf16_t, _Float16, bf16_t);
-        KDA_RUN(64, bf16_t, _Float16, float);
-    }
-    if (out_bf16) KDA_RUN(64, float, float, bf16_t);
-    KDA_RUN(64, float, float, float);
-#undef KDA_RUN
+    if (in_bf16) return run_norm<64, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, ov, st);
+    return run_norm<64, float, float>(a, out_bf16, qk_norm, nwin, bv, ov, st);
 }
 
 }  // namespace kda

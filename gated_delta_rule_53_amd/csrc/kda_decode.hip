@@ -14,6 +14,14 @@
 // coalesced).  The three dot products over c are reduced with a cross-lane
 // shuffle inside the wave and through LDS across the four waves, in a fixed
 // order, so results are deterministic.
+//
+// Layer prologue and epilogue ("Kimi Delta Attention" section: the head
+// L2-normalises q and k, takes its per-channel decay from a projection output
+// and passes o through a head-wise RMSNorm and a sigmoid output gate), each
+// switched on by the DecodeLayer argument: q, k / sqrt(sum of squares + eps);
+// alpha = sigmoid(-g) = 1 / (1 + e^g) from the bf16 pre-activation g; and
+// y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z) over the dv outputs of the
+// (sequence, head), which one wave holds.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -24,7 +32,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
                                                      const IT* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
                                                      const float* __restrict__ beta, float* __restrict__ state,
-                                                     OUT* __restrict__ out, int gate_per_head) {
+                                                     OUT* __restrict__ out, int gate_per_head, DecodeLayer L) {
     constexpr int CG = D / 4;       // float4 column groups
     constexpr int RG = 256 / CG;    // row groups
     constexpr int RPT = D / RG;     // rows per thread
@@ -46,12 +54,46 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
 
     __shared__ float s_alpha[D], s_k[D], s_q[D], s_v[D];
     __shared__ float s_red[4][CG][9];
+    __shared__ float s_nrm[2][D / 64];
     const size_t vec = (size_t)unit * D;
+    float kt = 0.f, qt = 0.f;
     if (t < D) {
-        s_alpha[t] = fast_exp(gate_per_head ? log_alpha[unit] : log_alpha[vec + t]);
-        s_k[t] = to_f32(k[vec + t]);
-        s_q[t] = to_f32(q[vec + t]);
+        if (L.gate) {
+            const float g = bf16_bits_to_f32(L.gate[gate_per_head ? (size_t)unit : vec + t]);
+            s_alpha[t] = __builtin_amdgcn_rcpf(1.f + fast_exp(g));
+        } else {
+            s_alpha[t] = fast_exp(gate_per_head ? log_alpha[unit] : log_alpha[vec + t]);
+        }
+        kt = to_f32(k[vec + t]);
+        qt = to_f32(q[vec + t]);
         s_v[t] = to_f32(v[vec + t]);
+    }
+    if (L.qk_norm) {
+        // sums of squares over the D channels: inside each wave, then across the D / 64 waves
+        float sk = kt * kt, sq = qt * qt;
+#pragma unroll
+        for (int off = 1; off < 64; off *= 2) {
+            sk += __shfl_xor(sk, off);
+            sq += __shfl_xor(sq, off);
+        }
+        if (lane == 0 && wave < D / 64) {
+            s_nrm[0][wave] = sk;
+            s_nrm[1][wave] = sq;
+        }
+        __syncthreads();
+        sk = 0.f;
+        sq = 0.f;
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) {
+            sk += s_nrm[0][w];
+            sq += s_nrm[1][w];
+        }
+        kt *= __builtin_amdgcn_rsqf(sk + L.l2_eps);
+        qt *= __builtin_amdgcn_rsqf(sq + L.l2_eps);
+    }
+    if (t < D) {
+        s_k[t] = kt;
+        s_q[t] = qt;
     }
     const float b = beta[unit];
     __syncthreads();
@@ -116,26 +158,42 @@ __global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, c
         for (int e = 0; e < 4; ++e) n[e] = S[i][e] + kc * u[e];
         __builtin_nontemporal_store(n, reinterpret_cast<floatx4*>(S_base + (size_t)(rg * RPT + i) * D + 4 * jg));
     }
-    if (rg == 0) {
+    if (rg == 0) {  // lanes 0 .. CG-1 of wave 0 hold the D outputs, four each
+        float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[vec + 4 * jg + e] = from_f32<OUT>(rr[e] + qq * u[e]);
+        for (int e = 0; e < 4; ++e) o[e] = rr[e] + qq * u[e];
+        if (L.out_gate) {
+            float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+            for (int off = 1; off < CG; off *= 2) ss += __shfl_xor(ss, off);
+            const float rs = __builtin_amdgcn_rsqf(ss * (1.f / D) + L.rms_eps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * jg + e;
+                const float z = bf16_bits_to_f32(L.out_gate[vec + j]);
+                const float w = L.norm_weight ? L.norm_weight[j] : 1.f;
+                o[e] = o[e] * rs * w * __builtin_amdgcn_rcpf(1.f + fast_exp(-z));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[vec + 4 * jg + e] = from_f32<OUT>(o[e]);
     }
 }
 
 template <int D, typename IT, typename OUT>
 hipError_t launch_decode(int units, bool gph, const void* q, const void* k, const void* v, const float* la,
-                         const float* beta, float* state, void* out, hipStream_t st) {
+                         const float* beta, float* state, void* out, const DecodeLayer& L, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<D, IT, OUT>), dim3(units), dim3(256), 0, st,
                        static_cast<const IT*>(q), static_cast<const IT*>(k), static_cast<const IT*>(v), la,
-                       beta, state, static_cast<OUT*>(out), gph ? 1 : 0);
+                       beta, state, static_cast<OUT*>(out), gph ? 1 : 0, L);
     return hipGetLastError();
 }
 
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
                            const void* k, const void* v, const float* la, const float* beta, float* state,
-                           void* out, hipStream_t st) {
+                           void* out, const DecodeLayer& layer, hipStream_t st) {
 #define KDA_DEC(DD, IT, OT) \
-    return launch_decode<DD, IT, OT>(units, gate_per_head, q, k, v, la, beta, state, out, st)
+    return launch_decode<DD, IT, OT>(units, gate_per_head, q, k, v, la, beta, state, out, layer, st)
     if (d == 128) {
         if (in_bf16) {
             if (out_bf16) KDA_DEC(128, bf16_t, bf16_t);

@@ -29,6 +29,7 @@ struct bf16_t {
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     // round to nearest even; inputs here are finite

@@ -32,6 +32,22 @@ struct ChunkArgs {
     float* seg_B = nullptr;           // end state of each segment from a zero state
     float* seg_M = nullptr;           // transition product of each segment
     float* seg_init = nullptr;        // true initial state of each segment
+    // layer prologue and epilogue (null pointers: off)
+    const uint16_t* gate = nullptr;       // bf16 gate pre-activation g replacing la: alpha = sigmoid(-g)
+    float l2_eps = 0.f;                   // q, k / sqrt(sum of squares + l2_eps) when normalised
+    const uint16_t* out_gate = nullptr;   // bf16 [tokens, H, D] output-gate pre-activation
+    const float* norm_weight = nullptr;   // fp32 [D] RMSNorm weight, or null for ones
+    float rms_eps = 0.f;
+};
+
+// Layer prologue and epilogue of one decode step (null pointers: off).
+struct DecodeLayer {
+    const uint16_t* gate = nullptr;       // bf16 [batch, H, D] or [batch, H]: alpha = sigmoid(-g)
+    int qk_norm = 0;
+    float l2_eps = 0.f;
+    const uint16_t* out_gate = nullptr;   // bf16 [batch, H, D]
+    const float* norm_weight = nullptr;
+    float rms_eps = 0.f;
 };
 
 // Resources for overlapping the two passes of the chunked prefill: an
@@ -48,10 +64,14 @@ int chunk_value_slice(int d, int64_t units);
 // Segments per sequence for the sequence-parallel state pass (0: windows), and
 // the chunks per segment.  KDA_SEGMENTS=0 turns it off, KDA_SEGMENTS=n asks for n.
 int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks_per_segment);
-hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin,
+// qk_norm: q and k L2-normalised per (token, head) in the chunk-local pass.
+// With a.out_gate set, the state pass writes o to `out` (fp16 when out_bf16,
+// else fp32) and an epilogue pass after each window replaces it in place by
+// RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
+hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
                           const Overlap& ov, hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
                            const void* k, const void* v, const float* la, const float* beta, float* state,
-                           void* out, hipStream_t st);
+                           void* out, const DecodeLayer& layer, hipStream_t st);
 
 }  // namespace kda

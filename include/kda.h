@@ -149,6 +149,54 @@ kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t d
                              const void* k, const void* v, const float* log_alpha,
                              const float* beta, float* state_inout, void* out, void* stream);
 
+/* Layer prologue and epilogue fused around the operator.  The "Kimi Linear"
+ * page ("Kimi Delta Attention" section) has each KDA head L2-normalise its
+ * queries and keys, compute its per-channel decay through a low-rank
+ * projection, and pass its output through a head-wise RMSNorm and a sigmoid
+ * output gate.  The page fixes neither the map from the projection to the
+ * decay nor the constants; this library takes log alpha = -softplus(g) (alpha
+ * = sigmoid(-g)) and the epsilons below inside the square roots.
+ *   qk_l2norm    1: q and k of every (token, head) are divided by
+ *                sqrt(sum over the dk channels of x^2 + l2_eps) before use;
+ *                0: used as given
+ *   l2_eps       >= 0 (with 0, an all-zero q or k row gives non-finite results)
+ *   gate         required, bf16 gate pre-activation g (the projection output),
+ *                [.., H, dk], or [.., H] when gate_per_head = 1; it replaces
+ *                log_alpha: log alpha = -softplus(g).  The chunked path needs
+ *                g <= 10 (log alpha >= -10 per token).
+ *   out_gate     bf16 [.., H, dv] output-gate pre-activation z, or NULL for no
+ *                epilogue (the output is then o itself)
+ *   norm_weight  fp32 [dv] RMSNorm weight shared by the heads, or NULL (ones)
+ *   rms_eps      >= 0: y = o / sqrt(mean over dv of o^2 + rms_eps) * w * sigmoid(z)
+ * The pointers are device pointers owned by the caller, 16-byte aligned. */
+typedef struct {
+    int32_t qk_l2norm;
+    float l2_eps;
+    const void* gate;
+    const void* out_gate;
+    const float* norm_weight;
+    float rms_eps;
+} kda_layer_t;
+
+/* Chunked prefill of the layer: kda_chunk_fwd with the prologue and epilogue
+ * of `layer` (log_alpha replaced by layer->gate).  Arguments, layouts and the
+ * workspace (kda_chunk_fwd_workspace_size of the same shape) are those of
+ * kda_chunk_fwd; `out` holds y.  With an epilogue the state pass first writes
+ * o into `out` (fp16 when out_dtype is bf16, so |o| must stay below 6.5e4) and
+ * a last pass per window rewrites it in place as y. */
+kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
+                           const void* v, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* One decode step of the layer: kda_decode_step with the prologue and epilogue
+ * of `layer` (log_alpha replaced by layer->gate, [batch, H, dk] or [batch, H];
+ * out_gate [batch, H, dv]); `out` holds y. */
+kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                   kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
+                                   const void* q, const void* k, const void* v, const float* beta,
+                                   float* state_inout, void* out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status_t st);
 

@@ -25,6 +25,16 @@ Recipe (every tensor is drawn block-wise so any subset can be regenerated):
   4,096 per sequence, floored, with the remainder handed to the largest
   fractional parts (ties to the lower index).
 
+Layer inputs (the prologue and epilogue around the operator, ``gen_layer_tokens``):
+
+* q, k ~ N(0, 1) per element, not normalised (the layer normalises them);
+  v and beta as above.
+* the gate pre-activation g ~ N(mu, 1) per (token, head, key channel), or per
+  (token, head), rounded to bf16, with mu = log(0.69 s) so that the median
+  decay -softplus(g) ~ -e^g matches the -s * softplus(N(0, 1)) draw above.
+* the output-gate pre-activation z ~ N(0, 1), bf16; the RMSNorm weight
+  1 + 0.1 N(0, 1) fp32 [dv].
+
 bf16 tensors are returned as ``numpy.uint16`` arrays holding the bf16 bit
 patterns; fp32 tensors as ``numpy.float32``.
 """
@@ -39,7 +49,8 @@ import numpy as np
 BLOCK = 16384  # tokens per independently seeded block
 
 # tensor ids used in the spawn keys
-_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "log_alpha": 4, "init": 5, "lengths": 6, "log_alpha_head": 7}
+_TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "log_alpha": 4, "init": 5, "lengths": 6, "log_alpha_head": 7,
+        "q_raw": 8, "k_raw": 9, "gate_pre": 10, "gate_pre_head": 11, "out_gate": 12, "norm_weight": 13}
 
 
 @dataclass(frozen=True)
@@ -193,6 +204,55 @@ def gen_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_sca
     return out
 
 
+def layer_gate_mu(gate_scale: float) -> float:
+    """Mean of the gate pre-activation draw for a workload's gate scale."""
+    return float(np.log(0.69 * gate_scale))
+
+
+def gen_layer_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_mu: float,
+                     heads=None, threads=None, gate: str = "channel") -> dict:
+    """Layer inputs for T packed tokens: q, k [T,Hs,dk] (not normalised), v [T,Hs,dv],
+    beta [T,Hs], g bf16 [T,Hs,dk] (or [T,Hs] for ``gate="head"``), out_gate bf16 [T,Hs,dv]."""
+    heads = list(range(H)) if heads is None else list(heads)
+    Hs = len(heads)
+    threads = _threads() if threads is None else threads
+    dt = np.uint16 if dtype == "bf16" else np.float32
+    assert gate in ("channel", "head"), gate
+    out = {
+        "q": np.empty((T, Hs, dk), dt),
+        "k": np.empty((T, Hs, dk), dt),
+        "v": np.empty((T, Hs, dv), dt),
+        "beta": np.empty((T, Hs), np.float32),
+        "g": np.empty((T, Hs, dk) if gate == "channel" else (T, Hs), np.uint16),
+        "out_gate": np.empty((T, Hs, dv), np.uint16),
+    }
+
+    def normal(width, dtype_out, mu=0.0):
+        def fn(r, n):
+            x = (mu + r.standard_normal((n, width) if width else n)).astype(np.float32)
+            return f32_to_bf16_bits(x) if dtype_out == "bf16" else x
+        return fn
+    _fill_blocks(seed, "q_raw", T, heads, dk, normal(dk, dtype), out["q"], threads)
+    _fill_blocks(seed, "k_raw", T, heads, dk, normal(dk, dtype), out["k"], threads)
+    _fill_blocks(seed, "v", T, heads, dv, normal(dv, dtype), out["v"], threads)
+
+    def bfn(r, n):
+        z = r.standard_normal(n)
+        return (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    _fill_blocks(seed, "beta", T, heads, None, bfn, out["beta"], threads)
+    if gate == "channel":
+        _fill_blocks(seed, "gate_pre", T, heads, dk, normal(dk, "bf16", gate_mu), out["g"], threads)
+    else:
+        _fill_blocks(seed, "gate_pre_head", T, heads, None, normal(None, "bf16", gate_mu), out["g"], threads)
+    _fill_blocks(seed, "out_gate", T, heads, dv, normal(dv, "bf16"), out["out_gate"], threads)
+    return out
+
+
+def gen_norm_weight(seed: int, dv: int) -> np.ndarray:
+    """RMSNorm weight [dv] fp32 ~ 1 + 0.1 N(0, 1)."""
+    return (1.0 + 0.1 * _rng(seed, "norm_weight", 0, 0).standard_normal(dv)).astype(np.float32)
+
+
 def gen_states(seed: int, N: int, H: int, dk: int, dv: int, std: float, heads=None,
                seqs=None, tag: int = 0) -> np.ndarray:
     """Initial states [Ns, Hs, dk, dv] fp32 ~ N(0, std^2); one stream per (sequence, head)."""
@@ -280,4 +340,41 @@ def random_small(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "f32"
     d = gen_tokens(seed, int(cu[-1]), H, dk, dv, dtype, gate_scale, threads=1, gate=gate)
     d["cu_seqlens"] = cu
     d["init"] = None if init_std is None else gen_states(seed, len(lens), H, dk, dv, init_std)
+    return d
+
+
+def make_layer_prefill(w: Workload, heads=None, threads=None, gate: str = "channel") -> dict:
+    """Layer inputs for a "prefill" or "varlen" workload (same lengths, seed and initial states)."""
+    if w.kind == "varlen":
+        lens = dirichlet_lengths(w.seed, w.seqlen, w.num_seqs, w.min_len)
+    elif w.kind == "prefill":
+        lens = np.full(w.batch, w.seqlen, np.int64)
+    else:
+        raise ValueError(w.kind)
+    cu = cu_from_lengths(lens)
+    d = gen_layer_tokens(w.seed, int(cu[-1]), w.heads, w.dk, w.dv, w.dtype, layer_gate_mu(w.gate_scale),
+                         heads=heads, threads=threads, gate=gate)
+    d["cu_seqlens"] = cu
+    d["init"] = None if w.init_std is None else gen_states(
+        w.seed, len(lens), w.heads, w.dk, w.dv, w.init_std, heads=heads)
+    d["norm_weight"] = gen_norm_weight(w.seed, w.dv)
+    return d
+
+
+def make_layer_decode_step(w: Workload, step: int, heads=None, gate: str = "channel") -> dict:
+    """Layer inputs of one decode step (see ``make_decode_step``)."""
+    assert w.kind == "decode"
+    return gen_layer_tokens(w.seed * 1000003 + 7919 * (step + 1), w.batch, w.heads, w.dk, w.dv, w.dtype,
+                            layer_gate_mu(w.gate_scale), heads=heads, gate=gate)
+
+
+def layer_small(seed: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", gate_mu: float = -3.0,
+                init_std: float | None = 0.02, batch: int = 1, lens=None, gate: str = "channel") -> dict:
+    """Small ad-hoc layer workload (tests); ``lens`` gives varlen."""
+    lens = np.full(batch, T, np.int64) if lens is None else np.asarray(lens, np.int64)
+    cu = cu_from_lengths(lens)
+    d = gen_layer_tokens(seed, int(cu[-1]), H, dk, dv, dtype, gate_mu, threads=1, gate=gate)
+    d["cu_seqlens"] = cu
+    d["init"] = None if init_std is None else gen_states(seed, len(lens), H, dk, dv, init_std)
+    d["norm_weight"] = gen_norm_weight(seed, dv)
     return d

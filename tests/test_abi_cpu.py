@@ -146,3 +146,45 @@ def test_workspace_size_windows(L):
     s = _shape(1, 65536, 64, 1024, 32, 128, 128, BF16, F32)
     state = 64 * 32 * 128 * 128 * 4
     assert L.kda_chunk_fwd_workspace_size(s) == state + 64 * 32 * rec
+
+
+def _layer(norm=1, l2=1e-6, gate=True, og=True, w=True, rms=1e-6, base=40):
+    addr = lambda i: (base + i) * A
+    return _lib.Layer(norm, l2, addr(0) if gate else None, addr(1) if og else None, addr(2) if w else None, rms)
+
+
+def _layer_fwd(L, layer, ws_bytes=0):
+    s = _shape(1, 256, 0, 0, 2, 64, 64, BF16, BF16)
+    q, k, v, b, out, ws = (i * A for i in (2, 4, 6, 8, 10, 12))
+    return L.kda_layer_fwd(s, layer, q, k, v, b, None, None, out, None, ws, ws_bytes, None)
+
+
+def test_layer_fwd_validation(L):
+    """Valid layer options reach the workspace check; bad ones stop before it."""
+    assert _layer_fwd(L, _layer()) == WORKSPACE
+    assert _layer_fwd(L, _layer(og=False, w=False)) == WORKSPACE  # no epilogue
+    assert _layer_fwd(L, _layer(norm=0)) == WORKSPACE
+    assert _layer_fwd(L, None) == INVALID
+    assert _layer_fwd(L, _layer(norm=2)) == INVALID
+    assert _layer_fwd(L, _layer(l2=-1.0)) == INVALID
+    assert _layer_fwd(L, _layer(rms=float("nan"))) == INVALID
+    assert _layer_fwd(L, _layer(rms=float("inf"))) == INVALID
+    assert _layer_fwd(L, _layer(gate=False)) == INVALID  # the gate pre-activation is required
+    # output overlapping the output gate or the weight
+    s = _shape(1, 256, 0, 0, 2, 64, 64, BF16, BF16)
+    lay = _lib.Layer(1, 1e-6, 40 * A, 10 * A + 64, 42 * A, 1e-6)
+    q, k, v, b, out, ws = (i * A for i in (2, 4, 6, 8, 10, 12))
+    assert L.kda_layer_fwd(s, lay, q, k, v, b, None, None, out, None, ws, 0, None) == INVALID
+
+
+def test_layer_decode_validation(L):
+    """Rejections of kda_layer_decode_step, all before any launch."""
+    q, k, v, b, st, out = (i * A for i in (2, 4, 6, 8, 10, 14))
+    call = lambda lay, gph=0: L.kda_layer_decode_step(4, 2, 64, 64, BF16, F32, gph, lay, q, k, v, b, st, out, None)
+    assert call(None) == INVALID
+    assert call(_layer(norm=3)) == INVALID
+    assert call(_layer(l2=float("nan"))) == INVALID
+    assert call(_layer(rms=-1e-3)) == INVALID
+    assert call(_layer(gate=False)) == INVALID
+    assert call(_layer(), gph=2) == INVALID
+    assert L.kda_layer_decode_step(4, 2, 96, 96, BF16, F32, 0, _layer(), q, k, v, b, st, out, None) == UNSUPPORTED
