@@ -11,7 +11,9 @@ prefill (outside its events) so no input is served from L2 or the MALL.
 Prints one JSON line.  ``value`` is prefill tokens/s; the decode HBM
 bandwidth is in ``decode``.  ``roofline`` describes the dominant kernel of a
 step (the decode kernel: 100 launches per step); ``prefill_roofline`` the
-prefill call.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
+prefill call.  ``layer`` times the fused layer (q/k L2 norm, gate from its
+projection output, RMSNorm with sigmoid output gate, bf16 y) on the same
+shapes.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
 on the prefill workload (by default all of it: about 5-15 s on 16 host cores).
 """
 from __future__ import annotations
@@ -53,6 +55,17 @@ def prefill_bytes(tokens, heads, d, in_b=2, out_b=4, states=1, gate_per_head=Fal
 def decode_bytes(units, d, in_b=2, out_b=4, gate_per_head=False):
     """State read + write, plus q,k,v, log_alpha, beta and out, per (sequence, head)."""
     return units * (2 * d * d * 4 + 3 * d * in_b + 4 * (1 if gate_per_head else d) + 4 + d * out_b)
+
+
+def layer_prefill_bytes(tokens, heads, d, states=1):
+    """Algorithmic HBM bytes of the fused layer prefill: bf16 q,k,v, gate pre-activation, output
+    gate and y, fp32 beta, plus state in/out and the RMSNorm weight."""
+    return tokens * heads * (3 * d * 2 + d * 2 + 4 + d * 2 + d * 2) + 2 * states * heads * d * d * 4 + d * 4
+
+
+def layer_decode_bytes(units, d):
+    """State read + write plus the layer's per-(sequence, head) inputs and bf16 y."""
+    return units * (2 * d * d * 4 + 3 * d * 2 + d * 2 + 4 + d * 2 + d * 2) + d * 4
 
 
 def to_dev(x, torch):
@@ -113,6 +126,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill (tuning runs)")
     ap.add_argument("--gate", choices=("channel", "head"), default="channel",
                     help="channel: KDA (log_alpha [.., H, dk]); head: one gate per head (Gated DeltaNet)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip the fused layer (q/k L2 norm, gate from its projection, RMSNorm-sigmoid epilogue)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -245,10 +260,65 @@ def main():
         "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
                    "(model level, hardware not stated)",
     }
+    if not (args.no_layer or args.prefill_only or gph):
+        res["layer"] = bench_layer(kda, torch, synth, wp, wd, args, flush, stream)
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         res["cpu_baseline"] = cpu_baseline(wp, d, args.cpu_sample, threads)
     print(json.dumps(res), flush=True)
+
+
+def bench_layer(kda, torch, synth, wp, wd, args, flush, stream):
+    """The fused layer on the same shapes: prefill (bf16 y) and 100 decode steps (bf16 y), timed
+    after the main steps with their own warm-up."""
+    t0 = time.time()
+    d = synth.make_layer_prefill(wp)
+    T, H, D = wp.seqlen, wp.heads, wp.dk
+    q, k, v, g, be, z = (to_dev(d[x], torch).unsqueeze(0) for x in ("q", "k", "v", "g", "beta", "out_gate"))
+    init, wt = to_dev(d["init"], torch), to_dev(d["norm_weight"], torch)
+    del d
+    y = torch.empty((1, T, H, D), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    state = to_dev(synth.make_decode_state(wd), torch)
+    steps = []
+    for s in range(args.decode_steps):
+        st = synth.make_layer_decode_step(wd, s)
+        steps.append(tuple(to_dev(st[x], torch) for x in ("q", "k", "v", "g", "beta", "out_gate")))
+    dy = torch.empty((wd.batch, wd.heads, wd.dv), dtype=torch.bfloat16, device="cuda")
+    log(f"layer inputs generated in {time.time() - t0:.1f}s")
+
+    def prefill():
+        kda.layer_fwd(q, k, v, g, be, init, None, out_gate=z, norm_weight=wt, out=y, final_state=fin,
+                      workspace=ws)
+
+    def decode_all():
+        for (sq, sk, sv, sg, sb, sz) in steps:
+            kda.layer_decode_step(sq, sk, sv, sg, sb, state, out_gate=sz, norm_weight=wt, out=dy)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode_all()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        flush.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        prefill()
+        ev[i][1].record(stream)
+        decode_all()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    pre_s = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])) / 1e3
+    dec_s = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])) / 1e3 / len(steps)
+    pb, db = layer_prefill_bytes(T, H, D), layer_decode_bytes(wd.batch * wd.heads, D)
+    return {"what": "q/k L2 norm + log alpha = -softplus(bf16 gate) + recurrence + RMSNorm * sigmoid(bf16 gate), "
+                    "bf16 y",
+            "prefill": {"ms": pre_s * 1e3, "tokens_per_s": T / pre_s, "algorithmic_bytes": pb,
+                        "hbm_gbs": pb / pre_s / 1e9, "frac": pb / pre_s / 1e9 / HBM_PEAK_GBS},
+            "decode": {"us_per_step": dec_s * 1e6, "algorithmic_bytes": db, "hbm_gbs": db / dec_s / 1e9,
+                       "frac": db / dec_s / 1e9 / HBM_PEAK_GBS}}
 
 
 if __name__ == "__main__":

@@ -235,6 +235,32 @@ struct QKReg<bf16_t, true> {
     using type = Pair8<_Float16>;
 };
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f32(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Sum of x over the NP lanes (64 or 32) that hold one row, in every lane: inside
+// each 16-lane row through DPP (lane pairs, quads, mirrored half-rows, mirrored
+// rows), then across the rows through lane reads -- no LDS traffic.
+template <int NP>
+__device__ __forceinline__ float row_sum(float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    const float a = lane_f32(x, 0), b = lane_f32(x, 16), c = lane_f32(x, 32), d = lane_f32(x, 48);
+    if constexpr (NP == 64) {
+        return (a + b) + (c + d);
+    } else {
+        static_assert(NP == 32, "rows span 32 or 64 lanes");
+        return (__lane_id() < 32) ? a + b : c + d;
+    }
+}
+
 // q and k of a thread's eight rows divided by their L2 norms over the key
 // channels (the NP lanes that hold a row share its sum of squares).
 template <int NP, typename IT, typename QT>
@@ -243,12 +269,7 @@ __device__ __forceinline__ void l2norm_rows(const Pair8<IT>& kr, const Pair8<IT>
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float k0 = kr.get(i, 0), k1 = kr.get(i, 1), q0 = qr.get(i, 0), q1 = qr.get(i, 1);
-        float sk = k0 * k0 + k1 * k1, sq = q0 * q0 + q1 * q1;
-#pragma unroll
-        for (int off = 1; off < NP; off *= 2) {
-            sk += __shfl_xor(sk, off);
-            sq += __shfl_xor(sq, off);
-        }
+        const float sk = row_sum<NP>(k0 * k0 + k1 * k1), sq = row_sum<NP>(q0 * q0 + q1 * q1);
         const float rk = __builtin_amdgcn_rsqf(sk + eps), rq = __builtin_amdgcn_rsqf(sq + eps);
         kk.set(i, k0 * rk, k1 * rk);
         qq.set(i, q0 * rq, q1 * rq);
@@ -279,7 +300,7 @@ __device__ __forceinline__ void put2<float>(float* dst, float a, float b) {
 constexpr float F16_OPERAND_LIMIT = 6.0e4f;
 constexpr float F16_FACTOR_LIMIT = 256.f;
 
-template <int D, typename IT, typename OT, bool QKN>
+template <int D, typename IT, typename OT, bool QKN, bool GPRE>
 __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
     using C = LocalCfg<D, OT>;
     using R = Rec<D, OT>;
@@ -332,34 +353,36 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     float al[8][2];
     float bval;
     {
-        float2 lr[8];
-        size_t off[8];
-        if (a.gate) {  // bf16 gate pre-activation g of the layer: alpha = sigmoid(-g)
+        // Raw gate words: an fp32 pair (log_alpha per channel) or one fp32 (per
+        // head); with GPRE (the layer's gate pre-activation) a bf16 pair or one
+        // bf16.  The branches only issue loads; the words are decoded after k, q
+        // and v are in flight, so no branch waits for its own loads.
+        uint32_t g0[8], g1[8];
+        size_t off[8], th[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const size_t th = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
-                off[i] = th * D + ch;
-                if (a.gate_per_head) {
-                    const float g = bf16_bits_to_f32(a.gate[th]);
-                    lr[i] = make_float2(g, g);
-                } else {
-                    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.gate + off[i]));
-                    lr[i] = make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
-                }
-            }
-        } else if (a.gate_per_head) {  // one gate per (token, head), shared by every key channel
+        for (int i = 0; i < 8; ++i) {
+            th[i] = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
+            off[i] = th[i] * D + ch;
+        }
+        if constexpr (GPRE) {
+            if (a.gate_per_head) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const size_t th = (size_t)(tok0 + min(r0 + i, n - 1)) * H + h;
-                off[i] = th * D + ch;
-                const float g = a.la[th];
-                lr[i] = make_float2(g, g);
+                for (int i = 0; i < 8; ++i) g0[i] = a.gate[th[i]], g1[i] = 0u;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    g0[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.gate + off[i])), g1[i] = 0u;
             }
         } else {
+            if (a.gate_per_head) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                off[i] = ((size_t)(tok0 + min(r0 + i, n - 1)) * H + h) * D + ch;
-                lr[i] = make_float2(__builtin_nontemporal_load(a.la + off[i]), __builtin_nontemporal_load(a.la + off[i] + 1));
+                for (int i = 0; i < 8; ++i) g1[i] = g0[i] = __float_as_uint(a.la[th[i]]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    g0[i] = __float_as_uint(__builtin_nontemporal_load(a.la + off[i]));
+                    g1[i] = __float_as_uint(__builtin_nontemporal_load(a.la + off[i] + 1));
+                }
             }
         }
         // every thread loads a beta (no branch around a load); thread t < 64 stores row t
@@ -370,17 +393,19 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         for (int i = 0; i < 8; ++i) qraw.load(i, q + off[i]);
 #pragma unroll
         for (int i = 0; i < 8; ++i) vv.load(i, v + off[i]);
-        if (a.gate) {  // 1 / (1 + e^g)
+        if constexpr (GPRE) {  // bf16 gate pre-activation g: alpha = sigmoid(-g) = 1 / (1 + e^g)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                al[i][0] = __builtin_amdgcn_rcpf(1.f + fast_exp(lr[i].x));
-                al[i][1] = __builtin_amdgcn_rcpf(1.f + fast_exp(lr[i].y));
+                const float x0 = __uint_as_float(g0[i] << 16);
+                const float x1 = a.gate_per_head ? x0 : __uint_as_float(g0[i] & 0xFFFF0000u);
+                al[i][0] = __builtin_amdgcn_rcpf(1.f + fast_exp(x0));
+                al[i][1] = __builtin_amdgcn_rcpf(1.f + fast_exp(x1));
             }
-        } else {
+        } else {  // log_alpha
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                al[i][0] = fast_exp(lr[i].x);
-                al[i][1] = fast_exp(lr[i].y);
+                al[i][0] = fast_exp(__uint_as_float(g0[i]));
+                al[i][1] = fast_exp(__uint_as_float(g1[i]));
             }
         }
         // rows past the end decay by nothing (only in a sequence's last chunk; testing
@@ -939,8 +964,11 @@ __device__ __forceinline__ void store_out(float* p, float x) { __builtin_nontemp
 __device__ __forceinline__ void store_out(bf16_t* p, float x) {
     __builtin_nontemporal_store(f32_to_bf16(x).bits, reinterpret_cast<uint16_t*>(p));
 }
-// fp16 o for the layer epilogue, which reads it back right away: a plain store
-__device__ __forceinline__ void store_out(_Float16* p, float x) { *p = (_Float16)x; }
+// fp16 o for the layer epilogue: non-temporal too (plain stores allocate in the
+// last-level cache and evict the records the state pass still reads)
+__device__ __forceinline__ void store_out(_Float16* p, float x) {
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, (_Float16)x), reinterpret_cast<uint16_t*>(p));
+}
 
 template <typename OT>
 struct Frag;
@@ -1265,7 +1293,7 @@ __global__ void __launch_bounds__(256) chunk_segment_combine_kernel(ChunkArgs a)
 // ---------------------------------------------------------------------------
 // Head-wise RMSNorm and sigmoid output gate ("Kimi Delta Attention" section):
 // y = o / sqrt(mean_j o_j^2 + eps) * w * sigmoid(z) per (token, head), in place
-// in `out` over the chunks of one window.  o is what the state pass wrote (OI:
+// in `out` over chunks win * Wc .. win * Wc + Wc - 1 of every sequence.  o is what the state pass wrote (OI:
 // fp16 when y is bf16, else fp32); the mean needs a row's dv values, which the
 // state pass spreads over its value-slice workgroups, hence a pass of its own.
 // One workgroup per (head, chunk); LPR lanes hold a row, eight values each.
@@ -1367,7 +1395,7 @@ int chunk_value_slice(int d, int64_t units) {
 // more, the chunk-local pass of window w+1 (caller's stream) overlaps the state
 // pass of window w (the auxiliary stream), the records alternating between two
 // buffers: the local pass of window w+2 waits for the state pass of window w.
-template <int D, typename IT, typename OT, typename OUT, bool QKN, int BV>
+template <int D, typename IT, typename OT, typename OUT, bool QKN, bool GPRE, int BV>
 static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     const int units = base.N * base.H;
@@ -1378,7 +1406,8 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
         if (two) a.rec = base.rec + (size_t)(w & 1) * ov.buffer_bytes;
         hipError_t e;
         if (two && w >= 2 && (e = hipStreamWaitEvent(st, ov.inter_done[w & 1], 0)) != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st, a);
+        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st,
+                           a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipStream_t is = st;
         if (two) {
@@ -1388,22 +1417,33 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
         }
         hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, is, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (a.out_gate && (e = launch_epilogue<D, OUT>(a, is)) != hipSuccess) return e;
         if (two && (e = hipEventRecord(ov.inter_done[w & 1], ov.side)) != hipSuccess) return e;
     }
-    if (two) return hipStreamWaitEvent(st, ov.inter_done[(nwin - 1) & 1], 0);
+    if (two) {
+        hipError_t e = hipStreamWaitEvent(st, ov.inter_done[(nwin - 1) & 1], 0);
+        if (e != hipSuccess) return e;
+    }
+    if (!base.out_gate) return hipSuccess;
+    // the epilogue after the last state pass (between state passes it would
+    // evict the records they read), window by window to keep the grid small
+    for (int w = 0; w < nwin; ++w) {
+        ChunkArgs a = base;
+        a.win = w;
+        hipError_t e = launch_epilogue<D, OUT>(a, st);
+        if (e != hipSuccess) return e;
+    }
     return hipSuccess;
 }
 
 // Sequence-parallel state pass: all records in one buffer (a.win = 0, a.Wc =
 // every chunk), a.G segments of a.Sc chunks per sequence.
-template <int D, typename IT, typename OT, typename OUT, bool QKN>
+template <int D, typename IT, typename OT, typename OUT, bool QKN, bool GPRE>
 static hipError_t run_segments(const ChunkArgs& a, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     constexpr int BV = SEGMENT_BV;
     const int NH = a.N * a.H;
     hipError_t e;
-    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
+    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 1>), dim3(NH * 2 * (D / BV) * a.G), dim3(512), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1436,28 +1476,31 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
     return (int)((max_chunks + sc - 1) / sc);
 }
 
-template <int D, typename IT, typename OT, typename OUT, bool QKN>
+template <int D, typename IT, typename OT, typename OUT, bool QKN, bool GPRE>
 static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, const Overlap& ov, hipStream_t st) {
-    if (a.G > 0) return run_segments<D, IT, OT, OUT, QKN>(a, st);
-    if (bv == 16) return run_windows<D, IT, OT, OUT, QKN, 16>(a, nwin, ov, st);
-    if (bv == 32) return run_windows<D, IT, OT, OUT, QKN, 32>(a, nwin, ov, st);
-    return run_windows<D, IT, OT, OUT, QKN, 64>(a, nwin, ov, st);
+    if (a.G > 0) return run_segments<D, IT, OT, OUT, QKN, GPRE>(a, st);
+    if (bv == 16) return run_windows<D, IT, OT, OUT, QKN, GPRE, 16>(a, nwin, ov, st);
+    if (bv == 32) return run_windows<D, IT, OT, OUT, QKN, GPRE, 32>(a, nwin, ov, st);
+    return run_windows<D, IT, OT, OUT, QKN, GPRE, 64>(a, nwin, ov, st);
 }
 
 // Output type of the state pass: the result's type, or fp16 in place of bf16
 // when the layer epilogue follows (it reads o back and writes bf16 over it).
-template <int D, typename IT, typename OT, bool QKN>
+template <int D, typename IT, typename OT, bool QKN, bool GPRE>
 static hipError_t run_out(const ChunkArgs& a, bool out_bf16, int nwin, int bv, const Overlap& ov, hipStream_t st) {
-    if (!out_bf16) return run_bv<D, IT, OT, float, QKN>(a, nwin, bv, ov, st);
-    if (a.out_gate) return run_bv<D, IT, OT, _Float16, QKN>(a, nwin, bv, ov, st);
-    return run_bv<D, IT, OT, bf16_t, QKN>(a, nwin, bv, ov, st);
+    if (!out_bf16) return run_bv<D, IT, OT, float, QKN, GPRE>(a, nwin, bv, ov, st);
+    if (a.out_gate) return run_bv<D, IT, OT, _Float16, QKN, GPRE>(a, nwin, bv, ov, st);
+    return run_bv<D, IT, OT, bf16_t, QKN, GPRE>(a, nwin, bv, ov, st);
 }
 
+// The plain operator (log_alpha, q and k as given) or the layer (gate
+// pre-activation, q and k normalised or not).
 template <int D, typename IT, typename OT>
 static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int nwin, int bv, const Overlap& ov,
                            hipStream_t st) {
-    if (qk_norm) return run_out<D, IT, OT, true>(a, out_bf16, nwin, bv, ov, st);
-    return run_out<D, IT, OT, false>(a, out_bf16, nwin, bv, ov, st);
+    if (!a.gate) return run_out<D, IT, OT, false, false>(a, out_bf16, nwin, bv, ov, st);
+    if (qk_norm) return run_out<D, IT, OT, true, true>(a, out_bf16, nwin, bv, ov, st);
+    return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, ov, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,

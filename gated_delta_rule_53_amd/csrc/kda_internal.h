@@ -66,8 +66,8 @@ int chunk_value_slice(int d, int64_t units);
 int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks_per_segment);
 // qk_norm: q and k L2-normalised per (token, head) in the chunk-local pass.
 // With a.out_gate set, the state pass writes o to `out` (fp16 when out_bf16,
-// else fp32) and an epilogue pass after each window replaces it in place by
-// RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
+// else fp32) and an epilogue pass after the last window replaces it in place
+// by RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
                           const Overlap& ov, hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,

@@ -183,7 +183,7 @@ typedef struct {
  * workspace (kda_chunk_fwd_workspace_size of the same shape) are those of
  * kda_chunk_fwd; `out` holds y.  With an epilogue the state pass first writes
  * o into `out` (fp16 when out_dtype is bf16, so |o| must stay below 6.5e4) and
- * a last pass per window rewrites it in place as y. */
+ * a last pass rewrites it in place as y. */
 kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
                            const void* v, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
