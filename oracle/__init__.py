@@ -10,6 +10,8 @@ Attention", "Why channel-wise gating matters" and "The constrained DPLR form
 and the chunkwise algorithm"):
 
 * ``recurrent``   -- plain C, fp64, token by token (kda_oracle.c); the oracle.
+* ``backward``    -- its reverse mode: the adjoint of each token step, fp64,
+  in the same C file; pinned by finite differences and a closed form.
 * ``forms.brute`` -- explicit dk x dk transition matrices and the
   "query dotted with keys weighted by a cumulative product of transitions"
   expansion; numpy fp64, tiny sizes only.
@@ -61,6 +63,10 @@ def _lib(mutant: int = 0):
                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    b = lib.kda_oracle_backward
+    b.restype = ctypes.c_int
+    b.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 14 + [ctypes.c_int]
     _LIBS[mutant] = lib
     return lib
 
@@ -121,6 +127,51 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed ({rc})")
     return out.reshape(vshape), fin
+
+
+def backward(q, k, v, log_alpha, beta, d_out, init_state=None, d_final=None, cu_seqlens=None, threads=None):
+    """fp64 gradients of L = sum(d_out * out) + sum(d_final * final_state) through the recurrence.
+
+    Inputs as for ``recurrent`` (packed [T, H, d]; float32, bf16 bits or float64);
+    d_out [T, H, dv] and d_final [N, H, dk, dv] (or None) any float dtype.  The
+    reverse mode is the hand-derived adjoint of each token step
+    (kda_oracle_backward in kda_oracle.c).  A per-head log_alpha [T, H] gets the
+    sum over key channels of the per-channel gradient.
+    Returns dict dq, dk [T, H, dk], dv [T, H, dv], dlog_alpha (shape of
+    log_alpha), dbeta [T, H], dinit [N, H, dk, dv], all fp64.
+    """
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], np.int64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    assert int(cu[-1]) == T
+    bf16 = q.dtype == np.uint16
+    f64 = q.dtype == np.float64
+    kind = 2 if f64 else int(bf16)
+    want = np.float64 if f64 else (np.uint16 if bf16 else np.float32)
+    fwant = np.float64 if f64 else np.float32
+    q, k, v = (np.ascontiguousarray(x, dtype=want) for x in (q, k, v))
+    per_head = np.asarray(log_alpha).ndim == 2
+    la = np.ascontiguousarray(log_alpha, dtype=fwant)
+    if per_head:
+        la = np.ascontiguousarray(np.broadcast_to(la[:, :, None], (T, H, dk)))
+    be = np.ascontiguousarray(beta, dtype=fwant).reshape(T, H)
+    init = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float64)
+    dO = np.ascontiguousarray(d_out, dtype=np.float64)
+    dF = None if d_final is None else np.ascontiguousarray(d_final, dtype=np.float64)
+    g = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+         "dlog_alpha": np.zeros((T, H, dk)), "dbeta": np.zeros((T, H)), "dinit": np.zeros((N, H, dk, dv))}
+    nt = threads or max(1, min(64, os.cpu_count() or 1))
+    rc = _lib(0).kda_oracle_backward(N, cu.ctypes.data, H, dk, dv, kind, _ptr(q), _ptr(k), _ptr(v), _ptr(la),
+                                     _ptr(be), _ptr(init), _ptr(dO), _ptr(dF), _ptr(g["dq"]), _ptr(g["dk"]),
+                                     _ptr(g["dv"]), _ptr(g["dlog_alpha"]), _ptr(g["dbeta"]), _ptr(g["dinit"]), nt)
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed ({rc})")
+    if per_head:
+        g["dlog_alpha"] = g["dlog_alpha"].sum(axis=2)
+    return g
 
 
 def decode_steps(state, steps, threads=None, mutant: int = 0):

@@ -240,3 +240,222 @@ int kda_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, i
 }
 
 int kda_oracle_mutant(void) { return KDA_ORACLE_MUTANT; }
+
+/*
+ * Reverse mode of the same recurrence (the gradients of a loss L through every
+ * token step above), fp64.  Per (sequence, head), with S_prev the state before
+ * token t, S' = Diag(alpha) S_prev, p = S'^T k, u = beta (v - p),
+ * S_t = S' + k u^T and o_t = S_t^T q, walking t backwards with dS = dL/dS_t:
+ *     dS     += q do_t^T                       (o_t = S_t^T q)
+ *     dq_t    = S_t do_t
+ *     dk_t    = dS u ;  du = dS^T k            (S_t = S' + k u^T, dS' = dS)
+ *     dbeta_t = du . (v - p) ;  dv_t = beta du ;  dp = -beta du
+ *     dS'    += k dp^T ;  dk_t += S' dp        (p = S'^T k)
+ *     dlog_alpha_t[c] = alpha_c sum_j S_prev[c][j] dS'[c][j]
+ *     dS      = Diag(alpha) dS'                (dL/dS_prev)
+ * and dL/dS_0 is dS after the first token.  States are checkpointed every 64
+ * tokens on the way forward and each segment is recomputed before it is walked
+ * back.  dO [T_total, heads, dv] and dS_final [num_seqs, heads, dk, dv] (or
+ * NULL: zero) are fp64; inputs as for kda_oracle_forward; outputs fp64: dq, dk
+ * [T_total, heads, dk], dv [T_total, heads, dv], dlog_alpha [T_total, heads,
+ * dk], dbeta [T_total, heads], dS0 [num_seqs, heads, dk, dv].
+ */
+#define BWD_SEG 64
+
+typedef struct {
+    job_t f;
+    const double *dO, *dS_final;
+    double *dq, *dk, *dv, *dla, *dbeta, *dS0;
+} bjob_t;
+
+static void load_token(const job_t* J, int64_t th, double* kv, double* qv, double* vv, double* av, double* b) {
+    const int dk = J->dk, dv = J->dv;
+    for (int c = 0; c < dk; ++c) {
+        kv[c] = load_in(J->k, J->in_bf16, th * dk + c);
+        qv[c] = load_in(J->q, J->in_bf16, th * dk + c);
+        av[c] = exp(load_gate(J, th * dk + c));
+    }
+    for (int j = 0; j < dv; ++j) vv[j] = load_in(J->v, J->in_bf16, th * dv + j);
+    *b = J->in_bf16 == 2 ? ((const double*)J->beta)[th] : (double)((const float*)J->beta)[th];
+}
+
+/* one forward token step: S (state before) -> S (state after); u and p returned */
+static void step_fwd(double* S, int dk, int dv, const double* kv, const double* vv, const double* av, double b,
+                     double* p, double* u) {
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j) S[c * dv + j] *= av[c];
+    for (int j = 0; j < dv; ++j) p[j] = 0.0;
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j) p[j] += S[c * dv + j] * kv[c];
+    for (int j = 0; j < dv; ++j) u[j] = b * (vv[j] - p[j]);
+    for (int c = 0; c < dk; ++c)
+        for (int j = 0; j < dv; ++j) S[c * dv + j] += kv[c] * u[j];
+}
+
+static int bwd_unit(bjob_t* B, int64_t unit) {
+    job_t* J = &B->f;
+    const int H = J->heads, dk = J->dk, dv = J->dv;
+    const int64_t s = unit / H, h = unit % H;
+    const int64_t t0 = J->cu[s], t1 = J->cu[s + 1], n = t1 - t0;
+    const size_t SS = (size_t)dk * dv;
+    const int64_t nseg = (n + BWD_SEG - 1) / BWD_SEG;
+    double* ck = (double*)malloc(sizeof(double) * SS * (size_t)(nseg > 0 ? nseg : 1));  /* state before each segment */
+    double* seg = (double*)malloc(sizeof(double) * SS * BWD_SEG);                      /* state before each token */
+    double* S = (double*)malloc(sizeof(double) * SS);
+    double* Sp = (double*)malloc(sizeof(double) * SS);  /* S' */
+    double* dS = (double*)malloc(sizeof(double) * SS);
+    const int dm = dk > dv ? dk : dv;
+    double* buf = (double*)malloc(sizeof(double) * (size_t)dm * 8);
+    if (!ck || !seg || !S || !Sp || !dS || !buf) {
+        free(ck); free(seg); free(S); free(Sp); free(dS); free(buf);
+        return 1;
+    }
+    double *kv = buf, *qv = buf + dm, *vv = buf + 2 * dm, *av = buf + 3 * dm, *p = buf + 4 * dm, *u = buf + 5 * dm,
+           *du = buf + 6 * dm, *dp = buf + 7 * dm;
+    double b;
+    for (size_t i = 0; i < SS; ++i) S[i] = J->init ? J->init[(s * H + h) * SS + i] : 0.0;
+    for (int64_t m = 0; m < nseg; ++m) {
+        memcpy(ck + (size_t)m * SS, S, sizeof(double) * SS);
+        const int64_t e = t0 + (m + 1) * BWD_SEG < t1 ? t0 + (m + 1) * BWD_SEG : t1;
+        for (int64_t t = t0 + m * BWD_SEG; t < e; ++t) {
+            load_token(J, t * H + h, kv, qv, vv, av, &b);
+            step_fwd(S, dk, dv, kv, vv, av, b, p, u);
+        }
+    }
+    for (size_t i = 0; i < SS; ++i) dS[i] = B->dS_final ? B->dS_final[(s * H + h) * SS + i] : 0.0;
+    for (int64_t m = nseg - 1; m >= 0; --m) {
+        const int64_t a = t0 + m * BWD_SEG, e = a + BWD_SEG < t1 ? a + BWD_SEG : t1;
+        memcpy(S, ck + (size_t)m * SS, sizeof(double) * SS);
+        for (int64_t t = a; t < e; ++t) {
+            memcpy(seg + (size_t)(t - a) * SS, S, sizeof(double) * SS);
+            load_token(J, t * H + h, kv, qv, vv, av, &b);
+            step_fwd(S, dk, dv, kv, vv, av, b, p, u);
+        }
+        for (int64_t t = e - 1; t >= a; --t) {
+            const int64_t th = t * H + h;
+            const double* Sprev = seg + (size_t)(t - a) * SS;
+            load_token(J, th, kv, qv, vv, av, &b);
+            /* recompute S', p, u and S_t */
+            for (int c = 0; c < dk; ++c)
+                for (int j = 0; j < dv; ++j) Sp[c * dv + j] = av[c] * Sprev[c * dv + j];
+            for (int j = 0; j < dv; ++j) p[j] = 0.0;
+            for (int c = 0; c < dk; ++c)
+                for (int j = 0; j < dv; ++j) p[j] += Sp[c * dv + j] * kv[c];
+            for (int j = 0; j < dv; ++j) u[j] = b * (vv[j] - p[j]);
+            const double* doo = B->dO + th * dv;
+            /* output: dS += q do^T, dq = S_t do with S_t = S' + k u^T */
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    acc += (Sp[c * dv + j] + kv[c] * u[j]) * doo[j];
+                    dS[c * dv + j] += qv[c] * doo[j];
+                }
+                B->dq[th * dk + c] = acc;
+            }
+            /* write: dk = dS u, du = dS^T k */
+            for (int j = 0; j < dv; ++j) du[j] = 0.0;
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    acc += dS[c * dv + j] * u[j];
+                    du[j] += dS[c * dv + j] * kv[c];
+                }
+                B->dk[th * dk + c] = acc;
+            }
+            /* correction: dbeta, dv, dp */
+            double db = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                db += du[j] * (vv[j] - p[j]);
+                B->dv[th * dv + j] = b * du[j];
+                dp[j] = -b * du[j];
+            }
+            B->dbeta[th] = db;
+            /* prediction: dS' = dS + k dp^T, dk += S' dp */
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    dS[c * dv + j] += kv[c] * dp[j];
+                    acc += Sp[c * dv + j] * dp[j];
+                }
+                B->dk[th * dk + c] += acc;
+            }
+            /* decay: dlog_alpha, dS_prev = Diag(alpha) dS' */
+            for (int c = 0; c < dk; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += Sprev[c * dv + j] * dS[c * dv + j];
+                B->dla[th * dk + c] = av[c] * acc;
+                for (int j = 0; j < dv; ++j) dS[c * dv + j] *= av[c];
+            }
+        }
+    }
+    memcpy(B->dS0 + (s * H + h) * SS, dS, sizeof(double) * SS);
+    free(ck); free(seg); free(S); free(Sp); free(dS); free(buf);
+    return 0;
+}
+
+static void* bwd_worker(void* arg) {
+    bjob_t* B = (bjob_t*)arg;
+    job_t* J = &B->f;
+    const int64_t units = J->num_seqs * J->heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        const int64_t unit = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (unit >= units) break;
+        if (bwd_unit(B, unit)) return (void*)1;
+    }
+    return NULL;
+}
+
+int kda_oracle_backward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, int dk, int dv, int in_bf16,
+                        const void* q, const void* k, const void* v, const void* log_alpha, const void* beta,
+                        const double* init_state, const double* dO, const double* dS_final, double* dq,
+                        double* dk_out, double* dv_out, double* dla, double* dbeta, double* dS0, int nthreads) {
+    if (num_seqs < 0 || heads <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens || cu_seqlens[0] != 0) return 1;
+    for (int64_t s = 0; s < num_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return 1;
+    if (!dS0) return 1;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !log_alpha || !beta || !dO || !dq || !dk_out || !dv_out ||
+                                     !dla || !dbeta))
+        return 1;
+    bjob_t B;
+    memset(&B, 0, sizeof B);
+    B.f.num_seqs = num_seqs;
+    B.f.cu = cu_seqlens;
+    B.f.heads = heads;
+    B.f.dk = dk;
+    B.f.dv = dv;
+    B.f.in_bf16 = in_bf16;
+    B.f.q = q;
+    B.f.k = k;
+    B.f.v = v;
+    B.f.log_alpha = log_alpha;
+    B.f.beta = beta;
+    B.f.init = init_state;
+    B.f.next_unit = 0;
+    B.dO = dO;
+    B.dS_final = dS_final;
+    B.dq = dq;
+    B.dk = dk_out;
+    B.dv = dv_out;
+    B.dla = dla;
+    B.dbeta = dbeta;
+    B.dS0 = dS0;
+    pthread_mutex_init(&B.f.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int rc = 0, started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, bwd_worker, &B) != 0) break;
+        ++started;
+    }
+    if (started == 0) rc = bwd_worker(&B) != NULL;
+    for (int i = 0; i < started; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r) rc = 2;
+    }
+    pthread_mutex_destroy(&B.f.lock);
+    return rc;
+}
