@@ -11,7 +11,7 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size", "KdaError"]
 
 
 def _torch():
@@ -236,3 +236,58 @@ def layer_decode_step(q, k, v, gate, beta, state, *, out_gate=None, norm_weight=
                                      beta.data_ptr(), state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
     _lib.check(st, "kda_layer_decode_step")
     return out
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final=None, cu_seqlens=None, *,
+              max_seqlen=None, want_d_init=True, workspace=None):
+    """Gradients of sum(d_out * out) + sum(d_final * final_state) through the chunked prefill.
+
+    Inputs as for ``chunk_fwd``; d_out [B,T,H,dv] (the dtype ``out`` had), d_final
+    [N,H,dk,dv] fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha
+    (the shape of log_alpha), dbeta and, with ``want_d_init``, d_init.
+    """
+    torch = _torch()
+    _check_dev(q, "q")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _check_dev(k, "k", q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (B, T, H, dv))
+    gate_per_head = log_alpha.dim() == 3
+    _check_dev(log_alpha, "log_alpha", torch.float32, (B, T, H) if gate_per_head else (B, T, H, dk))
+    _check_dev(beta, "beta", torch.float32, (B, T, H))
+    _check_dev(d_out, "d_out", None, (B, T, H, dv))
+    if cu_seqlens is not None:
+        _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if B != 1:
+            raise ValueError("varlen inputs must have batch 1")
+        N = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            max_seqlen = T
+    else:
+        N = B
+    if init_state is not None:
+        _check_dev(init_state, "init_state", torch.float32, (N, H, dk, dv))
+    if d_final is not None:
+        _check_dev(d_final, "d_final", torch.float32, (N, H, dk, dv))
+    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
+                       _dtype_code(q.dtype), _dtype_code(d_out.dtype), int(gate_per_head))
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+         "dv": torch.empty((B, T, H, dv), **f32), "dlog_alpha": torch.empty(tuple(log_alpha.shape), **f32),
+         "dbeta": torch.empty((B, T, H), **f32)}
+    if want_d_init:
+        g["d_init"] = torch.empty((N, H, dk, dv), **f32)
+    L = lib()
+    need = int(L.kda_chunk_bwd_workspace_size(shape))
+    if need == 0:
+        raise KdaError(2, "kda_chunk_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_dev(workspace, "workspace", torch.uint8)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = L.kda_chunk_bwd(shape, ptr(q), ptr(k), ptr(v), ptr(log_alpha), ptr(beta), ptr(init_state),
+                         ptr(cu_seqlens), ptr(d_out), ptr(d_final), ptr(g["dq"]), ptr(g["dk"]), ptr(g["dv"]),
+                         ptr(g["dlog_alpha"]), ptr(g["dbeta"]), ptr(g.get("d_init")), ptr(workspace),
+                         workspace.numel(), _stream_handle(q.device))
+    _lib.check(st, "kda_chunk_bwd")
+    return g

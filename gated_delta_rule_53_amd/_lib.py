@@ -13,7 +13,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
           4: "KDA_ERR_HIP"}
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step", "kda_layer_fwd",
-           "kda_layer_decode_step", "kda_status_string")
+           "kda_layer_decode_step", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -62,6 +62,10 @@ def lib():
     L.kda_layer_decode_step.restype = ctypes.c_int
     L.kda_layer_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, i32,
                                         ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp]
+    L.kda_chunk_bwd_workspace_size.restype = sz
+    L.kda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+    L.kda_chunk_bwd.restype = ctypes.c_int
+    L.kda_chunk_bwd.argtypes = [ctypes.POINTER(Shape)] + [vp] * 16 + [sz, vp]
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_status_string.argtypes = [ctypes.c_int]
     _LIB = L

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_backward.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled: plain float code only.

@@ -379,4 +379,119 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
                        state_inout, out, stream);
 }
 
+// Workspace of the backward: state buffer, then per (chunk, head) the forward
+// record, the state snapshot, the fp32 backward record, the gradient snapshot
+// and dU, then (one gate per head) a per-channel gate-gradient scratch.
+struct BwdLayout {
+    size_t state, rec, snap, brec, dsnap, du, dg, total;
+};
+
+static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l) {
+    kda_status_t st = chunk_plan_full(s, varlen, p);
+    if (st != KDA_OK) return st;
+    const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    if (p.N * all > 65535) return KDA_ERR_UNSUPPORTED;
+    const size_t units = (size_t)p.N * all * s->heads, d = p.d;
+    l.state = 0;
+    l.rec = p.state_bytes;
+    l.snap = l.rec + align256(units * p.rec);
+    l.brec = l.snap + align256(units * d * d * 4);
+    l.dsnap = l.brec + align256(units * kda::bwd_record_bytes(p.d));
+    l.du = l.dsnap + align256(units * d * d * 4);
+    l.dg = l.du + align256(units * CHUNK * d * 4);
+    l.total = l.dg + (s->gate_per_head ? align256((size_t)p.tokens * s->heads * d * 4) : 0) + 256;
+    return KDA_OK;
+}
+
+size_t kda_chunk_bwd_workspace_size(const kda_shape_t* s) {
+    Plan p;
+    BwdLayout l;
+    if (!s || bwd_layout(s, s->num_seqs > 0, p, l) != KDA_OK) return 0;
+    return l.total;
+}
+
+kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, const void* d_out, const float* d_final_state, float* dq,
+                           float* dk, float* dv, float* dlog_alpha, float* dbeta, float* d_init_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p;
+    BwdLayout l;
+    kda_status_t st = bwd_layout(s, cu_seqlens != nullptr, p, l);
+    if (st != KDA_OK) return st;
+    const int H = s->heads, d = p.d;
+    const size_t tok = (size_t)p.tokens * H * d;
+    const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
+    const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok) * 4;
+    const size_t st_bytes = (size_t)p.N * H * d * d * 4, tb4 = (size_t)p.tokens * H * 4;
+    if (p.tokens > 0) {
+        if (!q || !k || !v || !log_alpha || !beta || !d_out || !dq || !dk || !dv || !dlog_alpha || !dbeta)
+            return KDA_ERR_INVALID_ARG;
+        const void* ptrs[] = {q, k, v, log_alpha, beta, d_out, dq, dk, dv, dlog_alpha, dbeta};
+        for (const void* x : ptrs)
+            if (!aligned16(x)) return KDA_ERR_INVALID_ARG;
+    }
+    if ((cu_seqlens && !aligned16(cu_seqlens)) || (init_state && !aligned16(init_state)) ||
+        (d_final_state && !aligned16(d_final_state)) || (d_init_state && !aligned16(d_init_state)))
+        return KDA_ERR_INVALID_ARG;
+    {  // outputs against inputs and one another
+        const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta, d_init_state};
+        const size_t osz[] = {tok * 4, tok * 4, tok * 4, la_bytes, tb4, st_bytes};
+        const void* ins[] = {q, k, v, log_alpha, beta, init_state, cu_seqlens, d_out, d_final_state};
+        const size_t isz[] = {tok * in_b, tok * in_b, tok * in_b, la_bytes, tb4, st_bytes,
+                              (size_t)(p.N + 1) * 4, tok * out_b, st_bytes};
+        for (int i = 0; i < 6; ++i) {
+            for (int j = 0; j < 9; ++j)
+                if (overlaps(outs[i], osz[i], ins[j], isz[j])) return KDA_ERR_INVALID_ARG;
+            for (int j = i + 1; j < 6; ++j)
+                if (overlaps(outs[i], osz[i], outs[j], osz[j])) return KDA_ERR_INVALID_ARG;
+        }
+    }
+    if (p.N == 0) return KDA_OK;
+    if (cu_seqlens) {
+        const char* chk = getenv("KDA_CHECK");
+        if (chk && chk[0] == '1') {
+            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, static_cast<hipStream_t>(stream));
+            if (cs != KDA_OK) return cs;
+        }
+    }
+    if (!workspace || !aligned16(workspace) || workspace_bytes < l.total) return KDA_ERR_WORKSPACE;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    kda::BwdArgs b;
+    kda::ChunkArgs& a = b.fwd;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.la = log_alpha;
+    a.gate_per_head = s->gate_per_head;
+    a.beta = beta;
+    a.cu = cu_seqlens;
+    a.T = s->seqlen;
+    a.H = H;
+    a.N = (int)p.N;
+    a.Wc = (int)(p.max_chunks > 0 ? p.max_chunks : 1);
+    a.win = 0;
+    a.state_buf = reinterpret_cast<float*>(ws + l.state);
+    a.rec = ws + l.rec;
+    a.rec_bytes = p.rec;
+    a.init = init_state;
+    a.out = nullptr;
+    a.snap = reinterpret_cast<float*>(ws + l.snap);
+    b.brec = reinterpret_cast<float*>(ws + l.brec);
+    b.dO = d_out;
+    b.dfinal = d_final_state;
+    b.dsnap = reinterpret_cast<float*>(ws + l.dsnap);
+    b.dU = reinterpret_cast<float*>(ws + l.du);
+    b.dinit = d_init_state;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dG = s->gate_per_head ? reinterpret_cast<float*>(ws + l.dg) : dlog_alpha;
+    b.dla_head = s->gate_per_head ? dlog_alpha : nullptr;
+    b.dbeta = dbeta;
+    hipError_t e = kda::bwd_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, b,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

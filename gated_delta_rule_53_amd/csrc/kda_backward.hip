@@ -1,0 +1,660 @@
+// kda_backward.hip -- reverse mode of the chunked KDA prefill (gfx950, wave64).
+//
+// The gradients of L = sum(dO * O) + sum(dS_T * S_T) with respect to q, k, v,
+// log_alpha, beta and the initial state, through the chunkwise form of the
+// recurrence ("Kimi Linear" page, "The constrained DPLR form and the chunkwise
+// algorithm").  Per chunk j with state S_j (entering the chunk), G the
+// inclusive cumulative log-gate inside the chunk, Kg = K e^G, Qg = Q e^G,
+// Kh = K e^{G_last - G}, gamma = e^{G_last}, A0 the strictly lower 64x64
+// product A0[r][i] = sum_c k_rc k_ic e^{G_rc - G_ic}, Atil = diag(beta) A0,
+// P the inclusive lower product with q in place of the row's k,
+// T = (I + Atil)^-1, Bk = diag(beta) Kg, Bv = diag(beta) V, W = T Bk,
+// Ut = T Bv:
+//     U = Ut - W S_j,  O = Qg S_j + P U,  S_{j+1} = Diag(gamma) S_j + Kh^T U.
+// Walking the chunks backwards with dS = dL/dS_{j+1}:
+//     dU  = P^T dO + Kh dS
+//     dS_j = Qg^T dO + Diag(gamma) dS - W^T dU
+// and inside the chunk
+//     dQg = dO S_j^T,  dP = tril(dO U^T),  dKh = U dS^T,  dgamma = rowsum(S_j o dS),
+//     dW = -dU S_j^T,  dT = dW Bk^T + dU Bv^T,  dBk = T^T dW,  dBv = T^T dU,
+//     dAtil = -T^T dT T^T (strictly lower),
+// and the decay-weighted products of dP and diag(beta) dAtil with K and Q
+// (row and column forms, below) carry the rest to q, k and G; dlog_alpha is
+// the reverse cumulative sum of dG over the chunk's rows.
+//
+// Kernels (all fp32 arithmetic, fp32 matrix cores):
+//   chunk_local_kernel + chunk_inter_kernel (the forward's, with state
+//     snapshots): S_j for every chunk;
+//   bwd_prep_kernel   one workgroup per (chunk, head): G, A0, P, T, W, Ut, Qg,
+//                     Kh, gamma -> an fp32 record;
+//   bwd_chain_kernel  one workgroup per (sequence, head, 16 value columns):
+//                     the reverse chain over chunks, writing dS_{j+1} and dU_j;
+//   bwd_local_kernel  one workgroup per (chunk, head): every parameter gradient.
+//
+// Decay factors e^{G_r - G_i} of the pairwise products are split about an
+// anchor row so each matrix-core operand carries one bounded factor: for a
+// 16-row block pair the first row of the later block (both factors <= 1), for a
+// diagonal block its ninth row (factors bounded by eight tokens of decay).
+#include "kda_device.h"
+#include "kda_internal.h"
+
+#include <type_traits>
+
+namespace kda {
+
+namespace {
+
+constexpr int BW_T = 256;  // threads of the prep and local kernels (4 waves)
+constexpr int BW_W = BW_T / 64;
+
+// fp32 record of one (chunk, head), offsets in floats
+template <int D>
+struct BRec {
+    static constexpr size_t T = 0;
+    static constexpr size_t A0 = T + CH * CH;
+    static constexpr size_t P = A0 + CH * CH;
+    static constexpr size_t W = P + CH * CH;
+    static constexpr size_t UT = W + CH * D;
+    static constexpr size_t QG = UT + CH * D;
+    static constexpr size_t KH = QG + CH * D;
+    static constexpr size_t G = KH + CH * D;
+    static constexpr size_t GAM = G + CH * D;
+    static constexpr size_t FLOATS = ((GAM + D + 63) / 64) * 64;
+};
+
+__device__ __forceinline__ void seq_range(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
+    if (a.cu) {
+        t0 = a.cu[s];
+        L = (int64_t)a.cu[s + 1] - t0;
+    } else {
+        t0 = (int64_t)s * a.T;
+        L = a.T;
+    }
+}
+
+template <typename X>
+__device__ __forceinline__ float ld(const X* p, size_t i) {
+    return to_f32(p[i]);
+}
+
+// One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1 (K % 4 == 0),
+// with lane l feeding A(m0 + (l & 15), k) and B(k, n0 + (l & 15)) through the loaders;
+// acc[r] of lane l ends as C(m0 + 4 (l >> 4) + r, n0 + (l & 15)).
+template <typename FA, typename FB>
+__device__ __forceinline__ void tile_f32(floatx4& acc, int K, int lane, FA&& a, FB&& b) {
+    const int g = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + g), b(k0 + g), acc, 0, 0, 0);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// prep: the chunk's forward quantities in fp32
+// ---------------------------------------------------------------------------
+template <int D, typename IT>
+__global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec) {
+    using R = BRec<D>;
+    constexpr int DP = D + 1;
+    __shared__ float sK[CH * DP];
+    __shared__ float sX[CH * DP];  // q, then v
+    __shared__ float sG[CH * DP];
+    __shared__ float sA[CH * (CH + 1)];  // A0
+    __shared__ float sT[CH * (CH + 1)];
+    __shared__ float sB[CH];
+    constexpr int AP = CH + 1;
+
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, j = blockIdx.y % a.Wc;
+    int64_t tb, L;
+    seq_range(a, s, tb, L);
+    const int64_t c0 = (int64_t)j * CH;
+    if (c0 >= L) return;
+    const int n = (int)min<int64_t>(CH, L - c0);
+    const int H = a.H;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
+    const IT* q = static_cast<const IT*>(a.q);
+    const IT* k = static_cast<const IT*>(a.k);
+    const IT* v = static_cast<const IT*>(a.v);
+    float* rec = brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS;
+
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        const size_t th = (size_t)(tb + c0 + r) * H + h;
+        const bool ok = r < n;
+        sK[r * DP + c] = ok ? ld(k, th * D + c) : 0.f;
+        sX[r * DP + c] = ok ? ld(q, th * D + c) : 0.f;
+        sG[r * DP + c] = ok ? (a.gate_per_head ? a.la[th] : a.la[th * D + c]) : 0.f;
+    }
+    if (t < CH) sB[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
+    __syncthreads();
+    if (t < D) {  // inclusive cumulative log-gate per channel
+        float acc = 0.f;
+        for (int r = 0; r < CH; ++r) {
+            acc += sG[r * DP + t];
+            sG[r * DP + t] = acc;
+        }
+    }
+    __syncthreads();
+
+    // A0 (strict) and P (inclusive) by 16x16 blocks, anchored: row a for an
+    // off-diagonal block (the later block's first row), the block's ninth row
+    // for a diagonal one
+    for (int task = wave; task < 20; task += BW_W) {
+        const bool isP = task >= 10;
+        const int bt = task % 10;
+        const int rb = bt < 1 ? 0 : bt < 3 ? 1 : bt < 6 ? 2 : 3;
+        const int cb = bt - rb * (rb + 1) / 2;
+        const int an = cb < rb ? 16 * rb : 16 * rb + 8;
+        const float* X = isP ? sX : sK;
+        const int rr = 16 * rb + li, ii = 16 * cb + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, D, lane,
+                 [&](int c) { return X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[an * DP + c]); },
+                 [&](int c) { return sK[ii * DP + c] * fast_exp(sG[an * DP + c] - sG[ii * DP + c]); });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
+            const bool keep = cb < rb || (isP ? row >= col : row > col);
+            const float x = keep ? acc[r] : 0.f;
+            if (isP) rec[R::P + row * CH + col] = x;
+            else sA[row * AP + col] = x;
+        }
+    }
+    // zero upper blocks of A0; P's upper blocks in the record
+    for (int idx = t; idx < CH * CH; idx += BW_T) {
+        const int r = idx / CH, c = idx % CH;
+        if ((c >> 4) > (r >> 4)) {
+            sA[r * AP + c] = 0.f;
+            rec[R::P + idx] = 0.f;
+        }
+    }
+    __syncthreads();
+    // T = (I + diag(beta) A0)^-1 by forward substitution, one wave, row by row
+    if (wave == 0) {
+        const int cc = lane;  // column
+        for (int r = 0; r < CH; ++r) {
+            float x = r == cc ? 1.f : 0.f;
+            for (int jj = cc; jj < r; ++jj) x -= sB[r] * sA[r * AP + jj] * sT[jj * AP + cc];
+            sT[r * AP + cc] = cc <= r ? x : 0.f;
+            wave_lds_sync();
+        }
+    }
+    __syncthreads();
+    for (int idx = t; idx < CH * CH; idx += BW_T) {
+        const int r = idx / CH, c = idx % CH;
+        rec[R::T + idx] = sT[r * AP + c];
+        rec[R::A0 + idx] = sA[r * AP + c];
+    }
+    // W = T Bk (Bk = beta K e^G), Qg, Kh, G, gamma
+    const float* GL = sG + (n - 1) * DP;
+    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
+        const int mt = task / (D / 16), nt = task % (D / 16);
+        const int cc = 16 * nt + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
+                 [&](int i) { return sB[i] * sK[i * DP + cc] * fast_exp(sG[i * DP + cc]); });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rec[R::W + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
+    }
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        const float g = sG[r * DP + c];
+        rec[R::QG + idx] = sX[r * DP + c] * fast_exp(g);
+        rec[R::KH + idx] = sK[r * DP + c] * fast_exp(GL[c] - g);
+        rec[R::G + idx] = g;
+    }
+    if (t < D) rec[R::GAM + t] = fast_exp(GL[t]);
+    __syncthreads();
+    // Ut = T Bv (Bv = beta V)
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        sX[r * DP + c] = r < n ? sB[r] * ld(v, ((size_t)(tb + c0 + r) * H + h) * D + c) : 0.f;
+    }
+    __syncthreads();
+    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
+        const int mt = task / (D / 16), nt = task % (D / 16);
+        const int cc = 16 * nt + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
+                 [&](int i) { return sX[i * DP + cc]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rec[R::UT + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reverse chain over the chunks of one (sequence, head), 16 value columns
+// ---------------------------------------------------------------------------
+template <int D, typename GT>
+__global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float* brec, const GT* dO,
+                                                        const float* dfinal, float* dsnap, float* dU, float* dinit) {
+    using R = BRec<D>;
+    constexpr int SP = 17;
+    __shared__ float sdS[D * SP];
+    __shared__ float sdO[CH * SP];
+    __shared__ float sdU[CH * SP];
+    const int H = a.H, NH = a.N * H;
+    const int u = blockIdx.x % NH, z = blockIdx.x / NH;
+    const int s = u / H, h = u % H, col0 = 16 * z;
+    int64_t tb, L;
+    seq_range(a, s, tb, L);
+    const int nch = (int)((L + CH - 1) / CH);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
+
+    for (int idx = t; idx < D * 16; idx += 256) {
+        const int c = idx / 16, vv = idx % 16;
+        sdS[c * SP + vv] = dfinal ? dfinal[((size_t)u * D + c) * D + col0 + vv] : 0.f;
+    }
+    __syncthreads();
+    for (int j = nch - 1; j >= 0; --j) {
+        const size_t ch = (size_t)(s * a.Wc + j) * H + h;
+        const float* rec = brec + ch * R::FLOATS;
+        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
+        float* snap = dsnap + ch * D * D;
+        for (int idx = t; idx < D * 16; idx += 256) {
+            const int c = idx / 16, vv = idx % 16;
+            snap[(size_t)c * D + col0 + vv] = sdS[c * SP + vv];  // dL/dS_{j+1}
+        }
+        for (int idx = t; idx < CH * 16; idx += 256) {
+            const int r = idx / 16, vv = idx % 16;
+            sdO[r * SP + vv] = r < n ? ld(dO, ((size_t)(tb + (int64_t)j * CH + r) * H + h) * D + col0 + vv) : 0.f;
+        }
+        __syncthreads();
+        {  // dU = P^T dO + Kh dS: wave w owns rows 16w .. 16w+15
+            const int ii = 16 * wave + li;
+            floatx4 acc = zero4();
+            tile_f32(acc, CH, lane, [&](int r) { return rec[R::P + r * CH + ii]; },
+                     [&](int r) { return sdO[r * SP + li]; });
+            tile_f32(acc, D, lane, [&](int c) { return rec[R::KH + (size_t)ii * D + c]; },
+                     [&](int c) { return sdS[c * SP + li]; });
+            float* du = dU + ch * CH * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * wave + 4 * gq + r;
+                sdU[row * SP + li] = acc[r];
+                du[(size_t)row * D + col0 + li] = acc[r];
+            }
+        }
+        __syncthreads();
+        // dS <- Qg^T dO + Diag(gamma) dS - W^T dU: wave w owns rows of D / 4
+        for (int rt = 0; rt < D / 64; ++rt) {
+            const int cb = wave * (D / 4) + 16 * rt;
+            const int cc = cb + li;
+            floatx4 acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = cb + 4 * gq + r;
+                acc[r] = rec[R::GAM + row] * sdS[row * SP + li];
+            }
+            tile_f32(acc, CH, lane, [&](int r) { return rec[R::QG + (size_t)r * D + cc]; },
+                     [&](int r) { return sdO[r * SP + li]; });
+            tile_f32(acc, CH, lane, [&](int r) { return -rec[R::W + (size_t)r * D + cc]; },
+                     [&](int r) { return sdU[r * SP + li]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sdS[(cb + 4 * gq + r) * SP + li] = acc[r];
+        }
+        __syncthreads();
+    }
+    if (dinit)
+        for (int idx = t; idx < D * 16; idx += 256) {
+            const int c = idx / 16, vv = idx % 16;
+            dinit[((size_t)u * D + c) * D + col0 + vv] = sdS[c * SP + vv];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// local: every parameter gradient of one (chunk, head)
+// ---------------------------------------------------------------------------
+template <int D, typename IT, typename GT>
+__global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
+    const ChunkArgs& a = b.fwd;
+    const float* brec = b.brec;
+    const GT* dO = static_cast<const GT*>(b.dO);
+    float *dq = b.dq, *dk = b.dk, *dv = b.dv, *dG = b.dG;
+    using R = BRec<D>;
+    constexpr int DP = D + 4;
+    constexpr int AP = CH + 1;
+    __shared__ float sG[CH * D];
+    __shared__ float sT[CH * AP];
+    __shared__ float sX[CH * DP];   // U, then dW, then T^T dT
+    __shared__ float sY[CH * DP];   // dO, then Bk, then Bv
+    __shared__ float sP[CH * AP];   // dP
+    __shared__ float sM[CH * AP];   // dT, then diag(beta) dAtil
+    __shared__ float sGL[D];        // dL/dG_last per channel
+    __shared__ float sdB[CH];
+    __shared__ float sBeta[CH];
+
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, j = blockIdx.y % a.Wc;
+    int64_t tb, L;
+    seq_range(a, s, tb, L);
+    const int64_t c0 = (int64_t)j * CH;
+    if (c0 >= L) return;
+    const int n = (int)min<int64_t>(CH, L - c0);
+    const int H = a.H;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
+    const IT* q = static_cast<const IT*>(a.q);
+    const IT* k = static_cast<const IT*>(a.k);
+    const IT* v = static_cast<const IT*>(a.v);
+    const size_t ch = (size_t)(s * a.Wc + j) * H + h;
+    const float* rec = brec + ch * R::FLOATS;
+    const float* S = a.snap + ch * D * D;
+    const float* dS = b.dsnap + ch * D * D;
+    const float* dU = b.dU + ch * CH * D;
+    auto tok = [&](int r) { return ((size_t)(tb + c0 + r) * H + h) * D; };  // row r of a [T, H, D] tensor
+    auto qv = [&](int r, int c) { return r < n ? ld(q, tok(r) + c) : 0.f; };
+    auto kv = [&](int r, int c) { return r < n ? ld(k, tok(r) + c) : 0.f; };
+    auto vv = [&](int r, int c) { return r < n ? ld(v, tok(r) + c) : 0.f; };
+    // gradient accumulators: rows r < n of this chunk belong to this workgroup alone
+    auto acc_to = [&](float* base, int r, int c, float x) {
+        if (r < n) base[tok(r) + c] += x;
+    };
+
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        sG[idx] = rec[R::G + idx];
+        if (r < n) {
+            const size_t o = tok(r) + c;
+            dq[o] = 0.f;
+            dk[o] = 0.f;
+            dv[o] = 0.f;
+            dG[o] = 0.f;
+        }
+    }
+    for (int idx = t; idx < CH * CH; idx += BW_T) sT[(idx / CH) * AP + idx % CH] = rec[R::T + idx];
+    if (t < D) sGL[t] = 0.f;
+    if (t < CH) {
+        sdB[t] = 0.f;
+        sBeta[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
+    }
+    __syncthreads();
+    const float* GL = sG + (n - 1) * D;
+
+    // U = Ut - W S_j
+    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
+        const int mt = task / (D / 16), nt = task % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
+                 [&](int c) { return S[(size_t)c * D + cc]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r;
+            sX[row * DP + cc] = rec[R::UT + (size_t)row * D + cc] - acc[r];
+        }
+    }
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        sY[r * DP + c] = r < n ? ld(dO, tok(r) + c) : 0.f;
+    }
+    __syncthreads();
+    // dP = tril(dO U^T)
+    for (int task = wave; task < 16; task += BW_W) {
+        const int mt = task / 4, nt = task % 4;
+        floatx4 acc = zero4();
+        tile_f32(acc, D, lane, [&](int c) { return sY[(16 * mt + li) * DP + c]; },
+                 [&](int c) { return sX[(16 * nt + li) * DP + c]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+            sP[row * AP + col] = (row >= col && row < n) ? acc[r] : 0.f;
+        }
+    }
+    // dQg = dO S^T -> dq, dG;  dKh = U dS^T -> dk, dG, dG_last
+    for (int task = wave; task < 8 * (D / 16); task += BW_W) {
+        const bool kh = task >= 4 * (D / 16);
+        const int tt = task % (4 * (D / 16));
+        const int mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
+        floatx4 acc = zero4();
+        if (!kh)
+            tile_f32(acc, D, lane, [&](int c) { return sY[rr * DP + c]; },
+                     [&](int c) { return S[(size_t)cc * D + c]; });
+        else
+            tile_f32(acc, D, lane, [&](int c) { return sX[rr * DP + c]; },
+                     [&](int c) { return dS[(size_t)cc * D + c]; });
+        float gl = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r;
+            if (row >= n) continue;
+            const float g = sG[row * D + cc];
+            if (!kh) {
+                const float e = fast_exp(g);
+                acc_to(dq, row, cc, acc[r] * e);
+                acc_to(dG, row, cc, acc[r] * qv(row, cc) * e);
+            } else {
+                const float f = fast_exp(GL[cc] - g), x = acc[r] * kv(row, cc) * f;
+                acc_to(dk, row, cc, acc[r] * f);
+                acc_to(dG, row, cc, -x);
+                gl += x;
+            }
+        }
+        if (kh) atomicAdd(&sGL[cc], gl);
+    }
+    // dgamma_c = sum_v S[c][v] dS[c][v]
+    for (int c = wave; c < D; c += BW_W) {
+        float x = 0.f;
+        for (int vv2 = lane; vv2 < D; vv2 += 64) x += S[(size_t)c * D + vv2] * dS[(size_t)c * D + vv2];
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        if (lane == 0) atomicAdd(&sGL[c], x * fast_exp(GL[c]));
+    }
+    __syncthreads();
+    // dW = -dU S^T (into sX); Bk = beta K e^G (into sY)
+    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
+        const int mt = task / (D / 16), nt = task % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
+                 [&](int c) { return S[(size_t)cc * D + c]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
+    }
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        sY[r * DP + c] = sBeta[r] * kv(r, c) * fast_exp(sG[r * D + c]);
+    }
+    __syncthreads();
+    // dT = dW Bk^T (lower part);  dBk = T^T dW -> dk, dG, dbeta
+    for (int task = wave; task < 16 + 4 * (D / 16); task += BW_W) {
+        if (task < 16) {
+            const int mt = task / 4, nt = task % 4;
+            floatx4 acc = zero4();
+            tile_f32(acc, D, lane, [&](int c) { return sX[(16 * mt + li) * DP + c]; },
+                     [&](int c) { return sY[(16 * nt + li) * DP + c]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+                sM[row * AP + col] = row >= col ? acc[r] : 0.f;
+            }
+        } else {
+            const int tt = task - 16, mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, ii = 16 * mt + li;
+            floatx4 acc = zero4();
+            tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
+                     [&](int r) { return sX[r * DP + cc]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r;
+                if (row >= n) continue;
+                const float e = fast_exp(sG[row * D + cc]), kk = kv(row, cc), b = sBeta[row];
+                acc_to(dk, row, cc, b * e * acc[r]);
+                acc_to(dG, row, cc, acc[r] * b * kk * e);
+                atomicAdd(&sdB[row], acc[r] * kk * e);
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        sY[r * DP + c] = sBeta[r] * vv(r, c);
+    }
+    __syncthreads();
+    // dT += dU Bv^T (lower part);  dBv = T^T dU -> dv, dbeta
+    for (int task = wave; task < 16 + 4 * (D / 16); task += BW_W) {
+        if (task < 16) {
+            const int mt = task / 4, nt = task % 4;
+            floatx4 acc = zero4();
+            tile_f32(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
+                     [&](int c) { return sY[(16 * nt + li) * DP + c]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+                if (row >= col) sM[row * AP + col] += acc[r];
+            }
+        } else {
+            const int tt = task - 16, mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, ii = 16 * mt + li;
+            floatx4 acc = zero4();
+            tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
+                     [&](int r) { return dU[(size_t)r * D + cc]; });
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * mt + 4 * gq + r;
+                if (row >= n) continue;
+                acc_to(dv, row, cc, sBeta[row] * acc[r]);
+                atomicAdd(&sdB[row], acc[r] * vv(row, cc));
+            }
+        }
+    }
+    __syncthreads();
+    // X = T^T dT (into sX as 64 x 64), then dAtil = -X T^T (strictly lower, into sM)
+    for (int task = wave; task < 16; task += BW_W) {
+        const int mt = task / 4, nt = task % 4;
+        floatx4 acc = zero4();
+        tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + 16 * mt + li]; },
+                 [&](int r) { return sM[r * AP + 16 * nt + li]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + 16 * nt + li] = acc[r];
+    }
+    __syncthreads();
+    for (int task = wave; task < 16; task += BW_W) {
+        const int mt = task / 4, nt = task % 4;
+        floatx4 acc = zero4();
+        tile_f32(acc, CH, lane, [&](int jj) { return sX[(16 * mt + li) * DP + jj]; },
+                 [&](int jj) { return sT[(16 * nt + li) * AP + jj]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+            sM[row * AP + col] = (row > col && row < n) ? -acc[r] : 0.f;
+        }
+    }
+    __syncthreads();
+    // dbeta += sum_i dAtil[r][i] A0[r][i];  then sM <- diag(beta) dAtil
+    for (int r = wave; r < CH; r += BW_W) {
+        float x = sM[r * AP + lane] * rec[R::A0 + r * CH + lane];
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+        if (lane == 0) sdB[r] += x;
+        sM[r * AP + lane] *= sBeta[r];
+    }
+    __syncthreads();
+
+    // Decay-weighted products of a lower-triangular M (dP or diag(beta) dAtil):
+    //   row form  Y[r][c] = sum_i M[r][i] X[i][c] e^{G_rc - G_ic}
+    //   col form  Z[i][c] = sum_r M[r][i] X[r][c] e^{G_rc - G_ic}
+    // one task per (form, 16-row block, 16 channels), the off-diagonal blocks
+    // anchored at the block boundary, the diagonal block at its ninth row.
+    //   R1 = row(dP, K) -> dq, +q dG     C1 = col(dP, Q) -> dk, -k dG
+    //   R2 = row(M2, K) -> dk, +k dG     C2 = col(M2, K) -> dk, -k dG
+    for (int task = wave; task < 4 * 4 * (D / 16); task += BW_W) {
+        const int form = task / (4 * (D / 16));
+        const int tt = task % (4 * (D / 16));
+        const int blk = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li;
+        const float* M = (form == 0 || form == 1) ? sP : sM;
+        const bool col = form == 1 || form == 3;
+        auto Xv = [&](int r, int c) { return form == 1 ? qv(r, c) : kv(r, c); };
+        floatx4 off = zero4(), dia = zero4();
+        const int m = 16 * blk + 8;
+        if (!col) {
+            const int an = 16 * blk;  // rows of the block see earlier rows i < an
+            const int mr = 16 * blk + li;
+            if (blk > 0)
+                tile_f32(off, an, lane, [&](int i) { return M[mr * AP + i]; },
+                         [&](int i) { return Xv(i, cc) * fast_exp(sG[an * D + cc] - sG[i * D + cc]); });
+            tile_f32(dia, 16, lane, [&](int i) { return M[mr * AP + 16 * blk + i]; },
+                     [&](int i) {
+                         const int ii = 16 * blk + i;
+                         return Xv(ii, cc) * fast_exp(sG[m * D + cc] - sG[ii * D + cc]);
+                     });
+        } else {
+            const int bn = 16 * blk + 15;  // columns of the block see later rows r > bn
+            const int mi = 16 * blk + li;
+            if (blk < 3)
+                tile_f32(off, CH - 16 * (blk + 1), lane, [&](int r) { return M[(bn + 1 + r) * AP + mi]; },
+                         [&](int r) {
+                             const int rr = bn + 1 + r;
+                             return Xv(rr, cc) * fast_exp(sG[rr * D + cc] - sG[bn * D + cc]);
+                         });
+            tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
+                     [&](int r) {
+                         const int rr = 16 * blk + r;
+                         return Xv(rr, cc) * fast_exp(sG[rr * D + cc] - sG[m * D + cc]);
+                     });
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * blk + 4 * gq + r;
+            if (row >= n) continue;
+            const float g = sG[row * D + cc];
+            float y;
+            if (!col) {
+                y = dia[r] * fast_exp(g - sG[m * D + cc]);
+                if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * D + cc]);
+            } else {
+                y = dia[r] * fast_exp(sG[m * D + cc] - g);
+                if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * D + cc] - g);
+            }
+            if (form == 0) {
+                acc_to(dq, row, cc, y);
+                acc_to(dG, row, cc, y * qv(row, cc));
+            } else {
+                acc_to(dk, row, cc, y);
+                acc_to(dG, row, cc, (form == 2 ? 1.f : -1.f) * y * kv(row, cc));
+            }
+        }
+    }
+    __syncthreads();
+    // dlog_alpha = reverse cumulative sum of dG over the chunk's rows (dG_last on the last row)
+    if (t < D) {
+        float acc = sGL[t];
+        for (int r = n - 1; r >= 0; --r) {
+            const size_t o = tok(r) + t;
+            acc += dG[o];
+            dG[o] = acc;
+        }
+    }
+    if (t < n) b.dbeta[(size_t)(tb + c0 + t) * H + h] = sdB[t];
+    if (b.dla_head) {  // one gate per head: its gradient is the sum over the key channels
+        __syncthreads();
+        if (t < n) {
+            float x = 0.f;
+            for (int c = 0; c < D; ++c) x += dG[tok(t) + c];
+            b.dla_head[(size_t)(tb + c0 + t) * H + h] = x;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------
+size_t bwd_record_bytes(int d) { return (d == 128 ? BRec<128>::FLOATS : BRec<64>::FLOATS) * sizeof(float); }
+
+template <int D, typename IT, typename GT>
+static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
+    const ChunkArgs& a = b.fwd;
+    hipError_t e;
+    const dim3 chunks(a.H, a.N * a.Wc);
+    const int units = a.N * a.H;
+    if ((e = chunk_snapshot_dispatch(D, std::is_same<IT, bf16_t>::value, a, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_prep_kernel<D, IT>), chunks, dim3(BW_T), 0, st, a, b.brec);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, a, b.brec,
+                       static_cast<const GT*>(b.dO), b.dfinal, b.dsnap, b.dU, b.dinit);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BW_T), 0, st, b);
+    return hipGetLastError();
+}
+
+hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st) {
+    if (d == 128) {
+        if (in_bf16) return dout_bf16 ? bwd_run<128, bf16_t, bf16_t>(b, st) : bwd_run<128, bf16_t, float>(b, st);
+        return dout_bf16 ? bwd_run<128, float, bf16_t>(b, st) : bwd_run<128, float, float>(b, st);
+    }
+    if (in_bf16) return dout_bf16 ? bwd_run<64, bf16_t, bf16_t>(b, st) : bwd_run<64, bf16_t, float>(b, st);
+    return dout_bf16 ? bwd_run<64, float, bf16_t>(b, st) : bwd_run<64, float, float>(b, st);
+}
+
+}  // namespace kda

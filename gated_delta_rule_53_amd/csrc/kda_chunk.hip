@@ -1107,6 +1107,17 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
         };
         auto step = [&](ChainBuf& f, ChainBuf& fn, int jn, int j) {
             const int cur = (j - jb) & 1;
+            if (MODE == 0 && a.snap) {  // the state entering chunk j, for the backward pass
+                float* dst = a.snap + ((size_t)(s * a.Wc + (j - jrec0)) * H + h) * D * D;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            dst[(size_t)(w * (D / 4) + 16 * rt + 4 * gq + r) * D + col0 + 16 * ct + li] =
+                                Sacc[rt][ct][r];
+            }
             float g[RT][4];  // gamma of the four state rows each accumulator lane holds
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
@@ -1199,6 +1210,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                 const OT* bt = sU[cur] + (16 * ct + li) * UP;
 #pragma unroll
                 for (int e = 0; e < NFT; ++e) accO[ct] = FR::mma(f.P[e], bt + e * KS, gq, accO[ct]);
+                if (!out) continue;  // state snapshots only
                 OUT* o = out + ((size_t)(tok0 + 16 * w + 4 * gq) * H + h) * D + col0 + 16 * ct + li;
                 if (n == CH) {
 #pragma unroll
@@ -1501,6 +1513,21 @@ static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int 
     if (!a.gate) return run_out<D, IT, OT, false, false>(a, out_bf16, nwin, bv, ov, st);
     if (qk_norm) return run_out<D, IT, OT, true, true>(a, out_bf16, nwin, bv, ov, st);
     return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, ov, st);
+}
+
+template <int D, typename IT, typename OT>
+static hipError_t run_snapshots(const ChunkArgs& a, hipStream_t st) {
+    using C = LocalCfg<D, OT>;
+    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, false, false>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float>), dim3(a.N * a.H * (D / 16)), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, hipStream_t st) {
+    if (d == 128) return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, st) : run_snapshots<128, float, float>(a, st);
+    return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, st) : run_snapshots<64, float, float>(a, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,

@@ -38,6 +38,9 @@ struct ChunkArgs {
     const uint16_t* out_gate = nullptr;   // bf16 [tokens, H, D] output-gate pre-activation
     const float* norm_weight = nullptr;   // fp32 [D] RMSNorm weight, or null for ones
     float rms_eps = 0.f;
+    // backward recompute: the state entering every chunk, [chunk-in-buffer][H][D][D]
+    // fp32 indexed like the records (null: not written); a null `out` skips the outputs
+    float* snap = nullptr;
 };
 
 // Layer prologue and epilogue of one decode step (null pointers: off).
@@ -58,6 +61,28 @@ struct Overlap {
     hipEvent_t inter_done[2] = {nullptr, nullptr};
     size_t buffer_bytes = 0;
 };
+
+// Reverse mode of the chunked prefill (kda_backward.hip).  fwd: the forward's
+// arguments with every chunk in one window (win = 0, Wc = the longest
+// sequence's chunks), rec / state_buf in the workspace, snap set and out null.
+struct BwdArgs {
+    ChunkArgs fwd;
+    float* brec;          // fp32 per-(chunk, head) records of the backward
+    const void* dO;       // dL/dout, [tokens, H, D] (out dtype)
+    const float* dfinal;  // dL/dfinal_state [N, H, D, D] or null
+    float* dsnap;         // dL/dS_{j+1} per (chunk, head), [D, D]
+    float* dU;            // dL/dU per (chunk, head), [64, D]
+    float* dinit;         // dL/dinit_state [N, H, D, D] or null
+    float *dq, *dk, *dv;  // [tokens, H, D] fp32
+    float* dG;            // [tokens, H, D] fp32: dL/dlog_alpha per channel
+    float* dla_head;      // [tokens, H] fp32 when the gate is per head (dG is then scratch), else null
+    float* dbeta;         // [tokens, H] fp32
+};
+size_t bwd_record_bytes(int d);
+hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st);
+// The forward recompute of the backward: chunk-local records and the state
+// snapshots (a.snap) of every chunk; no outputs.
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, hipStream_t st);
 
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);

@@ -197,6 +197,30 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
                                    const void* q, const void* k, const void* v, const float* beta,
                                    float* state_inout, void* out, void* stream);
 
+/* Reverse mode of the chunked prefill: the gradients of
+ *     L = sum(d_out * out) + sum(d_final_state * final_state)
+ * with respect to q, k, v, log_alpha, beta and init_state, through the same
+ * chunkwise form ("Kimi Linear" page, "The constrained DPLR form and the
+ * chunkwise algorithm"; the page gives the form's cost as a training cost).
+ * The forward quantities are recomputed from the inputs (nothing is kept from
+ * a forward call).  Shape, dtypes and input layouts as for kda_chunk_fwd
+ * (d_out has out_dtype and the layout of out); every chunk of every sequence
+ * is held in the workspace at once, so the batch must satisfy
+ * N * ceil(max_seqlen / 64) <= 65535.
+ *   d_final_state [N, H, dk, dv] fp32, or NULL (zero)
+ *   dq, dk        [B, T, H, dk] fp32;   dv [B, T, H, dv] fp32
+ *   dlog_alpha    fp32, the layout of log_alpha
+ *   dbeta         [B, T, H] fp32
+ *   d_init_state  [N, H, dk, dv] fp32, or NULL (not returned)
+ *   workspace     device scratch of workspace_bytes >= kda_chunk_bwd_workspace_size
+ * Outputs must not overlap any input or one another. */
+size_t kda_chunk_bwd_workspace_size(const kda_shape_t* s);
+kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                           const float* log_alpha, const float* beta, const float* init_state,
+                           const int32_t* cu_seqlens, const void* d_out, const float* d_final_state, float* dq,
+                           float* dk, float* dv, float* dlog_alpha, float* dbeta, float* d_init_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status_t st);
 

@@ -188,3 +188,13 @@ def test_layer_decode_validation(L):
     assert call(_layer(gate=False)) == INVALID
     assert call(_layer(), gph=2) == INVALID
     assert L.kda_layer_decode_step(4, 2, 96, 96, BF16, F32, 0, _layer(), q, k, v, b, st, out, None) == UNSUPPORTED
+
+
+def test_binding_argument_counts_match_header(L):
+    """Each ctypes prototype has exactly the parameters include/kda.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in _lib.EXPORTS:
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(getattr(L, name).argtypes) == len(params), name
