@@ -13,7 +13,7 @@ bandwidth is in ``decode``.  ``roofline`` describes the dominant kernel of a
 step (the decode kernel: 100 launches per step); ``prefill_roofline`` the
 prefill call.  ``layer`` times the fused layer (q/k L2 norm, gate from its
 projection output, RMSNorm with sigmoid output gate, bf16 y) on the same
-shapes.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
+shapes; ``backward`` the gradients of the 64K prefill.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
 on the prefill workload (by default all of it: about 5-15 s on 16 host cores).
 """
 from __future__ import annotations
@@ -66,6 +66,13 @@ def layer_prefill_bytes(tokens, heads, d, states=1):
 def layer_decode_bytes(units, d):
     """State read + write plus the layer's per-(sequence, head) inputs and bf16 y."""
     return units * (2 * d * d * 4 + 3 * d * 2 + d * 2 + 4 + d * 2 + d * 2) + d * 4
+
+
+def backward_bytes(tokens, heads, d, states=1):
+    """Algorithmic HBM bytes of the backward: bf16 q,k,v, fp32 log_alpha, beta and d_out read,
+    fp32 dq, dk, dv, dlog_alpha, dbeta written, plus the initial state and the final-state
+    gradient read and the initial-state gradient written."""
+    return tokens * heads * (3 * d * 2 + d * 4 + 4 + d * 4 + 4 * d * 4 + 4) + 3 * states * heads * d * d * 4
 
 
 def to_dev(x, torch):
@@ -128,6 +135,7 @@ def main():
                     help="channel: KDA (log_alpha [.., H, dk]); head: one gate per head (Gated DeltaNet)")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the fused layer (q/k L2 norm, gate from its projection, RMSNorm-sigmoid epilogue)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward pass of the prefill")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -260,12 +268,47 @@ def main():
         "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
                    "(model level, hardware not stated)",
     }
+    if not (args.no_backward or args.prefill_only or gph):
+        res["backward"] = bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream)
     if not (args.no_layer or args.prefill_only or gph):
         res["layer"] = bench_layer(kda, torch, synth, wp, wd, args, flush, stream)
     if not args.no_cpu_baseline:
         threads = max(1, min(16, os.cpu_count() or 1))
         res["cpu_baseline"] = cpu_baseline(wp, d, args.cpu_sample, threads)
     print(json.dumps(res), flush=True)
+
+
+def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):
+    """Gradients of the 64K-token prefill (fp32 d_out and final-state gradient), timed after
+    the main steps: one call recomputes the forward's records and states, then runs the
+    reverse chain and the per-chunk gradients."""
+    T, H, D = wp.seqlen, wp.heads, wp.dk
+    gen = torch.Generator(device="cuda").manual_seed(wp.seed)
+    d_out = torch.randn((1, T, H, D), dtype=torch.float32, device="cuda", generator=gen)
+    d_fin = torch.randn((1, H, D, D), dtype=torch.float32, device="cuda", generator=gen)
+
+    def call():
+        return kda.chunk_bwd(q, k, v, la, be, d_out, init, d_fin)
+
+    for _ in range(min(args.warmup, 2)):
+        call()
+    torch.cuda.synchronize()
+    ms = []
+    for i in range(max(3, args.steps // 4)):
+        flush.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    s = float(np.median(ms)) / 1e3
+    b = backward_bytes(T, H, D)
+    return {"what": "dq, dk, dv, dlog_alpha, dbeta, d_init of the 64K x 32-head prefill (bf16 in, fp32 d_out "
+                    "and gradients), forward recompute included",
+            "ms": s * 1e3, "tokens_per_s": T / s, "algorithmic_bytes": b, "hbm_gbs": b / s / 1e9,
+            "frac": b / s / 1e9 / HBM_PEAK_GBS}
 
 
 def bench_layer(kda, torch, synth, wp, wd, args, flush, stream):

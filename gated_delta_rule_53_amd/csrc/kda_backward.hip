@@ -77,13 +77,24 @@ __device__ __forceinline__ float ld(const X* p, size_t i) {
     return to_f32(p[i]);
 }
 
-// One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1 (K % 4 == 0),
+// One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1 (K % 16 == 0),
 // with lane l feeding A(m0 + (l & 15), k) and B(k, n0 + (l & 15)) through the loaders;
-// acc[r] of lane l ends as C(m0 + 4 (l >> 4) + r, n0 + (l & 15)).
+// acc[r] of lane l ends as C(m0 + 4 (l >> 4) + r, n0 + (l & 15)).  K advances in
+// groups of 16 whose eight operand loads are issued before their four products, so
+// the latency of loads from memory overlaps instead of adding up.
 template <typename FA, typename FB>
 __device__ __forceinline__ void tile_f32(floatx4& acc, int K, int lane, FA&& a, FB&& b) {
     const int g = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(k0 + g), b(k0 + g), acc, 0, 0, 0);
+    for (int k0 = 0; k0 < K; k0 += 16) {
+        float x[4], y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a(k0 + 4 * e + g);
+            y[e] = b(k0 + 4 * e + g);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
+    }
 }
 
 }  // namespace
@@ -168,22 +179,125 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         }
     }
     __syncthreads();
-    // T = (I + diag(beta) A0)^-1 by forward substitution, one wave, row by row
-    if (wave == 0) {
-        const int cc = lane;  // column
-        for (int r = 0; r < CH; ++r) {
-            float x = r == cc ? 1.f : 0.f;
-            for (int jj = cc; jj < r; ++jj) x -= sB[r] * sA[r * AP + jj] * sT[jj * AP + cc];
-            sT[r * AP + cc] = cc <= r ? x : 0.f;
+    for (int idx = t; idx < CH * CH; idx += BW_T) {  // A0 to the record, then Atil = diag(beta) A0 in LDS
+        const int r = idx / CH, c = idx % CH;
+        rec[R::A0 + idx] = sA[r * AP + c];
+        sA[r * AP + c] *= sB[r];
+        sT[r * AP + c] = 0.f;
+    }
+    __syncthreads();
+    // T = (I + Atil)^-1: diagonal 16x16 blocks as (I - A)(I + A^2)(I + A^4)(I + A^8)
+    // (A strictly lower, so A^16 = 0), one wave each, with three blocks of the
+    // upper triangle of sT as the wave's scratch; off-diagonal blocks by 2x2 block
+    // inversion: T10 = -T11 A10 T00, T32 = -T33 A32 T22, then T_hi,lo = -T_hi (A_hi,lo T_lo).
+    {
+        auto blk = [&](float* M, int r, int c) { return M + (16 * r) * AP + 16 * c; };
+        auto tload = [&](const float* M) {
+            floatx4 x;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] = M[(4 * gq + r) * AP + li];
+            return x;
+        };
+        auto tstore = [&](float* M, floatx4 x, float sign) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) M[(4 * gq + r) * AP + li] = sign * x[r];
+        };
+        auto prod = [&](floatx4& acc, const float* X, const float* Y) {
+            tile_f32(acc, 16, lane, [&](int kk) { return X[li * AP + kk]; }, [&](int kk) { return Y[kk * AP + li]; });
+        };
+        {
+            const int d = wave;
+            constexpr int SR[4][3] = {{0, 0, 0}, {1, 1, 2}, {2, 3, 2}, {3, 3, 1}};
+            constexpr int SC[4][3] = {{1, 2, 3}, {2, 3, 3}, {0, 0, 1}, {1, 2, 0}};
+            float* S0 = blk(sT, SR[d][0], SC[d][0]);
+            float* S1 = blk(sT, SR[d][1], SC[d][1]);
+            float* S2 = blk(sT, SR[d][2], SC[d][2]);
+            const float* Ad = blk(sA, d, d);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * gq + r;
+                const float x = li < row ? Ad[row * AP + li] : 0.f;
+                S0[row * AP + li] = x;
+                S1[row * AP + li] = (li == row ? 1.f : 0.f) - x;
+            }
             wave_lds_sync();
+            floatx4 m = zero4();
+            prod(m, S0, S0);  // A^2
+            tstore(S2, m, 1.f);
+            wave_lds_sync();
+            m = zero4();
+            prod(m, S2, S2);  // A^4
+            floatx4 x = tload(S1);
+            prod(x, S1, S2);  // (I - A)(I + A^2)
+            wave_lds_sync();
+            tstore(S0, m, 1.f);
+            tstore(S1, x, 1.f);
+            wave_lds_sync();
+            m = zero4();
+            prod(m, S0, S0);  // A^8
+            x = tload(S1);
+            prod(x, S1, S0);  // ... (I + A^4)
+            wave_lds_sync();
+            tstore(S2, m, 1.f);
+            tstore(S1, x, 1.f);
+            wave_lds_sync();
+            x = tload(S1);
+            prod(x, S1, S2);  // ... (I + A^8)
+            tstore(blk(sT, d, d), x, 1.f);
+            if (d == 0 || d == 2) {  // A_{d+1,d} T_dd, kept in S0: (0,1) for d = 0, (2,0) for d = 2
+                wave_lds_sync();
+                floatx4 y = zero4();
+                prod(y, blk(sA, d + 1, d), blk(sT, d, d));
+                tstore(S0, y, 1.f);
+            }
+        }
+        __syncthreads();
+        for (int task = wave; task < 6; task += BW_W) {
+            floatx4 acc = zero4();
+            switch (task) {
+                case 0: prod(acc, blk(sT, 1, 1), blk(sT, 0, 1)); tstore(blk(sT, 1, 0), acc, -1.f); break;
+                case 1: prod(acc, blk(sT, 3, 3), blk(sT, 2, 0)); tstore(blk(sT, 3, 2), acc, -1.f); break;
+                case 2: prod(acc, blk(sA, 2, 1), blk(sT, 1, 1)); tstore(blk(sT, 1, 2), acc, 1.f); break;
+                case 3: prod(acc, blk(sA, 3, 1), blk(sT, 1, 1)); tstore(blk(sT, 1, 3), acc, 1.f); break;
+                case 4: prod(acc, blk(sA, 2, 0), blk(sT, 0, 0)); tstore(blk(sT, 0, 2), acc, 1.f); break;
+                default: prod(acc, blk(sA, 3, 0), blk(sT, 0, 0)); tstore(blk(sT, 0, 3), acc, 1.f); break;
+            }
+        }
+        __syncthreads();
+        {
+            floatx4 acc;
+            switch (wave) {
+                case 0: acc = tload(blk(sT, 0, 2)); prod(acc, blk(sA, 2, 1), blk(sT, 1, 0)); tstore(blk(sT, 0, 2), acc, 1.f); break;
+                case 1: acc = tload(blk(sT, 0, 3)); prod(acc, blk(sA, 3, 1), blk(sT, 1, 0)); tstore(blk(sT, 0, 3), acc, 1.f); break;
+                case 2: acc = zero4(); prod(acc, blk(sT, 2, 2), blk(sT, 1, 2)); tstore(blk(sT, 2, 1), acc, -1.f); break;
+                default:
+                    acc = zero4();
+                    prod(acc, blk(sT, 3, 2), blk(sT, 1, 2));
+                    prod(acc, blk(sT, 3, 3), blk(sT, 1, 3));
+                    tstore(blk(sT, 3, 1), acc, -1.f);
+                    break;
+            }
+        }
+        __syncthreads();
+        if (wave < 2) {
+            floatx4 acc = zero4();
+            if (wave == 0) {
+                prod(acc, blk(sT, 2, 2), blk(sT, 0, 2));
+                tstore(blk(sT, 2, 0), acc, -1.f);
+            } else {
+                prod(acc, blk(sT, 3, 2), blk(sT, 0, 2));
+                prod(acc, blk(sT, 3, 3), blk(sT, 0, 3));
+                tstore(blk(sT, 3, 0), acc, -1.f);
+            }
+        }
+        __syncthreads();
+        for (int idx = t; idx < CH * CH; idx += BW_T) {  // the scratch blocks above the diagonal read as zero
+            const int r = idx / CH, c = idx % CH;
+            if ((c >> 4) > (r >> 4)) sT[r * AP + c] = 0.f;
         }
     }
     __syncthreads();
-    for (int idx = t; idx < CH * CH; idx += BW_T) {
-        const int r = idx / CH, c = idx % CH;
-        rec[R::T + idx] = sT[r * AP + c];
-        rec[R::A0 + idx] = sA[r * AP + c];
-    }
+    for (int idx = t; idx < CH * CH; idx += BW_T) rec[R::T + idx] = sT[(idx / CH) * AP + idx % CH];
     // W = T Bk (Bk = beta K e^G), Qg, Kh, G, gamma
     const float* GL = sG + (n - 1) * DP;
     for (int task = wave; task < 4 * (D / 16); task += BW_W) {
