@@ -46,6 +46,8 @@ namespace {
 
 constexpr int BW_T = 256;  // threads of the prep and local kernels (4 waves)
 constexpr int BW_W = BW_T / 64;
+constexpr int BL_T = 512;  // threads of the local kernel (8 waves)
+constexpr int BL_W = BL_T / 64;
 
 // fp32 record of one (chunk, head), offsets in floats
 template <int D>
@@ -77,23 +79,23 @@ __device__ __forceinline__ float ld(const X* p, size_t i) {
     return to_f32(p[i]);
 }
 
-// One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1 (K % 16 == 0),
+// One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1,
 // with lane l feeding A(m0 + (l & 15), k) and B(k, n0 + (l & 15)) through the loaders;
 // acc[r] of lane l ends as C(m0 + 4 (l >> 4) + r, n0 + (l & 15)).  K advances in
-// groups of 16 whose eight operand loads are issued before their four products, so
-// the latency of loads from memory overlaps instead of adding up.
-template <typename FA, typename FB>
+// groups of 4 GS (K % (4 GS) == 0) whose 2 GS operand loads are issued before their
+// GS products, so the latency of loads from memory overlaps instead of adding up.
+template <int GS = 4, typename FA, typename FB>
 __device__ __forceinline__ void tile_f32(floatx4& acc, int K, int lane, FA&& a, FB&& b) {
     const int g = lane >> 4;
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        float x[4], y[4];
+    for (int k0 = 0; k0 < K; k0 += 4 * GS) {
+        float x[GS], y[GS];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < GS; ++e) {
             x[e] = a(k0 + 4 * e + g);
             y[e] = b(k0 + 4 * e + g);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
+        for (int e = 0; e < GS; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
     }
 }
 
@@ -418,20 +420,27 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
 // ---------------------------------------------------------------------------
 // local: every parameter gradient of one (chunk, head)
 // ---------------------------------------------------------------------------
+// Eight waves; wave w owns the 16x16 tiles w, w + 8, ... of every 64 x D
+// gradient and keeps dq, dk and the k-part of dG for them in registers across
+// all products: every dq contribution carries dG += q o dq and every dk
+// contribution dG += +-k o dk, so dG = q o dq + k o (signed dk part) needs no
+// pass over memory.  Inputs are read branch-free (rows past the sequence end
+// clamped, then zeroed).
 template <int D, typename IT, typename GT>
-__global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
+__global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     const ChunkArgs& a = b.fwd;
     const float* brec = b.brec;
     const GT* dO = static_cast<const GT*>(b.dO);
-    float *dq = b.dq, *dk = b.dk, *dv = b.dv, *dG = b.dG;
     using R = BRec<D>;
     constexpr int DP = D + 4;
     constexpr int AP = CH + 1;
+    constexpr int NB = D / 16;            // 16-column blocks of a 64 x D matrix
+    constexpr int TPW = 4 * NB / BL_W;    // tiles of such a matrix per wave
     __shared__ float sG[CH * D];
     __shared__ float sT[CH * AP];
-    __shared__ float sX[CH * DP];   // U, then dW, then T^T dT
-    __shared__ float sY[CH * DP];   // dO, then Bk, then Bv
-    __shared__ float sP[CH * AP];   // dP
+    __shared__ float sX[CH * DP];   // U, dW, T^T dT, q, dG
+    __shared__ float sY[CH * DP];   // dO, Bk, Bv, k
+    __shared__ float sP[CH * AP];   // dP, then column partial sums
     __shared__ float sM[CH * AP];   // dT, then diag(beta) dAtil
     __shared__ float sGL[D];        // dL/dG_last per channel
     __shared__ float sdB[CH];
@@ -453,27 +462,20 @@ __global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
     const float* S = a.snap + ch * D * D;
     const float* dS = b.dsnap + ch * D * D;
     const float* dU = b.dU + ch * CH * D;
-    auto tok = [&](int r) { return ((size_t)(tb + c0 + r) * H + h) * D; };  // row r of a [T, H, D] tensor
-    auto qv = [&](int r, int c) { return r < n ? ld(q, tok(r) + c) : 0.f; };
-    auto kv = [&](int r, int c) { return r < n ? ld(k, tok(r) + c) : 0.f; };
-    auto vv = [&](int r, int c) { return r < n ? ld(v, tok(r) + c) : 0.f; };
-    // gradient accumulators: rows r < n of this chunk belong to this workgroup alone
-    auto acc_to = [&](float* base, int r, int c, float x) {
-        if (r < n) base[tok(r) + c] += x;
+    // row r of a [T, H, D] tensor, clamped to the chunk's last row
+    auto tok = [&](int r) { return ((size_t)(tb + c0 + min(r, n - 1)) * H + h) * D; };
+    auto in = [&](const IT* p, int r, int c) {
+        const float x = ld(p, tok(r) + c);
+        return r < n ? x : 0.f;
     };
+    auto mt_of = [&](int i) { return (wave + BL_W * i) / NB; };
+    auto nt_of = [&](int i) { return (wave + BL_W * i) % NB; };
+    floatx4 aq[TPW], ak[TPW], aks[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) aq[i] = ak[i] = aks[i] = zero4();
 
-    for (int idx = t; idx < CH * D; idx += BW_T) {
-        const int r = idx / D, c = idx % D;
-        sG[idx] = rec[R::G + idx];
-        if (r < n) {
-            const size_t o = tok(r) + c;
-            dq[o] = 0.f;
-            dk[o] = 0.f;
-            dv[o] = 0.f;
-            dG[o] = 0.f;
-        }
-    }
-    for (int idx = t; idx < CH * CH; idx += BW_T) sT[(idx / CH) * AP + idx % CH] = rec[R::T + idx];
+    for (int idx = t; idx < CH * D; idx += BL_T) sG[idx] = rec[R::G + idx];
+    for (int idx = t; idx < CH * CH; idx += BL_T) sT[(idx / CH) * AP + idx % CH] = rec[R::T + idx];
     if (t < D) sGL[t] = 0.f;
     if (t < CH) {
         sdB[t] = 0.f;
@@ -483,150 +485,142 @@ __global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
     const float* GL = sG + (n - 1) * D;
 
     // U = Ut - W S_j
-    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
-        const int mt = task / (D / 16), nt = task % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
-                 [&](int c) { return S[(size_t)c * D + cc]; });
+        tile_f32<8>(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
+                    [&](int c) { return S[(size_t)c * D + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             sX[row * DP + cc] = rec[R::UT + (size_t)row * D + cc] - acc[r];
         }
     }
-    for (int idx = t; idx < CH * D; idx += BW_T) {
+    for (int idx = t; idx < CH * D; idx += BL_T) {
         const int r = idx / D, c = idx % D;
-        sY[r * DP + c] = r < n ? ld(dO, tok(r) + c) : 0.f;
+        const float x = ld(dO, tok(r) + c);
+        sY[r * DP + c] = r < n ? x : 0.f;
     }
     __syncthreads();
     // dP = tril(dO U^T)
-    for (int task = wave; task < 16; task += BW_W) {
+    for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
-        tile_f32(acc, D, lane, [&](int c) { return sY[(16 * mt + li) * DP + c]; },
-                 [&](int c) { return sX[(16 * nt + li) * DP + c]; });
+        if (nt <= mt)
+            tile_f32(acc, D, lane, [&](int c) { return sY[(16 * mt + li) * DP + c]; },
+                     [&](int c) { return sX[(16 * nt + li) * DP + c]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
             sP[row * AP + col] = (row >= col && row < n) ? acc[r] : 0.f;
         }
     }
-    // dQg = dO S^T -> dq, dG;  dKh = U dS^T -> dk, dG, dG_last
-    for (int task = wave; task < 8 * (D / 16); task += BW_W) {
-        const bool kh = task >= 4 * (D / 16);
-        const int tt = task % (4 * (D / 16));
-        const int mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
-        floatx4 acc = zero4();
-        if (!kh)
-            tile_f32(acc, D, lane, [&](int c) { return sY[rr * DP + c]; },
-                     [&](int c) { return S[(size_t)cc * D + c]; });
-        else
-            tile_f32(acc, D, lane, [&](int c) { return sX[rr * DP + c]; },
-                     [&](int c) { return dS[(size_t)cc * D + c]; });
+    // dQg = dO S^T -> dq;  dKh = U dS^T -> dk, dG_last
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
+        floatx4 x = zero4(), y = zero4();
+        tile_f32(x, D, lane, [&](int c) { return sY[rr * DP + c]; }, [&](int c) { return S[(size_t)cc * D + c]; });
+        tile_f32(y, D, lane, [&](int c) { return sX[rr * DP + c]; }, [&](int c) { return dS[(size_t)cc * D + c]; });
         float gl = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
-            if (row >= n) continue;
             const float g = sG[row * D + cc];
-            if (!kh) {
-                const float e = fast_exp(g);
-                acc_to(dq, row, cc, acc[r] * e);
-                acc_to(dG, row, cc, acc[r] * qv(row, cc) * e);
-            } else {
-                const float f = fast_exp(GL[cc] - g), x = acc[r] * kv(row, cc) * f;
-                acc_to(dk, row, cc, acc[r] * f);
-                acc_to(dG, row, cc, -x);
-                gl += x;
-            }
+            aq[i][r] += x[r] * fast_exp(g);
+            const float f = y[r] * fast_exp(GL[cc] - g);
+            ak[i][r] += f;
+            aks[i][r] -= f;
+            gl += f * in(k, row, cc);
         }
-        if (kh) atomicAdd(&sGL[cc], gl);
+        atomicAdd(&sGL[cc], gl);
     }
     // dgamma_c = sum_v S[c][v] dS[c][v]
-    for (int c = wave; c < D; c += BW_W) {
+    for (int c = wave; c < D; c += BL_W) {
         float x = 0.f;
-        for (int vv2 = lane; vv2 < D; vv2 += 64) x += S[(size_t)c * D + vv2] * dS[(size_t)c * D + vv2];
+        for (int v2 = lane; v2 < D; v2 += 64) x += S[(size_t)c * D + v2] * dS[(size_t)c * D + v2];
         for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
         if (lane == 0) atomicAdd(&sGL[c], x * fast_exp(GL[c]));
     }
     __syncthreads();
     // dW = -dU S^T (into sX); Bk = beta K e^G (into sY)
-    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
-        const int mt = task / (D / 16), nt = task % (D / 16), cc = 16 * nt + li, rr = 16 * mt + li;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
-                 [&](int c) { return S[(size_t)cc * D + c]; });
+        tile_f32<8>(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
+                    [&](int c) { return S[(size_t)cc * D + c]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
     }
-    for (int idx = t; idx < CH * D; idx += BW_T) {
+    for (int idx = t; idx < CH * D; idx += BL_T) {
         const int r = idx / D, c = idx % D;
-        sY[r * DP + c] = sBeta[r] * kv(r, c) * fast_exp(sG[r * D + c]);
+        sY[r * DP + c] = sBeta[r] * in(k, r, c) * fast_exp(sG[r * D + c]);
     }
     __syncthreads();
-    // dT = dW Bk^T (lower part);  dBk = T^T dW -> dk, dG, dbeta
-    for (int task = wave; task < 16 + 4 * (D / 16); task += BW_W) {
-        if (task < 16) {
-            const int mt = task / 4, nt = task % 4;
-            floatx4 acc = zero4();
+    // dT = tril(dW Bk^T);  dBk = T^T dW -> dk, dbeta
+    for (int task = wave; task < 16; task += BL_W) {
+        const int mt = task / 4, nt = task % 4;
+        floatx4 acc = zero4();
+        if (nt <= mt)
             tile_f32(acc, D, lane, [&](int c) { return sX[(16 * mt + li) * DP + c]; },
                      [&](int c) { return sY[(16 * nt + li) * DP + c]; });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
-                sM[row * AP + col] = row >= col ? acc[r] : 0.f;
-            }
-        } else {
-            const int tt = task - 16, mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, ii = 16 * mt + li;
-            floatx4 acc = zero4();
-            tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
-                     [&](int r) { return sX[r * DP + cc]; });
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+            sM[row * AP + col] = row >= col ? acc[r] : 0.f;
+        }
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * gq + r;
-                if (row >= n) continue;
-                const float e = fast_exp(sG[row * D + cc]), kk = kv(row, cc), b = sBeta[row];
-                acc_to(dk, row, cc, b * e * acc[r]);
-                acc_to(dG, row, cc, acc[r] * b * kk * e);
-                atomicAdd(&sdB[row], acc[r] * kk * e);
-            }
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
+        floatx4 acc = zero4();
+        tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; }, [&](int r) { return sX[r * DP + cc]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r;
+            const float e = fast_exp(sG[row * D + cc]), dkc = sBeta[row] * e * acc[r];
+            ak[i][r] += dkc;
+            aks[i][r] += dkc;
+            atomicAdd(&sdB[row], acc[r] * in(k, row, cc) * e);
         }
     }
     __syncthreads();
-    for (int idx = t; idx < CH * D; idx += BW_T) {
+    for (int idx = t; idx < CH * D; idx += BL_T) {
         const int r = idx / D, c = idx % D;
-        sY[r * DP + c] = sBeta[r] * vv(r, c);
+        sY[r * DP + c] = sBeta[r] * in(v, r, c);
     }
     __syncthreads();
-    // dT += dU Bv^T (lower part);  dBv = T^T dU -> dv, dbeta
-    for (int task = wave; task < 16 + 4 * (D / 16); task += BW_W) {
-        if (task < 16) {
-            const int mt = task / 4, nt = task % 4;
-            floatx4 acc = zero4();
-            tile_f32(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
-                     [&](int c) { return sY[(16 * nt + li) * DP + c]; });
+    // dT += tril(dU Bv^T) (the same tasks per wave as above);  dBv = T^T dU -> dv, dbeta
+    for (int task = wave; task < 16; task += BL_W) {
+        const int mt = task / 4, nt = task % 4;
+        if (nt > mt) continue;
+        floatx4 acc = zero4();
+        tile_f32<8>(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
+                    [&](int c) { return sY[(16 * nt + li) * DP + c]; });
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
-                if (row >= col) sM[row * AP + col] += acc[r];
-            }
-        } else {
-            const int tt = task - 16, mt = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li, ii = 16 * mt + li;
-            floatx4 acc = zero4();
-            tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
-                     [&](int r) { return dU[(size_t)r * D + cc]; });
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
+            if (row >= col) sM[row * AP + col] += acc[r];
+        }
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * mt + 4 * gq + r;
-                if (row >= n) continue;
-                acc_to(dv, row, cc, sBeta[row] * acc[r]);
-                atomicAdd(&sdB[row], acc[r] * vv(row, cc));
-            }
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
+        floatx4 acc = zero4();
+        tile_f32<8>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
+                    [&](int r) { return dU[(size_t)r * D + cc]; });
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r;
+            if (row < n) b.dv[tok(row) + cc] = sBeta[row] * acc[r];
+            atomicAdd(&sdB[row], acc[r] * in(v, row, cc));
         }
     }
     __syncthreads();
     // X = T^T dT (into sX as 64 x 64), then dAtil = -X T^T (strictly lower, into sM)
-    for (int task = wave; task < 16; task += BW_W) {
+    for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
         tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + 16 * mt + li]; },
@@ -635,7 +629,7 @@ __global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + 16 * nt + li] = acc[r];
     }
     __syncthreads();
-    for (int task = wave; task < 16; task += BW_W) {
+    for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
         tile_f32(acc, CH, lane, [&](int jj) { return sX[(16 * mt + li) * DP + jj]; },
@@ -647,96 +641,132 @@ __global__ void __launch_bounds__(BW_T) bwd_local_kernel(BwdArgs b) {
         }
     }
     __syncthreads();
-    // dbeta += sum_i dAtil[r][i] A0[r][i];  then sM <- diag(beta) dAtil
-    for (int r = wave; r < CH; r += BW_W) {
+    // dbeta += sum_i dAtil[r][i] A0[r][i];  then sM <- diag(beta) dAtil;  q, k to LDS
+    for (int r = wave; r < CH; r += BL_W) {
         float x = sM[r * AP + lane] * rec[R::A0 + r * CH + lane];
         for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
         if (lane == 0) sdB[r] += x;
         sM[r * AP + lane] *= sBeta[r];
+    }
+    for (int idx = t; idx < CH * D; idx += BL_T) {
+        const int r = idx / D, c = idx % D;
+        sX[r * DP + c] = in(q, r, c);
+        sY[r * DP + c] = in(k, r, c);
     }
     __syncthreads();
 
     // Decay-weighted products of a lower-triangular M (dP or diag(beta) dAtil):
     //   row form  Y[r][c] = sum_i M[r][i] X[i][c] e^{G_rc - G_ic}
     //   col form  Z[i][c] = sum_r M[r][i] X[r][c] e^{G_rc - G_ic}
-    // one task per (form, 16-row block, 16 channels), the off-diagonal blocks
-    // anchored at the block boundary, the diagonal block at its ninth row.
-    //   R1 = row(dP, K) -> dq, +q dG     C1 = col(dP, Q) -> dk, -k dG
+    // per tile of the wave and form, the off-diagonal blocks anchored at the
+    // block boundary, the diagonal block at its ninth row.
+    //   R1 = row(dP, K) -> dq     C1 = col(dP, Q) -> dk, -k dG
     //   R2 = row(M2, K) -> dk, +k dG     C2 = col(M2, K) -> dk, -k dG
-    for (int task = wave; task < 4 * 4 * (D / 16); task += BW_W) {
-        const int form = task / (4 * (D / 16));
-        const int tt = task % (4 * (D / 16));
-        const int blk = tt / (D / 16), nt = tt % (D / 16), cc = 16 * nt + li;
-        const float* M = (form == 0 || form == 1) ? sP : sM;
-        const bool col = form == 1 || form == 3;
-        auto Xv = [&](int r, int c) { return form == 1 ? qv(r, c) : kv(r, c); };
-        floatx4 off = zero4(), dia = zero4();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int blk = mt_of(i), cc = 16 * nt_of(i) + li;
         const int m = 16 * blk + 8;
-        if (!col) {
-            const int an = 16 * blk;  // rows of the block see earlier rows i < an
-            const int mr = 16 * blk + li;
-            if (blk > 0)
-                tile_f32(off, an, lane, [&](int i) { return M[mr * AP + i]; },
-                         [&](int i) { return Xv(i, cc) * fast_exp(sG[an * D + cc] - sG[i * D + cc]); });
-            tile_f32(dia, 16, lane, [&](int i) { return M[mr * AP + 16 * blk + i]; },
-                     [&](int i) {
-                         const int ii = 16 * blk + i;
-                         return Xv(ii, cc) * fast_exp(sG[m * D + cc] - sG[ii * D + cc]);
-                     });
-        } else {
-            const int bn = 16 * blk + 15;  // columns of the block see later rows r > bn
-            const int mi = 16 * blk + li;
-            if (blk < 3)
-                tile_f32(off, CH - 16 * (blk + 1), lane, [&](int r) { return M[(bn + 1 + r) * AP + mi]; },
-                         [&](int r) {
-                             const int rr = bn + 1 + r;
-                             return Xv(rr, cc) * fast_exp(sG[rr * D + cc] - sG[bn * D + cc]);
+#pragma unroll 1
+        for (int form = 0; form < 4; ++form) {
+            const float* M = form < 2 ? sP : sM;
+            const float* X = form == 1 ? sX : sY;
+            const bool col = form == 1 || form == 3;
+            floatx4 off = zero4(), dia = zero4();
+            if (!col) {
+                const int an = 16 * blk, mr = 16 * blk + li;
+                if (blk > 0)
+                    tile_f32(off, an, lane, [&](int ii) { return M[mr * AP + ii]; },
+                             [&](int ii) { return X[ii * DP + cc] * fast_exp(sG[an * D + cc] - sG[ii * D + cc]); });
+                tile_f32(dia, 16, lane, [&](int ii) { return M[mr * AP + 16 * blk + ii]; },
+                         [&](int ii) {
+                             const int i2 = 16 * blk + ii;
+                             return X[i2 * DP + cc] * fast_exp(sG[m * D + cc] - sG[i2 * D + cc]);
                          });
-            tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
-                     [&](int r) {
-                         const int rr = 16 * blk + r;
-                         return Xv(rr, cc) * fast_exp(sG[rr * D + cc] - sG[m * D + cc]);
-                     });
+            } else {
+                const int bn = 16 * blk + 15, mi = 16 * blk + li;
+                if (blk < 3)
+                    tile_f32(off, CH - 16 * (blk + 1), lane, [&](int r) { return M[(bn + 1 + r) * AP + mi]; },
+                             [&](int r) {
+                                 const int rr = bn + 1 + r;
+                                 return X[rr * DP + cc] * fast_exp(sG[rr * D + cc] - sG[bn * D + cc]);
+                             });
+                tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
+                         [&](int r) {
+                             const int rr = 16 * blk + r;
+                             return X[rr * DP + cc] * fast_exp(sG[rr * D + cc] - sG[m * D + cc]);
+                         });
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * blk + 4 * gq + r;
+                const float g = sG[row * D + cc];
+                float y;
+                if (!col) {
+                    y = dia[r] * fast_exp(g - sG[m * D + cc]);
+                    if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * D + cc]);
+                } else {
+                    y = dia[r] * fast_exp(sG[m * D + cc] - g);
+                    if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * D + cc] - g);
+                }
+                if (form == 0) {
+                    aq[i][r] += y;
+                } else {
+                    ak[i][r] += y;
+                    aks[i][r] += form == 2 ? y : -y;
+                }
+            }
         }
+    }
+    // dq, dk out; dG = q o dq + k o (signed dk part)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * blk + 4 * gq + r;
-            if (row >= n) continue;
-            const float g = sG[row * D + cc];
-            float y;
-            if (!col) {
-                y = dia[r] * fast_exp(g - sG[m * D + cc]);
-                if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * D + cc]);
-            } else {
-                y = dia[r] * fast_exp(sG[m * D + cc] - g);
-                if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * D + cc] - g);
-            }
-            if (form == 0) {
-                acc_to(dq, row, cc, y);
-                acc_to(dG, row, cc, y * qv(row, cc));
-            } else {
-                acc_to(dk, row, cc, y);
-                acc_to(dG, row, cc, (form == 2 ? 1.f : -1.f) * y * kv(row, cc));
+            const int row = 16 * mt + 4 * gq + r;
+            aks[i][r] = sX[row * DP + cc] * aq[i][r] + sY[row * DP + cc] * aks[i][r];
+            if (row < n) {
+                b.dq[tok(row) + cc] = aq[i][r];
+                b.dk[tok(row) + cc] = ak[i][r];
             }
         }
     }
     __syncthreads();
-    // dlog_alpha = reverse cumulative sum of dG over the chunk's rows (dG_last on the last row)
-    if (t < D) {
-        float acc = sGL[t];
-        for (int r = n - 1; r >= 0; --r) {
-            const size_t o = tok(r) + t;
-            acc += dG[o];
-            dG[o] = acc;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int mt = mt_of(i), cc = 16 * nt_of(i) + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = aks[i][r];
+    }
+    __syncthreads();
+    // dlog_alpha = reverse cumulative sum of dG down the chunk's rows, dG_last
+    // entering at the last row: column c, row range part of PARTS
+    constexpr int PARTS = BL_T / D, RPP = CH / PARTS;
+    const int cg = t % D, part = t / D;
+    {
+        float x = 0.f;
+        for (int r = 0; r < RPP; ++r) x += sX[(part * RPP + r) * DP + cg];
+        sP[part * D + cg] = x;
+    }
+    __syncthreads();
+    {
+        float carry = sGL[cg];
+        for (int p = part + 1; p < PARTS; ++p) carry += sP[p * D + cg];
+        for (int r = RPP - 1; r >= 0; --r) {
+            const int row = part * RPP + r;
+            carry += sX[row * DP + cg];
+            if (b.dla_head) sX[row * DP + cg] = carry;
+            else if (row < n) b.dG[tok(row) + cg] = carry;
         }
     }
     if (t < n) b.dbeta[(size_t)(tb + c0 + t) * H + h] = sdB[t];
     if (b.dla_head) {  // one gate per head: its gradient is the sum over the key channels
         __syncthreads();
-        if (t < n) {
+        for (int r = wave; r < n; r += BL_W) {
             float x = 0.f;
-            for (int c = 0; c < D; ++c) x += dG[tok(t) + c];
-            b.dla_head[(size_t)(tb + c0 + t) * H + h] = x;
+            for (int c = lane; c < D; c += 64) x += sX[r * DP + c];
+            for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            if (lane == 0) b.dla_head[(size_t)(tb + c0 + r) * H + h] = x;
         }
     }
 }
@@ -758,7 +788,7 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
     hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, a, b.brec,
                        static_cast<const GT*>(b.dO), b.dfinal, b.dsnap, b.dU, b.dinit);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BW_T), 0, st, b);
+    hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BL_T), 0, st, b);
     return hipGetLastError();
 }
 
