@@ -49,19 +49,38 @@ constexpr int BW_W = BW_T / 64;
 constexpr int BL_T = 512;  // threads of the local kernel (8 waves)
 constexpr int BL_W = BL_T / 64;
 
-// fp32 record of one (chunk, head), offsets in floats
+// Operands of one wave of the reverse chain for one chunk, in the order its
+// matrix-core steps consume them: step e feeds lane l = li + 16 g the A value of
+// row li and reduction index 4 (e - base) + g, and four consecutive steps form
+// one float4 per lane.  Wave w owns dU rows 16w .. 16w+15 (steps P^T over the
+// chunk's rows, then Kh over the key channels) and NRT 16-row tiles of dS at
+// rows w D/4 + 16 rt (steps Qg^T, then -W^T, over the chunk's rows); after the
+// steps, one float4 per tile holds gamma of the lane's four dS rows.
+template <int D>
+struct ChainRec {
+    static constexpr int NRT = D / 64;
+    static constexpr int EP = CH / 4, EK = D / 4, EQ = CH / 4;
+    static constexpr int E = EP + EK + NRT * 2 * EQ;
+    static constexpr int Q4 = E / 4 + NRT;
+    static constexpr int FLOATS = 4 * Q4 * 64 * 4;
+    __device__ static int at(int w, int e, int lane) { return ((w * Q4 + (e >> 2)) * 64 + lane) * 4 + (e & 3); }
+    // dS tile of key channel c: wave, tile, and the step base of its Qg^T part
+    __device__ static int wave_of(int c) { return c / (D / 4); }
+    __device__ static int tile_of(int c) { return (c % (D / 4)) >> 4; }
+    __device__ static int qbase(int c) { return EP + EK + tile_of(c) * 2 * EQ; }
+};
+
+// fp32 record of one (chunk, head), offsets in floats: what the local pass
+// reads row-major, then the chain's operands
 template <int D>
 struct BRec {
     static constexpr size_t T = 0;
     static constexpr size_t A0 = T + CH * CH;
-    static constexpr size_t P = A0 + CH * CH;
-    static constexpr size_t W = P + CH * CH;
+    static constexpr size_t W = A0 + CH * CH;
     static constexpr size_t UT = W + CH * D;
-    static constexpr size_t QG = UT + CH * D;
-    static constexpr size_t KH = QG + CH * D;
-    static constexpr size_t G = KH + CH * D;
-    static constexpr size_t GAM = G + CH * D;
-    static constexpr size_t FLOATS = ((GAM + D + 63) / 64) * 64;
+    static constexpr size_t G = UT + CH * D;
+    static constexpr size_t CR = G + CH * D;
+    static constexpr size_t FLOATS = CR + ChainRec<D>::FLOATS;
 };
 
 __device__ __forceinline__ void seq_range(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
@@ -107,6 +126,7 @@ __device__ __forceinline__ void tile_f32(floatx4& acc, int K, int lane, FA&& a, 
 template <int D, typename IT>
 __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec) {
     using R = BRec<D>;
+    using C = ChainRec<D>;
     constexpr int DP = D + 1;
     __shared__ float sK[CH * DP];
     __shared__ float sX[CH * DP];  // q, then v
@@ -168,7 +188,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
             const bool keep = cb < rb || (isP ? row >= col : row > col);
             const float x = keep ? acc[r] : 0.f;
-            if (isP) rec[R::P + row * CH + col] = x;
+            if (isP) rec[R::CR + C::at(col >> 4, row >> 2, (col & 15) + 16 * (row & 3))] = x;
             else sA[row * AP + col] = x;
         }
     }
@@ -177,7 +197,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int r = idx / CH, c = idx % CH;
         if ((c >> 4) > (r >> 4)) {
             sA[r * AP + c] = 0.f;
-            rec[R::P + idx] = 0.f;
+            rec[R::CR + C::at(c >> 4, r >> 2, (c & 15) + 16 * (r & 3))] = 0.f;
         }
     }
     __syncthreads();
@@ -309,16 +329,24 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
                  [&](int i) { return sB[i] * sK[i * DP + cc] * fast_exp(sG[i * DP + cc]); });
 #pragma unroll
-        for (int r = 0; r < 4; ++r) rec[R::W + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * gq + r;
+            rec[R::W + row * D + cc] = acc[r];
+            rec[R::CR + C::at(C::wave_of(cc), C::qbase(cc) + C::EQ + (row >> 2), li + 16 * (row & 3))] = -acc[r];
+        }
     }
     for (int idx = t; idx < CH * D; idx += BW_T) {
         const int r = idx / D, c = idx % D;
         const float g = sG[r * DP + c];
-        rec[R::QG + idx] = sX[r * DP + c] * fast_exp(g);
-        rec[R::KH + idx] = sK[r * DP + c] * fast_exp(GL[c] - g);
+        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + (r >> 2), (c & 15) + 16 * (r & 3))] =
+            sX[r * DP + c] * fast_exp(g);
+        rec[R::CR + C::at(r >> 4, C::EP + (c >> 2), (r & 15) + 16 * (c & 3))] = sK[r * DP + c] * fast_exp(GL[c] - g);
         rec[R::G + idx] = g;
     }
-    if (t < D) rec[R::GAM + t] = fast_exp(GL[t]);
+    for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
+        const int c = idx / 16, l = (idx % 16) + 16 * ((c & 15) >> 2);
+        rec[R::CR + ((C::wave_of(c) * C::Q4 + C::E / 4 + C::tile_of(c)) * 64 + l) * 4 + (c & 3)] = fast_exp(GL[c]);
+    }
     __syncthreads();
     // Ut = T Bv (Bv = beta V)
     for (int idx = t; idx < CH * D; idx += BW_T) {
@@ -340,13 +368,19 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
 // ---------------------------------------------------------------------------
 // reverse chain over the chunks of one (sequence, head), 16 value columns
 // ---------------------------------------------------------------------------
+// Each wave's operands for chunk j - 1 (its slice of the chain record, one
+// float4 per four matrix-core steps) and the next dO slice are loaded into
+// registers while chunk j is computed, so the serial chain waits on the
+// matrix cores and two barriers per chunk, not on memory.
 template <int D, typename GT>
 __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float* brec, const GT* dO,
                                                         const float* dfinal, float* dsnap, float* dU, float* dinit) {
     using R = BRec<D>;
+    using C = ChainRec<D>;
     constexpr int SP = 17;
+    constexpr int DO_PER = CH * 16 / 256;  // dO values per thread and chunk
     __shared__ float sdS[D * SP];
-    __shared__ float sdO[CH * SP];
+    __shared__ float sdO[2][CH * SP];
     __shared__ float sdU[CH * SP];
     const int H = a.H, NH = a.N * H;
     const int u = blockIdx.x % NH, z = blockIdx.x / NH;
@@ -355,33 +389,69 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     seq_range(a, s, tb, L);
     const int nch = (int)((L + CH - 1) / CH);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
-
+    auto crec = [&](int j) {
+        return reinterpret_cast<const float4*>(brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS + R::CR) +
+               (size_t)wave * C::Q4 * 64 + lane;
+    };
+    // dO of chunk j, rows past the sequence end as zero; thread t holds rows (t + 256 i) / 16
+    auto load_do = [&](int j, float* x) {
+        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
+#pragma unroll
+        for (int i = 0; i < DO_PER; ++i) {
+            const int idx = t + 256 * i, r = idx / 16, vv = idx % 16;
+            const float y = ld(dO, ((size_t)(tb + (int64_t)j * CH + min(r, n - 1)) * H + h) * D + col0 + vv);
+            x[i] = r < n ? y : 0.f;
+        }
+    };
+    auto store_do = [&](int buf, const float* x) {
+#pragma unroll
+        for (int i = 0; i < DO_PER; ++i) {
+            const int idx = t + 256 * i;
+            sdO[buf][(idx / 16) * SP + idx % 16] = x[i];
+        }
+    };
+    float4 cur[C::Q4], nxt[C::Q4];
+    float don[DO_PER];
+    if (nch > 0) {
+        const float4* p = crec(nch - 1);
+#pragma unroll
+        for (int i = 0; i < C::Q4; ++i) cur[i] = p[i * 64];
+        load_do(nch - 1, don);
+        store_do(0, don);
+    }
+    auto opnd = [&](const float4* x, int e) {
+        const float4 f = x[e >> 2];
+        return (e & 3) == 0 ? f.x : (e & 3) == 1 ? f.y : (e & 3) == 2 ? f.z : f.w;
+    };
     for (int idx = t; idx < D * 16; idx += 256) {
         const int c = idx / 16, vv = idx % 16;
         sdS[c * SP + vv] = dfinal ? dfinal[((size_t)u * D + c) * D + col0 + vv] : 0.f;
     }
     __syncthreads();
-    for (int j = nch - 1; j >= 0; --j) {
+    for (int jj = 0; jj < nch; ++jj) {
+        const int j = nch - 1 - jj, buf = jj & 1;
+        if (j > 0) {
+            const float4* p = crec(j - 1);
+#pragma unroll
+            for (int i = 0; i < C::Q4; ++i) nxt[i] = p[i * 64];
+            load_do(j - 1, don);
+        }
         const size_t ch = (size_t)(s * a.Wc + j) * H + h;
-        const float* rec = brec + ch * R::FLOATS;
-        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
         float* snap = dsnap + ch * D * D;
         for (int idx = t; idx < D * 16; idx += 256) {
             const int c = idx / 16, vv = idx % 16;
             snap[(size_t)c * D + col0 + vv] = sdS[c * SP + vv];  // dL/dS_{j+1}
         }
-        for (int idx = t; idx < CH * 16; idx += 256) {
-            const int r = idx / 16, vv = idx % 16;
-            sdO[r * SP + vv] = r < n ? ld(dO, ((size_t)(tb + (int64_t)j * CH + r) * H + h) * D + col0 + vv) : 0.f;
-        }
-        __syncthreads();
-        {  // dU = P^T dO + Kh dS: wave w owns rows 16w .. 16w+15
-            const int ii = 16 * wave + li;
+        const float* sO = sdO[buf];
+        {  // dU = P^T dO + Kh dS: rows 16 wave .. 16 wave + 15
             floatx4 acc = zero4();
-            tile_f32(acc, CH, lane, [&](int r) { return rec[R::P + r * CH + ii]; },
-                     [&](int r) { return sdO[r * SP + li]; });
-            tile_f32(acc, D, lane, [&](int c) { return rec[R::KH + (size_t)ii * D + c]; },
-                     [&](int c) { return sdS[c * SP + li]; });
+#pragma unroll
+            for (int e = 0; e < C::EP; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, e), sO[(4 * e + gq) * SP + li], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < C::EK; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, C::EP + e), sdS[(4 * e + gq) * SP + li], acc,
+                                                           0, 0, 0);
             float* du = dU + ch * CH * D;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -391,24 +461,32 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
             }
         }
         __syncthreads();
-        // dS <- Qg^T dO + Diag(gamma) dS - W^T dU: wave w owns rows of D / 4
-        for (int rt = 0; rt < D / 64; ++rt) {
-            const int cb = wave * (D / 4) + 16 * rt;
-            const int cc = cb + li;
-            floatx4 acc;
+        // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = cb + 4 * gq + r;
-                acc[r] = rec[R::GAM + row] * sdS[row * SP + li];
-            }
-            tile_f32(acc, CH, lane, [&](int r) { return rec[R::QG + (size_t)r * D + cc]; },
-                     [&](int r) { return sdO[r * SP + li]; });
-            tile_f32(acc, CH, lane, [&](int r) { return -rec[R::W + (size_t)r * D + cc]; },
-                     [&](int r) { return sdU[r * SP + li]; });
+        for (int rt = 0; rt < C::NRT; ++rt) {
+            const int cb = wave * (D / 4) + 16 * rt, eb = C::EP + C::EK + rt * 2 * C::EQ;
+            const float4 gm = cur[C::E / 4 + rt];
+            floatx4 acc;
+            acc[0] = gm.x * sdS[(cb + 4 * gq) * SP + li];
+            acc[1] = gm.y * sdS[(cb + 4 * gq + 1) * SP + li];
+            acc[2] = gm.z * sdS[(cb + 4 * gq + 2) * SP + li];
+            acc[3] = gm.w * sdS[(cb + 4 * gq + 3) * SP + li];
+#pragma unroll
+            for (int e = 0; e < C::EQ; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, eb + e), sO[(4 * e + gq) * SP + li], acc, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < C::EQ; ++e)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, eb + C::EQ + e), sdU[(4 * e + gq) * SP + li],
+                                                           acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sdS[(cb + 4 * gq + r) * SP + li] = acc[r];
         }
+        if (j > 0) store_do(buf ^ 1, don);
         __syncthreads();
+        if (j > 0) {
+#pragma unroll
+            for (int i = 0; i < C::Q4; ++i) cur[i] = nxt[i];
+        }
     }
     if (dinit)
         for (int idx = t; idx < D * 16; idx += 256) {
