@@ -44,7 +44,7 @@ namespace kda {
 
 namespace {
 
-constexpr int BW_T = 256;  // threads of the prep and local kernels (4 waves)
+constexpr int BW_T = 512;  // threads of the prep kernel (8 waves)
 constexpr int BW_W = BW_T / 64;
 constexpr int BL_T = 512;  // threads of the local kernel (8 waves)
 constexpr int BL_W = BL_T / 64;
@@ -149,13 +149,21 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     const IT* v = static_cast<const IT*>(a.v);
     float* rec = brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS;
 
-    for (int idx = t; idx < CH * D; idx += BW_T) {
-        const int r = idx / D, c = idx % D;
-        const size_t th = (size_t)(tb + c0 + r) * H + h;
+    // inputs, branch-free: rows past the sequence end clamped, then zeroed; v
+    // stays in registers until Ut
+    constexpr int PER = CH * D / BW_T;
+    float vr[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = t + BW_T * i, r = idx / D, c = idx % D;
+        const size_t th = (size_t)(tb + c0 + min(r, n - 1)) * H + h;
         const bool ok = r < n;
-        sK[r * DP + c] = ok ? ld(k, th * D + c) : 0.f;
-        sX[r * DP + c] = ok ? ld(q, th * D + c) : 0.f;
-        sG[r * DP + c] = ok ? (a.gate_per_head ? a.la[th] : a.la[th * D + c]) : 0.f;
+        const float kx = ld(k, th * D + c), qx = ld(q, th * D + c), vx = ld(v, th * D + c);
+        const float gx = a.gate_per_head ? a.la[th] : a.la[th * D + c];
+        sK[r * DP + c] = ok ? kx : 0.f;
+        sX[r * DP + c] = ok ? qx : 0.f;
+        sG[r * DP + c] = ok ? gx : 0.f;
+        vr[i] = ok ? vx : 0.f;
     }
     if (t < CH) sB[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
     __syncthreads();
@@ -227,7 +235,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         auto prod = [&](floatx4& acc, const float* X, const float* Y) {
             tile_f32(acc, 16, lane, [&](int kk) { return X[li * AP + kk]; }, [&](int kk) { return Y[kk * AP + li]; });
         };
-        {
+        if (wave < 4) {
             const int d = wave;
             constexpr int SR[4][3] = {{0, 0, 0}, {1, 1, 2}, {2, 3, 2}, {3, 3, 1}};
             constexpr int SC[4][3] = {{1, 2, 3}, {2, 3, 3}, {0, 0, 1}, {1, 2, 0}};
@@ -286,7 +294,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             }
         }
         __syncthreads();
-        {
+        if (wave < 4) {
             floatx4 acc;
             switch (wave) {
                 case 0: acc = tload(blk(sT, 0, 2)); prod(acc, blk(sA, 2, 1), blk(sT, 1, 0)); tstore(blk(sT, 0, 2), acc, 1.f); break;
@@ -349,9 +357,10 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     }
     __syncthreads();
     // Ut = T Bv (Bv = beta V)
-    for (int idx = t; idx < CH * D; idx += BW_T) {
-        const int r = idx / D, c = idx % D;
-        sX[r * DP + c] = r < n ? sB[r] * ld(v, ((size_t)(tb + c0 + r) * H + h) * D + c) : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int idx = t + BW_T * i, r = idx / D, c = idx % D;
+        sX[r * DP + c] = sB[r] * vr[i];
     }
     __syncthreads();
     for (int task = wave; task < 4 * (D / 16); task += BW_W) {
@@ -567,7 +576,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<8>(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
+        tile_f32<D / 4>(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
                     [&](int c) { return S[(size_t)c * D + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -599,8 +608,8 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 x = zero4(), y = zero4();
-        tile_f32(x, D, lane, [&](int c) { return sY[rr * DP + c]; }, [&](int c) { return S[(size_t)cc * D + c]; });
-        tile_f32(y, D, lane, [&](int c) { return sX[rr * DP + c]; }, [&](int c) { return dS[(size_t)cc * D + c]; });
+        tile_f32<D / 4>(x, D, lane, [&](int c) { return sY[rr * DP + c]; }, [&](int c) { return S[(size_t)cc * D + c]; });
+        tile_f32<D / 4>(y, D, lane, [&](int c) { return sX[rr * DP + c]; }, [&](int c) { return dS[(size_t)cc * D + c]; });
         float gl = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -627,7 +636,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<8>(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
+        tile_f32<D / 4>(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
                     [&](int c) { return S[(size_t)cc * D + c]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
@@ -675,7 +684,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         const int mt = task / 4, nt = task % 4;
         if (nt > mt) continue;
         floatx4 acc = zero4();
-        tile_f32<8>(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
+        tile_f32<D / 4>(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
                     [&](int c) { return sY[(16 * nt + li) * DP + c]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -687,7 +696,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<8>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
+        tile_f32<CH / 4>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
                     [&](int r) { return dU[(size_t)r * D + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
