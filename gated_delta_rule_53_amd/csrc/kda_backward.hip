@@ -98,6 +98,14 @@ __device__ __forceinline__ float ld(const X* p, size_t i) {
     return to_f32(p[i]);
 }
 
+// four consecutive elements from p + i (i % 4 == 0), as fp32
+__device__ __forceinline__ float4 ld4(const float* p, size_t i) { return *reinterpret_cast<const float4*>(p + i); }
+__device__ __forceinline__ float4 ld4(const bf16_t* p, size_t i) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xffff0000u));
+}
+
 // One 16x16 fp32 tile product acc += sum_k A(m, k) B(k, n), k = 0 .. K-1,
 // with lane l feeding A(m0 + (l & 15), k) and B(k, n0 + (l & 15)) through the loaders;
 // acc[r] of lane l ends as C(m0 + 4 (l >> 4) + r, n0 + (l & 15)).  K advances in
@@ -117,6 +125,33 @@ __device__ __forceinline__ void tile_f32(floatx4& acc, int K, int lane, FA&& a, 
         for (int e = 0; e < GS; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], y[e], acc, 0, 0, 0);
     }
 }
+
+// The same product with operands fetched four reduction indices at a time: the
+// loaders return A(m0 + (l & 15), k .. k+3) and B(k .. k+3, n0 + (l & 15)) for
+// k = k0 + 4 (l >> 4), and the four components feed four consecutive matrix-core
+// steps (lane group g supplies index k0 + 4 g + e at step e; A and B agree, so
+// the sum is the same).  K % (16 GS) == 0.
+template <int GS = 2, typename FA, typename FB>
+__device__ __forceinline__ void tile_f32_v(floatx4& acc, int K, int lane, FA&& a, FB&& b) {
+    const int g4 = 4 * (lane >> 4);
+    for (int k0 = 0; k0 < K; k0 += 16 * GS) {
+        float4 x[GS], y[GS];
+#pragma unroll
+        for (int e = 0; e < GS; ++e) {
+            x[e] = a(k0 + 16 * e + g4);
+            y[e] = b(k0 + 16 * e + g4);
+        }
+#pragma unroll
+        for (int e = 0; e < GS; ++e) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e].x, y[e].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e].y, y[e].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e].z, y[e].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e].w, y[e].w, acc, 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 }  // namespace
 
@@ -523,10 +558,10 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     constexpr int AP = CH + 1;
     constexpr int NB = D / 16;            // 16-column blocks of a 64 x D matrix
     constexpr int TPW = 4 * NB / BL_W;    // tiles of such a matrix per wave
-    __shared__ float sG[CH * D];
+    __shared__ __align__(16) float sG[CH * D];
     __shared__ float sT[CH * AP];
-    __shared__ float sX[CH * DP];   // U, dW, T^T dT, q, dG
-    __shared__ float sY[CH * DP];   // dO, Bk, Bv, k
+    __shared__ __align__(16) float sX[CH * DP];   // U, dW, T^T dT, q, dG
+    __shared__ __align__(16) float sY[CH * DP];   // dO, Bk, Bv, k
     __shared__ float sP[CH * AP];   // dP, then column partial sums
     __shared__ float sM[CH * AP];   // dT, then diag(beta) dAtil
     __shared__ float sGL[D];        // dL/dG_last per channel
@@ -561,8 +596,46 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) aq[i] = ak[i] = aks[i] = zero4();
 
-    for (int idx = t; idx < CH * D; idx += BL_T) sG[idx] = rec[R::G + idx];
-    for (int idx = t; idx < CH * CH; idx += BL_T) sT[(idx / CH) * AP + idx % CH] = rec[R::T + idx];
+    // copies to LDS: every thread's loads are issued before its stores
+    constexpr int V4 = CH * D / 4 / BL_T;  // float4s of a 64 x D matrix per thread
+    {
+        float4 g[V4], tt[CH * CH / 4 / BL_T];
+#pragma unroll
+        for (int i = 0; i < V4; ++i) g[i] = ld4(rec + R::G, 4 * (t + BL_T * i));
+#pragma unroll
+        for (int i = 0; i < CH * CH / 4 / BL_T; ++i) tt[i] = ld4(rec + R::T, 4 * (t + BL_T * i));
+#pragma unroll
+        for (int i = 0; i < V4; ++i) reinterpret_cast<float4*>(sG)[t + BL_T * i] = g[i];
+#pragma unroll
+        for (int i = 0; i < CH * CH / 4 / BL_T; ++i) {
+            const int idx = 4 * (t + BL_T * i), r = idx / CH, c = idx % CH;
+            sT[r * AP + c] = tt[i].x;
+            sT[r * AP + c + 1] = tt[i].y;
+            sT[r * AP + c + 2] = tt[i].z;
+            sT[r * AP + c + 3] = tt[i].w;
+        }
+    }
+    // rows r (clamped, zeroed past the sequence end) of a [T, H, D] tensor to a
+    // 64 x D LDS matrix, scaled per element by f(r, c, x)
+    auto stage = [&](auto* src, float* dst, auto&& f) {
+        float4 x[V4];
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int idx = 4 * (t + BL_T * i), r = idx / D, c = idx % D;
+            x[i] = ld4(src, tok(r) + c);
+        }
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int idx = 4 * (t + BL_T * i), r = idx / D, c = idx % D;
+            const float m = r < n ? 1.f : 0.f;
+            float* d = dst + r * DP + c;
+            d[0] = f(r, c, m * x[i].x);
+            d[1] = f(r, c + 1, m * x[i].y);
+            d[2] = f(r, c + 2, m * x[i].z);
+            d[3] = f(r, c + 3, m * x[i].w);
+        }
+    };
+    auto same = [](int, int, float x) { return x; };
     if (t < D) sGL[t] = 0.f;
     if (t < CH) {
         sdB[t] = 0.f;
@@ -576,27 +649,26 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<D / 4>(acc, D, lane, [&](int c) { return rec[R::W + (size_t)rr * D + c]; },
-                    [&](int c) { return S[(size_t)c * D + cc]; });
+        tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(rec + R::W, (size_t)rr * D + c); },
+                      [&](int c) {
+                          const float* p = S + (size_t)c * D + cc;
+                          return make_float4(p[0], p[D], p[2 * D], p[3 * D]);
+                      });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             sX[row * DP + cc] = rec[R::UT + (size_t)row * D + cc] - acc[r];
         }
     }
-    for (int idx = t; idx < CH * D; idx += BL_T) {
-        const int r = idx / D, c = idx % D;
-        const float x = ld(dO, tok(r) + c);
-        sY[r * DP + c] = r < n ? x : 0.f;
-    }
+    stage(dO, sY, same);
     __syncthreads();
     // dP = tril(dO U^T)
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
         if (nt <= mt)
-            tile_f32(acc, D, lane, [&](int c) { return sY[(16 * mt + li) * DP + c]; },
-                     [&](int c) { return sX[(16 * nt + li) * DP + c]; });
+            tile_f32_v(acc, D, lane, [&](int c) { return lds4(sY + (16 * mt + li) * DP + c); },
+                       [&](int c) { return lds4(sX + (16 * nt + li) * DP + c); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
@@ -608,8 +680,10 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 x = zero4(), y = zero4();
-        tile_f32<D / 4>(x, D, lane, [&](int c) { return sY[rr * DP + c]; }, [&](int c) { return S[(size_t)cc * D + c]; });
-        tile_f32<D / 4>(y, D, lane, [&](int c) { return sX[rr * DP + c]; }, [&](int c) { return dS[(size_t)cc * D + c]; });
+        tile_f32_v<4>(x, D, lane, [&](int c) { return lds4(sY + rr * DP + c); },
+                      [&](int c) { return ld4(S, (size_t)cc * D + c); });
+        tile_f32_v<4>(y, D, lane, [&](int c) { return lds4(sX + rr * DP + c); },
+                      [&](int c) { return ld4(dS, (size_t)cc * D + c); });
         float gl = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -624,11 +698,23 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         atomicAdd(&sGL[cc], gl);
     }
     // dgamma_c = sum_v S[c][v] dS[c][v]
-    for (int c = wave; c < D; c += BL_W) {
-        float x = 0.f;
-        for (int v2 = lane; v2 < D; v2 += 64) x += S[(size_t)c * D + v2] * dS[(size_t)c * D + v2];
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-        if (lane == 0) atomicAdd(&sGL[c], x * fast_exp(GL[c]));
+#pragma unroll 1
+    for (int c0w = 0; c0w < D / BL_W; c0w += 4) {  // four channels of the wave at a time
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const size_t o = (size_t)(wave + BL_W * (c0w + i)) * D + lane;
+            x[i] = 0.f;
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) x[i] += S[o + 64 * e] * dS[o + 64 * e];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float y = x[i];
+            for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off);
+            const int c = wave + BL_W * (c0w + i);
+            if (lane == 0) atomicAdd(&sGL[c], y * fast_exp(GL[c]));
+        }
     }
     __syncthreads();
     // dW = -dU S^T (into sX); Bk = beta K e^G (into sY)
@@ -636,23 +722,20 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<D / 4>(acc, D, lane, [&](int c) { return dU[(size_t)rr * D + c]; },
-                    [&](int c) { return S[(size_t)cc * D + c]; });
+        tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(dU, (size_t)rr * D + c); },
+                      [&](int c) { return ld4(S, (size_t)cc * D + c); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
     }
-    for (int idx = t; idx < CH * D; idx += BL_T) {
-        const int r = idx / D, c = idx % D;
-        sY[r * DP + c] = sBeta[r] * in(k, r, c) * fast_exp(sG[r * D + c]);
-    }
+    stage(k, sY, [&](int r, int c, float x) { return sBeta[r] * x * fast_exp(sG[r * D + c]); });
     __syncthreads();
     // dT = tril(dW Bk^T);  dBk = T^T dW -> dk, dbeta
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
         if (nt <= mt)
-            tile_f32(acc, D, lane, [&](int c) { return sX[(16 * mt + li) * DP + c]; },
-                     [&](int c) { return sY[(16 * nt + li) * DP + c]; });
+            tile_f32_v(acc, D, lane, [&](int c) { return lds4(sX + (16 * mt + li) * DP + c); },
+                       [&](int c) { return lds4(sY + (16 * nt + li) * DP + c); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
@@ -674,18 +757,15 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         }
     }
     __syncthreads();
-    for (int idx = t; idx < CH * D; idx += BL_T) {
-        const int r = idx / D, c = idx % D;
-        sY[r * DP + c] = sBeta[r] * in(v, r, c);
-    }
+    stage(v, sY, [&](int r, int, float x) { return sBeta[r] * x; });
     __syncthreads();
     // dT += tril(dU Bv^T) (the same tasks per wave as above);  dBv = T^T dU -> dv, dbeta
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         if (nt > mt) continue;
         floatx4 acc = zero4();
-        tile_f32<D / 4>(acc, D, lane, [&](int c) { return dU[(size_t)(16 * mt + li) * D + c]; },
-                    [&](int c) { return sY[(16 * nt + li) * DP + c]; });
+        tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(dU, (size_t)(16 * mt + li) * D + c); },
+                      [&](int c) { return lds4(sY + (16 * nt + li) * DP + c); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
@@ -696,7 +776,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<CH / 4>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
+        tile_f32<8>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
                     [&](int r) { return dU[(size_t)r * D + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -729,17 +809,21 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     }
     __syncthreads();
     // dbeta += sum_i dAtil[r][i] A0[r][i];  then sM <- diag(beta) dAtil;  q, k to LDS
-    for (int r = wave; r < CH; r += BL_W) {
-        float x = sM[r * AP + lane] * rec[R::A0 + r * CH + lane];
-        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-        if (lane == 0) sdB[r] += x;
-        sM[r * AP + lane] *= sBeta[r];
+    {
+        float a0[CH / BL_W];
+#pragma unroll
+        for (int i = 0; i < CH / BL_W; ++i) a0[i] = rec[R::A0 + (wave + BL_W * i) * CH + lane];
+#pragma unroll
+        for (int i = 0; i < CH / BL_W; ++i) {
+            const int r = wave + BL_W * i;
+            float x = sM[r * AP + lane] * a0[i];
+            for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+            if (lane == 0) sdB[r] += x;
+            sM[r * AP + lane] *= sBeta[r];
+        }
     }
-    for (int idx = t; idx < CH * D; idx += BL_T) {
-        const int r = idx / D, c = idx % D;
-        sX[r * DP + c] = in(q, r, c);
-        sY[r * DP + c] = in(k, r, c);
-    }
+    stage(q, sX, same);
+    stage(k, sY, same);
     __syncthreads();
 
     // Decay-weighted products of a lower-triangular M (dP or diag(beta) dAtil):
