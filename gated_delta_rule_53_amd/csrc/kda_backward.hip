@@ -679,6 +679,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
+        float kk[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kk[r] = in(k, 16 * mt + 4 * gq + r, cc);
         floatx4 x = zero4(), y = zero4();
         tile_f32_v<4>(x, D, lane, [&](int c) { return lds4(sY + rr * DP + c); },
                       [&](int c) { return ld4(S, (size_t)cc * D + c); });
@@ -693,7 +696,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             const float f = y[r] * fast_exp(GL[cc] - g);
             ak[i][r] += f;
             aks[i][r] -= f;
-            gl += f * in(k, row, cc);
+            gl += f * kk[r];
         }
         atomicAdd(&sGL[cc], gl);
     }
@@ -717,7 +720,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         }
     }
     __syncthreads();
-    // dW = -dU S^T (into sX); Bk = beta K e^G (into sY)
+    // dW = -dU S^T (into sX); Kg = K e^G (into sY; Bk = diag(beta) Kg)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
@@ -727,15 +730,19 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
     }
-    stage(k, sY, [&](int r, int c, float x) { return sBeta[r] * x * fast_exp(sG[r * D + c]); });
+    stage(k, sY, [&](int r, int c, float x) { return x * fast_exp(sG[r * D + c]); });
     __syncthreads();
     // dT = tril(dW Bk^T);  dBk = T^T dW -> dk, dbeta
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
+        const float bc = sBeta[16 * nt + li];
         if (nt <= mt)
             tile_f32_v(acc, D, lane, [&](int c) { return lds4(sX + (16 * mt + li) * DP + c); },
-                       [&](int c) { return lds4(sY + (16 * nt + li) * DP + c); });
+                       [&](int c) {
+                           const float4 y = lds4(sY + (16 * nt + li) * DP + c);
+                           return make_float4(bc * y.x, bc * y.y, bc * y.z, bc * y.w);
+                       });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
@@ -750,22 +757,26 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
-            const float e = fast_exp(sG[row * D + cc]), dkc = sBeta[row] * e * acc[r];
+            const float dkc = sBeta[row] * fast_exp(sG[row * D + cc]) * acc[r];
             ak[i][r] += dkc;
             aks[i][r] += dkc;
-            atomicAdd(&sdB[row], acc[r] * in(k, row, cc) * e);
+            atomicAdd(&sdB[row], acc[r] * sY[row * DP + cc]);
         }
     }
     __syncthreads();
-    stage(v, sY, [&](int r, int, float x) { return sBeta[r] * x; });
+    stage(v, sY, same);
     __syncthreads();
-    // dT += tril(dU Bv^T) (the same tasks per wave as above);  dBv = T^T dU -> dv, dbeta
+    // dT += tril(dU Bv^T) (the same tasks per wave as above, Bv = diag(beta) V);  dBv = T^T dU -> dv, dbeta
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         if (nt > mt) continue;
         floatx4 acc = zero4();
+        const float bc = sBeta[16 * nt + li];
         tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(dU, (size_t)(16 * mt + li) * D + c); },
-                      [&](int c) { return lds4(sY + (16 * nt + li) * DP + c); });
+                      [&](int c) {
+                          const float4 y = lds4(sY + (16 * nt + li) * DP + c);
+                          return make_float4(bc * y.x, bc * y.y, bc * y.z, bc * y.w);
+                      });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
@@ -782,7 +793,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             if (row < n) b.dv[tok(row) + cc] = sBeta[row] * acc[r];
-            atomicAdd(&sdB[row], acc[r] * in(v, row, cc));
+            atomicAdd(&sdB[row], acc[r] * sY[row * DP + cc]);
         }
     }
     __syncthreads();
