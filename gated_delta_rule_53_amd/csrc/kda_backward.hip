@@ -437,31 +437,33 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         return reinterpret_cast<const float4*>(brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS + R::CR) +
                (size_t)wave * C::Q4 * 64 + lane;
     };
-    // dO of chunk j, rows past the sequence end as zero; thread t holds rows (t + 256 i) / 16
-    auto load_do = [&](int j, float* x) {
-        const int n = (int)min<int64_t>(CH, L - (int64_t)j * CH);
+    // dO of chunk j: thread t holds rows (t + 256 i) / 16, clamped to the sequence;
+    // rows past its end are zeroed when stored to LDS, so the loads stay in flight
+    auto rows = [&](int j) { return (int)min<int64_t>(CH, L - (int64_t)j * CH); };
+    auto load_do = [&](int j, GT* x) {
+        const int n = rows(j);
 #pragma unroll
         for (int i = 0; i < DO_PER; ++i) {
             const int idx = t + 256 * i, r = idx / 16, vv = idx % 16;
-            const float y = ld(dO, ((size_t)(tb + (int64_t)j * CH + min(r, n - 1)) * H + h) * D + col0 + vv);
-            x[i] = r < n ? y : 0.f;
+            x[i] = dO[((size_t)(tb + (int64_t)j * CH + min(r, n - 1)) * H + h) * D + col0 + vv];
         }
     };
-    auto store_do = [&](int buf, const float* x) {
+    auto store_do = [&](int buf, int j, const GT* x) {
+        const int n = rows(j);
 #pragma unroll
         for (int i = 0; i < DO_PER; ++i) {
             const int idx = t + 256 * i;
-            sdO[buf][(idx / 16) * SP + idx % 16] = x[i];
+            sdO[buf][(idx / 16) * SP + idx % 16] = idx / 16 < n ? to_f32(x[i]) : 0.f;
         }
     };
     float4 cur[C::Q4], nxt[C::Q4];
-    float don[DO_PER];
+    GT don[DO_PER];
     if (nch > 0) {
         const float4* p = crec(nch - 1);
 #pragma unroll
         for (int i = 0; i < C::Q4; ++i) cur[i] = p[i * 64];
         load_do(nch - 1, don);
-        store_do(0, don);
+        store_do(0, nch - 1, don);
     }
     auto opnd = [&](const float4* x, int e) {
         const float4 f = x[e >> 2];
@@ -475,10 +477,10 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     for (int jj = 0; jj < nch; ++jj) {
         const int j = nch - 1 - jj, buf = jj & 1;
         if (j > 0) {
+            load_do(j - 1, don);
             const float4* p = crec(j - 1);
 #pragma unroll
             for (int i = 0; i < C::Q4; ++i) nxt[i] = p[i * 64];
-            load_do(j - 1, don);
         }
         const size_t ch = (size_t)(s * a.Wc + j) * H + h;
         float* snap = dsnap + ch * D * D;
@@ -525,7 +527,7 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
 #pragma unroll
             for (int r = 0; r < 4; ++r) sdS[(cb + 4 * gq + r) * SP + li] = acc[r];
         }
-        if (j > 0) store_do(buf ^ 1, don);
+        if (j > 0) store_do(buf ^ 1, j - 1, don);
         __syncthreads();
         if (j > 0) {
 #pragma unroll
