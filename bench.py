@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
 PAGE_FLOP_PER_TOKEN_HEAD = lambda d, C=64: 6 * d * d + 3 * C * d + C * C  # cost per head, per token
 METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode-step HBM GB/s, 1 MI355X"
@@ -73,6 +74,22 @@ def backward_bytes(tokens, heads, d, states=1):
     fp32 dq, dk, dv, dlog_alpha, dbeta written, plus the initial state and the final-state
     gradient read and the initial-state gradient written."""
     return tokens * heads * (3 * d * 2 + d * 4 + 4 + d * 4 + 4 * d * 4 + 4) + 3 * states * heads * d * d * 4
+
+
+def backward_matrix_flops(tokens, heads, d, c=64):
+    """fp32 matrix-core FLOPs of the three backward kernels per call (2 m n k per product; lower
+    16x16 blocks only where a product is triangular).  Per chunk and head: prep A0 and P (10
+    lower blocks each over d), W and Ut (c x c by c x d); the chain dU = P^T dO + Kh dS and
+    dS = Qg^T dO - W^T dU; the local pass U, dQg, dKh and dW (c x d by d x d each), dP, dT and
+    its second term (10 lower blocks over d), dBk and dBv (c x c by c x d), T^T dT and dAtil
+    (c^3 each), and the four decay-weighted products (per 16-column block, 160 reduction
+    steps over the four row blocks: 96 below or right of the diagonal blocks, 64 in them)."""
+    chunks = -(-tokens // c) * heads
+    prep = 20 * (2 * 16 * 16 * d) + 2 * (2 * c * c * d)
+    chain = 2 * c * d * (c + d) + 2 * d * d * 2 * c
+    local = (4 * 2 * c * d * d + 3 * 10 * (2 * 16 * 16 * d) + 2 * (2 * c * c * d) + 2 * (2 * c ** 3)
+             + 4 * (d // 16) * 160 * 2 * 16 * 16)
+    return chunks * (prep + chain + local)
 
 
 def to_dev(x, torch):
@@ -305,10 +322,13 @@ def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):
         ms.append(e0.elapsed_time(e1))
     s = float(np.median(ms)) / 1e3
     b = backward_bytes(T, H, D)
+    f = backward_matrix_flops(T, H, D)
     return {"what": "dq, dk, dv, dlog_alpha, dbeta, d_init of the 64K x 32-head prefill (bf16 in, fp32 d_out "
                     "and gradients), forward recompute included",
             "ms": s * 1e3, "tokens_per_s": T / s, "algorithmic_bytes": b, "hbm_gbs": b / s / 1e9,
-            "frac": b / s / 1e9 / HBM_PEAK_GBS}
+            "frac": b / s / 1e9 / HBM_PEAK_GBS,
+            "mfma_fp32": {"flop_per_call": f, "achieved": f / s / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+                          "unit": "TFLOP/s", "frac": f / s / 1e12 / FP32_MFMA_PEAK_TFLOPS}}
 
 
 def bench_layer(kda, torch, synth, wp, wd, args, flush, stream):
