@@ -383,7 +383,7 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
 // record, the state snapshot, the fp32 backward record, the gradient snapshot
 // and dU, then (one gate per head) a per-channel gate-gradient scratch.
 struct BwdLayout {
-    size_t state, rec, snap, brec, dsnap, du, dg, total;
+    size_t state, rec, snap, brec, dsnap, du, total;
 };
 
 static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l) {
@@ -398,8 +398,7 @@ static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLa
     l.brec = l.snap + align256(units * d * d * 4);
     l.dsnap = l.brec + align256(units * kda::bwd_record_bytes(p.d));
     l.du = l.dsnap + align256(units * d * d * 4);
-    l.dg = l.du + align256(units * CHUNK * d * 4);
-    l.total = l.dg + (s->gate_per_head ? align256((size_t)p.tokens * s->heads * d * 4) : 0) + 256;
+    l.total = l.du + align256(units * CHUNK * d * 4) + 256;
     return KDA_OK;
 }
 
@@ -486,7 +485,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     b.dq = dq;
     b.dk = dk;
     b.dv = dv;
-    b.dG = s->gate_per_head ? reinterpret_cast<float*>(ws + l.dg) : dlog_alpha;
+    b.dG = s->gate_per_head ? nullptr : dlog_alpha;
     b.dla_head = s->gate_per_head ? dlog_alpha : nullptr;
     b.dbeta = dbeta;
     hipError_t e = kda::bwd_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, b,

@@ -50,12 +50,14 @@ constexpr int BL_T = 512;  // threads of the local kernel (8 waves)
 constexpr int BL_W = BL_T / 64;
 
 // Operands of one wave of the reverse chain for one chunk, in the order its
-// matrix-core steps consume them: step e feeds lane l = li + 16 g the A value of
-// row li and reduction index 4 (e - base) + g, and four consecutive steps form
-// one float4 per lane.  Wave w owns dU rows 16w .. 16w+15 (steps P^T over the
-// chunk's rows, then Kh over the key channels) and NRT 16-row tiles of dS at
-// rows w D/4 + 16 rt (steps Qg^T, then -W^T, over the chunk's rows); after the
-// steps, one float4 per tile holds gamma of the lane's four dS rows.
+// matrix-core steps consume them.  Reduction index k of a part (k = 16 b + 4 g + e)
+// is fed by lane l = li + 16 g at step 4 b + e of that part, so the four steps of
+// block b take one float4 per lane (k = 16 b + 4 g .. +3) and the B operand, kept
+// transposed in LDS, is one 16-byte read per lane as well.  Wave w owns dU rows
+// 16w .. 16w+15 (parts P^T over the chunk's rows, then Kh over the key channels)
+// and NRT 16-row tiles of dS at rows w D/4 + 16 rt (parts Qg^T, then -W^T, over
+// the chunk's rows); after the steps, one float4 per tile holds gamma of the
+// lane's four dS rows.
 template <int D>
 struct ChainRec {
     static constexpr int NRT = D / 64;
@@ -64,6 +66,9 @@ struct ChainRec {
     static constexpr int Q4 = E / 4 + NRT;
     static constexpr int FLOATS = 4 * Q4 * 64 * 4;
     __device__ static int at(int w, int e, int lane) { return ((w * Q4 + (e >> 2)) * 64 + lane) * 4 + (e & 3); }
+    // step offset and lane group of reduction index k within a part
+    __device__ static int ks(int k) { return 4 * (k >> 4) + (k & 3); }
+    __device__ static int kg(int k) { return (k >> 2) & 3; }
     // dS tile of key channel c: wave, tile, and the step base of its Qg^T part
     __device__ static int wave_of(int c) { return c / (D / 4); }
     __device__ static int tile_of(int c) { return (c % (D / 4)) >> 4; }
@@ -231,7 +236,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
             const bool keep = cb < rb || (isP ? row >= col : row > col);
             const float x = keep ? acc[r] : 0.f;
-            if (isP) rec[R::CR + C::at(col >> 4, row >> 2, (col & 15) + 16 * (row & 3))] = x;
+            if (isP) rec[R::CR + C::at(col >> 4, C::ks(row), (col & 15) + 16 * C::kg(row))] = x;
             else sA[row * AP + col] = x;
         }
     }
@@ -240,7 +245,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int r = idx / CH, c = idx % CH;
         if ((c >> 4) > (r >> 4)) {
             sA[r * AP + c] = 0.f;
-            rec[R::CR + C::at(c >> 4, r >> 2, (c & 15) + 16 * (r & 3))] = 0.f;
+            rec[R::CR + C::at(c >> 4, C::ks(r), (c & 15) + 16 * C::kg(r))] = 0.f;
         }
     }
     __syncthreads();
@@ -375,15 +380,15 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             rec[R::W + row * D + cc] = acc[r];
-            rec[R::CR + C::at(C::wave_of(cc), C::qbase(cc) + C::EQ + (row >> 2), li + 16 * (row & 3))] = -acc[r];
+            rec[R::CR + C::at(C::wave_of(cc), C::qbase(cc) + C::EQ + C::ks(row), li + 16 * C::kg(row))] = -acc[r];
         }
     }
     for (int idx = t; idx < CH * D; idx += BW_T) {
         const int r = idx / D, c = idx % D;
         const float g = sG[r * DP + c];
-        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + (r >> 2), (c & 15) + 16 * (r & 3))] =
+        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::ks(r), (c & 15) + 16 * C::kg(r))] =
             sX[r * DP + c] * fast_exp(g);
-        rec[R::CR + C::at(r >> 4, C::EP + (c >> 2), (r & 15) + 16 * (c & 3))] = sK[r * DP + c] * fast_exp(GL[c] - g);
+        rec[R::CR + C::at(r >> 4, C::EP + C::ks(c), (r & 15) + 16 * C::kg(c))] = sK[r * DP + c] * fast_exp(GL[c] - g);
         rec[R::G + idx] = g;
     }
     for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
@@ -421,11 +426,12 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
                                                         const float* dfinal, float* dsnap, float* dU, float* dinit) {
     using R = BRec<D>;
     using C = ChainRec<D>;
-    constexpr int SP = 17;
+    // B operands transposed: column li of the slice, reduction index contiguous
+    constexpr int KS = D + 4, KO = CH + 4;
     constexpr int DO_PER = CH * 16 / 256;  // dO values per thread and chunk
-    __shared__ float sdS[D * SP];
-    __shared__ float sdO[2][CH * SP];
-    __shared__ float sdU[CH * SP];
+    __shared__ __align__(16) float sdS[16 * KS];
+    __shared__ __align__(16) float sdO[2][16 * KO];
+    __shared__ __align__(16) float sdU[16 * KO];
     const int H = a.H, NH = a.N * H;
     const int u = blockIdx.x % NH, z = blockIdx.x / NH;
     const int s = u / H, h = u % H, col0 = 16 * z;
@@ -452,8 +458,8 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         const int n = rows(j);
 #pragma unroll
         for (int i = 0; i < DO_PER; ++i) {
-            const int idx = t + 256 * i;
-            sdO[buf][(idx / 16) * SP + idx % 16] = idx / 16 < n ? to_f32(x[i]) : 0.f;
+            const int idx = t + 256 * i, r = idx / 16;
+            sdO[buf][(idx % 16) * KO + r] = r < n ? to_f32(x[i]) : 0.f;
         }
     };
     float4 cur[C::Q4], nxt[C::Q4];
@@ -465,13 +471,15 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         load_do(nch - 1, don);
         store_do(0, nch - 1, don);
     }
-    auto opnd = [&](const float4* x, int e) {
-        const float4 f = x[e >> 2];
-        return (e & 3) == 0 ? f.x : (e & 3) == 1 ? f.y : (e & 3) == 2 ? f.z : f.w;
+    auto mfma4 = [](floatx4 acc, float4 x, float4 y) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.x, y.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.y, y.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x.z, y.z, acc, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(x.w, y.w, acc, 0, 0, 0);
     };
     for (int idx = t; idx < D * 16; idx += 256) {
         const int c = idx / 16, vv = idx % 16;
-        sdS[c * SP + vv] = dfinal ? dfinal[((size_t)u * D + c) * D + col0 + vv] : 0.f;
+        sdS[vv * KS + c] = dfinal ? dfinal[((size_t)u * D + c) * D + col0 + vv] : 0.f;
     }
     __syncthreads();
     for (int jj = 0; jj < nch; ++jj) {
@@ -486,46 +494,38 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         float* snap = dsnap + ch * D * D;
         for (int idx = t; idx < D * 16; idx += 256) {
             const int c = idx / 16, vv = idx % 16;
-            snap[(size_t)c * D + col0 + vv] = sdS[c * SP + vv];  // dL/dS_{j+1}
+            snap[(size_t)c * D + col0 + vv] = sdS[vv * KS + c];  // dL/dS_{j+1}
         }
-        const float* sO = sdO[buf];
+        const float* sO = sdO[buf] + li * KO + 4 * gq;
+        const float* sS = sdS + li * KS + 4 * gq;
         {  // dU = P^T dO + Kh dS: rows 16 wave .. 16 wave + 15
             floatx4 acc = zero4();
 #pragma unroll
-            for (int e = 0; e < C::EP; ++e)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, e), sO[(4 * e + gq) * SP + li], acc, 0, 0, 0);
+            for (int b = 0; b < C::EP / 4; ++b) acc = mfma4(acc, cur[b], lds4(sO + 16 * b));
 #pragma unroll
-            for (int e = 0; e < C::EK; ++e)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, C::EP + e), sdS[(4 * e + gq) * SP + li], acc,
-                                                           0, 0, 0);
+            for (int b = 0; b < C::EK / 4; ++b) acc = mfma4(acc, cur[C::EP / 4 + b], lds4(sS + 16 * b));
+            *reinterpret_cast<float4*>(sdU + li * KO + 16 * wave + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
             float* du = dU + ch * CH * D;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * wave + 4 * gq + r;
-                sdU[row * SP + li] = acc[r];
-                du[(size_t)row * D + col0 + li] = acc[r];
-            }
+            for (int r = 0; r < 4; ++r) du[(size_t)(16 * wave + 4 * gq + r) * D + col0 + li] = acc[r];
         }
         __syncthreads();
         // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
+        const float* sU = sdU + li * KO + 4 * gq;
 #pragma unroll
         for (int rt = 0; rt < C::NRT; ++rt) {
-            const int cb = wave * (D / 4) + 16 * rt, eb = C::EP + C::EK + rt * 2 * C::EQ;
-            const float4 gm = cur[C::E / 4 + rt];
+            const int cb = wave * (D / 4) + 16 * rt, qb = (C::EP + C::EK + rt * 2 * C::EQ) / 4;
+            const float4 gm = cur[C::E / 4 + rt], s4 = lds4(sS + cb);
             floatx4 acc;
-            acc[0] = gm.x * sdS[(cb + 4 * gq) * SP + li];
-            acc[1] = gm.y * sdS[(cb + 4 * gq + 1) * SP + li];
-            acc[2] = gm.z * sdS[(cb + 4 * gq + 2) * SP + li];
-            acc[3] = gm.w * sdS[(cb + 4 * gq + 3) * SP + li];
+            acc[0] = gm.x * s4.x;
+            acc[1] = gm.y * s4.y;
+            acc[2] = gm.z * s4.z;
+            acc[3] = gm.w * s4.w;
 #pragma unroll
-            for (int e = 0; e < C::EQ; ++e)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, eb + e), sO[(4 * e + gq) * SP + li], acc, 0, 0, 0);
+            for (int b = 0; b < C::EQ / 4; ++b) acc = mfma4(acc, cur[qb + b], lds4(sO + 16 * b));
 #pragma unroll
-            for (int e = 0; e < C::EQ; ++e)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(opnd(cur, eb + C::EQ + e), sdU[(4 * e + gq) * SP + li],
-                                                           acc, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sdS[(cb + 4 * gq + r) * SP + li] = acc[r];
+            for (int b = 0; b < C::EQ / 4; ++b) acc = mfma4(acc, cur[qb + C::EQ / 4 + b], lds4(sU + 16 * b));
+            *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         if (j > 0) store_do(buf ^ 1, j - 1, don);
         __syncthreads();
@@ -537,7 +537,7 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     if (dinit)
         for (int idx = t; idx < D * 16; idx += 256) {
             const int c = idx / 16, vv = idx % 16;
-            dinit[((size_t)u * D + c) * D + col0 + vv] = sdS[c * SP + vv];
+            dinit[((size_t)u * D + c) * D + col0 + vv] = sdS[vv * KS + c];
         }
 }
 

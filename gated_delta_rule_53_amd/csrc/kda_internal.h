@@ -74,8 +74,8 @@ struct BwdArgs {
     float* dU;            // dL/dU per (chunk, head), [64, D]
     float* dinit;         // dL/dinit_state [N, H, D, D] or null
     float *dq, *dk, *dv;  // [tokens, H, D] fp32
-    float* dG;            // [tokens, H, D] fp32: dL/dlog_alpha per channel
-    float* dla_head;      // [tokens, H] fp32 when the gate is per head (dG is then scratch), else null
+    float* dG;            // [tokens, H, D] fp32: dL/dlog_alpha per channel; null when the gate is per head
+    float* dla_head;      // [tokens, H] fp32 when the gate is per head, else null
     float* dbeta;         // [tokens, H] fp32
 };
 size_t bwd_record_bytes(int d);
