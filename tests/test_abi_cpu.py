@@ -98,6 +98,40 @@ def test_chunk_fwd_validation(L):
     assert _fwd(L, _shape(gph=1), la=4 * A, out=4 * A + la_head) == WORKSPACE  # passes validation
 
 
+def _bwd(L, s, q=A, k=2 * A, v=3 * A, la=4 * A, b=5 * A, init=None, cu=None, dout=6 * A, dfin=None,
+         dq=7 * A, dk=8 * A, dv=9 * A, dla=10 * A, db=11 * A, dinit=None, ws=None, wsb=0):
+    return L.kda_chunk_bwd(s, q, k, v, la, b, init, cu, dout, dfin, dq, dk, dv, dla, db, dinit, ws, wsb, None)
+
+
+def test_chunk_bwd_validation(L):
+    s = _shape()
+    assert _bwd(L, None) == INVALID
+    assert _bwd(L, _shape(dk=96, dv=96)) == UNSUPPORTED
+    assert _bwd(L, _shape(H=0)) == INVALID
+    assert _bwd(L, _shape(gph=2)) == INVALID
+    assert _bwd(L, s, dq=None) == INVALID
+    assert _bwd(L, s, dout=None) == INVALID
+    assert _bwd(L, s, dk=8 * A + 4) == INVALID                   # misaligned
+    assert _bwd(L, s, dv=A + 64) == INVALID                      # a gradient over q
+    assert _bwd(L, s, db=7 * A + 128) == INVALID                 # two gradients overlap
+    assert _bwd(L, s, init=12 * A, dinit=12 * A + 256) == INVALID  # d_init over init
+    assert _bwd(L, _shape(B=2), cu=13 * A) == INVALID           # varlen needs batch 1
+    assert _bwd(L, s, cu=13 * A, ws=14 * A, wsb=1 << 30) == OK   # varlen with zero sequences: no work
+    assert _bwd(L, s, ws=None) == WORKSPACE
+    assert _bwd(L, s, ws=14 * A, wsb=1024) == WORKSPACE
+    assert _bwd(L, s, ws=14 * A + 8, wsb=1 << 30) == WORKSPACE   # misaligned workspace
+    # dlog_alpha right after dv: overlaps a per-channel gate gradient only when it is per channel
+    la_head = 256 * 2 * 4
+    assert _bwd(L, s, dla=9 * A - la_head) == INVALID
+    assert _bwd(L, _shape(gph=1), dla=9 * A - la_head) == WORKSPACE  # passes validation
+    n = L.kda_chunk_bwd_workspace_size(s)
+    assert n > L.kda_chunk_fwd_workspace_size(s) > 0
+    assert L.kda_chunk_bwd_workspace_size(None) == 0
+    # every chunk of every sequence is held at once: N * chunks <= 65535
+    assert L.kda_chunk_bwd_workspace_size(_shape(B=1100, T=4096)) == 0
+    assert _bwd(L, _shape(B=1100, T=4096)) == UNSUPPORTED
+
+
 def test_decode_validation(L):
     f = L.kda_decode_step
     assert f(0, 2, 64, 64, F32, F32, 0, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
