@@ -157,7 +157,7 @@ def main():
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md on sharding)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path; pass --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
