@@ -25,11 +25,15 @@
 // Kernels (all fp32 arithmetic, fp32 matrix cores):
 //   chunk_local_kernel + chunk_inter_kernel (the forward's, with state
 //     snapshots): S_j for every chunk;
-//   bwd_prep_kernel   one workgroup per (chunk, head): G, A0, P, T, W, Ut, Qg,
-//                     Kh, gamma -> an fp32 record;
-//   bwd_chain_kernel  one workgroup per (sequence, head, 16 value columns):
-//                     the reverse chain over chunks, writing dS_{j+1} and dU_j;
-//   bwd_local_kernel  one workgroup per (chunk, head): every parameter gradient.
+//   bwd_prep_kernel   one 512-thread workgroup per (chunk, head): G, A0, P, T,
+//                     W, Ut, Qg, Kh, gamma -> an fp32 record (T, A0, W, Ut, G
+//                     row-major for the local pass; P^T, Kh, Qg^T, -W^T and
+//                     gamma in the chain's matrix-core order);
+//   bwd_chain_kernel  one 256-thread workgroup per (sequence, head, 16 value
+//                     columns): the reverse chain over chunks, writing dS_{j+1}
+//                     and dU_j, each chunk's operands loaded during the previous;
+//   bwd_local_kernel  one 512-thread workgroup per (chunk, head): every
+//                     parameter gradient.
 //
 // Decay factors e^{G_r - G_i} of the pairwise products are split about an
 // anchor row so each matrix-core operand carries one bounded factor: for a
