@@ -124,3 +124,21 @@ def test_backward_workload2_sampled(kda):
     for gk, rk in KEYS:
         got = g[gk][:, heads] if gk == "d_init" else g[gk][0][:, heads]
         assert_close(gk, got, ref[rk], TOL["bf16"])
+
+
+@pytest.mark.parametrize("B,T,D,dtype", [(3, 130, 64, "f32"), (2, 100, 128, "bf16")])
+def test_backward_dense_batch(kda, B, T, D, dtype):
+    """A dense batch [B, T, H, d] (no cu_seqlens): the same gradients as the B sequences packed."""
+    H = 2
+    d = random_small(B * 31 + D, 0, H, D, D, dtype=dtype, lens=[T] * B)
+    dO, dF = _grads(97, d)
+    dense = lambda x: to_dev(x, torch).reshape((B, T) + x.shape[1:])
+    q, k, v, la, b = (dense(d[x]) for x in ("q", "k", "v", "log_alpha", "beta"))
+    g = kda.chunk_bwd(q, k, v, la, b, dense(dO), to_dev(d["init"], torch), to_dev(dF, torch))
+    torch.cuda.synchronize()
+    ref = oracle_bwd(d, dO, dF)
+    for gk, rk in KEYS:
+        got = g[gk].cpu().numpy()
+        if gk != "d_init":
+            got = got.reshape((B * T,) + got.shape[2:])
+        assert_close(gk, got, ref[rk], TOL[dtype])
