@@ -162,6 +162,20 @@ __device__ __forceinline__ void tile_f32_v(floatx4& acc, int K, int lane, FA&& a
 
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of a row (lanes 16 g .. 16 g + 15), in every lane of the
+// row: lane pairs, quads, then the mirrored half-row and row.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp<0x141>(x);  // row_half_mirror
+    x += dpp<0x140>(x);  // row_mirror
+    return x;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -572,6 +586,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     __shared__ float sM[CH * AP];   // dT, then diag(beta) dAtil
     __shared__ float sGL[D];        // dL/dG_last per channel
     __shared__ float sdB[CH];
+    __shared__ float sdBw[BL_W][CH];  // each wave's dBk and dBv part of dbeta, per row
     __shared__ float sBeta[CH];
 
     const int h = blockIdx.x, s = blockIdx.y / a.Wc, j = blockIdx.y % a.Wc;
@@ -645,6 +660,8 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     if (t < D) sGL[t] = 0.f;
     if (t < CH) {
         sdB[t] = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < BL_W; ++w2) sdBw[w2][t] = 0.f;
         sBeta[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
     }
     __syncthreads();
@@ -755,6 +772,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             sM[row * AP + col] = row >= col ? acc[r] : 0.f;
         }
     }
+    float pb[TPW][4];
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
@@ -766,7 +784,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             const float dkc = sBeta[row] * fast_exp(sG[row * D + cc]) * acc[r];
             ak[i][r] += dkc;
             aks[i][r] += dkc;
-            atomicAdd(&sdB[row], acc[r] * sY[row * DP + cc]);
+            pb[i][r] = acc[r] * sY[row * DP + cc];  // with dBv's below: this lane's column of dbeta
         }
     }
     __syncthreads();
@@ -799,9 +817,18 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             if (row < n) b.dv[tok(row) + cc] = sBeta[row] * acc[r];
-            atomicAdd(&sdB[row], acc[r] * sY[row * DP + cc]);
+            pb[i][r] += acc[r] * sY[row * DP + cc];
         }
     }
+    // this wave's 16 columns of every row it holds: a row sum over the lanes, one
+    // writer per row (no two waves write one entry)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = row16_sum(pb[i][r]);
+            if (li == 0) sdBw[wave][16 * mt_of(i) + 4 * gq + r] = x;
+        }
     __syncthreads();
     // X = T^T dT (into sX as 64 x 64), then dAtil = -X T^T (strictly lower, into sM)
     for (int task = wave; task < 16; task += BL_W) {
@@ -947,7 +974,12 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             else if (row < n) b.dG[tok(row) + cg] = carry;
         }
     }
-    if (t < n) b.dbeta[(size_t)(tb + c0 + t) * H + h] = sdB[t];
+    if (t < n) {
+        float x = sdB[t];
+#pragma unroll
+        for (int w2 = 0; w2 < BL_W; ++w2) x += sdBw[w2][t];
+        b.dbeta[(size_t)(tb + c0 + t) * H + h] = x;
+    }
     if (b.dla_head) {  // one gate per head: its gradient is the sum over the key channels
         __syncthreads();
         for (int r = wave; r < n; r += BL_W) {
