@@ -575,10 +575,11 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     const GT* dO = static_cast<const GT*>(b.dO);
     using R = BRec<D>;
     constexpr int DP = D + 4;
+    constexpr int GD = D + 4;
     constexpr int AP = CH + 1;
     constexpr int NB = D / 16;            // 16-column blocks of a 64 x D matrix
     constexpr int TPW = 4 * NB / BL_W;    // tiles of such a matrix per wave
-    __shared__ __align__(16) float sG[CH * D];
+    __shared__ __align__(16) float sG[CH * GD];  // G, rows padded against bank conflicts
     __shared__ float sT[CH * AP];
     __shared__ __align__(16) float sX[CH * DP];   // U, dW, T^T dT, q, dG
     __shared__ __align__(16) float sY[CH * DP];   // dO, Bk, Bv, k
@@ -626,7 +627,10 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
         for (int i = 0; i < CH * CH / 4 / BL_T; ++i) tt[i] = ld4(rec + R::T, 4 * (t + BL_T * i));
 #pragma unroll
-        for (int i = 0; i < V4; ++i) reinterpret_cast<float4*>(sG)[t + BL_T * i] = g[i];
+        for (int i = 0; i < V4; ++i) {
+            const int idx = 4 * (t + BL_T * i);
+            *reinterpret_cast<float4*>(sG + (idx / D) * GD + idx % D) = g[i];
+        }
 #pragma unroll
         for (int i = 0; i < CH * CH / 4 / BL_T; ++i) {
             const int idx = 4 * (t + BL_T * i), r = idx / CH, c = idx % CH;
@@ -665,7 +669,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         sBeta[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
     }
     __syncthreads();
-    const float* GL = sG + (n - 1) * D;
+    const float* GL = sG + (n - 1) * GD;
 
     // U = Ut - W S_j
 #pragma unroll
@@ -698,7 +702,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             sP[row * AP + col] = (row >= col && row < n) ? acc[r] : 0.f;
         }
     }
-    // dQg = dO S^T -> dq;  dKh = U dS^T -> dk, dG_last
+    // dQg = dO S^T -> dq;  dKh = U dS^T -> dk, dG_last (every tile of a wave lies in
+    // one 16-column strip, so the wave's dG_last terms add up in registers first)
+    float gl = 0.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
@@ -710,19 +716,18 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                       [&](int c) { return ld4(S, (size_t)cc * D + c); });
         tile_f32_v<4>(y, D, lane, [&](int c) { return lds4(sX + rr * DP + c); },
                       [&](int c) { return ld4(dS, (size_t)cc * D + c); });
-        float gl = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
-            const float g = sG[row * D + cc];
+            const float g = sG[row * GD + cc];
             aq[i][r] += x[r] * fast_exp(g);
             const float f = y[r] * fast_exp(GL[cc] - g);
             ak[i][r] += f;
             aks[i][r] -= f;
             gl += f * kk[r];
         }
-        atomicAdd(&sGL[cc], gl);
     }
+    atomicAdd(&sGL[16 * nt_of(0) + li], gl);
     // dgamma_c = sum_v S[c][v] dS[c][v]
 #pragma unroll 1
     for (int c0w = 0; c0w < D / BL_W; c0w += 4) {  // four channels of the wave at a time
@@ -753,7 +758,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + cc] = -acc[r];
     }
-    stage(k, sY, [&](int r, int c, float x) { return x * fast_exp(sG[r * D + c]); });
+    stage(k, sY, [&](int r, int c, float x) { return x * fast_exp(sG[r * GD + c]); });
     __syncthreads();
     // dT = tril(dW Bk^T);  dBk = T^T dW -> dk, dbeta
     for (int task = wave; task < 16; task += BL_W) {
@@ -781,7 +786,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
-            const float dkc = sBeta[row] * fast_exp(sG[row * D + cc]) * acc[r];
+            const float dkc = sBeta[row] * fast_exp(sG[row * GD + cc]) * acc[r];
             ak[i][r] += dkc;
             aks[i][r] += dkc;
             pb[i][r] = acc[r] * sY[row * DP + cc];  // with dBv's below: this lane's column of dbeta
@@ -891,11 +896,11 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                 const int an = 16 * blk, mr = 16 * blk + li;
                 if (blk > 0)
                     tile_f32(off, an, lane, [&](int ii) { return M[mr * AP + ii]; },
-                             [&](int ii) { return X[ii * DP + cc] * fast_exp(sG[an * D + cc] - sG[ii * D + cc]); });
+                             [&](int ii) { return X[ii * DP + cc] * fast_exp(sG[an * GD + cc] - sG[ii * GD + cc]); });
                 tile_f32(dia, 16, lane, [&](int ii) { return M[mr * AP + 16 * blk + ii]; },
                          [&](int ii) {
                              const int i2 = 16 * blk + ii;
-                             return X[i2 * DP + cc] * fast_exp(sG[m * D + cc] - sG[i2 * D + cc]);
+                             return X[i2 * DP + cc] * fast_exp(sG[m * GD + cc] - sG[i2 * GD + cc]);
                          });
             } else {
                 const int bn = 16 * blk + 15, mi = 16 * blk + li;
@@ -903,25 +908,25 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                     tile_f32(off, CH - 16 * (blk + 1), lane, [&](int r) { return M[(bn + 1 + r) * AP + mi]; },
                              [&](int r) {
                                  const int rr = bn + 1 + r;
-                                 return X[rr * DP + cc] * fast_exp(sG[rr * D + cc] - sG[bn * D + cc]);
+                                 return X[rr * DP + cc] * fast_exp(sG[rr * GD + cc] - sG[bn * GD + cc]);
                              });
                 tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
                          [&](int r) {
                              const int rr = 16 * blk + r;
-                             return X[rr * DP + cc] * fast_exp(sG[rr * D + cc] - sG[m * D + cc]);
+                             return X[rr * DP + cc] * fast_exp(sG[rr * GD + cc] - sG[m * GD + cc]);
                          });
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * blk + 4 * gq + r;
-                const float g = sG[row * D + cc];
+                const float g = sG[row * GD + cc];
                 float y;
                 if (!col) {
-                    y = dia[r] * fast_exp(g - sG[m * D + cc]);
-                    if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * D + cc]);
+                    y = dia[r] * fast_exp(g - sG[m * GD + cc]);
+                    if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * GD + cc]);
                 } else {
-                    y = dia[r] * fast_exp(sG[m * D + cc] - g);
-                    if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * D + cc] - g);
+                    y = dia[r] * fast_exp(sG[m * GD + cc] - g);
+                    if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * GD + cc] - g);
                 }
                 if (form == 0) {
                     aq[i][r] += y;
