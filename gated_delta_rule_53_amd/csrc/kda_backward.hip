@@ -160,6 +160,37 @@ __device__ __forceinline__ void tile_f32_v(floatx4& acc, int K, int lane, FA&& a
     }
 }
 
+// Two products of one 16x16 tile shape, x += A1 B1 and y += A2 B2 (operands as for
+// tile_f32_v), in one loop that also adds to d this lane's share of
+// sum_k B1(k, n) B2(k, n) (its four reduction indices per 16).
+template <int GS, typename FA1, typename FB1, typename FA2, typename FB2>
+__device__ __forceinline__ void tile2_f32_v(floatx4& x, floatx4& y, float& d, int K, int lane, FA1&& a1, FB1&& b1,
+                                            FA2&& a2, FB2&& b2) {
+    const int g4 = 4 * (lane >> 4);
+    for (int k0 = 0; k0 < K; k0 += 16 * GS) {
+        float4 p[GS], q[GS], u[GS], w[GS];
+#pragma unroll
+        for (int e = 0; e < GS; ++e) {
+            p[e] = a1(k0 + 16 * e + g4);
+            q[e] = b1(k0 + 16 * e + g4);
+            u[e] = a2(k0 + 16 * e + g4);
+            w[e] = b2(k0 + 16 * e + g4);
+        }
+#pragma unroll
+        for (int e = 0; e < GS; ++e) {
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e].x, q[e].x, x, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(u[e].x, w[e].x, y, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e].y, q[e].y, x, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(u[e].y, w[e].y, y, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e].z, q[e].z, x, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(u[e].z, w[e].z, y, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(p[e].w, q[e].w, x, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(u[e].w, w[e].w, y, 0, 0, 0);
+            d += q[e].x * w[e].x + q[e].y * w[e].y + q[e].z * w[e].z + q[e].w * w[e].w;
+        }
+    }
+}
+
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 template <int CTRL>
@@ -510,9 +541,11 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         }
         const size_t ch = (size_t)(s * a.Wc + j) * H + h;
         float* snap = dsnap + ch * D * D;
-        for (int idx = t; idx < D * 16; idx += 256) {
-            const int c = idx / 16, vv = idx % 16;
-            snap[(size_t)c * D + col0 + vv] = sdS[vv * KS + c];  // dL/dS_{j+1}
+#pragma unroll
+        for (int i = 0; i < D * 4 / 256; ++i) {  // dL/dS_{j+1}, four columns per store
+            const int idx = t + 256 * i, c = idx / 4, v4 = 4 * (idx % 4);
+            *reinterpret_cast<float4*>(snap + (size_t)c * D + col0 + v4) =
+                make_float4(sdS[v4 * KS + c], sdS[(v4 + 1) * KS + c], sdS[(v4 + 2) * KS + c], sdS[(v4 + 3) * KS + c]);
         }
         const float* sO = sdO[buf] + li * KO + 4 * gq;
         const float* sS = sdS + li * KS + 4 * gq;
@@ -704,18 +737,20 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     }
     // dQg = dO S^T -> dq;  dKh = U dS^T -> dk, dG_last (every tile of a wave lies in
     // one 16-column strip, so the wave's dG_last terms add up in registers first)
-    float gl = 0.f;
+    // B of both products runs over whole rows of S_j and dS (the strip's channels),
+    // which also gives dgamma_c = sum_v S[c][v] dS[c][v] (from one tile per strip)
+    float gl = 0.f, dgam = 0.f;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
+        float dg = 0.f;
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
         float kk[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) kk[r] = in(k, 16 * mt + 4 * gq + r, cc);
         floatx4 x = zero4(), y = zero4();
-        tile_f32_v<4>(x, D, lane, [&](int c) { return lds4(sY + rr * DP + c); },
-                      [&](int c) { return ld4(S, (size_t)cc * D + c); });
-        tile_f32_v<4>(y, D, lane, [&](int c) { return lds4(sX + rr * DP + c); },
-                      [&](int c) { return ld4(dS, (size_t)cc * D + c); });
+        tile2_f32_v<2>(x, y, dg, D, lane, [&](int c) { return lds4(sY + rr * DP + c); },
+                       [&](int c) { return ld4(S, (size_t)cc * D + c); }, [&](int c) { return lds4(sX + rr * DP + c); },
+                       [&](int c) { return ld4(dS, (size_t)cc * D + c); });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
@@ -726,26 +761,15 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
             aks[i][r] -= f;
             gl += f * kk[r];
         }
+        if (i == 0) dgam = dg;
     }
-    atomicAdd(&sGL[16 * nt_of(0) + li], gl);
-    // dgamma_c = sum_v S[c][v] dS[c][v]
-#pragma unroll 1
-    for (int c0w = 0; c0w < D / BL_W; c0w += 4) {  // four channels of the wave at a time
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const size_t o = (size_t)(wave + BL_W * (c0w + i)) * D + lane;
-            x[i] = 0.f;
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) x[i] += S[o + 64 * e] * dS[o + 64 * e];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float y = x[i];
-            for (int off = 32; off >= 1; off >>= 1) y += __shfl_xor(y, off);
-            const int c = wave + BL_W * (c0w + i);
-            if (lane == 0) atomicAdd(&sGL[c], y * fast_exp(GL[c]));
-        }
+    {
+        const int c = 16 * nt_of(0) + li;
+        dgam += __shfl_xor(dgam, 16);
+        dgam += __shfl_xor(dgam, 32);
+        // the strip's channels once: the wave holding its first row block
+        if (mt_of(0) == 0) gl += gq == 0 ? dgam * fast_exp(GL[c]) : 0.f;
+        atomicAdd(&sGL[c], gl);
     }
     __syncthreads();
     // dW = -dU S^T (into sX); Kg = K e^G (into sY; Bk = diag(beta) Kg)
