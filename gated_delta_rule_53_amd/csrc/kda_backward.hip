@@ -417,32 +417,33 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     }
     __syncthreads();
     for (int idx = t; idx < CH * CH; idx += BW_T) rec[R::T + idx] = sT[(idx / CH) * AP + idx % CH];
-    // W = T Bk (Bk = beta K e^G), Qg, Kh, G, gamma
+    // Qg, Kh, G and gamma to the record; then Bk = beta K e^G replaces K in LDS and
+    // W = T Bk
     const float* GL = sG + (n - 1) * DP;
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        const float g = sG[r * DP + c], e = fast_exp(g), kx = sK[r * DP + c];
+        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::ks(r), (c & 15) + 16 * C::kg(r))] = sX[r * DP + c] * e;
+        rec[R::CR + C::at(r >> 4, C::EP + C::ks(c), (r & 15) + 16 * C::kg(c))] = kx * fast_exp(GL[c] - g);
+        rec[R::G + idx] = g;
+        sK[r * DP + c] = sB[r] * kx * e;
+    }
+    for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
+        const int c = idx / 16, l = (idx % 16) + 16 * ((c & 15) >> 2);
+        rec[R::CR + ((C::wave_of(c) * C::Q4 + C::E / 4 + C::tile_of(c)) * 64 + l) * 4 + (c & 3)] = fast_exp(GL[c]);
+    }
+    __syncthreads();
     for (int task = wave; task < 4 * (D / 16); task += BW_W) {
         const int mt = task / (D / 16), nt = task % (D / 16);
         const int cc = 16 * nt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
-                 [&](int i) { return sB[i] * sK[i * DP + cc] * fast_exp(sG[i * DP + cc]); });
+        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; }, [&](int i) { return sK[i * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             rec[R::W + row * D + cc] = acc[r];
             rec[R::CR + C::at(C::wave_of(cc), C::qbase(cc) + C::EQ + C::ks(row), li + 16 * C::kg(row))] = -acc[r];
         }
-    }
-    for (int idx = t; idx < CH * D; idx += BW_T) {
-        const int r = idx / D, c = idx % D;
-        const float g = sG[r * DP + c];
-        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::ks(r), (c & 15) + 16 * C::kg(r))] =
-            sX[r * DP + c] * fast_exp(g);
-        rec[R::CR + C::at(r >> 4, C::EP + C::ks(c), (r & 15) + 16 * C::kg(c))] = sK[r * DP + c] * fast_exp(GL[c] - g);
-        rec[R::G + idx] = g;
-    }
-    for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
-        const int c = idx / 16, l = (idx % 16) + 16 * ((c & 15) >> 2);
-        rec[R::CR + ((C::wave_of(c) * C::Q4 + C::E / 4 + C::tile_of(c)) * 64 + l) * 4 + (c & 3)] = fast_exp(GL[c]);
     }
     __syncthreads();
     // Ut = T Bv (Bv = beta V)
