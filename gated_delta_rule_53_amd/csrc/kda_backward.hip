@@ -437,7 +437,9 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int mt = task / (D / 16), nt = task % (D / 16);
         const int cc = 16 * nt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; }, [&](int i) { return sK[i * DP + cc]; });
+        // T is lower triangular: row block mt sees columns below 16 (mt + 1)
+        tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
+                 [&](int i) { return sK[i * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
@@ -457,7 +459,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int mt = task / (D / 16), nt = task % (D / 16);
         const int cc = 16 * nt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
+        tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
                  [&](int i) { return sX[i * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) rec[R::UT + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
@@ -807,7 +809,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; }, [&](int r) { return sX[r * DP + cc]; });
+        const int r0 = 16 * mt;  // T[r][ii] = 0 for r < ii: rows from the tile's own block
+        tile_f32(acc, CH - r0, lane, [&](int r) { return sT[(r0 + r) * AP + ii]; },
+                 [&](int r) { return sX[(r0 + r) * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
@@ -841,8 +845,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int i = 0; i < TPW; ++i) {
         const int mt = mt_of(i), cc = 16 * nt_of(i) + li, ii = 16 * mt + li;
         floatx4 acc = zero4();
-        tile_f32<8>(acc, CH, lane, [&](int r) { return sT[r * AP + ii]; },
-                    [&](int r) { return dU[(size_t)r * D + cc]; });
+        const int r0 = 16 * mt;
+        tile_f32(acc, CH - r0, lane, [&](int r) { return sT[(r0 + r) * AP + ii]; },
+                 [&](int r) { return dU[(size_t)(r0 + r) * D + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
@@ -864,8 +869,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int r) { return sT[r * AP + 16 * mt + li]; },
-                 [&](int r) { return sM[r * AP + 16 * nt + li]; });
+        const int r0 = 16 * max(mt, nt);  // T^T is upper and dT lower triangular
+        tile_f32(acc, CH - r0, lane, [&](int r) { return sT[(r0 + r) * AP + 16 * mt + li]; },
+                 [&](int r) { return sM[(r0 + r) * AP + 16 * nt + li]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) sX[(16 * mt + 4 * gq + r) * DP + 16 * nt + li] = acc[r];
     }
@@ -873,8 +879,9 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     for (int task = wave; task < 16; task += BL_W) {
         const int mt = task / 4, nt = task % 4;
         floatx4 acc = zero4();
-        tile_f32(acc, CH, lane, [&](int jj) { return sX[(16 * mt + li) * DP + jj]; },
-                 [&](int jj) { return sT[(16 * nt + li) * AP + jj]; });
+        if (nt <= mt)  // strictly lower result; T^T is upper triangular: columns below 16 (nt + 1)
+            tile_f32(acc, 16 * (nt + 1), lane, [&](int jj) { return sX[(16 * mt + li) * DP + jj]; },
+                     [&](int jj) { return sT[(16 * nt + li) * AP + jj]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r, col = 16 * nt + li;
