@@ -77,17 +77,23 @@ def backward_bytes(tokens, heads, d, states=1):
 
 
 def backward_matrix_flops(tokens, heads, d, c=64):
-    """fp32 matrix-core FLOPs of the three backward kernels per call (2 m n k per product; lower
-    16x16 blocks only where a product is triangular).  Per chunk and head: prep A0 and P (10
-    lower blocks each over d), W and Ut (c x c by c x d); the chain dU = P^T dO + Kh dS and
-    dS = Qg^T dO - W^T dU; the local pass U, dQg, dKh and dW (c x d by d x d each), dP, dT and
-    its second term (10 lower blocks over d), dBk and dBv (c x c by c x d), T^T dT and dAtil
-    (c^3 each), and the four decay-weighted products (per 16-column block, 160 reduction
-    steps over the four row blocks: 96 below or right of the diagonal blocks, 64 in them)."""
+    """fp32 matrix-core FLOPs of the three backward kernels per call (2 m n k per product, over
+    the 16x16 blocks each product needs: lower blocks of triangular results, and for a
+    lower-triangular T or dT operand only its nonzero 16-row blocks).  Per chunk and head:
+    prep A0 and P (10 lower blocks each over d), W = T Bk and Ut = T Bv; the chain
+    dU = P^T dO + Kh dS and dS = Qg^T dO - W^T dU; the local pass U, dQg, dKh and dW (c x d by
+    d x d each), dP, dT and its second term (10 lower blocks over d), dBk = T^T dW and
+    dBv = T^T dU, T^T dT and the strictly lower dAtil = -X T^T, and the four decay-weighted
+    products (per 16-column block, 160 reduction steps over the four row blocks)."""
     chunks = -(-tokens // c) * heads
-    prep = 20 * (2 * 16 * 16 * d) + 2 * (2 * c * c * d)
+    nb = c // 16
+    tri = 16 * nb * (nb + 1) // 2                                    # K summed over row blocks, T or T^T
+    t_prod = 2 * 16 * tri * d                                        # T (c x c) by a c x d operand
+    x_k = sum((2 * m + 1) * (c - 16 * m) for m in range(nb))         # T^T dT: K = c - 16 max(mt, nt)
+    a_k = sum(16 * (m + 1) * (m + 2) // 2 for m in range(nb))        # X T^T, lower blocks: K = 16 (nt + 1)
+    prep = 20 * (2 * 16 * 16 * d) + 2 * t_prod
     chain = 2 * c * d * (c + d) + 2 * d * d * 2 * c
-    local = (4 * 2 * c * d * d + 3 * 10 * (2 * 16 * 16 * d) + 2 * (2 * c * c * d) + 2 * (2 * c ** 3)
+    local = (4 * 2 * c * d * d + 3 * 10 * (2 * 16 * 16 * d) + 2 * t_prod + 2 * 16 * 16 * (x_k + a_k)
              + 4 * (d // 16) * 160 * 2 * 16 * 16)
     return chunks * (prep + chain + local)
 
