@@ -379,11 +379,12 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
                        state_inout, out, stream);
 }
 
-// Workspace of the backward: state buffer, then per (chunk, head) the forward
-// record, the state snapshot, the fp32 backward record, the gradient snapshot
-// and dU, then (one gate per head) a per-channel gate-gradient scratch.
+// Workspace of the backward: state buffer, the forward records of one window of
+// the recompute (at most the record budget), then per (chunk, head) the state
+// snapshot, the fp32 backward record, the gradient snapshot and dU.
 struct BwdLayout {
     size_t state, rec, snap, brec, dsnap, du, total;
+    int window;  // chunks per window of the forward recompute (its records fit the budget)
 };
 
 static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l) {
@@ -392,9 +393,11 @@ static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLa
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
     if (p.N * all > 65535) return KDA_ERR_UNSUPPORTED;
     const size_t units = (size_t)p.N * all * s->heads, d = p.d;
+    const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
+    l.window = per_chunk == 0 ? 1 : (int)std::min<int64_t>(all, std::max<size_t>(1, RECORD_BUDGET / per_chunk));
     l.state = 0;
     l.rec = p.state_bytes;
-    l.snap = l.rec + align256(units * p.rec);
+    l.snap = l.rec + align256(per_chunk * l.window);
     l.brec = l.snap + align256(units * d * d * 4);
     l.dsnap = l.brec + align256(units * kda::bwd_record_bytes(p.d));
     l.du = l.dsnap + align256(units * d * d * 4);
@@ -477,6 +480,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     a.out = nullptr;
     a.snap = reinterpret_cast<float*>(ws + l.snap);
     b.brec = reinterpret_cast<float*>(ws + l.brec);
+    b.snap_window = l.window;
     b.dO = d_out;
     b.dfinal = d_final_state;
     b.dsnap = reinterpret_cast<float*>(ws + l.dsnap);

@@ -1039,7 +1039,8 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
     hipError_t e;
     const dim3 chunks(a.H, a.N * a.Wc);
     const int units = a.N * a.H;
-    if ((e = chunk_snapshot_dispatch(D, std::is_same<IT, bf16_t>::value, a, st)) != hipSuccess) return e;
+    if ((e = chunk_snapshot_dispatch(D, std::is_same<IT, bf16_t>::value, a, b.snap_window, st)) != hipSuccess)
+        return e;
     hipLaunchKernelGGL((bwd_prep_kernel<D, IT>), chunks, dim3(BW_T), 0, st, a, b.brec);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, a, b.brec,

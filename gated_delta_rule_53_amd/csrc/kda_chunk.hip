@@ -1108,7 +1108,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
         auto step = [&](ChainBuf& f, ChainBuf& fn, int jn, int j) {
             const int cur = (j - jb) & 1;
             if (MODE == 0 && a.snap) {  // the state entering chunk j, for the backward pass
-                float* dst = a.snap + ((size_t)(s * a.Wc + (j - jrec0)) * H + h) * D * D;
+                float* dst = a.snap + ((size_t)(s * a.snap_wc + j) * H + h) * D * D;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -1515,19 +1515,31 @@ static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int 
     return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, ov, st);
 }
 
+// Windows of `window` chunks: the records of one window stay in the last-level
+// cache between its two passes, and the state pass carries S through state_buf.
 template <int D, typename IT, typename OT>
-static hipError_t run_snapshots(const ChunkArgs& a, hipStream_t st) {
+static hipError_t run_snapshots(const ChunkArgs& base, int window, hipStream_t st) {
     using C = LocalCfg<D, OT>;
-    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, false, false>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float>), dim3(a.N * a.H * (D / 16)), dim3(512), 0, st, a);
-    return hipGetLastError();
+    const int nwin = (base.Wc + window - 1) / window;
+    for (int w = 0; w < nwin; ++w) {
+        ChunkArgs a = base;
+        a.snap_wc = base.Wc;
+        a.Wc = window;
+        a.win = w;
+        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, false, false>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st,
+                           a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float>), dim3(a.N * a.H * (D / 16)), dim3(512), 0, st, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
-hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, hipStream_t st) {
-    if (d == 128) return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, st) : run_snapshots<128, float, float>(a, st);
-    return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, st) : run_snapshots<64, float, float>(a, st);
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, hipStream_t st) {
+    if (d == 128)
+        return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, window, st) : run_snapshots<128, float, float>(a, window, st);
+    return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, window, st) : run_snapshots<64, float, float>(a, window, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,

@@ -38,9 +38,11 @@ struct ChunkArgs {
     const uint16_t* out_gate = nullptr;   // bf16 [tokens, H, D] output-gate pre-activation
     const float* norm_weight = nullptr;   // fp32 [D] RMSNorm weight, or null for ones
     float rms_eps = 0.f;
-    // backward recompute: the state entering every chunk, [chunk-in-buffer][H][D][D]
-    // fp32 indexed like the records (null: not written); a null `out` skips the outputs
+    // backward recompute: the state entering every chunk, [sequence][chunk][H][D][D]
+    // fp32 with snap_wc chunks per sequence (null: not written); a null `out` skips
+    // the outputs
     float* snap = nullptr;
+    int snap_wc = 0;
 };
 
 // Layer prologue and epilogue of one decode step (null pointers: off).
@@ -63,10 +65,12 @@ struct Overlap {
 };
 
 // Reverse mode of the chunked prefill (kda_backward.hip).  fwd: the forward's
-// arguments with every chunk in one window (win = 0, Wc = the longest
-// sequence's chunks), rec / state_buf in the workspace, snap set and out null.
+// arguments with Wc = the longest sequence's chunks (the backward's own arrays
+// hold every chunk), rec / state_buf in the workspace, snap set and out null;
+// the forward recompute runs in windows of snap_window chunks through rec.
 struct BwdArgs {
     ChunkArgs fwd;
+    int snap_window;      // chunks per window of the forward recompute
     float* brec;          // fp32 per-(chunk, head) records of the backward
     const void* dO;       // dL/dout, [tokens, H, D] (out dtype)
     const float* dfinal;  // dL/dfinal_state [N, H, D, D] or null
@@ -81,8 +85,9 @@ struct BwdArgs {
 size_t bwd_record_bytes(int d);
 hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st);
 // The forward recompute of the backward: chunk-local records and the state
-// snapshots (a.snap) of every chunk; no outputs.
-hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, hipStream_t st);
+// snapshots (a.snap, a.Wc chunks per sequence) of every chunk, in windows of
+// `window` chunks through one record buffer; no outputs.
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, hipStream_t st);
 
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);
