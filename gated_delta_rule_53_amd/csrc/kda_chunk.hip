@@ -1001,7 +1001,9 @@ struct Frag<float> {
 //   outputs.
 // MODE 2 (second pass): each segment from its true initial state (seg_init),
 //   forming the outputs; the final state is written by the combine kernel.
-template <int D, int BV, typename OT, typename OUT, int MODE = 0>
+// SNAP (with MODE 0, no outputs): the chain waves leave the fp32 state entering
+//   each chunk in LDS and the output waves store it to a.snap, off the chain.
+template <int D, int BV, typename OT, typename OUT, int MODE = 0, bool SNAP = false>
 __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     using R = Rec<D, OT>;
     using FR = Frag<OT>;
@@ -1017,6 +1019,8 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     constexpr int RING = sizeof(OT) == 2 ? (BV <= 32 ? 3 : 2) : 1;
     __shared__ __align__(16) OT sS[2][BV * SP];
     __shared__ __align__(16) OT sU[2][BV * UP];
+    constexpr int SNP = BV + 1;
+    __shared__ float sSnap[SNAP ? D * SNP : 1];
 
     constexpr int ZS = D / BV;                   // slices of the value columns
     constexpr int Z = MODE == 1 ? 2 * ZS : ZS;  // the first segment pass also carries the transition product
@@ -1107,16 +1111,14 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
         };
         auto step = [&](ChainBuf& f, ChainBuf& fn, int jn, int j) {
             const int cur = (j - jb) & 1;
-            if (MODE == 0 && a.snap) {  // the state entering chunk j, for the backward pass
-                float* dst = a.snap + ((size_t)(s * a.snap_wc + j) * H + h) * D * D;
+            if constexpr (SNAP) {  // the state entering chunk j, for the backward pass
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            dst[(size_t)(w * (D / 4) + 16 * rt + 4 * gq + r) * D + col0 + 16 * ct + li] =
-                                Sacc[rt][ct][r];
+                            sSnap[(w * (D / 4) + 16 * rt + 4 * gq + r) * SNP + 16 * ct + li] = Sacc[rt][ct][r];
             }
             float g[RT][4];  // gamma of the four state rows each accumulator lane holds
 #pragma unroll
@@ -1168,6 +1170,17 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
                     if (j < je) step(buf[p], buf[(p + RING - 1) % RING], jn, j);
                 }
             }
+        }
+    } else if constexpr (SNAP) {
+        // no outputs: between the step's two barriers, store the chain's fp32 copy of S_j
+        for (int j = jb; j < je; ++j) {
+            lds_barrier();  // S_j is in sSnap
+            float* dst = a.snap + ((size_t)(s * a.snap_wc + j) * H + h) * D * D + col0;
+            for (int idx = t - 256; idx < D * BV; idx += 256) {
+                const int k = idx / BV, c = idx % BV;
+                dst[(size_t)k * D + c] = sSnap[k * SNP + c];
+            }
+            lds_barrier();
         }
     } else if constexpr (MODE == 1) {
         for (int j = jb; j < je; ++j) {  // no outputs in this pass; keep the barrier count
@@ -1530,7 +1543,8 @@ static hipError_t run_snapshots(const ChunkArgs& base, int window, hipStream_t s
                            a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float>), dim3(a.N * a.H * (D / 16)), dim3(512), 0, st, a);
+        hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float, 0, true>), dim3(a.N * a.H * (D / 16)), dim3(512), 0,
+                           st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
