@@ -11,7 +11,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size",
+           "bwd_workspace_size", "KdaError"]
 
 
 def _torch():
@@ -52,6 +53,15 @@ def workspace_size(batch, seqlen, heads, dk, dv, in_dtype, out_dtype=None, num_s
     shape = _lib.Shape(batch, seqlen, num_seqs, max_seqlen, heads, dk, dv, _dtype_code(in_dtype),
                        _dtype_code(out_dtype))
     return int(lib().kda_chunk_fwd_workspace_size(shape))
+
+
+def bwd_workspace_size(batch, seqlen, heads, dk, dv, in_dtype, dout_dtype=None, num_seqs=0, max_seqlen=0):
+    """Bytes of device workspace ``chunk_bwd`` needs (varlen iff num_seqs > 0)."""
+    torch = _torch()
+    dout_dtype = torch.float32 if dout_dtype is None else dout_dtype
+    shape = _lib.Shape(batch, seqlen, num_seqs, max_seqlen, heads, dk, dv, _dtype_code(in_dtype),
+                       _dtype_code(dout_dtype))
+    return int(lib().kda_chunk_bwd_workspace_size(shape))
 
 
 def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out=None,

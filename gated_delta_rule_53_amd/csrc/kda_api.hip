@@ -379,29 +379,53 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
                        state_inout, out, stream);
 }
 
-// Workspace of the backward: state buffer, the forward records of one window of
-// the recompute (at most the record budget), then per (chunk, head) the state
-// snapshot, the fp32 backward record, the gradient snapshot and dU.
+// Workspace of the backward: state buffer, the forward records of one record
+// window of the recompute (at most the record budget), then per (chunk, head)
+// of one backward window the state snapshot, the fp32 backward record, the
+// gradient snapshot and dU; with more than one backward window, the states
+// entering windows 1, 2, ... and the carried dL/dS.
 struct BwdLayout {
-    size_t state, rec, snap, brec, dsnap, du, total;
-    int window;  // chunks per window of the forward recompute (its records fit the budget)
+    size_t state, rec, snap, brec, dsnap, du, ckpt, dcarry, total;
+    int window;      // chunks per record window of the forward recompute
+    int bwd_window;  // chunks per sequence held by the per-chunk arrays
+    int nbw;         // backward windows
 };
+
+// Bytes of per-chunk backward arrays held at once before the backward walks
+// its chunks in windows (KDA_BWD_WINDOW=n forces n chunks per window).
+constexpr size_t BWD_BUDGET = size_t(24) << 30;
 
 static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l) {
     kda_status_t st = chunk_plan_full(s, varlen, p);
     if (st != KDA_OK) return st;
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
-    if (p.N * all > 65535) return KDA_ERR_UNSUPPORTED;
-    const size_t units = (size_t)p.N * all * s->heads, d = p.d;
-    const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
-    l.window = per_chunk == 0 ? 1 : (int)std::min<int64_t>(all, std::max<size_t>(1, RECORD_BUDGET / per_chunk));
+    const size_t d = p.d, H = s->heads;
+    const size_t per_chunk = (size_t)p.N * H * p.rec;  // forward records of one chunk index
+    const size_t per_bwd = (size_t)p.N * H * (kda::bwd_record_bytes(p.d) + (2 * d * d + CHUNK * d) * sizeof(float));
+    int64_t rw = per_chunk == 0 ? 1 : std::min<int64_t>(all, std::max<size_t>(1, RECORD_BUDGET / per_chunk));
+    int64_t wb = all;
+    const char* e = getenv("KDA_BWD_WINDOW");  // read per call
+    if (e && atoi(e) > 0) wb = std::min<int64_t>(all, atoi(e));
+    else if (per_bwd * all > BWD_BUDGET) wb = std::max<int64_t>(1, (int64_t)(BWD_BUDGET / per_bwd));
+    if (p.N > 0) wb = std::min<int64_t>(wb, 65535 / p.N);  // grid rows: sequences x chunks of a window
+    if (wb < 1) return KDA_ERR_UNSUPPORTED;
+    if (wb < all) {  // several backward windows: each a whole number of record windows
+        if (rw > wb) rw = wb;
+        else wb = wb / rw * rw;
+    }
+    l.window = (int)rw;
+    l.bwd_window = (int)wb;
+    l.nbw = (int)((all + wb - 1) / wb);
+    const size_t units = (size_t)p.N * wb * H;
     l.state = 0;
     l.rec = p.state_bytes;
-    l.snap = l.rec + align256(per_chunk * l.window);
+    l.snap = l.rec + align256(per_chunk * rw);
     l.brec = l.snap + align256(units * d * d * 4);
     l.dsnap = l.brec + align256(units * kda::bwd_record_bytes(p.d));
     l.du = l.dsnap + align256(units * d * d * 4);
-    l.total = l.du + align256(units * CHUNK * d * 4) + 256;
+    l.ckpt = l.du + align256(units * CHUNK * d * 4);
+    l.dcarry = l.ckpt + (l.nbw > 1 ? (size_t)(l.nbw - 1) * p.state_bytes : 0);
+    l.total = l.dcarry + (l.nbw > 1 ? p.state_bytes : 0) + 256;
     return KDA_OK;
 }
 
@@ -481,6 +505,9 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     a.snap = reinterpret_cast<float*>(ws + l.snap);
     b.brec = reinterpret_cast<float*>(ws + l.brec);
     b.snap_window = l.window;
+    b.bwd_window = l.bwd_window;
+    b.ckpt = l.nbw > 1 ? reinterpret_cast<float*>(ws + l.ckpt) : nullptr;
+    b.dcarry = l.nbw > 1 ? reinterpret_cast<float*>(ws + l.dcarry) : nullptr;
     b.dO = d_out;
     b.dfinal = d_final_state;
     b.dsnap = reinterpret_cast<float*>(ws + l.dsnap);

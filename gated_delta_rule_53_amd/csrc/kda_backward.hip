@@ -225,7 +225,8 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     __shared__ float sB[CH];
     constexpr int AP = CH + 1;
 
-    const int h = blockIdx.x, s = blockIdx.y / a.Wc, j = blockIdx.y % a.Wc;
+    // a.Wc chunks per sequence in this backward window, a.win its index
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc, j = a.win * a.Wc + jl;
     int64_t tb, L;
     seq_range(a, s, tb, L);
     const int64_t c0 = (int64_t)j * CH;
@@ -236,7 +237,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     const IT* q = static_cast<const IT*>(a.q);
     const IT* k = static_cast<const IT*>(a.k);
     const IT* v = static_cast<const IT*>(a.v);
-    float* rec = brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS;
+    float* rec = brec + ((size_t)(s * a.Wc + jl) * H + h) * R::FLOATS;
 
     // inputs, branch-free: rows past the sequence end clamped, then zeroed; v
     // stays in registers until Ut
@@ -473,9 +474,14 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
 // float4 per four matrix-core steps) and the next dO slice are loaded into
 // registers while chunk j is computed, so the serial chain waits on the
 // matrix cores and two barriers per chunk, not on memory.
+// Chunks a.win * a.Wc .. of each sequence (one backward window), from the last
+// to the first: dS starts as dS_in (dL/dS at the window's end; null: zero) and
+// its value entering the window goes to dS_out (null: not stored).  dS_in and
+// dS_out may be the same array: each workgroup reads and writes only its own
+// slice.
 template <int D, typename GT>
 __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float* brec, const GT* dO,
-                                                        const float* dfinal, float* dsnap, float* dU, float* dinit) {
+                                                        const float* dS_in, float* dsnap, float* dU, float* dS_out) {
     using R = BRec<D>;
     using C = ChainRec<D>;
     // B operands transposed: column li of the slice, reduction index contiguous
@@ -489,10 +495,11 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     const int s = u / H, h = u % H, col0 = 16 * z;
     int64_t tb, L;
     seq_range(a, s, tb, L);
-    const int nch = (int)((L + CH - 1) / CH);
+    const int j0 = a.win * a.Wc;
+    const int nch = (int)min<int64_t>((L + CH - 1) / CH, (int64_t)j0 + a.Wc);  // one past the window's last chunk
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
     auto crec = [&](int j) {
-        return reinterpret_cast<const float4*>(brec + ((size_t)(s * a.Wc + j) * H + h) * R::FLOATS + R::CR) +
+        return reinterpret_cast<const float4*>(brec + ((size_t)(s * a.Wc + (j - j0)) * H + h) * R::FLOATS + R::CR) +
                (size_t)wave * C::Q4 * 64 + lane;
     };
     // dO of chunk j: thread t holds rows (t + 256 i) / 16, clamped to the sequence;
@@ -516,7 +523,7 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     };
     float4 cur[C::Q4], nxt[C::Q4];
     GT don[DO_PER];
-    if (nch > 0) {
+    if (nch > j0) {
         const float4* p = crec(nch - 1);
 #pragma unroll
         for (int i = 0; i < C::Q4; ++i) cur[i] = p[i * 64];
@@ -531,18 +538,18 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
     };
     for (int idx = t; idx < D * 16; idx += 256) {
         const int c = idx / 16, vv = idx % 16;
-        sdS[vv * KS + c] = dfinal ? dfinal[((size_t)u * D + c) * D + col0 + vv] : 0.f;
+        sdS[vv * KS + c] = dS_in ? dS_in[((size_t)u * D + c) * D + col0 + vv] : 0.f;
     }
     __syncthreads();
-    for (int jj = 0; jj < nch; ++jj) {
+    for (int jj = 0; jj < nch - j0; ++jj) {
         const int j = nch - 1 - jj, buf = jj & 1;
-        if (j > 0) {
+        if (j > j0) {
             load_do(j - 1, don);
             const float4* p = crec(j - 1);
 #pragma unroll
             for (int i = 0; i < C::Q4; ++i) nxt[i] = p[i * 64];
         }
-        const size_t ch = (size_t)(s * a.Wc + j) * H + h;
+        const size_t ch = (size_t)(s * a.Wc + (j - j0)) * H + h;
         float* snap = dsnap + ch * D * D;
 #pragma unroll
         for (int i = 0; i < D * 4 / 256; ++i) {  // dL/dS_{j+1}, four columns per store
@@ -581,17 +588,17 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
             for (int b = 0; b < C::EQ / 4; ++b) acc = mfma4(acc, cur[qb + C::EQ / 4 + b], lds4(sU + 16 * b));
             *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
-        if (j > 0) store_do(buf ^ 1, j - 1, don);
+        if (j > j0) store_do(buf ^ 1, j - 1, don);
         __syncthreads();
-        if (j > 0) {
+        if (j > j0) {
 #pragma unroll
             for (int i = 0; i < C::Q4; ++i) cur[i] = nxt[i];
         }
     }
-    if (dinit)
+    if (dS_out)
         for (int idx = t; idx < D * 16; idx += 256) {
             const int c = idx / 16, vv = idx % 16;
-            dinit[((size_t)u * D + c) * D + col0 + vv] = sdS[vv * KS + c];
+            dS_out[((size_t)u * D + c) * D + col0 + vv] = sdS[vv * KS + c];
         }
 }
 
@@ -626,7 +633,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     __shared__ float sdBw[BL_W][CH];  // each wave's dBk and dBv part of dbeta, per row
     __shared__ float sBeta[CH];
 
-    const int h = blockIdx.x, s = blockIdx.y / a.Wc, j = blockIdx.y % a.Wc;
+    const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc, j = a.win * a.Wc + jl;
     int64_t tb, L;
     seq_range(a, s, tb, L);
     const int64_t c0 = (int64_t)j * CH;
@@ -637,7 +644,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     const IT* q = static_cast<const IT*>(a.q);
     const IT* k = static_cast<const IT*>(a.k);
     const IT* v = static_cast<const IT*>(a.v);
-    const size_t ch = (size_t)(s * a.Wc + j) * H + h;
+    const size_t ch = (size_t)(s * a.Wc + jl) * H + h;
     const float* rec = brec + ch * R::FLOATS;
     const float* S = a.snap + ch * D * D;
     const float* dS = b.dsnap + ch * D * D;
@@ -1033,21 +1040,51 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
 // ---------------------------------------------------------------------------
 size_t bwd_record_bytes(int d) { return (d == 128 ? BRec<128>::FLOATS : BRec<64>::FLOATS) * sizeof(float); }
 
+// Backward windows from the last to the first.  With more than one, a first
+// forward pass (no snapshots, no outputs) stores the state entering each later
+// window; each window then recomputes its forward records and state snapshots
+// from that state, and dL/dS entering it is carried to the next one down.
 template <int D, typename IT, typename GT>
 static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
-    const ChunkArgs& a = b.fwd;
+    const ChunkArgs& a = b.fwd;  // a.Wc: chunks of the longest sequence
+    constexpr bool BF = std::is_same<IT, bf16_t>::value;
+    const int all = a.Wc, wb = b.bwd_window, rw = b.snap_window;
+    const int nbw = (all + wb - 1) / wb;  // backward windows
+    const int rpb = (wb + rw - 1) / rw;   // record windows per backward window (exact when nbw > 1)
+    const int nrw = (all + rw - 1) / rw;  // record windows over every chunk
+    const size_t units = (size_t)a.N * a.H, sb = units * D * D * sizeof(float);
     hipError_t e;
-    const dim3 chunks(a.H, a.N * a.Wc);
-    const int units = a.N * a.H;
-    if ((e = chunk_snapshot_dispatch(D, std::is_same<IT, bf16_t>::value, a, b.snap_window, st)) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((bwd_prep_kernel<D, IT>), chunks, dim3(BW_T), 0, st, a, b.brec);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, a, b.brec,
-                       static_cast<const GT*>(b.dO), b.dfinal, b.dsnap, b.dU, b.dinit);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BL_T), 0, st, b);
-    return hipGetLastError();
+    for (int w = 0; w + 1 < nbw; ++w) {
+        if ((e = chunk_snapshot_dispatch(D, BF, a, rw, w * rpb, rpb, false, st)) != hipSuccess) return e;
+        if ((e = hipMemcpyAsync(b.ckpt + (size_t)w * units * D * D, a.state_buf, sb, hipMemcpyDeviceToDevice, st)) !=
+            hipSuccess)
+            return e;
+    }
+    for (int w = nbw - 1; w >= 0; --w) {
+        if (w > 0 && (e = hipMemcpyAsync(a.state_buf, b.ckpt + (size_t)(w - 1) * units * D * D, sb,
+                                         hipMemcpyDeviceToDevice, st)) != hipSuccess)
+            return e;
+        ChunkArgs r = a;
+        r.snap_wc = wb;
+        r.snap_j0 = w * wb;
+        if ((e = chunk_snapshot_dispatch(D, BF, r, rw, w * rpb, std::min(rpb, nrw - w * rpb), true, st)) !=
+            hipSuccess)
+            return e;
+        BwdArgs bw = b;
+        bw.fwd.Wc = wb;
+        bw.fwd.win = w;
+        const dim3 chunks(a.H, a.N * wb);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, IT>), chunks, dim3(BW_T), 0, st, bw.fwd, b.brec);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const float* din = w == nbw - 1 ? b.dfinal : b.dcarry;
+        float* dout = w == 0 ? b.dinit : b.dcarry;
+        hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, bw.fwd, b.brec,
+                           static_cast<const GT*>(b.dO), din, b.dsnap, b.dU, dout);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BL_T), 0, st, bw);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st) {

@@ -1175,7 +1175,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
         // no outputs: between the step's two barriers, store the chain's fp32 copy of S_j
         for (int j = jb; j < je; ++j) {
             lds_barrier();  // S_j is in sSnap
-            float* dst = a.snap + ((size_t)(s * a.snap_wc + j) * H + h) * D * D + col0;
+            float* dst = a.snap + ((size_t)(s * a.snap_wc + (j - a.snap_j0)) * H + h) * D * D + col0;
             for (int idx = t - 256; idx < D * BV; idx += 256) {
                 const int k = idx / BV, c = idx % BV;
                 dst[(size_t)k * D + c] = sSnap[k * SNP + c];
@@ -1528,32 +1528,40 @@ static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int 
     return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, ov, st);
 }
 
-// Windows of `window` chunks: the records of one window stay in the last-level
-// cache between its two passes, and the state pass carries S through state_buf.
+// Record windows w0 .. w0 + nw - 1 of `window` chunks: the records of one
+// window stay in the last-level cache between its two passes, and the state
+// pass carries S through state_buf.  With SNAP the state pass stores the state
+// entering every chunk; without it, it only carries S (no outputs either).
 template <int D, typename IT, typename OT>
-static hipError_t run_snapshots(const ChunkArgs& base, int window, hipStream_t st) {
+static hipError_t run_snapshots(const ChunkArgs& base, int window, int w0, int nw, bool snap, hipStream_t st) {
     using C = LocalCfg<D, OT>;
-    const int nwin = (base.Wc + window - 1) / window;
-    for (int w = 0; w < nwin; ++w) {
+    for (int w = w0; w < w0 + nw; ++w) {
         ChunkArgs a = base;
-        a.snap_wc = base.Wc;
         a.Wc = window;
         a.win = w;
+        a.out = nullptr;
         hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, false, false>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st,
                            a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float, 0, true>), dim3(a.N * a.H * (D / 16)), dim3(512), 0,
-                           st, a);
+        if (snap)
+            hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float, 0, true>), dim3(a.N * a.H * (D / 16)), dim3(512),
+                               0, st, a);
+        else
+            hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float, 0, false>), dim3(a.N * a.H * (D / 16)),
+                               dim3(512), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, hipStream_t st) {
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, int w0, int nw, bool snap,
+                                   hipStream_t st) {
     if (d == 128)
-        return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, window, st) : run_snapshots<128, float, float>(a, window, st);
-    return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, window, st) : run_snapshots<64, float, float>(a, window, st);
+        return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, window, w0, nw, snap, st)
+                       : run_snapshots<128, float, float>(a, window, w0, nw, snap, st);
+    return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, window, w0, nw, snap, st)
+                   : run_snapshots<64, float, float>(a, window, w0, nw, snap, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,

@@ -43,6 +43,7 @@ struct ChunkArgs {
     // the outputs
     float* snap = nullptr;
     int snap_wc = 0;
+    int snap_j0 = 0;  // chunk index of the snapshot array's first chunk
 };
 
 // Layer prologue and epilogue of one decode step (null pointers: off).
@@ -65,12 +66,20 @@ struct Overlap {
 };
 
 // Reverse mode of the chunked prefill (kda_backward.hip).  fwd: the forward's
-// arguments with Wc = the longest sequence's chunks (the backward's own arrays
-// hold every chunk), rec / state_buf in the workspace, snap set and out null;
-// the forward recompute runs in windows of snap_window chunks through rec.
+// arguments with Wc = the longest sequence's chunks, rec / state_buf in the
+// workspace, snap set and out null.  The backward walks windows of bwd_window
+// chunks per sequence from the last to the first; its per-chunk arrays (snap,
+// brec, dsnap, dU) hold one such window, indexed [sequence][chunk in window]
+// [head].  Each window's forward recompute runs in record windows of
+// snap_window chunks (bwd_window is a multiple of it) from the state entering
+// the window: the initial state, or a checkpoint stored by a first forward
+// pass when there is more than one window.
 struct BwdArgs {
     ChunkArgs fwd;
     int snap_window;      // chunks per window of the forward recompute
+    int bwd_window;       // chunks per sequence held by the backward's arrays
+    float* ckpt;          // [windows - 1][N, H, D, D]: state entering windows 1, 2, ...; null with one window
+    float* dcarry;        // [N, H, D, D]: dL/dS entering the window just walked; null with one window
     float* brec;          // fp32 per-(chunk, head) records of the backward
     const void* dO;       // dL/dout, [tokens, H, D] (out dtype)
     const float* dfinal;  // dL/dfinal_state [N, H, D, D] or null
@@ -84,10 +93,12 @@ struct BwdArgs {
 };
 size_t bwd_record_bytes(int d);
 hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st);
-// The forward recompute of the backward: chunk-local records and the state
-// snapshots (a.snap, a.Wc chunks per sequence) of every chunk, in windows of
-// `window` chunks through one record buffer; no outputs.
-hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, hipStream_t st);
+// The forward recompute of the backward: chunk-local records and, with `snap`,
+// the state entering each chunk (a.snap, a.snap_wc chunks per sequence from
+// chunk a.snap_j0), for record windows w0 .. w0 + nw - 1 of `window` chunks
+// through one record buffer, carrying S through a.state_buf; no outputs.
+hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, int w0, int nw, bool snap,
+                                   hipStream_t st);
 
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);

@@ -127,9 +127,28 @@ def test_chunk_bwd_validation(L):
     n = L.kda_chunk_bwd_workspace_size(s)
     assert n > L.kda_chunk_fwd_workspace_size(s) > 0
     assert L.kda_chunk_bwd_workspace_size(None) == 0
-    # every chunk of every sequence is held at once: N * chunks <= 65535
-    assert L.kda_chunk_bwd_workspace_size(_shape(B=1100, T=4096)) == 0
-    assert _bwd(L, _shape(B=1100, T=4096)) == UNSUPPORTED
+    # a backward window holds at most 65535 // N chunks per sequence, so only N > 65535 is refused
+    assert L.kda_chunk_bwd_workspace_size(_shape(B=1100, T=4096)) > 0
+    assert L.kda_chunk_bwd_workspace_size(_shape(B=70000, T=64)) == 0
+    assert _bwd(L, _shape(B=70000, T=64)) == UNSUPPORTED
+
+
+def test_backward_workspace_windows(L, monkeypatch):
+    """The backward holds one window of chunks: its workspace stays bounded for the 1M-token
+    varlen batch, and forcing short windows shrinks it further."""
+    w = WORKLOADS[4]
+    # every length is at least w.min_len, so no sequence is longer than the rest of the tokens
+    longest = w.seqlen - (w.num_seqs - 1) * w.min_len
+    s = _shape(1, w.seqlen, w.num_seqs, longest, w.heads, w.dk, w.dv, BF16, F32)
+    n = L.kda_chunk_bwd_workspace_size(s)
+    # 24 GiB of per-chunk arrays, one record window, and the state entering each of ~128 windows
+    assert 0 < n < 32 * (1 << 30)
+    full = _shape(1, 65536, 0, 0, 32, 128, 128, BF16, F32)
+    one = L.kda_chunk_bwd_workspace_size(full)        # 64K x 32 heads: one window, every chunk at once
+    assert 12 * (1 << 30) < one < 14 * (1 << 30)
+    monkeypatch.setenv("KDA_BWD_WINDOW", "128")
+    part = L.kda_chunk_bwd_workspace_size(full)
+    assert part < one / 4                             # 128 of 1,024 chunks per window, plus 7 checkpoints
 
 
 def test_decode_validation(L):

@@ -158,3 +158,51 @@ def test_backward_varlen_windows(kda):
     for gk, rk in KEYS:
         got = g[gk][:, heads] if gk == "d_init" else g[gk][0][:, heads]
         assert_close(gk, got, ref[rk], TOL["bf16"])
+
+
+@pytest.mark.parametrize("D,dtype,window", [(128, "bf16", "2"), (64, "f32", "3"), (128, "bf16", "5")])
+def test_backward_windows_same_bits(kda, monkeypatch, D, dtype, window):
+    """Backward windows of a few chunks (state checkpoints, carried dL/dS, per-window recompute)
+    give the same bits as one window; sequences end inside, at the edge of and before a window."""
+    d = random_small(D + int(window), 0, 3, D, D, dtype=dtype, lens=[700, 0, 130, 64, 1000, 1])
+    dO, dF = _grads(131, d)
+    monkeypatch.delenv("KDA_BWD_WINDOW", raising=False)
+    one = run_bwd(kda, d, dO, dF)
+    monkeypatch.setenv("KDA_BWD_WINDOW", window)
+    win = run_bwd(kda, d, dO, dF)
+    for gk, _ in KEYS:
+        assert np.array_equal(one[gk], win[gk]), gk
+    check(win, oracle_bwd(d, dO, dF), TOL[dtype])
+
+
+def test_backward_windows_span_record_windows(kda, monkeypatch):
+    """32 heads, sequences of 8,192 and 5,000 tokens: a record window holds 48 chunks of both
+    sequences, so a request for 100-chunk backward windows gets 96, two record windows each; the
+    shorter sequence ends inside the first backward window.  Same bits as one window."""
+    H = 32
+    d = random_small(123, 0, H, 128, 128, dtype="bf16", lens=[8192, 5000])
+    dO, dF = _grads(124, d)
+    monkeypatch.delenv("KDA_BWD_WINDOW", raising=False)
+    one = run_bwd(kda, d, dO, dF, max_seqlen=8192)
+    monkeypatch.setenv("KDA_BWD_WINDOW", "100")
+    win = run_bwd(kda, d, dO, dF, max_seqlen=8192)
+    for gk, _ in KEYS:
+        assert np.array_equal(one[gk], win[gk]), gk
+
+
+def test_backward_workload4_varlen_1m(kda):
+    """1M packed tokens in 16 Dirichlet-length sequences, four of the 32 heads (heads are
+    independent; the generator reproduces a head subset exactly): every gradient element against
+    the oracle.  Holding every chunk at once would take about 90 GB here, so the backward runs in
+    windows over the chunks with state checkpoints between them."""
+    w = WORKLOADS[4]
+    heads = (0, 11, 22, 31)
+    d = synth.make_prefill(w, heads=heads)
+    lens = np.diff(d["cu_seqlens"])
+    assert len(lens) == 16 and int(lens.sum()) == w.seqlen
+    dO, dF = _grads(141, d)
+    n_ws = kda.bwd_workspace_size(1, w.seqlen, len(heads), w.dk, w.dv, torch.bfloat16, torch.float32,
+                                  num_seqs=16, max_seqlen=int(lens.max()))
+    assert n_ws < 30 * (1 << 30)
+    g = run_bwd(kda, d, dO, dF, max_seqlen=int(lens.max()))
+    check(g, oracle_bwd(d, dO, dF), TOL["bf16"])
