@@ -204,9 +204,12 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
  * chunkwise algorithm"; the page gives the form's cost as a training cost).
  * The forward quantities are recomputed from the inputs (nothing is kept from
  * a forward call).  Shape, dtypes and input layouts as for kda_chunk_fwd
- * (d_out has out_dtype and the layout of out); every chunk of every sequence
- * is held in the workspace at once, so the batch must satisfy
- * N * ceil(max_seqlen / 64) <= 65535.
+ * (d_out has out_dtype and the layout of out).  The workspace holds one window
+ * of chunks per sequence: every chunk when those arrays fit 24 GiB, else the
+ * chunks are walked in windows from the last to the first after a forward
+ * pass that stores the state entering each window (the environment variable
+ * KDA_BWD_WINDOW=n asks for n chunks per window).  A window holds at most
+ * 65535 / N chunks, so N <= 65535 (else KDA_ERR_UNSUPPORTED).
  *   d_final_state [N, H, dk, dv] fp32, or NULL (zero)
  *   dq, dk        [B, T, H, dk] fp32;   dv [B, T, H, dv] fp32
  *   dlog_alpha    fp32, the layout of log_alpha

@@ -193,8 +193,8 @@ def test_backward_windows_span_record_windows(kda, monkeypatch):
 def test_backward_workload4_varlen_1m(kda):
     """1M packed tokens in 16 Dirichlet-length sequences, four of the 32 heads (heads are
     independent; the generator reproduces a head subset exactly): every gradient element against
-    the oracle.  Holding every chunk at once would take about 90 GB here, so the backward runs in
-    windows over the chunks with state checkpoints between them."""
+    the oracle.  Holding every chunk at once would take about 105 GB here, so the backward runs in
+    five windows of 960 chunks with a state checkpoint entering each."""
     w = WORKLOADS[4]
     heads = (0, 11, 22, 31)
     d = synth.make_prefill(w, heads=heads)
