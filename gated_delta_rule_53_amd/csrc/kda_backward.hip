@@ -81,6 +81,29 @@ struct ChainRec {
 
 // fp32 record of one (chunk, head), offsets in floats: what the local pass
 // reads row-major, then the chain's operands
+// The same operands as fp16 matrix-core fragments (bf16 inputs): per wave, the
+// 16 x 32 A fragments of P^T (two, over the chunk's rows), Kh (D / 32, over the
+// key channels), and for each dS tile those of Qg^T and -W^T (two each, over
+// the chunk's rows); lane l = li + 16 g of fragment f holds reduction indices
+// 32 (f - base) + 8 g .. + 7 of A-row li, 16 bytes.  gamma follows as fp32, one
+// float4 per tile and lane (the lane's four dS rows).
+template <int D>
+struct ChainRec16 {
+    static constexpr int NRT = D / 64;
+    static constexpr int FK = D / 32;
+    static constexpr int F = 2 + FK + 4 * NRT;           // fragments per wave
+    static constexpr int GAM = 4 * F * 64 * 8 / 2;        // float offset of gamma
+    static constexpr int FLOATS = GAM + 4 * NRT * 64 * 4;
+    static constexpr int FKH = 2;                          // first Kh fragment
+    __device__ static int fq(int rt) { return 2 + FK + 4 * rt; }      // first Qg^T fragment of tile rt
+    __device__ static int fw(int rt) { return 2 + FK + 4 * rt + 2; }  // first -W^T fragment of tile rt
+    // half offset of reduction index k of A-row li, in the fragments of wave w from fb
+    __device__ static int at(int w, int fb, int k, int li) {
+        return ((w * F + fb + (k >> 5)) * 64 + li + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+    }
+    __device__ static int gam(int w, int rt, int lane, int r) { return GAM + ((w * NRT + rt) * 64 + lane) * 4 + r; }
+};
+
 template <int D>
 struct BRec {
     static constexpr size_t T = 0;
@@ -90,6 +113,7 @@ struct BRec {
     static constexpr size_t G = UT + CH * D;
     static constexpr size_t CR = G + CH * D;
     static constexpr size_t FLOATS = CR + ChainRec<D>::FLOATS;
+    static_assert(ChainRec16<D>::FLOATS <= ChainRec<D>::FLOATS, "fp16 chain operands fit the chain region");
 };
 
 __device__ __forceinline__ void seq_range(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
@@ -216,6 +240,8 @@ template <int D, typename IT>
 __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec) {
     using R = BRec<D>;
     using C = ChainRec<D>;
+    using C16 = ChainRec16<D>;
+    constexpr bool H16 = std::is_same<IT, bf16_t>::value;  // chain operands as fp16 fragments
     constexpr int DP = D + 1;
     __shared__ float sK[CH * DP];
     __shared__ float sX[CH * DP];  // q, then v
@@ -238,6 +264,25 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     const IT* k = static_cast<const IT*>(a.k);
     const IT* v = static_cast<const IT*>(a.v);
     float* rec = brec + ((size_t)(s * a.Wc + jl) * H + h) * R::FLOATS;
+    _Float16* rec16 = reinterpret_cast<_Float16*>(rec + R::CR);
+    // chain operands: P[row][col] (A-row col of dU), Qg[r][c] and -W[r][c] (A-row c of
+    // dS), Kh[r][c] (A-row r of dU)
+    auto put_p = [&](int row, int col, float x) {
+        if constexpr (H16) rec16[C16::at(col >> 4, 0, row, col & 15)] = (_Float16)x;
+        else rec[R::CR + C::at(col >> 4, C::ks(row), (col & 15) + 16 * C::kg(row))] = x;
+    };
+    auto put_qg = [&](int r, int c, float x) {
+        if constexpr (H16) rec16[C16::at(C::wave_of(c), C16::fq(C::tile_of(c)), r, c & 15)] = (_Float16)x;
+        else rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::ks(r), (c & 15) + 16 * C::kg(r))] = x;
+    };
+    auto put_kh = [&](int r, int c, float x) {
+        if constexpr (H16) rec16[C16::at(r >> 4, C16::FKH, c, r & 15)] = (_Float16)x;
+        else rec[R::CR + C::at(r >> 4, C::EP + C::ks(c), (r & 15) + 16 * C::kg(c))] = x;
+    };
+    auto put_mw = [&](int r, int c, float x) {
+        if constexpr (H16) rec16[C16::at(C::wave_of(c), C16::fw(C::tile_of(c)), r, c & 15)] = (_Float16)x;
+        else rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::EQ + C::ks(r), (c & 15) + 16 * C::kg(r))] = x;
+    };
 
     // inputs, branch-free: rows past the sequence end clamped, then zeroed; v
     // stays in registers until Ut
@@ -286,7 +331,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
             const bool keep = cb < rb || (isP ? row >= col : row > col);
             const float x = keep ? acc[r] : 0.f;
-            if (isP) rec[R::CR + C::at(col >> 4, C::ks(row), (col & 15) + 16 * C::kg(row))] = x;
+            if (isP) put_p(row, col, x);
             else sA[row * AP + col] = x;
         }
     }
@@ -295,7 +340,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int r = idx / CH, c = idx % CH;
         if ((c >> 4) > (r >> 4)) {
             sA[r * AP + c] = 0.f;
-            rec[R::CR + C::at(c >> 4, C::ks(r), (c & 15) + 16 * C::kg(r))] = 0.f;
+            put_p(r, c, 0.f);
         }
     }
     __syncthreads();
@@ -424,14 +469,15 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     for (int idx = t; idx < CH * D; idx += BW_T) {
         const int r = idx / D, c = idx % D;
         const float g = sG[r * DP + c], e = fast_exp(g), kx = sK[r * DP + c];
-        rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::ks(r), (c & 15) + 16 * C::kg(r))] = sX[r * DP + c] * e;
-        rec[R::CR + C::at(r >> 4, C::EP + C::ks(c), (r & 15) + 16 * C::kg(c))] = kx * fast_exp(GL[c] - g);
+        put_qg(r, c, sX[r * DP + c] * e);
+        put_kh(r, c, kx * fast_exp(GL[c] - g));
         rec[R::G + idx] = g;
         sK[r * DP + c] = sB[r] * kx * e;
     }
     for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
         const int c = idx / 16, l = (idx % 16) + 16 * ((c & 15) >> 2);
-        rec[R::CR + ((C::wave_of(c) * C::Q4 + C::E / 4 + C::tile_of(c)) * 64 + l) * 4 + (c & 3)] = fast_exp(GL[c]);
+        if constexpr (H16) rec[R::CR + C16::gam(C::wave_of(c), C::tile_of(c), l, c & 3)] = fast_exp(GL[c]);
+        else rec[R::CR + ((C::wave_of(c) * C::Q4 + C::E / 4 + C::tile_of(c)) * 64 + l) * 4 + (c & 3)] = fast_exp(GL[c]);
     }
     __syncthreads();
     for (int task = wave; task < 4 * (D / 16); task += BW_W) {
@@ -445,7 +491,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
             rec[R::W + row * D + cc] = acc[r];
-            rec[R::CR + C::at(C::wave_of(cc), C::qbase(cc) + C::EQ + C::ks(row), li + 16 * C::kg(row))] = -acc[r];
+            put_mw(row, cc, -acc[r]);
         }
     }
     __syncthreads();
@@ -593,6 +639,148 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
         if (j > j0) {
 #pragma unroll
             for (int i = 0; i < C::Q4; ++i) cur[i] = nxt[i];
+        }
+    }
+    if (dS_out)
+        for (int idx = t; idx < D * 16; idx += 256) {
+            const int c = idx / 16, vv = idx % 16;
+            dS_out[((size_t)u * D + c) * D + col0 + vv] = sdS[vv * KS + c];
+        }
+}
+
+// four fp32 values as four adjacent fp16 operand elements
+__device__ __forceinline__ void put_h4(_Float16* dst, floatx4 x) {
+    half4 h;
+    h[0] = (_Float16)x[0];
+    h[1] = (_Float16)x[1];
+    h[2] = (_Float16)x[2];
+    h[3] = (_Float16)x[3];
+    *reinterpret_cast<half4*>(dst) = h;
+}
+
+// The reverse chain with fp16 matrix-core operands (bf16 inputs): the same
+// steps as bwd_chain_kernel, each wave's operands as ChainRec16 fragments and
+// the B operands dO^T, dS^T and dU^T as fp16 rows in LDS.  dS itself stays in
+// fp32 (the Diag(gamma) term, the stored gradient snapshots and the carried
+// value); only its copy used as an operand is rounded.
+template <int D, typename GT>
+__global__ void __launch_bounds__(256) bwd_chain16_kernel(ChunkArgs a, const float* brec, const GT* dO,
+                                                          const float* dS_in, float* dsnap, float* dU,
+                                                          float* dS_out) {
+    using R = BRec<D>;
+    using C = ChainRec16<D>;
+    constexpr int KS = D + 4;             // fp32 dS^T rows
+    constexpr int SP = D + 8, OP = CH + 8;  // fp16 operand rows (16-byte aligned, staggered banks)
+    constexpr int DO_PER = CH * 16 / 256;
+    __shared__ __align__(16) float sdS[16 * KS];
+    __shared__ __align__(16) _Float16 sS16[16 * SP];
+    __shared__ __align__(16) _Float16 sO16[2][16 * OP];
+    __shared__ __align__(16) _Float16 sU16[16 * OP];
+    const int H = a.H, NH = a.N * H;
+    const int u = blockIdx.x % NH, z = blockIdx.x / NH;
+    const int s = u / H, h = u % H, col0 = 16 * z;
+    int64_t tb, L;
+    seq_range(a, s, tb, L);
+    const int j0 = a.win * a.Wc;
+    const int nch = (int)min<int64_t>((L + CH - 1) / CH, (int64_t)j0 + a.Wc);  // one past the window's last chunk
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
+    auto crec = [&](int j) { return brec + ((size_t)(s * a.Wc + (j - j0)) * H + h) * R::FLOATS + R::CR; };
+    auto load_ops = [&](int j, half8* f, float4* g) {
+        const float* p = crec(j);
+        const half8* pf = reinterpret_cast<const half8*>(p) + (size_t)wave * C::F * 64 + lane;
+#pragma unroll
+        for (int i = 0; i < C::F; ++i) f[i] = pf[i * 64];
+#pragma unroll
+        for (int rt = 0; rt < C::NRT; ++rt) g[rt] = *reinterpret_cast<const float4*>(p + C::gam(wave, rt, lane, 0));
+    };
+    auto rows = [&](int j) { return (int)min<int64_t>(CH, L - (int64_t)j * CH); };
+    auto load_do = [&](int j, GT* x) {
+        const int n = rows(j);
+#pragma unroll
+        for (int i = 0; i < DO_PER; ++i) {
+            const int idx = t + 256 * i, r = idx / 16, vv = idx % 16;
+            x[i] = dO[((size_t)(tb + (int64_t)j * CH + min(r, n - 1)) * H + h) * D + col0 + vv];
+        }
+    };
+    auto store_do = [&](int buf, int j, const GT* x) {
+        const int n = rows(j);
+#pragma unroll
+        for (int i = 0; i < DO_PER; ++i) {
+            const int idx = t + 256 * i, r = idx / 16;
+            sO16[buf][(idx % 16) * OP + r] = (_Float16)(r < n ? to_f32(x[i]) : 0.f);
+        }
+    };
+    auto mfma = [](half8 x, const _Float16* y, floatx4 acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, *reinterpret_cast<const half8*>(y), acc, 0, 0, 0);
+    };
+    half8 cur[C::F], nxt[C::F];
+    float4 gc[C::NRT], gn[C::NRT];
+    GT don[DO_PER];
+    if (nch > j0) {
+        load_ops(nch - 1, cur, gc);
+        load_do(nch - 1, don);
+        store_do(0, nch - 1, don);
+    }
+    for (int idx = t; idx < D * 16; idx += 256) {
+        const int c = idx / 16, vv = idx % 16;
+        const float x = dS_in ? dS_in[((size_t)u * D + c) * D + col0 + vv] : 0.f;
+        sdS[vv * KS + c] = x;
+        sS16[vv * SP + c] = (_Float16)x;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < nch - j0; ++jj) {
+        const int j = nch - 1 - jj, buf = jj & 1;
+        if (j > j0) {
+            load_do(j - 1, don);
+            load_ops(j - 1, nxt, gn);
+        }
+        const size_t ch = (size_t)(s * a.Wc + (j - j0)) * H + h;
+        float* snap = dsnap + ch * D * D;
+#pragma unroll
+        for (int i = 0; i < D * 4 / 256; ++i) {  // dL/dS_{j+1}, four columns per store
+            const int idx = t + 256 * i, c = idx / 4, v4 = 4 * (idx % 4);
+            *reinterpret_cast<float4*>(snap + (size_t)c * D + col0 + v4) =
+                make_float4(sdS[v4 * KS + c], sdS[(v4 + 1) * KS + c], sdS[(v4 + 2) * KS + c], sdS[(v4 + 3) * KS + c]);
+        }
+        const _Float16* bO = sO16[buf] + li * OP + 8 * gq;
+        const _Float16* bS = sS16 + li * SP + 8 * gq;
+        {  // dU = P^T dO + Kh dS: rows 16 wave .. 16 wave + 15
+            floatx4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[kk], bO + 32 * kk, acc);
+#pragma unroll
+            for (int kk = 0; kk < C::FK; ++kk) acc = mfma(cur[C::FKH + kk], bS + 32 * kk, acc);
+            put_h4(sU16 + li * OP + 16 * wave + 4 * gq, acc);
+            float* du = dU + ch * CH * D;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) du[(size_t)(16 * wave + 4 * gq + r) * D + col0 + li] = acc[r];
+        }
+        __syncthreads();
+        // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
+        const _Float16* bU = sU16 + li * OP + 8 * gq;
+#pragma unroll
+        for (int rt = 0; rt < C::NRT; ++rt) {
+            const int cb = wave * (D / 4) + 16 * rt;
+            const float4 gm = gc[rt], s4 = *reinterpret_cast<const float4*>(sdS + li * KS + cb + 4 * gq);
+            floatx4 acc;
+            acc[0] = gm.x * s4.x;
+            acc[1] = gm.y * s4.y;
+            acc[2] = gm.z * s4.z;
+            acc[3] = gm.w * s4.w;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fq(rt) + kk], bO + 32 * kk, acc);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fw(rt) + kk], bU + 32 * kk, acc);
+            *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            put_h4(sS16 + li * SP + cb + 4 * gq, acc);
+        }
+        if (j > j0) store_do(buf ^ 1, j - 1, don);
+        __syncthreads();
+        if (j > j0) {
+#pragma unroll
+            for (int i = 0; i < C::F; ++i) cur[i] = nxt[i];
+#pragma unroll
+            for (int rt = 0; rt < C::NRT; ++rt) gc[rt] = gn[rt];
         }
     }
     if (dS_out)
@@ -1078,8 +1266,12 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         const float* din = w == nbw - 1 ? b.dfinal : b.dcarry;
         float* dout = w == 0 ? b.dinit : b.dcarry;
-        hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, bw.fwd, b.brec,
-                           static_cast<const GT*>(b.dO), din, b.dsnap, b.dU, dout);
+        if constexpr (BF)
+            hipLaunchKernelGGL((bwd_chain16_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, bw.fwd, b.brec,
+                               static_cast<const GT*>(b.dO), din, b.dsnap, b.dU, dout);
+        else
+            hipLaunchKernelGGL((bwd_chain_kernel<D, GT>), dim3(units * (D / 16)), dim3(256), 0, st, bw.fwd, b.brec,
+                               static_cast<const GT*>(b.dO), din, b.dsnap, b.dU, dout);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_local_kernel<D, IT, GT>), chunks, dim3(BL_T), 0, st, bw);
         if ((e = hipGetLastError()) != hipSuccess) return e;
