@@ -77,7 +77,8 @@ def backward_bytes(tokens, heads, d, states=1):
 
 
 def backward_matrix_flops(tokens, heads, d, c=64):
-    """fp32 matrix-core FLOPs of the three backward kernels per call (2 m n k per product, over
+    """Matrix-core FLOPs of the three backward kernels per call, as (fp32, fp16): with bf16
+    inputs the chain's products take fp16 operands, prep and local stay fp32 (2 m n k per product, over
     the 16x16 blocks each product needs: lower blocks of triangular results, and for a
     lower-triangular T or dT operand only its nonzero 16-row blocks).  Per chunk and head:
     prep A0 and P (10 lower blocks each over d), W = T Bk and Ut = T Bv; the chain
@@ -95,7 +96,7 @@ def backward_matrix_flops(tokens, heads, d, c=64):
     chain = 2 * c * d * (c + d) + 2 * d * d * 2 * c
     local = (4 * 2 * c * d * d + 3 * 10 * (2 * 16 * 16 * d) + 2 * t_prod + 2 * 16 * 16 * (x_k + a_k)
              + 4 * (d // 16) * 160 * 2 * 16 * 16)
-    return chunks * (prep + chain + local)
+    return chunks * (prep + local), chunks * chain
 
 
 def to_dev(x, torch):
@@ -328,13 +329,16 @@ def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):
         ms.append(e0.elapsed_time(e1))
     s = float(np.median(ms)) / 1e3
     b = backward_bytes(T, H, D)
-    f = backward_matrix_flops(T, H, D)
+    f32, f16 = backward_matrix_flops(T, H, D)
+    at_peak = f32 / (FP32_MFMA_PEAK_TFLOPS * 1e12) + f16 / (BF16_DENSE_TFLOPS * 1e12)
     return {"what": "dq, dk, dv, dlog_alpha, dbeta, d_init of the 64K x 32-head prefill (bf16 in, fp32 d_out "
                     "and gradients), forward recompute included",
             "ms": s * 1e3, "tokens_per_s": T / s, "algorithmic_bytes": b, "hbm_gbs": b / s / 1e9,
             "frac": b / s / 1e9 / HBM_PEAK_GBS,
-            "mfma_fp32": {"flop_per_call": f, "achieved": f / s / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
-                          "unit": "TFLOP/s", "frac": f / s / 1e12 / FP32_MFMA_PEAK_TFLOPS}}
+            "matrix": {"fp32_flop_per_call": f32, "fp16_flop_per_call": f16,
+                       "fp32_tflops": f32 / s / 1e12, "fp16_tflops": f16 / s / 1e12,
+                       "peaks_tflops": {"fp32": FP32_MFMA_PEAK_TFLOPS, "fp16": BF16_DENSE_TFLOPS},
+                       "ms_at_peaks": at_peak * 1e3, "frac": at_peak / s}}
 
 
 def bench_layer(kda, torch, synth, wp, wd, args, flush, stream):
