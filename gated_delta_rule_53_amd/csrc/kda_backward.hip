@@ -616,7 +616,7 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
 #pragma unroll
             for (int r = 0; r < 4; ++r) du[(size_t)(16 * wave + 4 * gq + r) * D + col0 + li] = acc[r];
         }
-        __syncthreads();
+        lds_barrier();  // orders LDS only: the next chunk's loads stay in flight
         // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
         const float* sU = sdU + li * KO + 4 * gq;
 #pragma unroll
@@ -635,7 +635,7 @@ __global__ void __launch_bounds__(256) bwd_chain_kernel(ChunkArgs a, const float
             *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
         if (j > j0) store_do(buf ^ 1, j - 1, don);
-        __syncthreads();
+        lds_barrier();  // orders LDS only: the next chunk's loads stay in flight
         if (j > j0) {
 #pragma unroll
             for (int i = 0; i < C::Q4; ++i) cur[i] = nxt[i];
@@ -713,13 +713,20 @@ __global__ void __launch_bounds__(256) bwd_chain16_kernel(ChunkArgs a, const flo
     auto mfma = [](half8 x, const _Float16* y, floatx4 acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(x, *reinterpret_cast<const half8*>(y), acc, 0, 0, 0);
     };
-    half8 cur[C::F], nxt[C::F];
-    float4 gc[C::NRT], gn[C::NRT];
-    GT don[DO_PER];
+    // operands of three chunks in flight: chunk j is computed from buffer p while
+    // chunk j - 2 is loaded into buffer p + 2 (mod 3); the loop is unrolled by three
+    // so the buffers rotate by name and no register copy waits on a load
+    half8 ops[3][C::F];
+    float4 gam[3][C::NRT];
+    GT dob[3][DO_PER];
     if (nch > j0) {
-        load_ops(nch - 1, cur, gc);
-        load_do(nch - 1, don);
-        store_do(0, nch - 1, don);
+        load_ops(nch - 1, ops[0], gam[0]);
+        load_do(nch - 1, dob[0]);
+        store_do(0, nch - 1, dob[0]);
+        if (nch - 2 >= j0) {
+            load_ops(nch - 2, ops[1], gam[1]);
+            load_do(nch - 2, dob[1]);
+        }
     }
     for (int idx = t; idx < D * 16; idx += 256) {
         const int c = idx / 16, vv = idx % 16;
@@ -728,59 +735,58 @@ __global__ void __launch_bounds__(256) bwd_chain16_kernel(ChunkArgs a, const flo
         sS16[vv * SP + c] = (_Float16)x;
     }
     __syncthreads();
-    for (int jj = 0; jj < nch - j0; ++jj) {
-        const int j = nch - 1 - jj, buf = jj & 1;
-        if (j > j0) {
-            load_do(j - 1, don);
-            load_ops(j - 1, nxt, gn);
-        }
-        const size_t ch = (size_t)(s * a.Wc + (j - j0)) * H + h;
-        float* snap = dsnap + ch * D * D;
+    for (int jj0 = 0; jj0 < nch - j0; jj0 += 3) {
 #pragma unroll
-        for (int i = 0; i < D * 4 / 256; ++i) {  // dL/dS_{j+1}, four columns per store
-            const int idx = t + 256 * i, c = idx / 4, v4 = 4 * (idx % 4);
-            *reinterpret_cast<float4*>(snap + (size_t)c * D + col0 + v4) =
-                make_float4(sdS[v4 * KS + c], sdS[(v4 + 1) * KS + c], sdS[(v4 + 2) * KS + c], sdS[(v4 + 3) * KS + c]);
-        }
-        const _Float16* bO = sO16[buf] + li * OP + 8 * gq;
-        const _Float16* bS = sS16 + li * SP + 8 * gq;
-        {  // dU = P^T dO + Kh dS: rows 16 wave .. 16 wave + 15
-            floatx4 acc = zero4();
+        for (int p = 0; p < 3; ++p) {
+            const int jj = jj0 + p, j = nch - 1 - jj, buf = jj & 1;
+            if (j < j0) break;
+            const half8* cur = ops[p];
+            if (j - 2 >= j0) {
+                load_ops(j - 2, ops[(p + 2) % 3], gam[(p + 2) % 3]);
+                load_do(j - 2, dob[(p + 2) % 3]);
+            }
+            const size_t ch = (size_t)(s * a.Wc + (j - j0)) * H + h;
+            float* snap = dsnap + ch * D * D;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[kk], bO + 32 * kk, acc);
+            for (int i = 0; i < D * 4 / 256; ++i) {  // dL/dS_{j+1}, four columns per store
+                const int idx = t + 256 * i, c = idx / 4, v4 = 4 * (idx % 4);
+                *reinterpret_cast<float4*>(snap + (size_t)c * D + col0 + v4) = make_float4(
+                    sdS[v4 * KS + c], sdS[(v4 + 1) * KS + c], sdS[(v4 + 2) * KS + c], sdS[(v4 + 3) * KS + c]);
+            }
+            const _Float16* bO = sO16[buf] + li * OP + 8 * gq;
+            const _Float16* bS = sS16 + li * SP + 8 * gq;
+            {  // dU = P^T dO + Kh dS: rows 16 wave .. 16 wave + 15
+                floatx4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < C::FK; ++kk) acc = mfma(cur[C::FKH + kk], bS + 32 * kk, acc);
-            put_h4(sU16 + li * OP + 16 * wave + 4 * gq, acc);
-            float* du = dU + ch * CH * D;
+                for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[kk], bO + 32 * kk, acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) du[(size_t)(16 * wave + 4 * gq + r) * D + col0 + li] = acc[r];
-        }
-        __syncthreads();
-        // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
-        const _Float16* bU = sU16 + li * OP + 8 * gq;
+                for (int kk = 0; kk < C::FK; ++kk) acc = mfma(cur[C::FKH + kk], bS + 32 * kk, acc);
+                put_h4(sU16 + li * OP + 16 * wave + 4 * gq, acc);
+                float* du = dU + ch * CH * D;
 #pragma unroll
-        for (int rt = 0; rt < C::NRT; ++rt) {
-            const int cb = wave * (D / 4) + 16 * rt;
-            const float4 gm = gc[rt], s4 = *reinterpret_cast<const float4*>(sdS + li * KS + cb + 4 * gq);
-            floatx4 acc;
-            acc[0] = gm.x * s4.x;
-            acc[1] = gm.y * s4.y;
-            acc[2] = gm.z * s4.z;
-            acc[3] = gm.w * s4.w;
+                for (int r = 0; r < 4; ++r) du[(size_t)(16 * wave + 4 * gq + r) * D + col0 + li] = acc[r];
+            }
+            lds_barrier();  // orders LDS only: the later chunks' loads stay in flight
+            // dS <- Diag(gamma) dS + Qg^T dO - W^T dU: tiles at rows wave D/4 + 16 rt
+            const _Float16* bU = sU16 + li * OP + 8 * gq;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fq(rt) + kk], bO + 32 * kk, acc);
+            for (int rt = 0; rt < C::NRT; ++rt) {
+                const int cb = wave * (D / 4) + 16 * rt;
+                const float4 gm = gam[p][rt], s4 = *reinterpret_cast<const float4*>(sdS + li * KS + cb + 4 * gq);
+                floatx4 acc;
+                acc[0] = gm.x * s4.x;
+                acc[1] = gm.y * s4.y;
+                acc[2] = gm.z * s4.z;
+                acc[3] = gm.w * s4.w;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fw(rt) + kk], bU + 32 * kk, acc);
-            *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            put_h4(sS16 + li * SP + cb + 4 * gq, acc);
-        }
-        if (j > j0) store_do(buf ^ 1, j - 1, don);
-        __syncthreads();
-        if (j > j0) {
+                for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fq(rt) + kk], bO + 32 * kk, acc);
 #pragma unroll
-            for (int i = 0; i < C::F; ++i) cur[i] = nxt[i];
-#pragma unroll
-            for (int rt = 0; rt < C::NRT; ++rt) gc[rt] = gn[rt];
+                for (int kk = 0; kk < 2; ++kk) acc = mfma(cur[C::fw(rt) + kk], bU + 32 * kk, acc);
+                *reinterpret_cast<float4*>(sdS + li * KS + cb + 4 * gq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                put_h4(sS16 + li * SP + cb + 4 * gq, acc);
+            }
+            if (j > j0) store_do(buf ^ 1, j - 1, dob[(p + 1) % 3]);
+            lds_barrier();
         }
     }
     if (dS_out)
