@@ -232,6 +232,10 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
     int G = overlap_enabled ? 0 : kda::chunk_segments(d, bv, p.N * H, p.max_chunks, sc);
     const size_t segb = G > 0 ? segment_bytes(p, H, G) : 0;
     if (G > 0 && avail < (size_t)all * per_chunk + 3 * segb) G = 0;  // workspace too small: windows
+    // grid rows of the chunk-local pass: sequences x chunks of a window <= 65535
+    const int64_t wc_max = 65535 / p.N;
+    if (wc_max < 1) return KDA_ERR_UNSUPPORTED;
+    if (G > 0 && all > wc_max) G = 0;  // the sequence-parallel pass launches every chunk at once
     int64_t wc;
     bool two = false;
     if ((size_t)all * per_chunk <= avail || G > 0) {
@@ -242,7 +246,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
     } else {
         wc = (int64_t)(avail / per_chunk);
     }
-    if (wc > INT32_MAX / 2) wc = INT32_MAX / 2;
+    if (wc > wc_max) wc = wc_max;
     const int64_t nwin64 = p.max_chunks > 0 ? (p.max_chunks + wc - 1) / wc : 1;
     if (nwin64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
 

@@ -127,7 +127,9 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s);
  *   final_state [N, H, dk, dv] fp32, or NULL; may equal init_state exactly
  *               (in-place continuation) but must not partially overlap it
  *   workspace   device scratch of workspace_bytes >= the size above
- * Sequences of length 0 return final_state = init_state. */
+ * Sequences of length 0 return final_state = init_state.  One launch holds at
+ * most 65535 / N chunks of every sequence (longer sequences run in windows),
+ * so N <= 65535, else KDA_ERR_UNSUPPORTED. */
 kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state,

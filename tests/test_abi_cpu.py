@@ -92,6 +92,10 @@ def test_chunk_fwd_validation(L):
     assert _fwd(L, s, ws=10 * A, wsb=1024) == WORKSPACE
     assert _fwd(L, s, ws=10 * A + 8, wsb=1 << 30) == WORKSPACE  # misaligned workspace
     assert _fwd(L, _shape(gph=2)) == INVALID                    # gate layout flag is 0 or 1
+    # one launch holds at most 65535 / N chunks of every sequence: N > 65535 is refused
+    F = 1 << 40  # pointers far enough apart that the large tensors do not overlap
+    assert _fwd(L, _shape(B=70000, T=64), q=F, k=2 * F, v=3 * F, la=4 * F, b=5 * F, out=6 * F,
+                ws=7 * F, wsb=1 << 39) == UNSUPPORTED
     # out right after log_alpha: overlaps a per-channel gate [T,H,dk] but not a per-head one [T,H]
     la_head = 256 * 2 * 4
     assert _fwd(L, s, la=4 * A, out=4 * A + la_head) == INVALID

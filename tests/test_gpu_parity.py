@@ -423,3 +423,18 @@ def test_dense_batch(kda, B, T, H, D, dtype):
     o_ref, S_ref = oracle_chunk(d)
     assert_close("out", out.cpu().numpy().reshape(B * T, H, D), o_ref, TOL[dtype])
     assert_close("state", fin.cpu().numpy(), S_ref, TOL[dtype])
+
+
+def test_many_sequences_grid_rows(kda):
+    """1,100 sequences with one of 64 chunks: 1,100 x 64 rows exceed the 65,535 a launch can
+    hold, so even with a workspace for every chunk the prefill runs in windows of 59 chunks."""
+    lens = [4096] + [1 + (i % 3) for i in range(1099)]
+    d = random_small(1100, 0, 2, 64, 64, dtype="bf16", lens=lens)
+    T = int(d["cu_seqlens"][-1])
+    # room for every chunk's record (41,216 bytes per chunk and head at d = 64) and the states
+    ws = torch.empty(1100 * 64 * 2 * 41216 + (64 << 20), dtype=torch.uint8, device="cuda")
+    o, S = run_chunk(kda, torch, d, workspace=ws, max_seqlen=4096)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+    assert T == 4096 + sum(lens[1:])
