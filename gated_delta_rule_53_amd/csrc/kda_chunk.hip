@@ -1336,22 +1336,34 @@ __global__ void __launch_bounds__(256) layer_epilogue_kernel(ChunkArgs a) {
     float w[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = a.norm_weight ? a.norm_weight[j0 + e] : 1.f;
-    for (int r = lr; r < n; r += RPP) {  // r is uniform over the LPR lanes of a row
-        const size_t base = ((size_t)(tb + c0 + r) * a.H + h) * D + j0;
-        float o[8], y[8];
+    // every row's o and z are loaded before any row is reduced (rows past the end
+    // read the chunk's last row and are not stored)
+    constexpr int NR = CH / RPP;  // rows per thread
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    float ov[NR][8];
+    u32x4 zv[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const size_t base = ((size_t)(tb + c0 + min(lr + RPP * i, n - 1)) * a.H + h) * D + j0;
         if constexpr (std::is_same<OI, float>::value) {
             const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.out) + base);
             const float4 x0 = src[0], x1 = src[1];
-            o[0] = x0.x; o[1] = x0.y; o[2] = x0.z; o[3] = x0.w;
-            o[4] = x1.x; o[5] = x1.y; o[6] = x1.z; o[7] = x1.w;
+            ov[i][0] = x0.x; ov[i][1] = x0.y; ov[i][2] = x0.z; ov[i][3] = x0.w;
+            ov[i][4] = x1.x; ov[i][5] = x1.y; ov[i][6] = x1.z; ov[i][7] = x1.w;
         } else {
             const half8 x = *reinterpret_cast<const half8*>(static_cast<const _Float16*>(a.out) + base);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = (float)x[e];
+            for (int e = 0; e < 8; ++e) ov[i][e] = (float)x[e];
         }
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 zb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.out_gate + base));
-        const uint32_t zw[4] = {zb[0], zb[1], zb[2], zb[3]};
+        zv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.out_gate + base));
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int r = lr + RPP * i;  // uniform over the LPR lanes of a row
+        const size_t base = ((size_t)(tb + c0 + min(r, n - 1)) * a.H + h) * D + j0;
+        const float* o = ov[i];
+        float y[8];
+        const uint32_t zw[4] = {zv[i][0], zv[i][1], zv[i][2], zv[i][3]};
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
@@ -1364,6 +1376,7 @@ __global__ void __launch_bounds__(256) layer_epilogue_kernel(ChunkArgs a) {
             const float z = __uint_as_float((e & 1) ? (zw2 & 0xFFFF0000u) : (zw2 << 16));
             y[e] = o[e] * rs * w[e] * __builtin_amdgcn_rcpf(1.f + fast_exp(-z));
         }
+        if (r >= n) continue;
         OF* dst = static_cast<OF*>(a.out) + base;
         if constexpr (std::is_same<OF, float>::value) {
             const floatx4 y0 = {y[0], y[1], y[2], y[3]}, y1 = {y[4], y[5], y[6], y[7]};
@@ -1450,7 +1463,14 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov
     }
     if (!base.out_gate) return hipSuccess;
     // the epilogue after the last state pass (between state passes it would
-    // evict the records they read), window by window to keep the grid small
+    // evict the records they read): one launch over every window's chunks when
+    // its grid rows (sequences x chunks) fit, else window by window
+    if ((int64_t)base.N * nwin * base.Wc <= 65535) {
+        ChunkArgs a = base;
+        a.win = 0;
+        a.Wc = nwin * base.Wc;
+        return launch_epilogue<D, OUT>(a, st);
+    }
     for (int w = 0; w < nwin; ++w) {
         ChunkArgs a = base;
         a.win = w;
