@@ -206,3 +206,13 @@ def test_backward_workload4_varlen_1m(kda):
     assert n_ws < 30 * (1 << 30)
     g = run_bwd(kda, d, dO, dF, max_seqlen=int(lens.max()))
     check(g, oracle_bwd(d, dO, dF), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_beta_up_to_two(kda, dtype):
+    """beta uniform in [0, 2]: gradients against the oracle's adjoint."""
+    d = random_small(151 if dtype == "f32" else 152, 200, 2, 128, 128, dtype=dtype)
+    d["beta"] = np.random.default_rng(6).uniform(0.0, 2.0, d["beta"].shape).astype(np.float32)
+    dO, dF = _grads(153, d)
+    g = run_bwd(kda, d, dO, dF)
+    check(g, oracle_bwd(d, dO, dF), TOL[dtype])

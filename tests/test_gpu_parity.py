@@ -438,3 +438,28 @@ def test_many_sequences_grid_rows(kda):
     assert_close("out", o, o_ref, TOL["bf16"])
     assert_close("state", S, S_ref, TOL["bf16"])
     assert T == 4096 + sum(lens[1:])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_beta_up_to_two(kda, dtype):
+    """beta uniform in [0, 2] (the method allows any finite beta; 2 is a reflection): parity with
+    the oracle, where the corrections of the WY form are twice as large as with beta <= 1."""
+    d = random_small(27 if dtype == "f32" else 28, 300, 2, 128, 128, dtype=dtype)
+    d["beta"] = np.random.default_rng(5).uniform(0.0, 2.0, d["beta"].shape).astype(np.float32)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL[dtype])
+    assert_close("state", S, S_ref, TOL[dtype])
+
+
+def test_householder_keeps_state_norm(kda):
+    """beta = 2, alpha = 1, v = 0: every step applies I - 2 k k^T to the state (unit k), an
+    orthogonal map, so the Frobenius norm of each head's state is unchanged (fp32 inputs)."""
+    d = random_small(31, 200, 2, 64, 64, dtype="f32")
+    d["beta"][:] = 2.0
+    d["log_alpha"][:] = 0.0
+    d["v"][:] = 0.0
+    _, S = run_chunk(kda, torch, d)
+    n0 = np.linalg.norm(d["init"].reshape(2, -1), axis=1)
+    n1 = np.linalg.norm(S.reshape(2, -1), axis=1)
+    np.testing.assert_allclose(n1, n0, rtol=1e-4)
