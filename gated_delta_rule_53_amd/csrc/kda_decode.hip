@@ -27,8 +27,9 @@
 
 namespace kda {
 
+// Five waves per SIMD (96 registers) rather than four: about 1% faster at 256 x 32 units.
 template <int D, typename IT, typename OUT>
-__global__ void __launch_bounds__(256) decode_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) decode_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
                                                      const IT* __restrict__ v,
                                                      const float* __restrict__ log_alpha,
                                                      const float* __restrict__ beta, float* __restrict__ state,
