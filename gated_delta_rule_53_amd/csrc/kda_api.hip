@@ -21,6 +21,8 @@ constexpr int CHUNK = 64;
 // outputs with non-temporal accesses, so records of up to about 230 MB stay
 // resident; past that the state pass starts missing.
 constexpr size_t RECORD_BUDGET = size_t(220) << 20;
+constexpr int64_t MIN_WINDOW = 32;
+constexpr size_t WINDOW_CAP = size_t(4) << 30;
 
 // Per-device overlap resources, created on first use and kept for the life of
 // the process.  The mutex serialises host-side enqueueing of calls on one device.
@@ -150,10 +152,15 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     if (G > 0)  // sequence-parallel state pass: every record plus three per-segment state blocks
         return p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G);
     if ((size_t)all * per_chunk <= RECORD_BUDGET) return p.state_bytes + (size_t)all * per_chunk;
-    const int64_t wc = (int64_t)(RECORD_BUDGET / 2 / per_chunk);
-    if (wc < 1)  // one chunk index of every unit already fills half the budget: single-index windows
-        return p.state_bytes + per_chunk;
-    return p.state_bytes + 2 * (size_t)wc * per_chunk;  // two windows, or one of twice the size
+    // two windows of half the record budget, or one of twice the size
+    int64_t wc = 2 * (int64_t)(RECORD_BUDGET / 2 / per_chunk);
+    // Many (sequence, head) pairs leave few chunks per window inside the budget,
+    // and then the per-window launch costs outweigh keeping the records in the
+    // last-level cache: windows of at least MIN_WINDOW chunks (records of at most
+    // WINDOW_CAP bytes; 512 pairs of the 1M-token batch: 5 -> 32 chunks, 1.3x).
+    const int64_t wide = std::min<int64_t>(MIN_WINDOW, (int64_t)(WINDOW_CAP / per_chunk));
+    wc = std::min<int64_t>(all, std::max<int64_t>(std::max<int64_t>(wc, wide), 1));
+    return p.state_bytes + (size_t)wc * per_chunk;
 }
 
 // The prefill behind kda_chunk_fwd (gate: fp32 log_alpha, layer null) and

@@ -191,18 +191,27 @@ def test_workspace_size_sequence_parallel(L, monkeypatch):
 
 
 def test_workspace_size_windows(L):
-    """Record windows stay within the 220 MiB record budget; one chunk index of every unit is the floor."""
+    """Record windows stay within the 220 MiB record budget unless that leaves fewer than 32 chunks
+    per window; then windows of 32 chunks (or every chunk), with at most 4 GiB of records."""
     rec = 74240
     # one 65,536-token sequence, 32 heads: 96-chunk windows (2 x 48 chunk indices)
     s = _shape(1, 65536, 0, 0, 32, 128, 128, BF16, F32)
     state = 32 * 128 * 128 * 4
     n = L.kda_chunk_fwd_workspace_size(s)
     assert n == state + 96 * 32 * rec and n - state <= (220 << 20)
-    # 64 sequences of 1,024 tokens: one chunk index of every (sequence, head) pair is 152 MB,
-    # so windows hold that single index
+    # 64 sequences of 1,024 tokens: one chunk index of every (sequence, head) pair is 152 MB, so
+    # the budget would hold a single index; the window holds all 16 chunks instead (2.4 GB)
     s = _shape(1, 65536, 64, 1024, 32, 128, 128, BF16, F32)
     state = 64 * 32 * 128 * 128 * 4
-    assert L.kda_chunk_fwd_workspace_size(s) == state + 64 * 32 * rec
+    assert L.kda_chunk_fwd_workspace_size(s) == state + 16 * 64 * 32 * rec
+    # the 1M-token batch of 16 sequences (longest 250,811 tokens): 32-chunk windows, 1.2 GB
+    s = _shape(1, 1 << 20, 16, 250811, 32, 128, 128, BF16, F32)
+    state = 16 * 32 * 128 * 128 * 4
+    assert L.kda_chunk_fwd_workspace_size(s) == state + 32 * 16 * 32 * rec
+    # 200 sequences of 4,096 tokens: 32 chunks would exceed 4 GiB of records, so 9 chunks
+    s = _shape(1, 200 * 4096, 200, 4096, 32, 128, 128, BF16, F32)
+    state = 200 * 32 * 128 * 128 * 4
+    assert L.kda_chunk_fwd_workspace_size(s) == state + ((4 << 30) // (200 * 32 * rec)) * 200 * 32 * rec
 
 
 def _layer(norm=1, l2=1e-6, gate=True, og=True, w=True, rms=1e-6, base=40):
