@@ -151,11 +151,11 @@ kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t d
                              const void* k, const void* v, const float* log_alpha,
                              const float* beta, float* state_inout, void* out, void* stream);
 
-/* Layer prologue and epilogue fused around the operator.  The "Kimi Linear"
- * page ("Kimi Delta Attention" section) has each KDA head L2-normalise its
- * queries and keys, compute its per-channel decay through a low-rank
- * projection, and pass its output through a head-wise RMSNorm and a sigmoid
- * output gate.  The page fixes neither the map from the projection to the
+/* Layer prologue and epilogue fused around the operator ("Kimi Linear" page,
+ * "Kimi Delta Attention" section): before the recurrence, q and k are scaled
+ * to unit L2 norm per head and the per-channel decay is formed from the
+ * output of a low-rank projection; after it, each head's output is divided
+ * by its RMS and multiplied by a sigmoid gate.  The page fixes neither the map from the projection to the
  * decay nor the constants; this library takes log alpha = -softplus(g) (alpha
  * = sigmoid(-g)) and the epsilons below inside the square roots.
  *   qk_l2norm    1: q and k of every (token, head) are divided by

@@ -10,11 +10,14 @@ Attention", "Why channel-wise gating matters" and "The constrained DPLR form
 and the chunkwise algorithm"):
 
 * ``recurrent``   -- plain C, fp64, token by token (kda_oracle.c); the oracle.
+* ``metrics`` / ``Metrics`` -- the parity figure max|x - ref| / RMS(ref), whole
+  or accumulated over pieces; pinned by hand-computed cases.
 * ``backward``    -- its reverse mode: the adjoint of each token step, fp64,
   in the same C file; pinned by finite differences and a closed form.
-* ``forms.brute`` -- explicit dk x dk transition matrices and the
-  "query dotted with keys weighted by a cumulative product of transitions"
-  expansion; numpy fp64, tiny sizes only.
+* ``forms.brute`` -- explicit dk x dk transition matrices, and the output
+  expanded as a sum over earlier tokens in which each key reaches the query
+  through the product of the transitions between them; numpy fp64, tiny
+  sizes only.
 * ``forms.chunkwise`` -- the chunked WY/UT form, fp64, written from the
   algebra of the recurrence; used to pin the recurrent form.
 """
@@ -193,13 +196,55 @@ def decode_steps(state, steps, threads=None, mutant: int = 0):
     return outs, S
 
 
+class Metrics:
+    """Parity figures over a tensor fed in pieces (so no full fp64 copy of a large
+    output is ever held): the largest |x - ref|, the sum of ref^2, the sum of
+    (x - ref)^2 and the element count, from which
+
+        max_over_rms = max_i |x_i - ref_i| / sqrt(mean_i ref_i^2)   (the parity figure)
+        max_abs      = max_i |x_i - ref_i|
+        rms_err      = sqrt(mean_i (x_i - ref_i)^2)
+        rms_ref      = sqrt(mean_i ref_i^2)
+
+    With RMS(ref) = 0 the figure is 0 when every error is 0, else infinite; an
+    empty tensor has no error.  A non-finite x gives a non-finite error (NaN
+    propagates through the maximum)."""
+
+    def __init__(self):
+        self.max_err = 0.0
+        self.sum_ref2 = 0.0
+        self.sum_err2 = 0.0
+        self.count = 0
+
+    def add(self, x, ref):
+        x = np.asarray(x, np.float64)
+        ref = np.asarray(ref, np.float64)
+        if x.shape != ref.shape:
+            raise ValueError(f"shape mismatch {x.shape} vs {ref.shape}")
+        if ref.size == 0:
+            return self
+        err = np.abs(x - ref)
+        m = float(np.max(err))
+        # NaN in x must not vanish in a max with an earlier finite value
+        self.max_err = m if (np.isnan(m) or m > self.max_err) else self.max_err
+        self.sum_ref2 += float(np.sum(ref * ref))
+        self.sum_err2 += float(np.sum(err * err))
+        self.count += ref.size
+        return self
+
+    def result(self):
+        if self.count == 0:
+            return {"max_over_rms": 0.0, "max_abs": 0.0, "rms_err": 0.0, "rms_ref": 0.0}
+        rms = float(np.sqrt(self.sum_ref2 / self.count))
+        mx = self.max_err
+        if rms > 0:
+            ratio = mx / rms
+        else:
+            ratio = 0.0 if mx == 0 else float("inf")
+        return {"max_over_rms": ratio, "max_abs": mx, "rms_err": float(np.sqrt(self.sum_err2 / self.count)),
+                "rms_ref": rms}
+
+
 def metrics(x, ref):
-    """max|x - ref| / RMS(ref) plus the absolute max and RMS errors."""
-    x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
-    err = np.abs(x - ref)
-    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
-    mx = float(err.max()) if err.size else 0.0
-    return {"max_over_rms": mx / rms if rms > 0 else (0.0 if mx == 0 else float("inf")),
-            "max_abs": mx, "rms_err": float(np.sqrt(np.mean(err * err))) if err.size else 0.0,
-            "rms_ref": rms}
+    """max|x - ref| / RMS(ref) plus the absolute max and RMS errors (see ``Metrics``)."""
+    return Metrics().add(x, ref).result()

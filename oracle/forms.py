@@ -42,10 +42,9 @@ def brute(q, k, v, log_alpha, beta, S0):
 def attention_form(q, k, v, log_alpha, beta, S0):
     """Unrolled sum: o_t = sum_i beta_i (k_i^T M_{t,i}^T q_t) v_i + (M_{t,-1} S0)^T q_t,
 
-    where M_{t,i} = A_t A_{t-1} ... A_{i+1} is the cumulative product of
-    transitions between write i and read t ("Kimi Linear" page, "Why
-    channel-wise gating matters": the query dotted with keys weighted by a
-    cumulative product of transition matrices).  O(T^2 dk^3): tiny T only.
+    where M_{t,i} = A_t A_{t-1} ... A_{i+1} carries write i forward to read t
+    (the expansion of the output over earlier keys that the "Kimi Linear" page
+    describes in "Why channel-wise gating matters").  O(T^2 dk^3): tiny T only.
     """
     A = transitions(k, log_alpha, beta)
     T, dk = k.shape

@@ -1,9 +1,10 @@
 """fp64 oracle of the KDA layer's prologue and epilogue -- TEST INFRASTRUCTURE ONLY.
 
-Around the recurrence, the "Kimi Linear" page ("Kimi Delta Attention"
-section) has each KDA head L2-normalise its queries and keys, compute its
-per-channel decay from a low-rank projection, and pass its output through a
-head-wise RMSNorm and a sigmoid output gate.  The page fixes neither the
+The "Kimi Linear" page ("Kimi Delta Attention" section) wraps the recurrence
+of every KDA head in a prologue and an epilogue: queries and keys are scaled to
+unit L2 norm, the per-channel decay comes out of a small low-rank projection,
+and the head's output is normalised by its RMS and multiplied by a sigmoid
+gate.  The page fixes neither the
 squashing of the projection into a decay nor the constants, so this module
 takes the plainest readings:
 
