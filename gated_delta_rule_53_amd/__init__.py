@@ -50,8 +50,8 @@ def workspace_size(batch, seqlen, heads, dk, dv, in_dtype, out_dtype=None, num_s
     """Bytes of device workspace ``chunk_fwd`` needs (varlen iff num_seqs > 0)."""
     torch = _torch()
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    shape = _lib.Shape(batch, seqlen, num_seqs, max_seqlen, heads, dk, dv, _dtype_code(in_dtype),
-                       _dtype_code(out_dtype))
+    shape = _lib.shape(batch, seqlen, num_seqs, heads, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype),
+                       max_seqlen)
     return int(lib().kda_chunk_fwd_workspace_size(shape))
 
 
@@ -59,8 +59,8 @@ def bwd_workspace_size(batch, seqlen, heads, dk, dv, in_dtype, dout_dtype=None, 
     """Bytes of device workspace ``chunk_bwd`` needs (varlen iff num_seqs > 0)."""
     torch = _torch()
     dout_dtype = torch.float32 if dout_dtype is None else dout_dtype
-    shape = _lib.Shape(batch, seqlen, num_seqs, max_seqlen, heads, dk, dv, _dtype_code(in_dtype),
-                       _dtype_code(dout_dtype))
+    shape = _lib.shape(batch, seqlen, num_seqs, heads, dk, dv, _dtype_code(in_dtype), _dtype_code(dout_dtype),
+                       max_seqlen)
     return int(lib().kda_chunk_bwd_workspace_size(shape))
 
 
@@ -105,8 +105,8 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
         final_state = None
     if final_state is not None:
         _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
-    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
-                       _dtype_code(q.dtype), _dtype_code(out_dtype), int(gate_per_head))
+    shape = _lib.shape(B, T, N if cu_seqlens is not None else 0, H, dk, dv, _dtype_code(q.dtype),
+                       _dtype_code(out_dtype), int(max_seqlen or 0), int(gate_per_head))
     L = lib()
     need = int(L.kda_chunk_fwd_workspace_size(shape))
     if workspace is None:
@@ -139,11 +139,11 @@ def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
     if out is None:
         out = torch.empty((N, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
     _check_dev(out, "out", None, (N, H, dv))
-    st = lib().kda_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), int(gate_per_head),
-                               q.data_ptr(),
-                               k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(),
-                               state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
-    _lib.check(st, "kda_decode_step")
+    name = "kda_decode_step_head_gate" if gate_per_head else "kda_decode_step"
+    st = getattr(lib(), name)(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), q.data_ptr(),
+                              k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(), state.data_ptr(),
+                              out.data_ptr(), _stream_handle(q.device))
+    _lib.check(st, name)
     return out
 
 
@@ -203,8 +203,8 @@ def layer_fwd(q, k, v, gate, beta, init_state=None, cu_seqlens=None, *, out_gate
         final_state = None
     if final_state is not None:
         _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
-    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
-                       _dtype_code(q.dtype), _dtype_code(out_dtype), int(gate_per_head))
+    shape = _lib.shape(B, T, N if cu_seqlens is not None else 0, H, dk, dv, _dtype_code(q.dtype),
+                       _dtype_code(out_dtype), int(max_seqlen or 0), int(gate_per_head))
     layer = _layer(gate, out_gate, norm_weight, qk_l2norm, l2_eps, rms_eps, dv)
     L = lib()
     need = int(L.kda_chunk_fwd_workspace_size(shape))
@@ -249,12 +249,13 @@ def layer_decode_step(q, k, v, gate, beta, state, *, out_gate=None, norm_weight=
 
 
 def chunk_bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final=None, cu_seqlens=None, *,
-              max_seqlen=None, want_d_init=True, workspace=None):
+              max_seqlen=None, want_d_init=True, workspace=None, out=None):
     """Gradients of sum(d_out * out) + sum(d_final * final_state) through the chunked prefill.
 
     Inputs as for ``chunk_fwd``; d_out [B,T,H,dv] (the dtype ``out`` had), d_final
     [N,H,dk,dv] fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha
-    (the shape of log_alpha), dbeta and, with ``want_d_init``, d_init.
+    (the shape of log_alpha), dbeta and, with ``want_d_init``, d_init.  ``out`` may hold
+    any of those tensors, preallocated; the rest are allocated here.
     """
     torch = _torch()
     _check_dev(q, "q")
@@ -279,14 +280,18 @@ def chunk_bwd(q, k, v, log_alpha, beta, d_out, init_state=None, d_final=None, cu
         _check_dev(init_state, "init_state", torch.float32, (N, H, dk, dv))
     if d_final is not None:
         _check_dev(d_final, "d_final", torch.float32, (N, H, dk, dv))
-    shape = _lib.Shape(B, T, N if cu_seqlens is not None else 0, int(max_seqlen or 0), H, dk, dv,
-                       _dtype_code(q.dtype), _dtype_code(d_out.dtype), int(gate_per_head))
+    shape = _lib.shape(B, T, N if cu_seqlens is not None else 0, H, dk, dv, _dtype_code(q.dtype),
+                       _dtype_code(d_out.dtype), int(max_seqlen or 0), int(gate_per_head))
     f32 = dict(dtype=torch.float32, device=q.device)
-    g = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
-         "dv": torch.empty((B, T, H, dv), **f32), "dlog_alpha": torch.empty(tuple(log_alpha.shape), **f32),
-         "dbeta": torch.empty((B, T, H), **f32)}
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dlog_alpha": tuple(log_alpha.shape),
+              "dbeta": (B, T, H)}
     if want_d_init:
-        g["d_init"] = torch.empty((N, H, dk, dv), **f32)
+        shapes["d_init"] = (N, H, dk, dv)
+    out = {} if out is None else out
+    g = {}
+    for name, shp in shapes.items():
+        g[name] = out[name] if name in out else torch.empty(shp, **f32)
+        _check_dev(g[name], name, torch.float32, shp)
     L = lib()
     need = int(L.kda_chunk_bwd_workspace_size(shape))
     if need == 0:

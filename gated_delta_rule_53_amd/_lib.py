@@ -12,8 +12,9 @@ DTYPE_BF16 = 1
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step", "kda_layer_fwd",
-           "kda_layer_decode_step", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_status_string")
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_decode_step", "kda_decode_step_head_gate",
+           "kda_layer_fwd", "kda_layer_decode_step", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+           "kda_status_string")
 
 
 class KdaError(RuntimeError):
@@ -25,9 +26,15 @@ class KdaError(RuntimeError):
 class Shape(ctypes.Structure):
     """kda_shape_t"""
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
-                ("max_seqlen", ctypes.c_int64), ("heads", ctypes.c_int32), ("dk", ctypes.c_int32),
-                ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int), ("max_seqlen", ctypes.c_int64),
                 ("gate_per_head", ctypes.c_int32)]
+
+
+def shape(batch, seqlen, num_seqs, heads, dk, dv, in_dtype, out_dtype, max_seqlen=0, gate_per_head=0):
+    """A kda_shape_t built by field name."""
+    return Shape(batch=batch, seqlen=seqlen, num_seqs=num_seqs, heads=heads, dk=dk, dv=dv, in_dtype=in_dtype,
+                 out_dtype=out_dtype, max_seqlen=max_seqlen, gate_per_head=gate_per_head)
 
 
 class Layer(ctypes.Structure):
@@ -53,9 +60,10 @@ def lib():
     L.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(Shape)]
     L.kda_chunk_fwd.restype = ctypes.c_int
     L.kda_chunk_fwd.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.kda_decode_step.restype = ctypes.c_int
-    L.kda_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, i32,
-                                  vp, vp, vp, vp, vp, vp, vp, vp]
+    for name in ("kda_decode_step", "kda_decode_step_head_gate"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kda_layer_fwd.restype = ctypes.c_int
     L.kda_layer_fwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 sz, vp]

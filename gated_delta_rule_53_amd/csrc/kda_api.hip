@@ -5,7 +5,6 @@
 
 #include <stdlib.h>
 
-#include <mutex>
 #include <vector>
 
 #include "../../include/kda.h"
@@ -24,35 +23,6 @@ constexpr size_t RECORD_BUDGET = size_t(220) << 20;
 constexpr int64_t MIN_WINDOW = 32;
 constexpr size_t WINDOW_CAP = size_t(4) << 30;
 
-// Per-device overlap resources, created on first use and kept for the life of
-// the process.  The mutex serialises host-side enqueueing of calls on one device.
-struct DeviceResources {
-    std::mutex mu;
-    bool ready = false;
-    kda::Overlap ov;
-};
-constexpr int MAX_DEVICES = 64;
-DeviceResources g_dev[MAX_DEVICES];
-
-DeviceResources* device_resources() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
-    DeviceResources* r = &g_dev[dev];
-    return r;
-}
-
-void init_overlap(DeviceResources* r) {
-    if (r->ready) return;
-    r->ready = true;
-    kda::Overlap ov;
-    if (hipStreamCreateWithFlags(&ov.side, hipStreamNonBlocking) != hipSuccess) return;
-    if (hipEventCreateWithFlags(&ov.local_done, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ov.inter_done[0], hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ov.inter_done[1], hipEventDisableTiming) != hipSuccess)
-        return;  // resources leak on this rare path; the overlap simply stays off
-    r->ov = ov;
-}
-
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -64,6 +34,19 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 }
 
 size_t dsize(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+// True when [x, x + xn) overlaps any of the ranges (null or empty ranges never do).
+template <size_t K>
+bool overlaps_any(const void* x, size_t xn, const Range (&rs)[K]) {
+    for (const Range& r : rs)
+        if (overlaps(x, xn, r.p, r.n)) return true;
+    return false;
+}
 
 struct Plan {
     int64_t N, tokens, max_len, max_chunks;
@@ -168,7 +151,7 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
 static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
                                    const void* v, const float* log_alpha, const float* beta,
                                    const float* init_state, const int32_t* cu_seqlens, void* out,
-                                   float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+                                   float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan p;
     kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p);
     if (st != KDA_OK) return st;
@@ -186,7 +169,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
             (layer->norm_weight && !aligned16(layer->norm_weight)))
             return KDA_ERR_INVALID_ARG;
     }
-    const size_t state_elems = (size_t)p.N * H * d * d;
+    const size_t state_bytes = (size_t)p.N * H * d * d * 4;
     if (p.tokens > 0) {
         if (!q || !k || !v || !gate || !beta || !out) return KDA_ERR_INVALID_ARG;
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out))
@@ -196,39 +179,39 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
     if ((init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
         return KDA_ERR_INVALID_ARG;
     if (init_state && final_state && init_state != final_state &&
-        overlaps(init_state, state_elems * 4, final_state, state_elems * 4))
+        overlaps(init_state, state_bytes, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
+    // every input (init_state is compared with final_state above)
+    const Range inputs[] = {{q, tok_bytes * in_b},
+                            {k, tok_bytes * in_b},
+                            {v, tok_bytes * in_b},
+                            {gate, la_bytes},
+                            {beta, (size_t)p.tokens * H * 4},
+                            {cu_seqlens, cu_seqlens ? (size_t)(p.N + 1) * 4 : 0},
+                            {layer ? layer->out_gate : nullptr, og_bytes},
+                            {layer ? layer->norm_weight : nullptr, (size_t)d * 4}};
     const size_t out_bytes = tok_bytes * out_b;
-    if (overlaps(out, out_bytes, q, tok_bytes * in_b) || overlaps(out, out_bytes, k, tok_bytes * in_b) ||
-        overlaps(out, out_bytes, v, tok_bytes * in_b) || overlaps(out, out_bytes, gate, la_bytes) ||
-        (layer && overlaps(out, out_bytes, layer->out_gate, og_bytes)) ||
-        (layer && overlaps(out, out_bytes, layer->norm_weight, (size_t)d * 4)) ||
-        overlaps(out, out_bytes, beta, (size_t)p.tokens * H * 4) ||
-        overlaps(out, out_bytes, init_state, state_elems * 4) ||
-        overlaps(out, out_bytes, final_state, state_elems * 4))
+    if (overlaps_any(out, out_bytes, inputs) || overlaps(out, out_bytes, init_state, state_bytes) ||
+        overlaps(out, out_bytes, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
-    if (final_state && (overlaps(final_state, state_elems * 4, q, tok_bytes * in_b) ||
-                        overlaps(final_state, state_elems * 4, k, tok_bytes * in_b) ||
-                        overlaps(final_state, state_elems * 4, v, tok_bytes * in_b)))
-        return KDA_ERR_INVALID_ARG;
+    if (final_state && overlaps_any(final_state, state_bytes, inputs)) return KDA_ERR_INVALID_ARG;
 
     const size_t per_chunk = (size_t)p.N * H * p.rec;
     if (p.N == 0) return KDA_OK;  // nothing to compute
+    if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
+        return KDA_ERR_WORKSPACE;
+    // the workspace is written by the kernels: it must not overlap any argument
+    if (overlaps_any(workspace, workspace_bytes, inputs) || overlaps(workspace, workspace_bytes, out, out_bytes) ||
+        overlaps(workspace, workspace_bytes, init_state, state_bytes) ||
+        overlaps(workspace, workspace_bytes, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
     if (cu_seqlens) {
         const char* chk = getenv("KDA_CHECK");
         if (chk && chk[0] == '1') {
-            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, static_cast<hipStream_t>(stream));
+            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
             if (cs != KDA_OK) return cs;
         }
     }
-    if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
-        return KDA_ERR_WORKSPACE;
-    // KDA_OVERLAP=1 runs the chunk-local pass of the next window concurrently with the
-    // state pass of the current one (two record buffers, an auxiliary stream).  Off by
-    // default: on MI355X the concurrent local pass slows the latency-bound state chain
-    // more than it saves.
-    const char* ov_env = getenv("KDA_OVERLAP");  // read per call (cheap next to any launch)
-    const bool overlap_enabled = ov_env && ov_env[0] == '1';
     // Few (sequence, head) pairs and a workspace for every record: the
     // sequence-parallel state pass.  Otherwise one buffer for every chunk if it
     // fits, else windows of chunks.
@@ -236,23 +219,14 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
     const int bv = kda::chunk_value_slice(d, p.N * H);
     int sc = 0;
-    int G = overlap_enabled ? 0 : kda::chunk_segments(d, bv, p.N * H, p.max_chunks, sc);
+    int G = kda::chunk_segments(d, bv, p.N * H, p.max_chunks, sc);
     const size_t segb = G > 0 ? segment_bytes(p, H, G) : 0;
     if (G > 0 && avail < (size_t)all * per_chunk + 3 * segb) G = 0;  // workspace too small: windows
     // grid rows of the chunk-local pass: sequences x chunks of a window <= 65535
     const int64_t wc_max = 65535 / p.N;
     if (wc_max < 1) return KDA_ERR_UNSUPPORTED;
     if (G > 0 && all > wc_max) G = 0;  // the sequence-parallel pass launches every chunk at once
-    int64_t wc;
-    bool two = false;
-    if ((size_t)all * per_chunk <= avail || G > 0) {
-        wc = all;
-    } else if (overlap_enabled && avail >= 2 * per_chunk) {
-        wc = (int64_t)(avail / 2 / per_chunk);
-        two = true;
-    } else {
-        wc = (int64_t)(avail / per_chunk);
-    }
+    int64_t wc = ((size_t)all * per_chunk <= avail || G > 0) ? all : (int64_t)(avail / per_chunk);
     if (wc > wc_max) wc = wc_max;
     const int64_t nwin64 = p.max_chunks > 0 ? (p.max_chunks + wc - 1) / wc : 1;
     if (nwin64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -291,25 +265,15 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         a.seg_M = reinterpret_cast<float*>(sb + segb);
         a.seg_init = reinterpret_cast<float*>(sb + 2 * segb);
     }
-    kda::Overlap ov;  // defaults: everything on the caller's stream
-    DeviceResources* res = two && nwin64 > 1 ? device_resources() : nullptr;
-    std::unique_lock<std::mutex> lock;
-    if (res) {
-        lock = std::unique_lock<std::mutex>(res->mu);
-        init_overlap(res);
-        ov = res->ov;
-        ov.buffer_bytes = (size_t)wc * per_chunk;
-    }
     hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16,
-                                       layer && layer->qk_l2norm, bv, a, (int)nwin64, ov,
-                                       static_cast<hipStream_t>(stream));
+                                       layer && layer->qk_l2norm, bv, a, (int)nwin64, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(s, nullptr, q, k, v, log_alpha, beta, init_state, cu_seqlens, out, final_state,
                           workspace, workspace_bytes, stream);
 }
@@ -317,7 +281,7 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
 kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
                            const void* v, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, hipStream_t stream) {
     if (!layer) return KDA_ERR_INVALID_ARG;
     return chunk_fwd_impl(s, layer, q, k, v, nullptr, beta, init_state, cu_seqlens, out, final_state, workspace,
                           workspace_bytes, stream);
@@ -326,7 +290,7 @@ kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const
 static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                 kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
                                 const void* q, const void* k, const void* v, const float* log_alpha,
-                                const float* beta, float* state_inout, void* out, void* stream) {
+                                const float* beta, float* state_inout, void* out, hipStream_t stream) {
     if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
     if (gate_per_head != 0 && gate_per_head != 1) return KDA_ERR_INVALID_ARG;
     if ((in_dtype != KDA_DTYPE_F32 && in_dtype != KDA_DTYPE_BF16) ||
@@ -347,16 +311,15 @@ static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_
     const size_t st_bytes = (size_t)units * dk * dv * 4, out_bytes = vec * out_b;
     const size_t la_bytes = (gate_per_head ? (size_t)units : vec) * (layer ? 2 : 4);
     const size_t og_bytes = layer && layer->out_gate ? vec * 2 : 0;
-    if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps(out, out_bytes, q, vec * in_b) ||
-        overlaps(out, out_bytes, k, vec * in_b) || overlaps(out, out_bytes, v, vec * in_b) ||
-        overlaps(out, out_bytes, gate, la_bytes) || overlaps(out, out_bytes, beta, (size_t)units * 4) ||
-        overlaps(state_inout, st_bytes, q, vec * in_b) || overlaps(state_inout, st_bytes, k, vec * in_b) ||
-        overlaps(state_inout, st_bytes, v, vec * in_b) || overlaps(state_inout, st_bytes, gate, la_bytes) ||
-        overlaps(state_inout, st_bytes, beta, (size_t)units * 4) ||
-        (layer && (overlaps(out, out_bytes, layer->out_gate, og_bytes) ||
-                   overlaps(out, out_bytes, layer->norm_weight, (size_t)dv * 4) ||
-                   overlaps(state_inout, st_bytes, layer->out_gate, og_bytes) ||
-                   overlaps(state_inout, st_bytes, layer->norm_weight, (size_t)dv * 4))))
+    const Range inputs[] = {{q, vec * in_b},
+                            {k, vec * in_b},
+                            {v, vec * in_b},
+                            {gate, la_bytes},
+                            {beta, (size_t)units * 4},
+                            {layer ? layer->out_gate : nullptr, og_bytes},
+                            {layer ? layer->norm_weight : nullptr, (size_t)dv * 4}};
+    if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps_any(out, out_bytes, inputs) ||
+        overlaps_any(state_inout, st_bytes, inputs))
         return KDA_ERR_INVALID_ARG;
     kda::DecodeLayer L;
     if (layer) {
@@ -369,22 +332,30 @@ static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_
     }
     hipError_t e = kda::decode_dispatch((int)units, dk, in_dtype == KDA_DTYPE_BF16, out_dtype == KDA_DTYPE_BF16,
                                         gate_per_head != 0, q, k, v, log_alpha, beta, state_inout, out, L,
-                                        static_cast<hipStream_t>(stream));
+                                        stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
-                             kda_dtype_t out_dtype, int32_t gate_per_head, const void* q, const void* k,
-                             const void* v, const float* log_alpha, const float* beta, float* state_inout,
-                             void* out, void* stream) {
-    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, gate_per_head, nullptr, q, k, v, log_alpha, beta,
-                       state_inout, out, stream);
+                             kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
+                             const float* log_alpha, const float* beta, float* state_inout, void* out,
+                             hipStream_t stream) {
+    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, 0, nullptr, q, k, v, log_alpha, beta, state_inout,
+                       out, stream);
+}
+
+kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                       kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
+                                       const float* log_alpha, const float* beta, float* state_inout, void* out,
+                                       hipStream_t stream) {
+    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, 1, nullptr, q, k, v, log_alpha, beta, state_inout,
+                       out, stream);
 }
 
 kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                    kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
                                    const void* q, const void* k, const void* v, const float* beta,
-                                   float* state_inout, void* out, void* stream) {
+                                   float* state_inout, void* out, hipStream_t stream) {
     if (!layer) return KDA_ERR_INVALID_ARG;
     return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, gate_per_head, layer, q, k, v, nullptr, beta,
                        state_inout, out, stream);
@@ -451,7 +422,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, const void* d_out, const float* d_final_state, float* dq,
                            float* dk, float* dv, float* dlog_alpha, float* dbeta, float* d_init_state,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Plan p;
     BwdLayout l;
     kda_status_t st = bwd_layout(s, cu_seqlens != nullptr, p, l);
@@ -488,11 +459,20 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     if (cu_seqlens) {
         const char* chk = getenv("KDA_CHECK");
         if (chk && chk[0] == '1') {
-            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, static_cast<hipStream_t>(stream));
+            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
             if (cs != KDA_OK) return cs;
         }
     }
     if (!workspace || !aligned16(workspace) || workspace_bytes < l.total) return KDA_ERR_WORKSPACE;
+    {  // the workspace is written by the kernels: it must not overlap any argument
+        const Range all[] = {{q, tok * in_b},       {k, tok * in_b},         {v, tok * in_b},
+                             {log_alpha, la_bytes}, {beta, tb4},             {init_state, st_bytes},
+                             {cu_seqlens, cu_seqlens ? (size_t)(p.N + 1) * 4 : 0},
+                             {d_out, tok * out_b},  {d_final_state, st_bytes}, {dq, tok * 4},
+                             {dk, tok * 4},         {dv, tok * 4},           {dlog_alpha, la_bytes},
+                             {dbeta, tb4},          {d_init_state, st_bytes}};
+        if (overlaps_any(workspace, workspace_bytes, all)) return KDA_ERR_INVALID_ARG;
+    }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     kda::BwdArgs b;
     kda::ChunkArgs& a = b.fwd;
@@ -531,7 +511,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     b.dla_head = s->gate_per_head ? dlog_alpha : nullptr;
     b.dbeta = dbeta;
     hipError_t e = kda::bwd_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, b,
-                                     static_cast<hipStream_t>(stream));
+                                     stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -1034,7 +1034,10 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     seq_bounds(a, s, tb, L);
     const int nchunks = (int)((L + CH - 1) / CH);
     const int jb = MODE == 0 ? a.win * a.Wc : seg * a.Sc;
-    const int je = min(nchunks, MODE == 0 ? jb + a.Wc : jb + a.Sc);
+    // the segment passes hold a record for each of the first Wc chunks only: a
+    // sequence longer than the launch was sized for is truncated there, as the
+    // windowed pass (whose chunk index never leaves its window) truncates it
+    const int je = min(MODE == 0 ? nchunks : min(nchunks, a.Wc), MODE == 0 ? jb + a.Wc : jb + a.Sc);
     if (MODE == 0 ? (jb >= je && a.win > 0) : jb >= je) return;
     const int jrec0 = MODE == 0 ? jb : 0;        // first chunk held by the record buffer
 
@@ -1294,7 +1297,7 @@ __global__ void __launch_bounds__(256) chunk_segment_combine_kernel(ChunkArgs a)
             sS[row][cb + c] = x[c];
         }
         __syncthreads();
-        if (g * a.Sc < nchunks) {  // uniform
+        if (g * a.Sc < min(nchunks, a.Wc)) {  // uniform; segments past the records hold no chunk
             float y[CPT];
 #pragma unroll
             for (int c = 0; c < CPT; ++c) y[c] = a.seg_B[blk + (size_t)row * D + c0 + cb + c];
@@ -1429,37 +1432,22 @@ int chunk_value_slice(int d, int64_t units) {
     return 64;
 }
 
-// Window loop.  With one window everything runs on the caller's stream.  With
-// more, the chunk-local pass of window w+1 (caller's stream) overlaps the state
-// pass of window w (the auxiliary stream), the records alternating between two
-// buffers: the local pass of window w+2 waits for the state pass of window w.
+// Window loop: per window of chunks, the chunk-local pass then the state pass,
+// both on the caller's stream; the records of one window live in the
+// workspace between the two.
 template <int D, typename IT, typename OT, typename OUT, bool QKN, bool GPRE, int BV>
-static hipError_t run_windows(const ChunkArgs& base, int nwin, const Overlap& ov, hipStream_t st) {
+static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
     using C = LocalCfg<D, OT>;
     const int units = base.N * base.H;
-    const bool two = nwin > 1 && ov.side;
     for (int w = 0; w < nwin; ++w) {
         ChunkArgs a = base;
         a.win = w;
-        if (two) a.rec = base.rec + (size_t)(w & 1) * ov.buffer_bytes;
-        hipError_t e;
-        if (two && w >= 2 && (e = hipStreamWaitEvent(st, ov.inter_done[w & 1], 0)) != hipSuccess) return e;
         hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st,
                            a);
+        hipError_t e;
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipStream_t is = st;
-        if (two) {
-            if ((e = hipEventRecord(ov.local_done, st)) != hipSuccess) return e;
-            if ((e = hipStreamWaitEvent(ov.side, ov.local_done, 0)) != hipSuccess) return e;
-            is = ov.side;
-        }
-        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, is, a);
+        hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (two && (e = hipEventRecord(ov.inter_done[w & 1], ov.side)) != hipSuccess) return e;
-    }
-    if (two) {
-        hipError_t e = hipStreamWaitEvent(st, ov.inter_done[(nwin - 1) & 1], 0);
-        if (e != hipSuccess) return e;
     }
     if (!base.out_gate) return hipSuccess;
     // the epilogue after the last state pass (between state passes it would
@@ -1522,30 +1510,29 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
 }
 
 template <int D, typename IT, typename OT, typename OUT, bool QKN, bool GPRE>
-static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, const Overlap& ov, hipStream_t st) {
+static hipError_t run_bv(const ChunkArgs& a, int nwin, int bv, hipStream_t st) {
     if (a.G > 0) return run_segments<D, IT, OT, OUT, QKN, GPRE>(a, st);
-    if (bv == 16) return run_windows<D, IT, OT, OUT, QKN, GPRE, 16>(a, nwin, ov, st);
-    if (bv == 32) return run_windows<D, IT, OT, OUT, QKN, GPRE, 32>(a, nwin, ov, st);
-    return run_windows<D, IT, OT, OUT, QKN, GPRE, 64>(a, nwin, ov, st);
+    if (bv == 16) return run_windows<D, IT, OT, OUT, QKN, GPRE, 16>(a, nwin, st);
+    if (bv == 32) return run_windows<D, IT, OT, OUT, QKN, GPRE, 32>(a, nwin, st);
+    return run_windows<D, IT, OT, OUT, QKN, GPRE, 64>(a, nwin, st);
 }
 
 // Output type of the state pass: the result's type, or fp16 in place of bf16
 // when the layer epilogue follows (it reads o back and writes bf16 over it).
 template <int D, typename IT, typename OT, bool QKN, bool GPRE>
-static hipError_t run_out(const ChunkArgs& a, bool out_bf16, int nwin, int bv, const Overlap& ov, hipStream_t st) {
-    if (!out_bf16) return run_bv<D, IT, OT, float, QKN, GPRE>(a, nwin, bv, ov, st);
-    if (a.out_gate) return run_bv<D, IT, OT, _Float16, QKN, GPRE>(a, nwin, bv, ov, st);
-    return run_bv<D, IT, OT, bf16_t, QKN, GPRE>(a, nwin, bv, ov, st);
+static hipError_t run_out(const ChunkArgs& a, bool out_bf16, int nwin, int bv, hipStream_t st) {
+    if (!out_bf16) return run_bv<D, IT, OT, float, QKN, GPRE>(a, nwin, bv, st);
+    if (a.out_gate) return run_bv<D, IT, OT, _Float16, QKN, GPRE>(a, nwin, bv, st);
+    return run_bv<D, IT, OT, bf16_t, QKN, GPRE>(a, nwin, bv, st);
 }
 
 // The plain operator (log_alpha, q and k as given) or the layer (gate
 // pre-activation, q and k normalised or not).
 template <int D, typename IT, typename OT>
-static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int nwin, int bv, const Overlap& ov,
-                           hipStream_t st) {
-    if (!a.gate) return run_out<D, IT, OT, false, false>(a, out_bf16, nwin, bv, ov, st);
-    if (qk_norm) return run_out<D, IT, OT, true, true>(a, out_bf16, nwin, bv, ov, st);
-    return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, ov, st);
+static hipError_t run_norm(const ChunkArgs& a, bool out_bf16, bool qk_norm, int nwin, int bv, hipStream_t st) {
+    if (!a.gate) return run_out<D, IT, OT, false, false>(a, out_bf16, nwin, bv, st);
+    if (qk_norm) return run_out<D, IT, OT, true, true>(a, out_bf16, nwin, bv, st);
+    return run_out<D, IT, OT, false, true>(a, out_bf16, nwin, bv, st);
 }
 
 // Record windows w0 .. w0 + nw - 1 of `window` chunks: the records of one
@@ -1585,13 +1572,13 @@ hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int 
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
-                          const Overlap& ov, hipStream_t st) {
+                          hipStream_t st) {
     if (d == 128) {
-        if (in_bf16) return run_norm<128, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, ov, st);
-        return run_norm<128, float, float>(a, out_bf16, qk_norm, nwin, bv, ov, st);
+        if (in_bf16) return run_norm<128, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, st);
+        return run_norm<128, float, float>(a, out_bf16, qk_norm, nwin, bv, st);
     }
-    if (in_bf16) return run_norm<64, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, ov, st);
-    return run_norm<64, float, float>(a, out_bf16, qk_norm, nwin, bv, ov, st);
+    if (in_bf16) return run_norm<64, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, st);
+    return run_norm<64, float, float>(a, out_bf16, qk_norm, nwin, bv, st);
 }
 
 }  // namespace kda

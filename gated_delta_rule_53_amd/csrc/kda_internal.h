@@ -56,15 +56,6 @@ struct DecodeLayer {
     float rms_eps = 0.f;
 };
 
-// Resources for overlapping the two passes of the chunked prefill: an
-// auxiliary stream and three events, plus the byte size of one record buffer.
-struct Overlap {
-    hipStream_t side = nullptr;  // null: run everything on the caller's stream
-    hipEvent_t local_done = nullptr;
-    hipEvent_t inter_done[2] = {nullptr, nullptr};
-    size_t buffer_bytes = 0;
-};
-
 // Reverse mode of the chunked prefill (kda_backward.hip).  fwd: the forward's
 // arguments with Wc = the longest sequence's chunks, rec / state_buf in the
 // workspace, snap set and out null.  The backward walks windows of bwd_window
@@ -110,7 +101,7 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
 // else fp32) and an epilogue pass after the last window replaces it in place
 // by RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
-                          const Overlap& ov, hipStream_t st);
+                          hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
                            const void* k, const void* v, const float* la, const float* beta, float* state,
                            void* out, const DecodeLayer& layer, hipStream_t st);

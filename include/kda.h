@@ -16,13 +16,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is a DEVICE pointer owned by the caller; the library
- *    allocates no device memory and, by default, keeps no state between
- *    calls.  With the environment variable KDA_OVERLAP=1 the prefill overlaps
- *    its two passes across windows of chunks; it then keeps, per device, one
- *    auxiliary non-blocking stream and three events (created on first use,
- *    kept until process exit, enqueueing serialised by a per-device mutex) and
- *    joins that stream back into `stream` before returning, so callers only
- *    ever synchronise their own stream.  KDA_VALUE_SLICE=16, 32 or 64
+ *    allocates no device memory and keeps no state between calls, so calls
+ *    are thread-safe and re-entrant per stream.  KDA_VALUE_SLICE=16, 32 or 64
  *    overrides the number of value columns each state-pass workgroup carries
  *    (by default 16 for at most 64 (sequence, head) pairs, 32 up to 256, else
  *    64; 32 for dk = 64).  With at most 32 state-pass workgroups (for
@@ -63,6 +58,7 @@
 #ifndef KDA_H_
 #define KDA_H_
 
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 #include <stddef.h>
 #include <stdint.h>
 
@@ -86,9 +82,11 @@ typedef enum {
  *   num_seqs    0 for a dense batch (N = batch); varlen: N = len(cu_seqlens) - 1
  *               (kda_chunk_fwd treats the call as varlen iff cu_seqlens != NULL;
  *               the workspace query treats the shape as varlen iff num_seqs > 0)
+ *   heads, dk, dv, in_dtype (q/k/v), out_dtype (out)
+ * Two trailing fields extend the description; zero-initialising them gives the
+ * plain per-channel KDA operator with launches sized from seqlen:
  *   max_seqlen  varlen: an upper bound on the longest sequence (host value,
  *               used to size the launch); 0 means "use seqlen"
- *   heads, dk, dv, in_dtype (q/k/v), out_dtype (out)
  *   gate_per_head  0: log_alpha holds one gate per key channel, [.., H, dk]
  *               (KDA); 1: one gate per head shared by all key channels,
  *               [.., H] (the scalar forget gate of Gated DeltaNet, "Kimi
@@ -98,12 +96,12 @@ typedef struct {
     int32_t batch;
     int64_t seqlen;
     int32_t num_seqs;
-    int64_t max_seqlen;
     int32_t heads;
     int32_t dk;
     int32_t dv;
     kda_dtype_t in_dtype;
     kda_dtype_t out_dtype;
+    int64_t max_seqlen;
     int32_t gate_per_head;
 } kda_shape_t;
 
@@ -125,15 +123,17 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s);
  *               for a dense batch (then N = B, each sequence T tokens)
  *   out         [B, T, H, dv]  out_dtype; must not alias any input
  *   final_state [N, H, dk, dv] fp32, or NULL; may equal init_state exactly
- *               (in-place continuation) but must not partially overlap it
- *   workspace   device scratch of workspace_bytes >= the size above
+ *               (in-place continuation) but must not partially overlap it, nor
+ *               overlap any other argument
+ *   workspace   device scratch of workspace_bytes >= the size above, overlapping
+ *               no other argument
  * Sequences of length 0 return final_state = init_state.  One launch holds at
  * most 65535 / N chunks of every sequence (longer sequences run in windows),
  * so N <= 65535, else KDA_ERR_UNSUPPORTED. */
 kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One recurrent decode step for `batch` independent sequences ("Kimi Linear"
  * page, "Why linear attention exists": decoding is a recurrent update whose
@@ -141,15 +141,24 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
  * update itself).  Per (sequence, head), with alpha = exp(log_alpha):
  *     S <- Diag(alpha) S;  u = beta (v - S^T k);  S <- S + k u^T;  o = S^T q.
  *   q, k        [batch, H, dk] in_dtype;   v [batch, H, dv] in_dtype
- *   log_alpha   [batch, H, dk] fp32 ([batch, H] when gate_per_head = 1,
- *               one gate shared by the key channels); beta [batch, H] fp32
+ *   log_alpha   [batch, H, dk] fp32;       beta [batch, H] fp32
  *   state_inout [batch, H, dk, dv] fp32, read and overwritten in place
- *   out         [batch, H, dv] out_dtype; must not alias any other argument */
+ *   out         [batch, H, dv] out_dtype
+ * No two of state_inout, out and the inputs may overlap (KDA_ERR_INVALID_ARG).
+ * batch = 0 does nothing and returns KDA_OK. */
 kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv,
-                             kda_dtype_t in_dtype, kda_dtype_t out_dtype, int32_t gate_per_head,
-                             const void* q,
-                             const void* k, const void* v, const float* log_alpha,
-                             const float* beta, float* state_inout, void* out, void* stream);
+                             kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                             const void* q, const void* k, const void* v, const float* log_alpha,
+                             const float* beta, float* state_inout, void* out, hipStream_t stream);
+
+/* kda_decode_step with one gate per (sequence, head) shared by the key
+ * channels: log_alpha is [batch, H] fp32 (the scalar forget gate of Gated
+ * DeltaNet, "Kimi Linear" page, "Background: from the delta rule to gated
+ * DeltaNet").  Every other argument as for kda_decode_step. */
+kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk, int32_t dv,
+                                       kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                       const void* q, const void* k, const void* v, const float* log_alpha,
+                                       const float* beta, float* state_inout, void* out, hipStream_t stream);
 
 /* Layer prologue and epilogue fused around the operator ("Kimi Linear" page,
  * "Kimi Delta Attention" section): before the recurrence, q and k are scaled
@@ -189,7 +198,7 @@ typedef struct {
 kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
                            const void* v, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* One decode step of the layer: kda_decode_step with the prologue and epilogue
  * of `layer` (log_alpha replaced by layer->gate, [batch, H, dk] or [batch, H];
@@ -197,7 +206,7 @@ kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const
 kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                    kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
                                    const void* q, const void* k, const void* v, const float* beta,
-                                   float* state_inout, void* out, void* stream);
+                                   float* state_inout, void* out, hipStream_t stream);
 
 /* Reverse mode of the chunked prefill: the gradients of
  *     L = sum(d_out * out) + sum(d_final_state * final_state)
@@ -218,13 +227,14 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
  *   dbeta         [B, T, H] fp32
  *   d_init_state  [N, H, dk, dv] fp32, or NULL (not returned)
  *   workspace     device scratch of workspace_bytes >= kda_chunk_bwd_workspace_size
- * Outputs must not overlap any input or one another. */
+ * Outputs must not overlap any input or one another, and the workspace must
+ * overlap no argument. */
 size_t kda_chunk_bwd_workspace_size(const kda_shape_t* s);
 kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
                            const float* log_alpha, const float* beta, const float* init_state,
                            const int32_t* cu_seqlens, const void* d_out, const float* d_final_state, float* dq,
                            float* dk, float* dv, float* dlog_alpha, float* dbeta, float* d_init_state,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* kda_status_string(kda_status_t st);

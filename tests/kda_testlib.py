@@ -31,15 +31,34 @@ def assert_close(name, got, ref, tol):
     return m
 
 
+def assert_metrics(name, acc, tol):
+    """assert_close for a figure accumulated over pieces (oracle.Metrics)."""
+    m = acc.result()
+    assert m["max_over_rms"] <= tol, (f"{name}: max|err|/rms = {m['max_over_rms']:.3e} > {tol:.1e} "
+                                      f"(max abs {m['max_abs']:.3e}, rms ref {m['rms_ref']:.3e})")
+    return m
+
+
+def nan_tensor(torch, shape, dtype=None, device="cuda"):
+    """An output buffer filled with NaN: an element the kernels never write stays NaN and fails
+    the comparison, whatever an earlier run left in that memory."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype or torch.float32, device=device)
+
+
 def run_chunk(kda, torch, d, out_dtype=None, final=True, workspace=None, max_seqlen=None):
-    """Run kda.chunk_fwd on a synth dict (packed [T, H, d] arrays); returns numpy (out [T,H,dv], final)."""
+    """Run kda.chunk_fwd on a synth dict (packed [T, H, d] arrays), into NaN-filled output
+    and final-state buffers; returns numpy (out [T,H,dv], final)."""
     q, k, v, la, b = (to_dev(d[x], torch).unsqueeze(0) for x in ("q", "k", "v", "log_alpha", "beta"))
     cu = d.get("cu_seqlens")
     varlen = cu is not None and len(cu) != 2
     cu_t = torch.from_numpy(np.asarray(cu, np.int32)).cuda() if varlen else None
     init = None if d.get("init") is None else to_dev(d["init"], torch)
-    out, fin = kda.chunk_fwd(q, k, v, la, b, init, cu_t, out_dtype=out_dtype or torch.float32,
-                             final_state=final, workspace=workspace, max_seqlen=max_seqlen)
+    N = len(cu) - 1 if varlen else 1
+    H, dk, dv = q.shape[2], q.shape[3], v.shape[3]
+    out = nan_tensor(torch, v.shape, out_dtype or torch.float32)
+    fin = nan_tensor(torch, (N, H, dk, dv)) if final else False
+    out, fin = kda.chunk_fwd(q, k, v, la, b, init, cu_t, out=out, final_state=fin, workspace=workspace,
+                             max_seqlen=max_seqlen)
     torch.cuda.synchronize()
     o = out[0].float().cpu().numpy()
     return o, (None if fin is None else fin.cpu().numpy())

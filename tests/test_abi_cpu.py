@@ -46,7 +46,7 @@ def test_status_strings(L):
 
 
 def _shape(B=1, T=256, N=0, maxT=0, H=2, dk=64, dv=64, i=F32, o=F32, gph=0):
-    return _lib.Shape(B, T, N, maxT, H, dk, dv, i, o, gph)
+    return _lib.shape(B, T, N, H, dk, dv, i, o, maxT, gph)
 
 
 def test_workspace_size(L):
@@ -156,18 +156,86 @@ def test_backward_workspace_windows(L, monkeypatch):
 
 
 def test_decode_validation(L):
-    f = L.kda_decode_step
-    assert f(0, 2, 64, 64, F32, F32, 0, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
-    assert f(-1, 2, 64, 64, F32, F32, 0, A, A, A, A, A, A, A, None) == INVALID
-    assert f(2, 2, 96, 96, F32, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 128, F32, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 64, 5, F32, 0, A, A, A, A, A, A, A, None) == UNSUPPORTED
-    assert f(2, 2, 64, 64, F32, F32, 0, None, A, A, A, A, A, A, None) == INVALID
-    st, out = 8 * A, 12 * A
-    assert f(2, 2, 64, 64, F32, F32, 0, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
-    assert f(2, 2, 64, 64, F32, F32, 0, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
-    assert f(2, 2, 64, 64, F32, F32, 0, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state
-    assert f(2, 2, 64, 64, F32, F32, 3, A, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # bad gate flag
+    for f in (L.kda_decode_step, L.kda_decode_step_head_gate):
+        assert f(0, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
+        assert f(-1, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, None) == INVALID
+        assert f(2, 2, 96, 96, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+        assert f(2, 2, 64, 128, F32, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+        assert f(2, 2, 64, 64, 5, F32, A, A, A, A, A, A, A, None) == UNSUPPORTED
+        assert f(2, 2, 64, 64, F32, F32, None, A, A, A, A, A, A, None) == INVALID
+        st, out = 8 * A, 12 * A
+        assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st + 4, out, None) == INVALID  # misaligned
+        assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, st, st + 256, None) == INVALID  # out in state
+        assert f(2, 2, 64, 64, F32, F32, st + 512, 2 * A, 3 * A, 4 * A, 5 * A, st, out, None) == INVALID  # q in state
+        assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, st + 64, st, out, None) == INVALID  # beta in state
+    # the state right after log_alpha: overlaps a per-channel gate [N,H,dk] only
+    la_head = 2 * 2 * 4
+    st = 8 * A
+    assert L.kda_decode_step(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, st - la_head, 5 * A, st, 12 * A,
+                             None) == INVALID
+
+
+def test_shape_struct_layout_matches_the_boundary():
+    """kda_shape_t starts with the fields batch, seqlen, num_seqs, heads, dk, dv, in_dtype,
+    out_dtype at the offsets a C compiler gives them, then max_seqlen and gate_per_head;
+    the ctypes mirror has the same offsets.  Compiled from include/kda.h with gcc as C11."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = ("batch", "seqlen", "num_seqs", "heads", "dk", "dv", "in_dtype", "out_dtype", "max_seqlen",
+             "gate_per_head")
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"kda.h\"\nint main(void) {\n"
+    src += "".join(f'  printf("%zu\\n", offsetof(kda_shape_t, {n}));\n' for n in names)
+    src += '  printf("%zu\\n", sizeof(kda_shape_t));\n  return 0;\n}\n'
+    with tempfile.TemporaryDirectory() as d:
+        c, exe = os.path.join(d, "t.c"), os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        "-I" + os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        got = [int(x) for x in subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()]
+    # int32 batch | pad | int64 seqlen | int32 num_seqs, heads, dk, dv, in, out | int64 max_seqlen | int32 gph
+    assert got == [0, 8, 16, 20, 24, 28, 32, 36, 40, 48, 56]
+    assert [getattr(_lib.Shape, n).offset for n in names] + [ctypes.sizeof(_lib.Shape)] == got
+
+
+def test_chunk_fwd_aliasing_of_final_state_and_workspace(L):
+    """final_state and the workspace are written by the kernels: overlapping any argument is
+    rejected before any launch."""
+    s = _shape()  # T = 256, H = 2, dk = dv = 64, fp32: token tensors 128 KiB, states 32 KiB
+    fin, ws = 20 * A, 30 * A
+    ok = dict(fin=fin, ws=ws, wsb=1 << 20)
+    assert _fwd(L, s, **dict(ok, fin=4 * A + 4096)) == INVALID              # final state over log_alpha
+    assert _fwd(L, s, **dict(ok, fin=5 * A)) == INVALID                     # over beta
+    sv = _shape(N=1, maxT=256)  # one packed sequence: cu_seqlens [2] is read
+    assert _fwd(L, sv, cu=fin + 16, **ok) == INVALID                        # over cu_seqlens
+    assert _fwd(L, s, **dict(ok, ws=A + 64)) == INVALID                     # workspace over q
+    assert _fwd(L, s, **dict(ok, ws=6 * A - 4096)) == INVALID               # over out
+    assert _fwd(L, s, init=ws + 1024, **ok) == INVALID                      # over init
+    assert _fwd(L, s, **dict(ok, ws=fin - (1 << 20) + 1024)) == INVALID     # over final state
+    assert _fwd(L, sv, cu=ws + 4096, **ok) == INVALID                       # over cu_seqlens
+
+
+def test_layer_fwd_aliasing_of_final_state(L):
+    s = _shape(1, 256, 0, 0, 2, 64, 64, BF16, BF16)
+    q, k, v, b, out, ws = (i * A for i in (2, 4, 6, 8, 10, 12))
+    lay = _layer()  # gate at 40 A, out_gate at 41 A, weight at 42 A
+    assert L.kda_layer_fwd(s, lay, q, k, v, b, None, None, out, 41 * A + 64, ws, 1 << 20, None) == INVALID
+    assert L.kda_layer_fwd(s, lay, q, k, v, b, None, None, out, 42 * A, ws, 1 << 20, None) == INVALID
+    assert L.kda_layer_fwd(s, lay, q, k, v, b, None, None, out, None, 41 * A - 64, 1 << 20, None) == INVALID
+
+
+def test_chunk_bwd_workspace_aliasing(L):
+    s = _shape()
+    n = L.kda_chunk_bwd_workspace_size(s)
+    ws = 20 * A
+    for over in (A + 64, 6 * A, 7 * A, 11 * A):  # q, d_out, dq, dbeta inside the workspace
+        assert _bwd(L, s, ws=over - 64, wsb=n) == INVALID
+    sv = _shape(N=1, maxT=256)
+    nv = L.kda_chunk_bwd_workspace_size(sv)
+    assert _bwd(L, sv, cu=ws + 256, ws=ws, wsb=nv) == INVALID
+    assert _bwd(L, s, init=ws + 512, ws=ws, wsb=n) == INVALID
 
 
 def test_missing_library_fails_loudly(monkeypatch):
@@ -246,7 +314,8 @@ def test_layer_fwd_validation(L):
 def test_layer_decode_validation(L):
     """Rejections of kda_layer_decode_step, all before any launch."""
     q, k, v, b, st, out = (i * A for i in (2, 4, 6, 8, 10, 14))
-    call = lambda lay, gph=0: L.kda_layer_decode_step(4, 2, 64, 64, BF16, F32, gph, lay, q, k, v, b, st, out, None)
+    call = lambda lay, gph=0: L.kda_layer_decode_step(4, 2, 64, 64, BF16, F32, gph, lay, q, k, v, b, st, out,
+                                                      None)
     assert call(None) == INVALID
     assert call(_layer(norm=3)) == INVALID
     assert call(_layer(l2=float("nan"))) == INVALID

@@ -13,7 +13,7 @@ import oracle
 import synth
 from synth import WORKLOADS, random_small
 
-from kda_testlib import TOL, assert_close, to_dev
+from kda_testlib import TOL, assert_close, to_dev, nan_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -48,8 +48,13 @@ def run_bwd(kda, d, dO, dF, max_seqlen=None):
     varlen = len(cu) != 2
     cu_t = torch.from_numpy(np.asarray(cu, np.int32)).cuda() if varlen else None
     init = None if d.get("init") is None else to_dev(d["init"], torch)
+    N, (H, dk), dv = len(cu) - 1, q.shape[2:], v.shape[3]
+    # NaN-filled gradient buffers: an element the kernels never write fails the comparison
+    bufs = {"dq": q.shape, "dk": q.shape, "dv": v.shape, "dlog_alpha": la.shape, "dbeta": b.shape,
+            "d_init": (N, H, dk, dv)}
+    out = {x: nan_tensor(torch, shp) for x, shp in bufs.items()}
     g = kda.chunk_bwd(q, k, v, la, b, to_dev(dO, torch).unsqueeze(0), init,
-                      None if dF is None else to_dev(dF, torch), cu_t, max_seqlen=max_seqlen)
+                      None if dF is None else to_dev(dF, torch), cu_t, max_seqlen=max_seqlen, out=out)
     torch.cuda.synchronize()
     return {x: t.cpu().numpy() for x, t in g.items()}
 

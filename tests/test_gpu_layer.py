@@ -27,7 +27,7 @@ import synth
 from oracle import layer as olayer
 from synth import WORKLOADS, layer_small, random_small
 
-from kda_testlib import DECODE_TOL, TOL, assert_close, to_dev
+from kda_testlib import DECODE_TOL, TOL, assert_close, to_dev, nan_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -50,8 +50,11 @@ def run_layer(kda, d, epilogue=True, qk_l2norm=True, out_dtype=torch.float32, ma
     init = None if d.get("init") is None else to_dev(d["init"], torch)
     og = to_dev(d["out_gate"], torch).unsqueeze(0) if epilogue else None
     w = to_dev(d["norm_weight"], torch) if epilogue else None
+    N = len(cu) - 1 if varlen else 1
+    y = nan_tensor(torch, v.shape, out_dtype)
+    fin = nan_tensor(torch, (N, q.shape[2], q.shape[3], v.shape[3]))
     y, fin = kda.layer_fwd(q, k, v, g, b, init, cu_t, out_gate=og, norm_weight=w, qk_l2norm=qk_l2norm,
-                           out_dtype=out_dtype, max_seqlen=max_seqlen)
+                           out=y, final_state=fin, max_seqlen=max_seqlen)
     torch.cuda.synchronize()
     return y[0].float().cpu().numpy(), fin.cpu().numpy()
 
@@ -170,7 +173,7 @@ def test_layer_decode(kda, N, H, D, dtype, gate, epi):
         a = [to_dev(st[x], torch) for x in ("q", "k", "v", "g", "beta")]
         og = to_dev(st["out_gate"], torch) if epi else None
         outs.append(kda.layer_decode_step(*a, state, out_gate=og, norm_weight=w if epi else None,
-                                          out_dtype=torch.float32).cpu().numpy())
+                                          out=nan_tensor(torch, a[2].shape)).cpu().numpy())
     torch.cuda.synchronize()
     ref_outs, S_ref = olayer.decode_steps(S0, seq, wt if epi else None, epilogue=epi)
     for i in range(len(seq)):
@@ -189,8 +192,8 @@ def test_layer_decode_workload_sampled(kda):
     for st in seq:
         a = [to_dev(st[x], torch) for x in ("q", "k", "v", "g", "beta")]
         outs.append(kda.layer_decode_step(*a, state, out_gate=to_dev(st["out_gate"], torch),
-                                          norm_weight=to_dev(wt, torch), out_dtype=torch.bfloat16).float()
-                    .cpu().numpy())
+                                          norm_weight=to_dev(wt, torch),
+                                          out=nan_tensor(torch, a[2].shape, torch.bfloat16)).float().cpu().numpy())
     torch.cuda.synchronize()
     heads = [0, 7, 19, 31]
     sub = [{x: st[x][:, heads] for x in st} for st in seq]
