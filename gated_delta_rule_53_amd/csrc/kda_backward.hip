@@ -48,6 +48,14 @@ namespace kda {
 
 namespace {
 
+// A diagonal 16-row block's single anchor (its ninth row) needs exponents up to the
+// gate's decay over eight rows in both directions; past kWideExp (fp32 operands keep
+// their products exact to far beyond what matters) the block is formed level by
+// level instead: a pair (r, i) is formed where r and i first fall into different
+// halves of an aligned sub-block of 16, 8, 4 or 2 rows, anchored at that
+// sub-block's middle row, so every exponent is at most 0 and any gate is in range.
+constexpr float kWideExp = 60.f;
+
 constexpr int BW_T = 512;  // threads of the prep kernel (8 waves)
 constexpr int BW_W = BW_T / 64;
 constexpr int BL_T = 512;  // threads of the local kernel (8 waves)
@@ -302,11 +310,11 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     }
     if (t < CH) sB[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
     __syncthreads();
-    if (t < D) {  // inclusive cumulative log-gate per channel
-        float acc = 0.f;
+    if (t < D) {  // inclusive cumulative log-gate per channel, summed in fp64 and rounded once
+        double acc = 0.0;
         for (int r = 0; r < CH; ++r) {
-            acc += sG[r * DP + t];
-            sG[r * DP + t] = acc;
+            acc += (double)sG[r * DP + t];
+            sG[r * DP + t] = (float)acc;
         }
     }
     __syncthreads();
@@ -323,9 +331,48 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const float* X = isP ? sX : sK;
         const int rr = 16 * rb + li, ii = 16 * cb + li;
         floatx4 acc = zero4();
-        tile_f32(acc, D, lane,
-                 [&](int c) { return X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[an * DP + c]); },
-                 [&](int c) { return sK[ii * DP + c] * fast_exp(sG[an * DP + c] - sG[ii * DP + c]); });
+        // a diagonal block whose single-anchor exponents pass kWideExp (in either direction:
+        // the block's first row over the anchor, the anchor over its last row) is formed in
+        // the multi-level form instead
+        bool wide = false;
+        if (cb == rb) {
+            float ex = 0.f;
+            for (int c = lane; c < D; c += 64)
+                ex = fmaxf(ex, fmaxf(sG[(16 * rb) * DP + c] - sG[an * DP + c], sG[an * DP + c] - sG[(16 * rb + 15) * DP + c]));
+            wide = __any(!(ex <= kWideExp));
+        }
+        if (!wide) {
+            tile_f32(acc, D, lane,
+                     [&](int c) { return X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[an * DP + c]); },
+                     [&](int c) { return sK[ii * DP + c] * fast_exp(sG[an * DP + c] - sG[ii * DP + c]); });
+        } else {
+            // level lev: pairs (r, i) in the later / earlier half of an aligned sub-block of
+            // sz rows, anchored at its middle row; a last level (isP only) for the diagonal
+            for (int lev = 0; lev < (isP ? 5 : 4); ++lev) {
+                const bool dg = lev == 4;
+                const int sz = dg ? 1 : 16 >> lev, hs = sz >> 1, msk = sz - 1;
+                const int ra = 16 * rb + (li & ~msk) + hs;  // anchor of row li / column li
+                floatx4 lv = zero4();
+                tile_f32(lv, D, lane,
+                         [&](int c) {
+                             return dg ? X[rr * DP + c]
+                                       : ((li & msk) >= hs ? X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[ra * DP + c])
+                                                           : 0.f);
+                         },
+                         [&](int c) {
+                             return dg ? sK[ii * DP + c]
+                                       : ((li & msk) < hs ? sK[ii * DP + c] * fast_exp(sG[ra * DP + c] - sG[ii * DP + c])
+                                                          : 0.f);
+                         });
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lr = 4 * gq + r;
+                    const bool pair = dg ? lr == li
+                                         : (lr & ~msk) == (li & ~msk) && (lr & msk) >= hs && (li & msk) < hs;
+                    if (pair) acc[r] = lv[r];
+                }
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * rb + 4 * gq + r, col = 16 * cb + li;
@@ -1112,13 +1159,16 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     //   row form  Y[r][c] = sum_i M[r][i] X[i][c] e^{G_rc - G_ic}
     //   col form  Z[i][c] = sum_r M[r][i] X[r][c] e^{G_rc - G_ic}
     // per tile of the wave and form, the off-diagonal blocks anchored at the
-    // block boundary, the diagonal block at its ninth row.
+    // block boundary, the diagonal block at its ninth row (or level by level,
+    // as in the prep kernel, when that anchor's exponents pass kWideExp).
     //   R1 = row(dP, K) -> dq     C1 = col(dP, Q) -> dk, -k dG
     //   R2 = row(M2, K) -> dk, +k dG     C2 = col(M2, K) -> dk, -k dG
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
         const int blk = mt_of(i), cc = 16 * nt_of(i) + li;
         const int m = 16 * blk + 8;
+        const bool wide = __any(!(fmaxf(sG[(16 * blk) * GD + cc] - sG[m * GD + cc],
+                                        sG[m * GD + cc] - sG[(16 * blk + 15) * GD + cc]) <= kWideExp));
 #pragma unroll 1
         for (int form = 0; form < 4; ++form) {
             const float* M = form < 2 ? sP : sM;
@@ -1130,11 +1180,12 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                 if (blk > 0)
                     tile_f32(off, an, lane, [&](int ii) { return M[mr * AP + ii]; },
                              [&](int ii) { return X[ii * DP + cc] * fast_exp(sG[an * GD + cc] - sG[ii * GD + cc]); });
-                tile_f32(dia, 16, lane, [&](int ii) { return M[mr * AP + 16 * blk + ii]; },
-                         [&](int ii) {
-                             const int i2 = 16 * blk + ii;
-                             return X[i2 * DP + cc] * fast_exp(sG[m * GD + cc] - sG[i2 * GD + cc]);
-                         });
+                if (!wide)
+                    tile_f32(dia, 16, lane, [&](int ii) { return M[mr * AP + 16 * blk + ii]; },
+                             [&](int ii) {
+                                 const int i2 = 16 * blk + ii;
+                                 return X[i2 * DP + cc] * fast_exp(sG[m * GD + cc] - sG[i2 * GD + cc]);
+                             });
             } else {
                 const int bn = 16 * blk + 15, mi = 16 * blk + li;
                 if (blk < 3)
@@ -1143,11 +1194,53 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                                  const int rr = bn + 1 + r;
                                  return X[rr * DP + cc] * fast_exp(sG[rr * GD + cc] - sG[bn * GD + cc]);
                              });
-                tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
-                         [&](int r) {
-                             const int rr = 16 * blk + r;
-                             return X[rr * DP + cc] * fast_exp(sG[rr * GD + cc] - sG[m * GD + cc]);
-                         });
+                if (!wide)
+                    tile_f32(dia, 16, lane, [&](int r) { return M[(16 * blk + r) * AP + mi]; },
+                             [&](int r) {
+                                 const int rr = 16 * blk + r;
+                                 return X[rr * DP + cc] * fast_exp(sG[rr * GD + cc] - sG[m * GD + cc]);
+                             });
+            }
+            if (wide) {
+                // the diagonal block level by level, each level's factors applied in full
+                // (dia then holds the finished contribution of the block), plus M's diagonal
+                const int b0 = 16 * blk;
+                for (int lev = 0; lev < 4; ++lev) {
+                    const int sz = 16 >> lev, hs = sz >> 1, msk = sz - 1;
+                    auto pair = [&](int r, int c) {
+                        return (r & ~msk) == (c & ~msk) && (r & msk) >= hs && (c & msk) < hs;
+                    };
+                    auto anc = [&](int x) { return b0 + (x & ~msk) + hs; };  // anchor of local row x
+                    floatx4 lv = zero4();
+                    if (!col) {
+                        tile_f32(lv, 16, lane, [&](int k) { return pair(li, k) ? M[(b0 + li) * AP + b0 + k] : 0.f; },
+                                 [&](int k) {
+                                     return (k & msk) < hs
+                                                ? X[(b0 + k) * DP + cc] * fast_exp(sG[anc(k) * GD + cc] - sG[(b0 + k) * GD + cc])
+                                                : 0.f;
+                                 });
+                    } else {
+                        tile_f32(lv, 16, lane, [&](int k) { return pair(k, li) ? M[(b0 + k) * AP + b0 + li] : 0.f; },
+                                 [&](int k) {
+                                     return (k & msk) >= hs
+                                                ? X[(b0 + k) * DP + cc] * fast_exp(sG[(b0 + k) * GD + cc] - sG[anc(k) * GD + cc])
+                                                : 0.f;
+                                 });
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int x = 4 * gq + r;  // output row (row form) or column (col form) of the block
+                        const bool keep = col ? (x & msk) < hs : (x & msk) >= hs;
+                        const float f = col ? fast_exp(sG[anc(x) * GD + cc] - sG[(b0 + x) * GD + cc])
+                                            : fast_exp(sG[(b0 + x) * GD + cc] - sG[anc(x) * GD + cc]);
+                        dia[r] += keep ? lv[r] * f : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = b0 + 4 * gq + r;
+                    dia[r] += M[row * AP + row] * X[row * DP + cc];
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1155,10 +1248,10 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
                 const float g = sG[row * GD + cc];
                 float y;
                 if (!col) {
-                    y = dia[r] * fast_exp(g - sG[m * GD + cc]);
+                    y = wide ? dia[r] : dia[r] * fast_exp(g - sG[m * GD + cc]);
                     if (blk > 0) y += off[r] * fast_exp(g - sG[16 * blk * GD + cc]);
                 } else {
-                    y = dia[r] * fast_exp(sG[m * GD + cc] - g);
+                    y = wide ? dia[r] : dia[r] * fast_exp(sG[m * GD + cc] - g);
                     if (blk < 3) y += off[r] * fast_exp(sG[(16 * blk + 15) * GD + cc] - g);
                 }
                 if (form == 0) {

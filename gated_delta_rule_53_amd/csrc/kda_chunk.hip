@@ -297,15 +297,25 @@ __device__ __forceinline__ void put2<float>(float* dst, float a, float b) {
 // then below 1/256, the partner operand may be an fp16 subnormal, and that
 // operand's absolute rounding error times the large factor would no longer be
 // negligible next to the entry being formed (it stays below 2^-17 of |k_r k_i|).
+// With fp32 operands (fp32 inputs) only the range matters: a factor up to 2^64
+// keeps its partner's absolute error below 2^64 times the smallest subnormal.
+// Past either limit the sub-blocks are formed in the multi-level form below,
+// whose factors never exceed 1, so no gate value is out of range.
 constexpr float F16_OPERAND_LIMIT = 6.0e4f;
 constexpr float F16_FACTOR_LIMIT = 256.f;
+constexpr float F32_FACTOR_LIMIT = 1.8446744e19f;  // 2^64
 
-template <int D, typename IT, typename OT, bool QKN, bool GPRE>
-__global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
+// The chunk-local work of one workgroup.  WIDE = false: the diagonal sub-blocks in
+// the single-anchor form; it returns false, before storing anything, when their
+// factors leave that form's range (uniformly over the workgroup).  WIDE = true:
+// the multi-level form, valid for every gate.  The kernel runs the second only
+// after the first declined, so the rarely taken form adds nothing to the
+// registers of the common one.
+template <int D, typename IT, typename OT, bool QKN, bool GPRE, bool WIDE>
+__device__ __forceinline__ bool chunk_local_body(const ChunkArgs& a, unsigned char* smem, int bx, int by, int tid) {
     using C = LocalCfg<D, OT>;
     using R = Rec<D, OT>;
     using FO = FragOrder<OT>;
-    __shared__ __align__(16) unsigned char smem[C::SMEM];
     OT* sOp = reinterpret_cast<OT*>(smem);
     float* sOp32 = reinterpret_cast<float*>(smem);
     float* sT = reinterpret_cast<float*>(smem);
@@ -318,11 +328,11 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     OT* sP = reinterpret_cast<OT*>(smem + C::R2);
     float* sBeta = reinterpret_cast<float*>(smem + C::R3);
 
-    const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc;
+    const int h = bx, s = by / a.Wc, jl = by % a.Wc;
     int64_t tb, L;
     seq_bounds(a, s, tb, L);
     const int64_t c0 = (int64_t)(a.win * a.Wc + jl) * CH;
-    if (c0 >= L) return;  // whole workgroup: no chunk here
+    if (c0 >= L) return true;  // whole workgroup: no chunk here
     const int n = (int)min<int64_t>(CH, L - c0);
     const int64_t tok0 = tb + c0;
     const int H = a.H;
@@ -331,7 +341,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     const IT* k = static_cast<const IT*>(a.k);
     const IT* v = static_cast<const IT*>(a.v);
 
-    const int t = threadIdx.x;
+    const int t = tid;
     // the wave index is uniform: held in a scalar register, loop bounds and tile
     // indices derived from it stay off the vector ALU
     const int lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -443,7 +453,9 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     lds_barrier();
 
     // per-channel products over blocks, half-blocks and anchors
-    float PB[4][2], A0[4][2], E[2], Sfx[2], HPo[2], HP0[2], L7[2], A8[2];
+    // (gam, the whole chunk's decay, and the record stores' starting factors Fs and Ks
+    // are formed here, so the products they come from need not stay live to the end)
+    float PB[4][2], A0[4][2], E[2], Sfx[2], HPo[2], HP0[2], L7[2], A8[2], gam[2], Fs[2], Ks[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
 #pragma unroll
@@ -458,10 +470,15 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
             if (x < b) E[e] *= PB[x][e];
             if (x > b) Sfx[e] *= PB[x][e];
         }
+        gam[e] = ((PB[0][e] * PB[1][e]) * PB[2][e]) * PB[3][e];
         HPo[e] = sX[(2 * b + 1 - hh) * D + ch + e];  // the other half of this block
         HP0[e] = sX[(2 * b) * D + ch + e];           // the first half of this block
         L7[e] = sX[(16 + 2 * b) * D + ch + e];       // prod_{1..7} of the first half
         A8[e] = sX[(8 + 2 * b + 1) * D + ch + e];    // gate of the block's row 8
+        // what the record stores need at the end: e^{G} of the row before this
+        // thread's first, and e^{G_last - G} of its last row over the later rows
+        Fs[e] = E[e] * (hh ? HP0[e] : 1.f);
+        Ks[e] = Sfx[e] * (hh ? 1.f : HPo[e]);
     }
     const float* bb = sBeta + r0;  // beta of this thread's rows (LDS broadcast reads)
     lds_barrier();                 // sX is overwritten by the operands below
@@ -575,40 +592,46 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
             visit(i, f[0], f[1]);
         }
     };
-    int wide = 0;
-    if (C::F16) {
-        // bound on every diagonal operand of this thread: the largest |k|, |q| and
-        // |beta| over its rows times the largest row and column factors
-        float km[2] = {0.f, 0.f}, qm[2] = {0.f, 0.f}, sb = 1.f, dlm[2] = {0.f, 0.f}, drm[2] = {0.f, 0.f};
+    const int rowB = 16 * b + ib0;  // first row of this thread in [0, 64)
+    if constexpr (!WIDE) {
+        // Range check of the single-anchor form: the largest row and column factors
+        // (and, for fp16 operands, every operand's bound: the largest |k|, |q| and
+        // |beta| over the thread's rows times those factors).  A zero gate can make a
+        // factor infinite, and a later one in the same chain infinite times zero, but
+        // the infinity comes first and already sets the maximum.
+        int wide;
+        {
+            float km[2] = {0.f, 0.f}, qm[2] = {0.f, 0.f}, sb = 1.f, dlm[2] = {0.f, 0.f}, drm[2] = {0.f, 0.f};
+            if (C::F16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+                for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        km[e] = fmaxf(km[e], fabsf(kk.get(i, e)));
+                        qm[e] = fmaxf(qm[e], fabsf(qq.get(i, e)));
+                    }
+                    sb = fmaxf(sb, fabsf(bb[i]));
+                }
+            }
+            dl_rows([&](int, float f0, float f1) {
+                dlm[0] = fmaxf(dlm[0], f0);
+                dlm[1] = fmaxf(dlm[1], f1);
+            });
+            dr_rows([&](int, float f0, float f1) {
+                drm[0] = fmaxf(drm[0], f0);
+                drm[1] = fmaxf(drm[1], f1);
+            });
+            float mx = 0.f, fx = 0.f;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                km[e] = fmaxf(km[e], fabsf(kk.get(i, e)));
-                qm[e] = fmaxf(qm[e], fabsf(qq.get(i, e)));
+                mx = fmaxf(mx, fmaxf(fmaxf(km[e], qm[e]) * sb * dlm[e], km[e] * drm[e]));
+                fx = fmaxf(fx, fmaxf(dlm[e], drm[e]));
             }
-            sb = fmaxf(sb, fabsf(bb[i]));
+            wide = C::F16 ? __syncthreads_or(!(mx <= F16_OPERAND_LIMIT) || !(fx <= F16_FACTOR_LIMIT))
+                          : __syncthreads_or(!(fx <= F32_FACTOR_LIMIT));
         }
-        dl_rows([&](int, float f0, float f1) {
-            dlm[0] = fmaxf(dlm[0], f0);
-            dlm[1] = fmaxf(dlm[1], f1);
-        });
-        dr_rows([&](int, float f0, float f1) {
-            drm[0] = fmaxf(drm[0], f0);
-            drm[1] = fmaxf(drm[1], f1);
-        });
-        float mx = 0.f, fx = 0.f;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            mx = fmaxf(mx, fmaxf(fmaxf(km[e], qm[e]) * sb * dlm[e], km[e] * drm[e]));
-            fx = fmaxf(fx, fmaxf(dlm[e], drm[e]));
-        }
-        wide = __syncthreads_or(!(mx <= F16_OPERAND_LIMIT) || !(fx <= F16_FACTOR_LIMIT));
-    } else {
-        __syncthreads();
-    }
-    const int rowB = 16 * b + ib0;  // first row of this thread in [0, 64)
-    if (!wide) {
+        if (wide) return false;
+
         dl_rows([&](int i, float dl0, float dl1) {
             put2<OT>(sOp + (rowB + i) * C::DP + ch, bb[i] * kk.get(i, 0) * dl0, bb[i] * kk.get(i, 1) * dl1);
             put2<OT>(sOp + (64 + rowB + i) * C::DP + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
@@ -634,37 +657,83 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
         __syncthreads();
     } else {
-        // fp16 would overflow: fp32 operands, two blocks at a time
+        // Multi-level form (fp32 operands, two blocks at a time).  A pair (r, i),
+        // i < r, of a diagonal block is formed at the level where r and i first
+        // fall into different halves of an aligned sub-block of sz = 16, 8, 4, 2
+        // rows.  The anchor is that sub-block's middle row m (the first row of its
+        // later half): row r carries prod_{m < t <= r} alpha_t, column i carries
+        // prod_{i < t <= m} alpha_t, both at most 1, so no gate is out of range.
+        // Each level's product is kept only at its own pairs; the first level
+        // also clears the rest of the block.  A last level (sz = 1) forms P's
+        // diagonal, whose factor is 1.
+#pragma unroll 1
+        for (int lev = 0; lev < 5; ++lev) {
+            const bool dg = lev == 4;
+            const int sz = dg ? 1 : 16 >> lev, hs = sz >> 1, msk = sz - 1;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            if ((b >> 1) == half) {
-                const int rr0 = 16 * (b & 1) + ib0;
-                dl_rows([&](int i, float dl0, float dl1) {
-                    put2<float>(sOp32 + (rr0 + i) * C::DP32 + ch, bb[i] * kk.get(i, 0) * dl0,
-                                bb[i] * kk.get(i, 1) * dl1);
-                    put2<float>(sOp32 + (32 + rr0 + i) * C::DP32 + ch, qq.get(i, 0) * dl0, qq.get(i, 1) * dl1);
-                });
-                dr_rows([&](int i, float dr0, float dr1) {
-                    put2<float>(sOp32 + (64 + rr0 + i) * C::DP32 + ch, kk.get(i, 0) * dr0, kk.get(i, 1) * dr1);
-                });
-            }
-            __syncthreads();
-            for (int p = wave; p < 4; p += C::NW) {
-                const int hbk = p & 1, db = 2 * half + hbk;
-                floatx4 acc = zero4();
-                mma_tile<float>(acc, sOp32 + ((p < 2 ? 0 : 32) + 16 * hbk) * C::DP32, C::DP32,
-                                sOp32 + (64 + 16 * hbk) * C::DP32, C::DP32, D, lane);
+            for (int half = 0; half < 2; ++half) {
+                if ((b >> 1) == half) {
+                    // Level 0 splits the block at its row 8: this thread's rows are the
+                    // later half when hh = 1, the earlier half when hh = 0, and the earlier
+                    // rows' anchor gate is that of the block's row 8 (another thread's row).
+                    // Deeper levels split inside the thread's eight rows.
+                    const int rr0 = 16 * (b & 1) + ib0;
+                    float f0 = 1.f, f1 = 1.f;  // row factor, ascending
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int lr = 4 * gq + r;
-                    const int row = 16 * db + lr, col = 16 * db + li;
-                    if (p < 2)
-                        sAt[row * C::AP + col] = acc[r];
-                    else
-                        sP[row * CH + col] = from_f32<OT>(lr >= li ? acc[r] : 0.f);
+                    for (int i = 0; i < 8; ++i) {
+                        const bool start = dg || (lev == 0 ? i == 0 : (i & msk) == hs);  // the anchor row
+                        const bool later = dg || (lev == 0 ? hh == 1 : (i & msk) >= hs);
+                        if (i > 0) {
+                            f0 = start ? 1.f : f0 * al[i][0];
+                            f1 = start ? 1.f : f1 * al[i][1];
+                        }
+                        const float m0 = later ? f0 : 0.f, m1 = later ? f1 : 0.f;
+                        put2<float>(sOp32 + (rr0 + i) * C::DP32 + ch, bb[i] * kk.get(i, 0) * m0,
+                                    bb[i] * kk.get(i, 1) * m1);
+                        put2<float>(sOp32 + (32 + rr0 + i) * C::DP32 + ch, qq.get(i, 0) * m0, qq.get(i, 1) * m1);
+                    }
+                    float g0 = 1.f, g1 = 1.f;  // column factor, descending
+#pragma unroll
+                    for (int i = 7; i >= 0; --i) {
+                        const bool last = lev == 0 ? i == 7 : (i & msk) == hs - 1;  // the row before the anchor
+                        const bool earlier = lev == 0 ? hh == 0 : (i & msk) < hs;
+                        // the gate of the block's row 8 is DR7 in the threads with hh = 0, the
+                        // only ones whose level-0 column operands are kept
+                        const float a0 = i == 7 ? DR7[0] : al[i < 7 ? i + 1 : 7][0];
+                        const float a1 = i == 7 ? DR7[1] : al[i < 7 ? i + 1 : 7][1];
+                        g0 = last ? a0 : g0 * a0;
+                        g1 = last ? a1 : g1 * a1;
+                        const float c0 = dg ? 1.f : (earlier ? g0 : 0.f), c1 = dg ? 1.f : (earlier ? g1 : 0.f);
+                        put2<float>(sOp32 + (64 + rr0 + i) * C::DP32 + ch, kk.get(i, 0) * c0, kk.get(i, 1) * c1);
+                    }
                 }
+                __syncthreads();
+                for (int p = dg ? wave + 2 : wave; p < 4; p += C::NW) {  // the diagonal: P only
+                    const int hbk = p & 1, db = 2 * half + hbk;
+                    floatx4 acc = zero4();
+                    // a short unroll: this rare path must not raise the kernel's register peak
+                    const float* pa = sOp32 + ((p < 2 ? 0 : 32) + 16 * hbk + li) * C::DP32 + gq;
+                    const float* pb = sOp32 + (64 + 16 * hbk + li) * C::DP32 + gq;
+#pragma unroll 4
+                    for (int k0 = 0; k0 < D; k0 += 4)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0], pb[k0], acc, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int lr = 4 * gq + r;
+                        const bool pair = dg ? lr == li
+                                             : (lr & ~msk) == (li & ~msk) && (lr & msk) >= hs && (li & msk) < hs;
+                        const int row = 16 * db + lr, col = 16 * db + li;
+                        if (pair || lev == 0) {
+                            const float x = pair ? acc[r] : 0.f;
+                            if (p < 2)
+                                sAt[row * C::AP + col] = x;
+                            else
+                                sP[row * CH + col] = from_f32<OT>(x);
+                        }
+                    }
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 
@@ -834,7 +903,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     for (int i = 0; i < 8; ++i)
         if (r0 + i >= n) vv.zero(i);
     {
-        float F[2] = {E[0] * (hh ? HP0[0] : 1.f), E[1] * (hh ? HP0[1] : 1.f)};  // e^{G} of the row before
+        float F[2] = {Fs[0], Fs[1]};  // e^{G} of the row before
         float x0[8], x1[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -889,7 +958,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
     }
     {
         // Qg: the two channels of a row are adjacent in fragment order (ch is even)
-        float F[2] = {E[0] * (hh ? HP0[0] : 1.f), E[1] * (hh ? HP0[1] : 1.f)};
+        float F[2] = {Fs[0], Fs[1]};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             F[0] *= al[i][0];
@@ -904,7 +973,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
         // Kh^T: 8 consecutive tokens of one channel are contiguous in fragment order (fp16)
         float x0[8], x1[8];
-        float Rb[2] = {Sfx[0] * (hh ? 1.f : HPo[0]), Sfx[1] * (hh ? 1.f : HPo[1])};  // e^{G_last - G_i}
+        float Rb[2] = {Ks[0], Ks[1]};  // e^{G_last - G_i}
 #pragma unroll
         for (int i = 7; i >= 0; --i) {
             if (i < 7) {
@@ -926,7 +995,7 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         }
         if (hb == 0)
             *reinterpret_cast<float2*>(rG + ch) =
-                make_float2(((PB[0][0] * PB[1][0]) * PB[2][0]) * PB[3][0], ((PB[0][1] * PB[1][1]) * PB[2][1]) * PB[3][1]);
+                make_float2(gam[0], gam[1]);
     }
     for (int f = t; f < CH * CH / FO::KE; f += C::NT) {  // P: one lane slot of one fragment per step
         const int l = f & 63, kk2 = (f >> 6) % (CH / FO::KS), rt = (f >> 6) / (CH / FO::KS);
@@ -937,6 +1006,76 @@ __global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4)))
         else
             dst[0] = src[0];
     }
+    return true;
+}
+
+// A chunk whose single-anchor factors leave their range is marked in its
+// record with an impossible decay (gamma[0] = -1) and formed by the next kernel.
+constexpr float WIDE_MARK = -1.f;
+
+template <int D, typename IT, typename OT, bool QKN, bool GPRE>
+__global__ void __launch_bounds__(4 * D) __attribute__((amdgpu_waves_per_eu(4))) chunk_local_kernel(ChunkArgs a) {
+    __shared__ __align__(16) unsigned char smem[LocalCfg<D, OT>::SMEM];
+    if (!chunk_local_body<D, IT, OT, QKN, GPRE, false>(a, smem, blockIdx.x, blockIdx.y, threadIdx.x) &&
+        threadIdx.x == 0) {
+        const int s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc;
+        unsigned char* rec = a.rec + ((size_t)(s * a.Wc + jl) * a.H + blockIdx.x) * a.rec_bytes;
+        reinterpret_cast<float*>(rec + Rec<D, OT>::GAM)[0] = WIDE_MARK;
+    }
+}
+
+// The chunks chunk_local_kernel declined, in the multi-level form.  A kernel of
+// its own, so the common form keeps its registers.  Workgroup w takes a
+// contiguous range of at most 4 D (its thread count) chunk slots of the window,
+// slot = (sequence, chunk in window, head); every thread reads one slot's mark,
+// and the workgroup then forms the marked chunks one after another.
+template <int D, typename IT, typename OT, bool QKN, bool GPRE>
+__global__ void __launch_bounds__(4 * D) chunk_local_wide_kernel(ChunkArgs a, int per_wg) {
+    constexpr int NT = 4 * D;
+    __shared__ __align__(16) unsigned char smem[LocalCfg<D, OT>::SMEM];
+    __shared__ int marked[NT];
+    __shared__ int nmarked;
+    const int t = threadIdx.x;
+    const int64_t slots = (int64_t)a.N * a.Wc * a.H;
+    const int64_t first = (int64_t)blockIdx.x * per_wg;
+    if (t == 0) nmarked = 0;
+    __syncthreads();
+    if (t < per_wg && first + t < slots) {
+        const int64_t slot = first + t;
+        const int h = (int)(slot % a.H), y = (int)(slot / a.H);  // y = s * Wc + jl
+        const int s = y / a.Wc, jl = y % a.Wc;
+        int64_t tb, L;
+        seq_bounds(a, s, tb, L);
+        // a slot past its sequence's end was not written this window: not a chunk
+        if ((int64_t)(a.win * a.Wc + jl) * CH < L) {
+            const unsigned char* rec = a.rec + (size_t)slot * a.rec_bytes;
+            if (reinterpret_cast<const float*>(rec + Rec<D, OT>::GAM)[0] == WIDE_MARK)
+                marked[atomicAdd(&nmarked, 1)] = (int)(slot - first);
+        }
+    }
+    __syncthreads();
+    const int n = nmarked;
+    for (int i = 0; i < n; ++i) {
+        const int64_t slot = first + marked[i];
+        chunk_local_body<D, IT, OT, QKN, GPRE, true>(a, smem, (int)(slot % a.H), (int)(slot / a.H), t);
+        __syncthreads();  // smem is reused by the next marked chunk
+    }
+}
+
+// Both chunk-local kernels over one window (or every chunk).
+template <int D, typename IT, typename OT, bool QKN, bool GPRE>
+static hipError_t launch_local(const ChunkArgs& a, hipStream_t st) {
+    using C = LocalCfg<D, OT>;
+    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // at most 256 workgroups (one per compute unit), each over a contiguous range of slots
+    const int64_t slots = (int64_t)a.N * a.Wc * a.H;
+    const int per_wg = (int)std::min<int64_t>(C::NT, std::max<int64_t>(1, (slots + 255) / 256));
+    const int64_t wgs = (slots + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL((chunk_local_wide_kernel<D, IT, OT, QKN, GPRE>), dim3((unsigned)wgs), dim3(C::NT), 0, st, a,
+                       per_wg);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -1442,10 +1581,8 @@ static hipError_t run_windows(const ChunkArgs& base, int nwin, hipStream_t st) {
     for (int w = 0; w < nwin; ++w) {
         ChunkArgs a = base;
         a.win = w;
-        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(base.H, base.N * base.Wc), dim3(C::NT), 0, st,
-                           a);
         hipError_t e;
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_local<D, IT, OT, QKN, GPRE>(a, st)) != hipSuccess) return e;
         hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT>), dim3(units * (D / BV)), dim3(512), 0, st, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1476,8 +1613,7 @@ static hipError_t run_segments(const ChunkArgs& a, hipStream_t st) {
     constexpr int BV = SEGMENT_BV;
     const int NH = a.N * a.H;
     hipError_t e;
-    hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, QKN, GPRE>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_local<D, IT, OT, QKN, GPRE>(a, st)) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_inter_kernel<D, BV, OT, OUT, 1>), dim3(NH * 2 * (D / BV) * a.G), dim3(512), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((chunk_segment_combine_kernel<D>), dim3(NH, D / 16), dim3(256), 0, st, a);
@@ -1547,9 +1683,7 @@ static hipError_t run_snapshots(const ChunkArgs& base, int window, int w0, int n
         a.Wc = window;
         a.win = w;
         a.out = nullptr;
-        hipLaunchKernelGGL((chunk_local_kernel<D, IT, OT, false, false>), dim3(a.H, a.N * a.Wc), dim3(C::NT), 0, st,
-                           a);
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_local<D, IT, OT, false, false>(a, st);
         if (e != hipSuccess) return e;
         if (snap)
             hipLaunchKernelGGL((chunk_inter_kernel<D, 16, OT, float, 0, true>), dim3(a.N * a.H * (D / 16)), dim3(512),

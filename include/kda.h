@@ -37,8 +37,10 @@
  *  - Supported head dims: dk == dv, and dk in {64, 128}.  q/k/v dtype is
  *    fp32 or bf16; log_alpha and beta are always fp32; out is fp32 or bf16.
  *  - Preconditions not checked on the device: log_alpha finite and <= 0
- *    (the chunked path also needs log_alpha >= -10 per token so that
- *    within-chunk decay ratios stay inside fp32 range); beta finite;
+ *    (any such value: a chunk whose decay ratios would leave the range of the
+ *    common single-anchor form is formed in a multi-level form whose factors are
+ *    all at most 1; the backward's fp32-input precision degrades in proportion to
+ *    the cumulative log decay inside a 64-token chunk past about 100); beta finite;
  *    cu_seqlens non-decreasing with cu_seqlens[0] = 0 and
  *    cu_seqlens[N] = total tokens, and no sequence longer than max_seqlen.
  *    With the environment variable KDA_CHECK=1, kda_chunk_fwd copies
@@ -173,8 +175,7 @@ kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk,
  *   l2_eps       >= 0 (with 0, an all-zero q or k row gives non-finite results)
  *   gate         required, bf16 gate pre-activation g (the projection output),
  *                [.., H, dk], or [.., H] when gate_per_head = 1; it replaces
- *                log_alpha: log alpha = -softplus(g).  The chunked path needs
- *                g <= 10 (log alpha >= -10 per token).
+ *                log_alpha: log alpha = -softplus(g), any finite g.
  *   out_gate     bf16 [.., H, dv] output-gate pre-activation z, or NULL for no
  *                epilogue (the output is then o itself)
  *   norm_weight  fp32 [dv] RMSNorm weight shared by the heads, or NULL (ones)

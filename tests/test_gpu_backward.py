@@ -75,6 +75,41 @@ def check(g, ref, tol):
         assert_close(gk, got, ref[rk], tol)
 
 
+def check_terms_scale(g, ref, d, dF, tol, bf16):
+    """check() for gates past any floor, with two gradients measured against the terms they
+    are formed from rather than their own RMS, which the strong gates make vanish:
+
+    * dlog_alpha is a reverse cumulative sum of q o dq and k o dk terms that cancel where the
+      gates are strong (at log alpha = -30 per token its RMS is ~1e-14 against terms of order
+      1), so its max error is taken over max(RMS(dlog_alpha), RMS(q o dq), RMS(k o dk));
+    * with bf16 inputs the reverse chain takes fp16 operands, which cannot hold contributions
+      below fp16's smallest subnormal (2^-24) of their scale: d_init, which strong gates
+      shrink to ~1e-13, is measured against max(RMS(d_init), 2^-20 RMS(d_final)).
+
+    Every other gradient keeps the plain bar (oracle values throughout)."""
+    rms = lambda x: float(np.sqrt(np.mean(np.square(x)))) if np.size(x) else 0.0
+
+    def bounded(name, got, ref_x, scale):
+        got = np.asarray(got, np.float64)
+        assert np.isfinite(got).all(), f"{name}: non-finite values"
+        err = float(np.max(np.abs(got - ref_x))) if got.size else 0.0
+        assert err <= tol * scale, f"{name}: max|err| {err:.3e} > {tol:.1e} x {scale:.3e}"
+
+    for gk, rk in KEYS:
+        got = g[gk][0] if gk not in ("d_init",) else g[gk]
+        if gk == "dlog_alpha":
+            q, k = synth.as_f64(d["q"]), synth.as_f64(d["k"])
+            if ref[rk].ndim == 2:  # one gate per head: the sums over the key channels
+                terms = max(rms((q * ref["dq"]).sum(-1)), rms((k * ref["dk"]).sum(-1)))
+            else:
+                terms = max(rms(q * ref["dq"]), rms(k * ref["dk"]))
+            bounded(gk, got, ref[rk], max(rms(ref[rk]), terms))
+        elif gk == "d_init" and bf16:
+            bounded(gk, got, ref[rk], max(rms(ref[rk]), 2.0 ** -20 * rms(dF)))
+        else:
+            assert_close(gk, got, ref[rk], tol)
+
+
 @pytest.mark.parametrize("T,H,D,dtype,lens,gate", [
     (130, 2, 64, "f32", None, "channel"),
     (200, 2, 128, "bf16", None, "channel"),
@@ -104,6 +139,76 @@ def test_backward_strong_decay(kda):
     dO, dF = _grads(72, d)
     g = run_bwd(kda, d, dO, dF)
     check(g, oracle_bwd(d, dO, dF), TOL["bf16"])
+
+
+def _wide_gates(kind, shape, rng):
+    """log alpha past any floor: uniform -30, channels split between -0.01 and -60, a draw
+    uniform in [-20, 0] per token, and the more extreme draws of the precision test below."""
+    if kind == "uniform30":
+        return np.full(shape, -30.0, np.float32)
+    if kind == "mixed":
+        la = np.full(shape, -0.01, np.float32)
+        la[..., 1::2] = -60.0
+        return la
+    if kind == "wild20":
+        return (-20.0 * rng.random(shape)).astype(np.float32)
+    if kind == "wild200":
+        return (-200.0 * rng.random(shape)).astype(np.float32)
+    la = (-0.05 * rng.random(shape)).astype(np.float32)  # "spikes"
+    la[5::64] = -1.0e4
+    la[37::64, :, ::3] = -80.0
+    return la
+
+
+def chunk_decay_max(d, chunk=64):
+    """G*: the largest |sum of log alpha| over the tokens of one 64-token chunk (per sequence,
+    head and channel) -- the magnitude of the backward's prefix sums G inside a chunk."""
+    la = np.asarray(d["log_alpha"], np.float64)
+    cu = d["cu_seqlens"]
+    best = 0.0
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        for c0 in range(int(s0), int(s1), chunk):
+            best = max(best, float(np.max(np.abs(la[c0:min(c0 + chunk, int(s1))].sum(axis=0)))))
+    return best
+
+
+def fp32_bar(d):
+    """The backward's bar with fp32 inputs: its decay factors are exponentials of differences of
+    fp32 prefix sums G, so each exponent carries up to about ulp(G*) ~ 2^-23 G*, and the sums a
+    gradient is formed from cancel by a few times more; the bar is max(1e-4, 2^-20 G*) -- the
+    plain bar up to G* of about 100 (a chunk-local decay of e^-100), in proportion beyond it."""
+    return max(TOL["f32"], 2.0 ** -20 * chunk_decay_max(d))
+
+
+def _run_wide(kda, kind, dtype, seed):
+    d = random_small(seed, 0, 2, 128, 128, dtype=dtype, init_std=0.5, lens=[200, 64, 1, 135])
+    d["log_alpha"] = _wide_gates(kind, d["log_alpha"].shape, np.random.default_rng(9))
+    dO, dF = _grads(seed + 50, d)
+    return d, dF, run_bwd(kda, d, dO, dF), oracle_bwd(d, dO, dF)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["uniform30", "mixed", "wild20", "wild200", "spikes"])
+def test_backward_full_gate_domain(kda, kind, dtype):
+    """Every gradient with gates past any floor (uniform -30; channels at -0.01 and -60; uniform
+    in [-20, 0] and [-200, 0] per token; one token per chunk at -1e4): the diagonal blocks whose
+    single-anchor exponents pass the limit are formed level by level (every exponent <= 0).
+    Bars: 2e-2 with bf16 inputs; with fp32 inputs fp32_bar (1e-4 up to a chunk-local cumulative
+    decay of about 100, then in proportion to it)."""
+    seed = {"uniform30": 601, "mixed": 603, "wild20": 605, "wild200": 621, "spikes": 623}[kind] + (dtype == "bf16")
+    d, dF, g, ref = _run_wide(kda, kind, dtype, seed)
+    check_terms_scale(g, ref, d, dF, TOL["bf16"] if dtype == "bf16" else fp32_bar(d), dtype == "bf16")
+
+
+def test_backward_full_gate_domain_d64_head_gate(kda):
+    """The same at d = 64 and with one gate per head, gates uniform in [-20, 0] per token."""
+    for gate, dtype in (("channel", "f32"), ("head", "bf16"), ("head", "f32")):
+        d = random_small(411, 0, 3, 64, 64, dtype=dtype, init_std=0.5, lens=[130, 77], gate=gate)
+        d["log_alpha"] = (-20.0 * np.random.default_rng(4).random(d["log_alpha"].shape)).astype(np.float32)
+        dO, dF = _grads(412, d)
+        g = run_bwd(kda, d, dO, dF)
+        check_terms_scale(g, oracle_bwd(d, dO, dF), d, dF, TOL["bf16"] if dtype == "bf16" else fp32_bar(d),
+                          dtype == "bf16")
 
 
 def test_backward_workload1(kda):

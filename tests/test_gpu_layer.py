@@ -105,9 +105,11 @@ def test_layer_prefill(kda, T, H, D, dtype, lens, gate, epi, out):
     assert_close("state", S, S_ref, TOL[dtype])
 
 
-@pytest.mark.parametrize("mu", [-6.0, 0.5, 2.5])
+@pytest.mark.parametrize("mu", [-6.0, 0.5, 2.5, 15.0, 100.0])
 def test_layer_prefill_gate_range(kda, mu):
-    """Gate pre-activations from weak (log alpha ~ -2.5e-3) to strong (~ -2.6 per token)."""
+    """Gate pre-activations from weak (log alpha ~ -2.5e-3) to strong (~ -2.6 per token), and
+    past any floor: g ~ 15 (log alpha ~ -15, the diagonal sub-blocks in the multi-level form)
+    and g ~ 100 (alpha = 1 / (1 + e^g) is 0 in fp32: the state forgets everything each token)."""
     d = layer_small(31, 260, 2, 128, 128, dtype="bf16", gate_mu=mu)
     y, S = run_layer(kda, d)
     _, S_ref, o_ref = oracle_layer(d)

@@ -116,7 +116,7 @@ def test_chunk_strong_decay(kda):
     assert_close("state", S, S_ref, TOL["bf16"])
 
 
-@pytest.mark.parametrize("la", [-10.0, -1.5, -1.2, -0.8, -0.6, -0.05])
+@pytest.mark.parametrize("la", [-50.0, -20.0, -11.0, -10.0, -1.5, -1.2, -0.8, -0.6, -0.05])
 def test_chunk_diagonal_operand_range(kda, la):
     """Uniform gates across the range of the diagonal-block factors (up to e^{8|la|} over
     eight rows): from -0.8 on they exceed what fp16 operands carry accurately (at -1.2
@@ -128,6 +128,48 @@ def test_chunk_diagonal_operand_range(kda, la):
     o_ref, S_ref = oracle_chunk(d)
     assert_close("out", o, o_ref, TOL["bf16"])
     assert_close("state", S, S_ref, TOL["bf16"])
+
+
+def _gates(kind, shape, rng):
+    """Gate layouts past any floor on log alpha: uniform -30, channels split between -0.01 and
+    -60, a draw up to -200 per token, and mild gates with one token per chunk near zero alpha."""
+    if kind == "uniform30":
+        return np.full(shape, -30.0, np.float32)
+    if kind == "mixed":
+        la = np.full(shape, -0.01, np.float32)
+        la[..., 1::2] = -60.0
+        return la
+    if kind == "wild":
+        return (-200.0 * rng.random(shape)).astype(np.float32)
+    la = (-0.05 * rng.random(shape)).astype(np.float32)  # "spikes"
+    la[5::64] = -1.0e4
+    la[37::64, :, ::3] = -80.0
+    return la
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["uniform30", "mixed", "wild", "spikes"])
+def test_chunk_full_gate_domain(kda, kind, dtype):
+    """Any finite log alpha <= 0: chunks whose single-anchor factors leave range are formed in
+    the multi-level form (every factor a product of gates, at most 1) and match the oracle."""
+    seed = {"uniform30": 501, "mixed": 503, "wild": 505, "spikes": 507}[kind] + (dtype == "bf16")
+    d = random_small(seed, 0, 2, 128, 128, dtype=dtype, init_std=0.5, lens=[200, 64, 1, 135])
+    d["log_alpha"] = _gates(kind, d["log_alpha"].shape, np.random.default_rng(7))
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL[dtype])
+    assert_close("state", S, S_ref, TOL[dtype])
+
+
+def test_chunk_full_gate_domain_d64_head_gate(kda):
+    """The same at d = 64 and with one gate per head (Gated DeltaNet), down to -40 per token."""
+    for gate, dtype in (("channel", "f32"), ("head", "bf16"), ("head", "f32")):
+        d = random_small(401, 0, 3, 64, 64, dtype=dtype, init_std=0.5, lens=[130, 77], gate=gate)
+        d["log_alpha"] = (-40.0 * np.random.default_rng(3).random(d["log_alpha"].shape)).astype(np.float32)
+        o, S = run_chunk(kda, torch, d)
+        o_ref, S_ref = oracle_chunk(d)
+        assert_close(f"out {gate} {dtype}", o, o_ref, TOL[dtype])
+        assert_close(f"state {gate} {dtype}", S, S_ref, TOL[dtype])
 
 
 def test_chunk_workspace_windows(kda):
