@@ -11,8 +11,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step", "workspace_size",
-           "bwd_workspace_size", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step",
+           "workspace_size", "bwd_workspace_size", "KdaError"]
 
 
 def _torch():
@@ -64,17 +64,8 @@ def bwd_workspace_size(batch, seqlen, heads, dk, dv, in_dtype, dout_dtype=None, 
     return int(lib().kda_chunk_bwd_workspace_size(shape))
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out=None,
-              out_dtype=None, final_state=True, max_seqlen=None, workspace=None):
-    """Chunked KDA prefill.
-
-    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16), log_alpha [B,T,H,dk] fp32
-    (or [B,T,H]: one gate per head shared by the key channels, the scalar gate
-    of Gated DeltaNet), beta [B,T,H] fp32; init_state [N,H,dk,dv] fp32 or None; cu_seqlens int32
-    [N+1] (GPU) or None.  ``final_state`` may be True (allocate), False/None
-    (skip) or a tensor to write into (may be ``init_state`` itself).
-    Returns (out, final_state or None).
-    """
+def _prefill_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out, out_dtype, final_state, max_seqlen):
+    """Check the prefill's tensors, allocate out / final_state if asked; returns (shape, out, final)."""
     torch = _torch()
     _check_dev(q, "q")
     B, T, H, dk = q.shape
@@ -107,6 +98,23 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
         _check_dev(final_state, "final_state", torch.float32, (N, H, dk, dv))
     shape = _lib.shape(B, T, N if cu_seqlens is not None else 0, H, dk, dv, _dtype_code(q.dtype),
                        _dtype_code(out_dtype), int(max_seqlen or 0), int(gate_per_head))
+    return shape, out, final_state
+
+
+def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out=None,
+              out_dtype=None, final_state=True, max_seqlen=None, workspace=None):
+    """Chunked KDA prefill.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (fp32 or bf16), log_alpha [B,T,H,dk] fp32
+    (or [B,T,H]: one gate per head shared by the key channels, the scalar gate
+    of Gated DeltaNet), beta [B,T,H] fp32; init_state [N,H,dk,dv] fp32 or None; cu_seqlens int32
+    [N+1] (GPU) or None.  ``final_state`` may be True (allocate), False/None
+    (skip) or a tensor to write into (may be ``init_state`` itself).
+    Returns (out, final_state or None).
+    """
+    torch = _torch()
+    shape, out, final_state = _prefill_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out, out_dtype,
+                                            final_state, max_seqlen)
     L = lib()
     need = int(L.kda_chunk_fwd_workspace_size(shape))
     if workspace is None:
@@ -117,6 +125,23 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
                          ptr(cu_seqlens), ptr(out), ptr(final_state), ptr(workspace), workspace.numel(),
                          _stream_handle(q.device))
     _lib.check(st, "kda_chunk_fwd")
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out, final_state=None,
+                      max_seqlen=None):
+    """``chunk_fwd`` without a workspace: the library's static per-device scratch of
+    ``_lib.NOALLOC_SCRATCH_BYTES`` serves instead, and nothing is allocated -- the caller
+    passes ``out`` and, if wanted, ``final_state`` (a tensor, or None to skip it).  Calls
+    overlapping in time on one device race on that scratch."""
+    if final_state is True or final_state is False:
+        raise TypeError("chunk_fwd_noalloc allocates nothing: pass final_state as a tensor or None")
+    shape, out, final_state = _prefill_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out, None,
+                                            final_state, max_seqlen)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib().kda_chunk_fwd_noalloc(shape, ptr(q), ptr(k), ptr(v), ptr(log_alpha), ptr(beta), ptr(init_state),
+                                     ptr(cu_seqlens), ptr(out), ptr(final_state), _stream_handle(q.device))
+    _lib.check(st, "kda_chunk_fwd_noalloc")
     return out, final_state
 
 

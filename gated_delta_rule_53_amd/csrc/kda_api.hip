@@ -5,6 +5,7 @@
 
 #include <stdlib.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/kda.h"
@@ -65,6 +66,37 @@ kda_status_t plan_chunk(const kda_shape_t* s, Plan& p) {
     if (s->gate_per_head != 0 && s->gate_per_head != 1) return KDA_ERR_INVALID_ARG;
     p.d = s->dk;
     return KDA_OK;
+}
+
+// Scratch of kda_chunk_fwd_noalloc: one array per device the library runs on,
+// held until the process ends.  Host code must never pass `scratch` itself to a
+// kernel (in host code the name is a stand-in, not a device address): the device
+// address is looked up once per device and kept in g_scratch.
+constexpr size_t NOALLOC_SCRATCH_BYTES = KDA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_scratch_once[MAX_DEVICES];
+void* g_scratch[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+
+// The current device's scratch address (null if the device index is out of range
+// or the lookup failed).
+void* device_scratch(hipError_t& err) {
+    int dev = -1;
+    err = hipGetDevice(&dev);
+    if (err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= MAX_DEVICES) {
+        err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    err = g_scratch_err[dev];
+    return g_scratch[dev];
 }
 
 }  // namespace
@@ -151,7 +183,8 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
 static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,
                                    const void* v, const float* log_alpha, const float* beta,
                                    const float* init_state, const int32_t* cu_seqlens, void* out,
-                                   float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                   float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                   bool static_scratch = false) {
     Plan p;
     kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p);
     if (st != KDA_OK) return st;
@@ -198,6 +231,12 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
 
     const size_t per_chunk = (size_t)p.N * H * p.rec;
     if (p.N == 0) return KDA_OK;  // nothing to compute
+    if (static_scratch) {  // kda_chunk_fwd_noalloc: the device's static array, once arguments are valid
+        if (workspace_bytes < p.state_bytes + per_chunk) return KDA_ERR_WORKSPACE;
+        hipError_t e;
+        workspace = device_scratch(e);
+        if (!workspace) return KDA_ERR_HIP;
+    }
     if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
         return KDA_ERR_WORKSPACE;
     // the workspace is written by the kernels: it must not overlap any argument
@@ -276,6 +315,13 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
                            size_t workspace_bytes, hipStream_t stream) {
     return chunk_fwd_impl(s, nullptr, q, k, v, log_alpha, beta, init_state, cu_seqlens, out, final_state,
                           workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* init_state,
+                                   const int32_t* cu_seqlens, void* out, float* final_state, hipStream_t stream) {
+    return chunk_fwd_impl(s, nullptr, q, k, v, log_alpha, beta, init_state, cu_seqlens, out, final_state, nullptr,
+                          NOALLOC_SCRATCH_BYTES, stream, /*static_scratch=*/true);
 }
 
 kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,

@@ -137,6 +137,24 @@ kda_status_t kda_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, c
                            const int32_t* cu_seqlens, void* out, float* final_state,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* kda_chunk_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, allocation-free serving loops, harnesses that forbid
+ * hipMalloc).  Arguments as for kda_chunk_fwd, without the workspace: scratch
+ * comes from a static device array of KDA_NOALLOC_SCRATCH_BYTES in the library,
+ * one per device it runs on, held until the process ends.  Nothing is allocated
+ * (no hipMalloc, hipFree or allocating library call).  The first call on a
+ * device looks up that device's array once.  Shapes whose least workspace (the
+ * state buffer when final_state is NULL, plus one chunk of records per
+ * (sequence, head)) exceeds the array return KDA_ERR_WORKSPACE.  Every call on a
+ * device uses that device's one array: calls that overlap in time on one device
+ * (other streams, other threads) race and must be serialised by the caller.  The
+ * array keeps the last call's contents; no call relies on any part of it
+ * starting at zero. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* s, const void* q, const void* k, const void* v,
+                                   const float* log_alpha, const float* beta, const float* init_state,
+                                   const int32_t* cu_seqlens, void* out, float* final_state, hipStream_t stream);
+
 /* One recurrent decode step for `batch` independent sequences ("Kimi Linear"
  * page, "Why linear attention exists": decoding is a recurrent update whose
  * cost does not depend on context length; "Kimi Delta Attention" for the

@@ -333,3 +333,20 @@ def test_binding_argument_counts_match_header(L):
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(getattr(L, name).argtypes) == len(params), name
+
+
+def test_noalloc_validation(L):
+    """kda_chunk_fwd_noalloc: the kda_chunk_fwd argument checks, and shapes whose least workspace
+    exceeds the static scratch rejected with KDA_ERR_WORKSPACE, all before any device call."""
+    call = lambda s, q=A, out=6 * A: L.kda_chunk_fwd_noalloc(s, q, 2 * A, 3 * A, 4 * A, 5 * A, None, None, out,
+                                                             None, None)
+    assert call(None) == INVALID
+    assert call(_shape(dk=96, dv=96)) == UNSUPPORTED
+    assert call(_shape(H=0)) == INVALID
+    assert call(_shape(), q=A + 4) == INVALID       # misaligned
+    assert call(_shape(), out=A + 64) == INVALID    # out over q
+    assert _lib.NOALLOC_SCRATCH_BYTES == 256 << 20
+    # 4,096 heads: one chunk of records per head is 4,096 x 74,240 bytes > 256 MiB
+    F = 1 << 40
+    big = _shape(1, 64, 0, 0, 4096, 128, 128, BF16, F32)
+    assert L.kda_chunk_fwd_noalloc(big, F, 2 * F, 3 * F, 4 * F, 5 * F, None, None, 6 * F, None, None) == WORKSPACE
