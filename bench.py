@@ -13,8 +13,10 @@ bandwidth is in ``decode``.  ``roofline`` describes the dominant kernel of a
 step (the decode kernel: 100 launches per step); ``prefill_roofline`` the
 prefill call.  ``layer`` times the fused layer (q/k L2 norm, gate from its
 projection output, RMSNorm with sigmoid output gate, bf16 y) on the same
-shapes; ``backward`` the gradients of the 64K prefill.  ``cpu_baseline`` times the fp64 oracle (test infrastructure)
-on the prefill workload (by default all of it: about 5-15 s on 16 host cores).
+shapes; ``backward`` the gradients of the 64K prefill; ``prefill_configs`` the other prefill
+workloads (4K x 32 heads, the 1M-token varlen batch, and the 64K workload with one gate per head).
+``cpu_baseline`` times the fp64 oracle (test infrastructure) on the 64K prefill (all of it, a few
+seconds on the host's cores), ``cpu_baseline_other_workloads`` on bounded samples of the others.
 """
 from __future__ import annotations
 
@@ -128,22 +130,73 @@ def traffic_from_profiles(kernel, key):
     return ent.get(key)
 
 
-def cpu_baseline(w, d, sample_tokens, threads):
+def oracle_threads(units):
+    """Host threads for the oracle: one per (sequence, head) unit, at most the 16 cores of the GPU
+    box's host share (and at most os.cpu_count())."""
+    return max(1, min(16, os.cpu_count() or 1, units))
+
+
+def cpu_baseline(w, d, sample_tokens):
     """Time the fp64 oracle on the first ``sample_tokens`` tokens of every head of workload w.
 
     ``d`` holds the workload's host inputs (the same arrays the GPU ran on).
     """
     import oracle
     n = min(sample_tokens, w.seqlen)
+    threads = oracle_threads(w.heads)
     oracle.build(force=False)
     t = time.perf_counter()
     oracle.recurrent(d["q"][:n], d["k"][:n], d["v"][:n], d["log_alpha"][:n], d["beta"][:n], d["init"],
                      threads=threads)
     dt = time.perf_counter() - t
     what = "all" if n == w.seqlen else f"the first {n} of the"
-    return {"value": n / dt, "unit": "tokens/s", "cores": min(threads, w.heads), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} {w.seqlen} tokens x {w.heads} heads of the {w.name} workload, "
                       f"fp64 token-by-token recurrence, {dt:.1f} s"}
+
+
+def cpu_baselines_other(synth, d1):
+    """The oracle on the other workloads, each on a bounded sample (seconds of host time):
+    the whole 4K x 32-head prefill; 100 decode steps of 32 of the 256 sequences (all 32 heads);
+    the 1M-token varlen batch on one of its 32 heads (all 16 sequences)."""
+    import oracle
+    from synth import WORKLOADS
+    oracle.build(force=False)
+    out = {}
+    w1 = WORKLOADS[1]
+    th = oracle_threads(w1.heads)
+    t = time.perf_counter()
+    oracle.recurrent(d1["q"], d1["k"], d1["v"], d1["log_alpha"], d1["beta"], d1["init"], threads=th)
+    dt = time.perf_counter() - t
+    out[w1.name] = {"value": w1.seqlen / dt, "unit": "tokens/s", "cores": th, "kind": "oracle",
+                    "sample": f"all {w1.seqlen} tokens x {w1.heads} heads, {dt:.2f} s"}
+    w3 = WORKLOADS[3]
+    nseq = 32
+    S = synth.make_decode_state(w3)[:nseq]
+    steps = [{x: y[:nseq] for x, y in synth.make_decode_step(w3, s).items()} for s in range(w3.steps)]
+    th = oracle_threads(nseq * w3.heads)
+    t = time.perf_counter()
+    for st in steps:
+        _, S = oracle.recurrent(st["q"], st["k"], st["v"], st["log_alpha"], st["beta"], S,
+                                np.arange(nseq + 1), threads=th)
+    dt = time.perf_counter() - t
+    updates = nseq * w3.heads * w3.steps
+    out[w3.name] = {"value": updates / dt, "unit": "sequence-head updates/s", "cores": th, "kind": "oracle",
+                    "full_step_ms": dt / w3.steps * (w3.batch / nseq) * 1e3,
+                    "sample": f"{w3.steps} steps of {nseq} of the {w3.batch} sequences x {w3.heads} heads, "
+                              f"{dt:.2f} s (full_step_ms scales it to all {w3.batch} sequences)"}
+    w4 = WORKLOADS[4]
+    d4 = synth.make_prefill(w4, heads=(0,))
+    th = oracle_threads(w4.num_seqs)
+    t = time.perf_counter()
+    oracle.recurrent(d4["q"], d4["k"], d4["v"], d4["log_alpha"], d4["beta"], d4["init"], d4["cu_seqlens"],
+                     threads=th)
+    dt = time.perf_counter() - t
+    out[w4.name] = {"value": w4.seqlen / dt, "unit": "token-heads/s", "cores": th, "kind": "oracle",
+                    "sample": f"all {w4.seqlen} tokens (16 sequences) of head 0 of {w4.heads}, {dt:.2f} s "
+                              f"(the longest sequence, {int(np.max(np.diff(d4['cu_seqlens'])))} tokens, "
+                              f"bounds the time)"}
+    return out
 
 
 def main():
@@ -160,6 +213,9 @@ def main():
     ap.add_argument("--no-layer", action="store_true",
                     help="skip the fused layer (q/k L2 norm, gate from its projection, RMSNorm-sigmoid epilogue)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward pass of the prefill")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill workloads (4K x 32, 1M varlen, one gate per head)")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the 1M-token varlen prefill")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -292,14 +348,124 @@ def main():
         "context": "pages quote up to 75% KV cache reduction and up to 6x decoding throughput at 1M context "
                    "(model level, hardware not stated)",
     }
+    d1 = None
+    if not (args.no_configs or args.prefill_only or gph):
+        del out, fin, ws
+        res["prefill_configs"], d1 = bench_prefill_configs(kda, torch, synth, args, flush, stream, q, k, v, be, init)
+        log("other prefill workloads timed")
     if not (args.no_backward or args.prefill_only or gph):
         res["backward"] = bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream)
+        log("backward timed")
     if not (args.no_layer or args.prefill_only or gph):
         res["layer"] = bench_layer(kda, torch, synth, wp, wd, args, flush, stream)
+        log("layer timed")
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        res["cpu_baseline"] = cpu_baseline(wp, d, args.cpu_sample, threads)
+        res["cpu_baseline"] = cpu_baseline(wp, d, args.cpu_sample)
+        if d1 is not None:
+            res["cpu_baseline_other_workloads"] = cpu_baselines_other(synth, d1)
+        log("oracle timed")
     print(json.dumps(res), flush=True)
+
+
+def time_calls(torch, call, n, warmup, flush, stream):
+    """Median and minimum HIP-event time (ms) of n calls on ``stream``, the 512 MiB buffer
+    rewritten before each so no input is left in L2 or the MALL."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = []
+    for i in range(n):
+        flush.fill_(i & 0xFF)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    return float(np.median(ms)), float(np.min(ms))
+
+
+def prefill_entry(name, ms, ms_min, tokens, heads, d, gate_per_head=False, states=1, extra=None):
+    b = prefill_bytes(tokens, heads, d, gate_per_head=gate_per_head, states=states)
+    e = {"workload": name, "ms": ms, "ms_min": ms_min, "tokens_per_s": tokens / (ms / 1e3),
+         "algorithmic_bytes": b, "hbm_gbs": b / (ms / 1e3) / 1e9, "hbm_frac": b / (ms / 1e3) / 1e9 / HBM_PEAK_GBS}
+    if extra:
+        e.update(extra)
+    return e
+
+
+def gpu_varlen_inputs(torch, synth, w):
+    """The 1M-token varlen workload drawn on the GPU (43 GB of inputs would take minutes on the
+    host): the synth recipe -- q, k ~ N(0,1) L2-normalised per (token, head) then bf16; v ~ N(0,1)
+    bf16; beta = sigmoid(N(0,1)); log_alpha = -s softplus(N(0,1)), s = 0.05; initial states
+    N(0, 0.02^2) -- from torch's seeded generator; the sequence lengths are synth's exactly."""
+    lens = synth.dirichlet_lengths(w.seed, w.seqlen, w.num_seqs, w.min_len)
+    cu = torch.from_numpy(synth.cu_from_lengths(lens).astype(np.int32)).cuda()
+    g = torch.Generator(device="cuda").manual_seed(1000 + w.seed)
+    T, H, D = w.seqlen, w.heads, w.dk
+    blk = 1 << 16
+    q, k, v = (torch.empty((1, T, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    la = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+    for t0 in range(0, T, blk):
+        t1 = min(T, t0 + blk)
+        for x in (q, k):
+            r = torch.randn((t1 - t0, H, D), generator=g, device="cuda")
+            x[0, t0:t1] = (r / r.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+        v[0, t0:t1] = torch.randn((t1 - t0, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        la[0, t0:t1] = -w.gate_scale * torch.nn.functional.softplus(
+            torch.randn((t1 - t0, H, D), generator=g, device="cuda"))
+    be = torch.sigmoid(torch.randn((1, T, H), generator=g, device="cuda"))
+    init = w.init_std * torch.randn((w.num_seqs, H, D, D), generator=g, device="cuda")
+    return q, k, v, la, be, init, cu, int(lens.max())
+
+
+def bench_prefill_configs(kda, torch, synth, args, flush, stream, q2, k2, v2, be2, init2):
+    """The other prefill workloads, as fields of the same line: 4K x 32 heads; the 1M-token
+    varlen batch; and the 64K x 32-head prefill with one gate per head (Gated DeltaNet)."""
+    from synth import WORKLOADS
+    out = {}
+    w1 = WORKLOADS[1]
+    d1 = synth.make_prefill(w1)
+    T, H, D = w1.seqlen, w1.heads, w1.dk
+    a = [to_dev(d1[x], torch).unsqueeze(0) for x in ("q", "k", "v", "log_alpha", "beta")]
+    o = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+    f = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+    ms, mn = time_calls(torch, lambda: kda.chunk_fwd(*a, None, None, out=o, final_state=f, workspace=ws),
+                        max(10, args.steps), args.warmup, flush, stream)
+    out[w1.name] = prefill_entry(w1.name, ms, mn, T, H, D, states=0)
+    del a, o, f, ws
+    w2 = WORKLOADS[2]
+    T, H, D = w2.seqlen, w2.heads, w2.dk
+    la_h = to_dev(synth.make_prefill(w2, gate="head")["log_alpha"], torch).unsqueeze(0)
+    o = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+    f = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32), dtype=torch.uint8,
+                     device="cuda")
+    ms, mn = time_calls(torch, lambda: kda.chunk_fwd(q2, k2, v2, la_h, be2, init2, None, out=o, final_state=f,
+                                                     workspace=ws), max(10, args.steps), args.warmup, flush, stream)
+    out[w2.name + " (one gate per head)"] = prefill_entry(w2.name + " (one gate per head)", ms, mn, T, H, D,
+                                                          gate_per_head=True)
+    del la_h, o, f, ws
+    if not args.no_varlen:
+        w4 = WORKLOADS[4]
+        q, k, v, la, be, init, cu, longest = gpu_varlen_inputs(torch, synth, w4)
+        T, H, D = w4.seqlen, w4.heads, w4.dk
+        o = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+        f = torch.empty((w4.num_seqs, H, D, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32, num_seqs=w4.num_seqs,
+                                            max_seqlen=longest), dtype=torch.uint8, device="cuda")
+        ms, mn = time_calls(torch, lambda: kda.chunk_fwd(q, k, v, la, be, init, cu, out=o, final_state=f,
+                                                         max_seqlen=longest, workspace=ws),
+                            5, 1, flush, stream)
+        out[w4.name] = prefill_entry(w4.name, ms, mn, T, H, D, states=w4.num_seqs,
+                                     extra={"inputs": "drawn on the GPU with the synth recipe (torch generator)",
+                                            "longest_sequence": longest})
+        del q, k, v, la, be, init, cu, o, f, ws
+    torch.cuda.empty_cache()
+    return out, d1
 
 
 def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):
