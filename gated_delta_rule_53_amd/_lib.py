@@ -5,7 +5,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkda.so")
+# KDA_LIBRARY names another build of the same library (the host-sanitizer build of
+# build.py --sanitize-host, for the CPU tests); by default the in-tree libkda.so.
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(HERE, "libkda.so")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 #include <vector>
@@ -34,7 +35,18 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
     return x < y + bn && y < x + an;
 }
 
-size_t dsize(kda_dtype_t t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
+// A C caller may store any int in an enum field or pass any int for an enum
+// parameter; in C++ a value outside the enumerators' range may not be read as the
+// enum type, so the library reads every caller-supplied enum's bits as an int.
+template <typename E>
+int enum_code(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "the ABI's enums are ints");
+    int x;
+    memcpy(&x, &e, sizeof(x));
+    return x;
+}
+
+size_t dsize(int t) { return t == KDA_DTYPE_BF16 ? 2 : 4; }
 
 struct Range {
     const void* p;
@@ -59,8 +71,8 @@ kda_status_t plan_chunk(const kda_shape_t* s, Plan& p) {
     if (!s) return KDA_ERR_INVALID_ARG;
     if (s->heads <= 0 || s->batch <= 0 || s->seqlen < 0 || s->dk <= 0 || s->dv <= 0 || s->max_seqlen < 0)
         return KDA_ERR_INVALID_ARG;
-    if ((s->in_dtype != KDA_DTYPE_F32 && s->in_dtype != KDA_DTYPE_BF16) ||
-        (s->out_dtype != KDA_DTYPE_F32 && s->out_dtype != KDA_DTYPE_BF16))
+    const int in_t = enum_code(s->in_dtype), out_t = enum_code(s->out_dtype);
+    if ((in_t != KDA_DTYPE_F32 && in_t != KDA_DTYPE_BF16) || (out_t != KDA_DTYPE_F32 && out_t != KDA_DTYPE_BF16))
         return KDA_ERR_UNSUPPORTED;
     if (s->dk != s->dv || (s->dk != 64 && s->dk != 128)) return KDA_ERR_UNSUPPORTED;
     if (s->gate_per_head != 0 && s->gate_per_head != 1) return KDA_ERR_INVALID_ARG;
@@ -104,7 +116,12 @@ void* device_scratch(hipError_t& err) {
 extern "C" {
 
 const char* kda_status_string(kda_status_t st) {
-    switch (st) {
+    // A C caller may pass any int; in C++ a value outside the enumerators' range may not
+    // be read as kda_status_t, so the argument's bits are read as an int.
+    int code;
+    static_assert(sizeof(code) == sizeof(st), "kda_status_t is an int");
+    memcpy(&code, &st, sizeof(code));
+    switch (code) {
         case KDA_OK: return "ok";
         case KDA_ERR_INVALID_ARG: return "invalid argument";
         case KDA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
@@ -150,7 +167,7 @@ static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) 
     }
     if (p.N * (int64_t)s->heads > INT32_MAX / 16) return KDA_ERR_UNSUPPORTED;
     p.max_chunks = (p.max_len + CHUNK - 1) / CHUNK;
-    p.rec = kda::chunk_record_bytes(p.d, s->in_dtype == KDA_DTYPE_BF16);
+    p.rec = kda::chunk_record_bytes(p.d, enum_code(s->in_dtype) == KDA_DTYPE_BF16);
     p.state_bytes = align256((size_t)p.N * s->heads * p.d * p.d * sizeof(float));
     return KDA_OK;
 }
@@ -189,7 +206,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
     kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p);
     if (st != KDA_OK) return st;
     const int H = s->heads, d = p.d;
-    const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
+    const size_t in_b = dsize(enum_code(s->in_dtype)), out_b = dsize(enum_code(s->out_dtype));
     const size_t tok_bytes = (size_t)p.tokens * H * d;
     const void* gate = layer ? layer->gate : static_cast<const void*>(log_alpha);
     const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok_bytes) * (layer ? 2 : 4);
@@ -304,7 +321,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         a.seg_M = reinterpret_cast<float*>(sb + segb);
         a.seg_init = reinterpret_cast<float*>(sb + 2 * segb);
     }
-    hipError_t e = kda::chunk_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16,
+    hipError_t e = kda::chunk_dispatch(d, enum_code(s->in_dtype) == KDA_DTYPE_BF16, enum_code(s->out_dtype) == KDA_DTYPE_BF16,
                                        layer && layer->qk_l2norm, bv, a, (int)nwin64, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -333,8 +350,8 @@ kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const
                           workspace_bytes, stream);
 }
 
-static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
-                                kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
+static kda_status_t decode_impl(int32_t batch, int32_t heads, int32_t dk, int32_t dv, int in_dtype,
+                                int out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
                                 const void* q, const void* k, const void* v, const float* log_alpha,
                                 const float* beta, float* state_inout, void* out, hipStream_t stream) {
     if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
@@ -386,7 +403,7 @@ kda_status_t kda_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t d
                              kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
                              const float* log_alpha, const float* beta, float* state_inout, void* out,
                              hipStream_t stream) {
-    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, 0, nullptr, q, k, v, log_alpha, beta, state_inout,
+    return decode_impl(batch, heads, dk, dv, enum_code(in_dtype), enum_code(out_dtype), 0, nullptr, q, k, v, log_alpha, beta, state_inout,
                        out, stream);
 }
 
@@ -394,7 +411,7 @@ kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk,
                                        kda_dtype_t out_dtype, const void* q, const void* k, const void* v,
                                        const float* log_alpha, const float* beta, float* state_inout, void* out,
                                        hipStream_t stream) {
-    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, 1, nullptr, q, k, v, log_alpha, beta, state_inout,
+    return decode_impl(batch, heads, dk, dv, enum_code(in_dtype), enum_code(out_dtype), 1, nullptr, q, k, v, log_alpha, beta, state_inout,
                        out, stream);
 }
 
@@ -403,7 +420,7 @@ kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int
                                    const void* q, const void* k, const void* v, const float* beta,
                                    float* state_inout, void* out, hipStream_t stream) {
     if (!layer) return KDA_ERR_INVALID_ARG;
-    return decode_impl(batch, heads, dk, dv, in_dtype, out_dtype, gate_per_head, layer, q, k, v, nullptr, beta,
+    return decode_impl(batch, heads, dk, dv, enum_code(in_dtype), enum_code(out_dtype), gate_per_head, layer, q, k, v, nullptr, beta,
                        state_inout, out, stream);
 }
 
@@ -475,7 +492,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     if (st != KDA_OK) return st;
     const int H = s->heads, d = p.d;
     const size_t tok = (size_t)p.tokens * H * d;
-    const size_t in_b = dsize(s->in_dtype), out_b = dsize(s->out_dtype);
+    const size_t in_b = dsize(enum_code(s->in_dtype)), out_b = dsize(enum_code(s->out_dtype));
     const size_t la_bytes = (s->gate_per_head ? (size_t)p.tokens * H : tok) * 4;
     const size_t st_bytes = (size_t)p.N * H * d * d * 4, tb4 = (size_t)p.tokens * H * 4;
     if (p.tokens > 0) {
@@ -556,7 +573,7 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
     b.dG = s->gate_per_head ? nullptr : dlog_alpha;
     b.dla_head = s->gate_per_head ? dlog_alpha : nullptr;
     b.dbeta = dbeta;
-    hipError_t e = kda::bwd_dispatch(d, s->in_dtype == KDA_DTYPE_BF16, s->out_dtype == KDA_DTYPE_BF16, b,
+    hipError_t e = kda::bwd_dispatch(d, enum_code(s->in_dtype) == KDA_DTYPE_BF16, enum_code(s->out_dtype) == KDA_DTYPE_BF16, b,
                                      stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

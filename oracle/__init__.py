@@ -35,8 +35,15 @@ _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIBS: dict = {}
 
 
+# KDA_ORACLE_SANITIZE=1 builds and loads the oracle with AddressSanitizer and
+# UndefinedBehaviorSanitizer (a separate library; the Python process must then
+# preload gcc's libasan and libubsan).
+_SANITIZE = os.environ.get("KDA_ORACLE_SANITIZE") == "1"
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
 def lib_path(mutant: int = 0) -> str:
-    name = "libkda_oracle.so" if mutant == 0 else f"libkda_oracle_m{mutant}.so"
+    name = "libkda_oracle" + ("" if mutant == 0 else f"_m{mutant}") + ("_san" if _SANITIZE else "") + ".so"
     return os.path.join(_BUILD, name)
 
 
@@ -46,7 +53,7 @@ def build(mutant: int = 0, force: bool = True) -> str:
     out = lib_path(mutant)
     if force or not os.path.exists(out):
         tmp = out + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", *(_SAN_FLAGS if _SANITIZE else []),
                f"-DKDA_ORACLE_MUTANT={mutant}", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, out)

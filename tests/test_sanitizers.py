@@ -1,0 +1,64 @@
+"""CPU sanitizer runs: AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
+
+* the fp64 oracle built with -fsanitize=address,undefined (KDA_ORACLE_SANITIZE=1),
+  running every oracle, layer-oracle, parity-figure and generator pin;
+* the library with its host code (argument validation, aliasing checks, workspace
+  planning) built with the same sanitizers (build.py --sanitize-host; device code
+  as usual), running the C ABI tests, none of which launches a kernel.
+
+Each suite runs in a subprocess with the sanitizer runtime preloaded (gcc's for the
+oracle, clang's for the hipcc-built library), reports go to a log file, and any
+report -- or a non-zero exit -- fails the test.
+"""
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(cmd, env, log_prefix):
+    for f in glob.glob(log_prefix + "*"):
+        os.remove(f)
+    r = subprocess.run(cmd, cwd=ROOT, env=env, capture_output=True, text=True, timeout=1500)
+    reports = "".join(open(f).read() for f in glob.glob(log_prefix + "*"))
+    assert r.returncode == 0 and not reports, (r.stdout[-3000:] + r.stderr[-3000:] + reports[:4000])
+
+
+def _san_env(tmp_path, preload):
+    env = dict(os.environ)
+    log = str(tmp_path / "san.log")
+    env["ASAN_OPTIONS"] = f"detect_leaks=0:abort_on_error=1:log_path={log}"
+    env["UBSAN_OPTIONS"] = f"halt_on_error=1:print_stacktrace=1:log_path={log}"
+    env["LD_PRELOAD"] = preload
+    return env, log
+
+
+def test_oracle_under_asan_ubsan(tmp_path):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    libs = [subprocess.run(["gcc", f"-print-file-name={n}"], capture_output=True, text=True).stdout.strip()
+            for n in ("libasan.so", "libubsan.so")]
+    if not all(os.path.isabs(p) and os.path.exists(p) for p in libs):
+        pytest.skip("gcc's sanitizer runtimes not available")
+    env, log = _san_env(tmp_path, ":".join(libs))
+    env["KDA_ORACLE_SANITIZE"] = "1"
+    tests = ["tests/test_oracle_pins.py", "tests/test_oracle_backward.py", "tests/test_layer_oracle.py",
+             "tests/test_metrics_pin.py", "tests/test_synth.py"]
+    _run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", *tests], env, log)
+
+
+def test_host_validation_under_asan_ubsan(tmp_path):
+    rt = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not rt or not os.path.exists(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc or clang's ASan runtime not available")
+    sys.path.insert(0, ROOT)
+    from gated_delta_rule_53_amd import build
+    lib = build.build(sanitize_host=True)
+    env, log = _san_env(tmp_path, rt[-1])
+    env["KDA_LIBRARY"] = lib
+    _run([sys.executable, "-m", "pytest", "-q", "-s", "-p", "no:cacheprovider", "tests/test_abi_cpu.py"], env, log)
