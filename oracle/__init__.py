@@ -20,6 +20,10 @@ and the chunkwise algorithm"):
   sizes only.
 * ``forms.chunkwise`` -- the chunked WY/UT form, fp64, written from the
   algebra of the recurrence; used to pin the recurrent form.
+* ``dplr_recurrent`` -- the general DPLR transition KDA constrains (section
+  "The constrained DPLR form and the chunkwise algorithm": independent a and
+  b), plain C fp64 token by token; pinned by its reduction to KDA and by
+  ``forms.dplr_brute`` / ``forms.dplr_chunkwise``.
 """
 from __future__ import annotations
 
@@ -77,6 +81,10 @@ def _lib(mutant: int = 0):
     b.restype = ctypes.c_int
     b.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
         [ctypes.c_void_p] * 14 + [ctypes.c_int]
+    d = lib.dplr_oracle_forward
+    d.restype = ctypes.c_int
+    d.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int] + \
+        [ctypes.c_void_p] * 9 + [ctypes.c_int]
     _LIBS[mutant] = lib
     return lib
 
@@ -136,6 +144,46 @@ def recurrent(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, thread
                                          _ptr(fin), nt)
     if rc != 0:
         raise RuntimeError(f"kda_oracle_forward failed ({rc})")
+    return out.reshape(vshape), fin
+
+
+def dplr_recurrent(q, k, v, a, b, log_alpha, init_state=None, cu_seqlens=None, threads=None, mutant: int = 0):
+    """fp64 token-by-token general DPLR forward:
+    S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t.
+
+    q, k, a, b [T, H, dk] and v [T, H, dv] as float32 or uint16 (bf16 bits), all
+    the same dtype; log_alpha float32 [T, H, dk]; init_state [N, H, dk, dv] or None;
+    cu_seqlens int [N+1] or None.  A leading batch axis [B, T, H, d] is accepted
+    without cu_seqlens.  Returns (out fp64 [.., H, dv], final_state fp64 [N, H, dk, dv]).
+    """
+    vshape = v.shape
+    if q.ndim == 4:
+        assert cu_seqlens is None
+        B, T = q.shape[:2]
+        q, k, v, a, b, log_alpha = (x.reshape((B * T,) + x.shape[2:]) for x in (q, k, v, a, b, log_alpha))
+        cu_seqlens = np.arange(B + 1, dtype=np.int64) * T
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], np.int64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    assert int(cu[-1]) == T, "cu_seqlens must cover every token"
+    bf16 = q.dtype == np.uint16
+    want = np.uint16 if bf16 else np.float32
+    q, k, v, a, b = (np.ascontiguousarray(x, dtype=want) for x in (q, k, v, a, b))
+    la = np.ascontiguousarray(log_alpha, dtype=np.float32)
+    assert la.shape == (T, H, dk) and a.shape == b.shape == (T, H, dk)
+    init = None if init_state is None else np.ascontiguousarray(init_state, dtype=np.float64)
+    if init is not None:
+        assert init.shape == (N, H, dk, dv)
+    out = np.zeros((T, H, dv), np.float64)
+    fin = np.zeros((N, H, dk, dv), np.float64)
+    nt = threads or max(1, min(64, os.cpu_count() or 1))
+    rc = _lib(mutant).dplr_oracle_forward(N, cu.ctypes.data, H, dk, dv, int(bf16), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(a), _ptr(b), _ptr(la), _ptr(init), _ptr(out), _ptr(fin), nt)
+    if rc != 0:
+        raise RuntimeError(f"dplr_oracle_forward failed ({rc})")
     return out.reshape(vshape), fin
 
 

@@ -116,3 +116,75 @@ def chunkwise(q, k, v, log_alpha, beta, S0, C=64, solve="substitution"):
         o[c0:c1] = (Q * np.exp(G)) @ S + P @ U
         S = np.exp(G[-1])[:, None] * S + (K * np.exp(G[-1][None, :] - G)).T @ U
     return o, S
+
+
+# ---------------------------------------------------------------------------
+# The general DPLR transition (independent a and b; "Kimi Linear" page, "The
+# constrained DPLR form and the chunkwise algorithm"):
+#     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t.
+# ---------------------------------------------------------------------------
+def dplr_transitions(a, b, log_alpha):
+    """Per-token dense dk x dk transitions Diag(alpha_t) - a_t b_t^T."""
+    T, dk = a.shape
+    return np.stack([np.diag(np.exp(log_alpha[t])) - np.outer(a[t], b[t]) for t in range(T)]) if T else \
+        np.zeros((0, dk, dk))
+
+
+def dplr_attention_form(q, k, v, a, b, log_alpha, S0):
+    """o_t = sum_{i<=t} (q_t^T M_{t,i} k_i) v_i + (M_{t,-1} S0)^T q_t with M_{t,i} the
+    product of the dense transitions of tokens i+1 .. t; O(T^2 dk^3), tiny T only."""
+    A = dplr_transitions(a, b, log_alpha)
+    T, dk = k.shape
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        M = np.eye(dk)
+        for i in range(t, -1, -1):
+            o[t] += (q[t] @ M @ k[i]) * v[i]
+            M = M @ A[i]
+        o[t] += (M @ S0).T @ q[t]
+    M = np.eye(dk)
+    for t in range(T):
+        M = A[t] @ M
+    S = M @ S0
+    for i in range(T):
+        P = np.eye(dk)
+        for t in range(i + 1, T):
+            P = A[t] @ P
+        S = S + P @ np.outer(k[i], v[i])
+    return o, S
+
+
+def dplr_chunkwise(q, k, v, a, b, log_alpha, S0, C=64):
+    """Chunked evaluation of the general DPLR recurrence (derived from it).
+
+    With w_r = b_r^T S_{r-1} (what the rank-one term reads), G the chunk-local
+    inclusive cumsum of log_alpha and Gx = G - log_alpha (exclusive):
+      Mba[r,i] = sum_c b_rc a_ic e^{Gx_rc - G_ic},  Mbk likewise with k   (i < r)
+      Mqa[r,i] = sum_c q_rc a_ic e^{G_rc - G_ic},   Mqk likewise with k   (i <= r)
+      (I + Mba) w = (B e^{Gx}) S + Mbk V
+      O      = (Q e^{G}) S + Mqk V - Mqa w
+      S_next = e^{G_last} S + (K e^{G_last - G})^T V - (A e^{G_last - G})^T w
+    b sees the state before its own token's decay (Gx), the other vectors after.
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.array(S0, dtype=np.float64)
+    o = np.empty((T, dv))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        Q, K, V, A_, B_ = q[c0:c1], k[c0:c1], v[c0:c1], a[c0:c1], b[c0:c1]
+        G = np.cumsum(log_alpha[c0:c1], axis=0)
+        Gx = G - log_alpha[c0:c1]
+        # [r, i, c]; only i < r (Dx) and i <= r (D) are used, where the exponent is <= 0
+        Dx = np.exp(np.minimum(Gx[:, None, :] - G[None, :, :], 0.0))
+        D = np.exp(np.minimum(G[:, None, :] - G[None, :, :], 0.0))
+        Mba = np.tril(np.einsum("rc,ic,ric->ri", B_, A_, Dx), -1)
+        Mbk = np.tril(np.einsum("rc,ic,ric->ri", B_, K, Dx), -1)
+        Mqa = np.tril(np.einsum("rc,ic,ric->ri", Q, A_, D))
+        Mqk = np.tril(np.einsum("rc,ic,ric->ri", Q, K, D))
+        n = c1 - c0
+        w = np.linalg.solve(np.eye(n) + Mba, (B_ * np.exp(Gx)) @ S + Mbk @ V)
+        o[c0:c1] = (Q * np.exp(G)) @ S + Mqk @ V - Mqa @ w
+        dec = np.exp(G[-1][None, :] - G)
+        S = np.exp(G[-1])[:, None] * S + (K * dec).T @ V - (A_ * dec).T @ w
+    return o, S

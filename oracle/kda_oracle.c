@@ -459,3 +459,162 @@ int kda_oracle_backward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, 
     pthread_mutex_destroy(&B.f.lock);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * General DPLR transition (the baseline KDA constrains; "Kimi Linear" page,
+ * section "The constrained DPLR form and the chunkwise algorithm"): a
+ * diagonal gate plus a rank-one term with two independent vectors a_t, b_t,
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,    o_t = S_t^T q_t.
+ *
+ * KDA is the case a = beta k, b = alpha (.) k with write key beta k.  Each
+ * step, in this order:
+ *   1. read:    p = S^T b_t          (from the state the step starts from)
+ *   2. decay:   S <- Diag(alpha_t) S
+ *   3. correct: S <- S - a_t p^T
+ *   4. write:   S <- S + k_t v_t^T
+ *   5. output:  o_t = S^T q_t
+ * Inputs as for kda_oracle_forward, with a and b laid out like k and no beta.
+ *
+ * KDA_ORACLE_MUTANT 8: b reads the decayed state (steps 1 and 2 swapped);
+ * 9: the roles of a and b exchanged (S <- S - b (a^T S)).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int64_t num_seqs;
+    const int64_t* cu;
+    int heads, dk, dv;
+    int in_bf16;
+    const void *q, *k, *v, *a, *b;
+    const float* log_alpha;
+    const double* init;
+    double *out, *final_state;
+    int64_t next_unit;
+    pthread_mutex_t lock;
+} djob_t;
+
+static void dplr_unit(djob_t* J, int64_t unit, double* S, double* buf) {
+    const int H = J->heads, dk = J->dk, dv = J->dv;
+    const int64_t s = unit / H, h = unit % H;
+    const int64_t t0 = J->cu[s], t1 = J->cu[s + 1];
+    double *qv = buf, *kv = buf + dk, *av = buf + 2 * dk, *bv = buf + 3 * dk, *al = buf + 4 * dk;
+    double *vv = buf + 5 * dk, *p = vv + dv;
+    for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+        S[i] = J->init ? J->init[(s * H + h) * (int64_t)dk * dv + i] : 0.0;
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t th = t * H + h;
+        for (int c = 0; c < dk; ++c) {
+            qv[c] = load_in(J->q, J->in_bf16, th * dk + c);
+            kv[c] = load_in(J->k, J->in_bf16, th * dk + c);
+            av[c] = load_in(J->a, J->in_bf16, th * dk + c);
+            bv[c] = load_in(J->b, J->in_bf16, th * dk + c);
+            al[c] = exp((double)J->log_alpha[th * dk + c]);
+        }
+        for (int j = 0; j < dv; ++j) vv[j] = load_in(J->v, J->in_bf16, th * dv + j);
+#if KDA_ORACLE_MUTANT == 8
+        for (int c = 0; c < dk; ++c) /* mutant: decay before the read */
+            for (int j = 0; j < dv; ++j) S[c * dv + j] *= al[c];
+#endif
+        /* 1. read through b */
+        const double* rd = bv;
+#if KDA_ORACLE_MUTANT == 9
+        rd = av; /* mutant: a and b exchanged */
+#endif
+        for (int j = 0; j < dv; ++j) p[j] = 0.0;
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) p[j] += rd[c] * S[c * dv + j];
+#if KDA_ORACLE_MUTANT != 8
+        /* 2. decay */
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) S[c * dv + j] *= al[c];
+#endif
+        /* 3-4. rank-one correction along a, then the write */
+        const double* wr = av;
+#if KDA_ORACLE_MUTANT == 9
+        wr = bv;
+#endif
+        for (int c = 0; c < dk; ++c)
+            for (int j = 0; j < dv; ++j) S[c * dv + j] += kv[c] * vv[j] - wr[c] * p[j];
+        /* 5. output */
+        for (int j = 0; j < dv; ++j) {
+            double o = 0.0;
+            for (int c = 0; c < dk; ++c) o += S[c * dv + j] * qv[c];
+            J->out[th * dv + j] = o;
+        }
+    }
+    if (J->final_state) memcpy(J->final_state + (s * H + h) * (int64_t)dk * dv, S, sizeof(double) * (size_t)dk * dv);
+}
+
+static void* dplr_worker(void* arg) {
+    djob_t* J = (djob_t*)arg;
+    double* S = (double*)malloc(sizeof(double) * (size_t)J->dk * J->dv);
+    double* buf = (double*)malloc(sizeof(double) * ((size_t)5 * J->dk + 2 * (size_t)J->dv));
+    if (!S || !buf) {
+        free(S);
+        free(buf);
+        return (void*)1;
+    }
+    const int64_t units = J->num_seqs * J->heads;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t unit = J->next_unit++;
+        pthread_mutex_unlock(&J->lock);
+        if (unit >= units) break;
+        dplr_unit(J, unit, S, buf);
+    }
+    free(S);
+    free(buf);
+    return NULL;
+}
+
+/*
+ * dplr_oracle_forward: every (sequence, head) unit of the general DPLR recurrence.
+ *   q, k, a, b  [T_total, heads, dk];  v [T_total, heads, dv]  (fp32, or bf16 bits if in_bf16)
+ *   log_alpha   fp32 [T_total, heads, dk]
+ *   init_state, out, final_state as for kda_oracle_forward.
+ */
+int dplr_oracle_forward(int64_t num_seqs, const int64_t* cu_seqlens, int heads, int dk, int dv, int in_bf16,
+                        const void* q, const void* k, const void* v, const void* a, const void* b,
+                        const float* log_alpha, const double* init_state, double* out, double* final_state,
+                        int nthreads) {
+    if (num_seqs < 0 || heads <= 0 || dk <= 0 || dv <= 0 || !cu_seqlens || (in_bf16 != 0 && in_bf16 != 1)) return 1;
+    if (cu_seqlens[0] != 0) return 1;
+    for (int64_t s = 0; s < num_seqs; ++s)
+        if (cu_seqlens[s + 1] < cu_seqlens[s]) return 1;
+    if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !a || !b || !log_alpha || !out)) return 1;
+    djob_t J;
+    J.num_seqs = num_seqs;
+    J.cu = cu_seqlens;
+    J.heads = heads;
+    J.dk = dk;
+    J.dv = dv;
+    J.in_bf16 = in_bf16;
+    J.q = q;
+    J.k = k;
+    J.v = v;
+    J.a = a;
+    J.b = b;
+    J.log_alpha = log_alpha;
+    J.init = init_state;
+    J.out = out;
+    J.final_state = final_state;
+    J.next_unit = 0;
+    pthread_mutex_init(&J.lock, NULL);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t th[256];
+    int rc = 0, started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, dplr_worker, &J) != 0) break;
+        ++started;
+    }
+    if (started == 0) {
+        if (dplr_worker(&J) != NULL) rc = 2;
+    }
+    for (int i = 0; i < started; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = 2;
+    }
+    pthread_mutex_destroy(&J.lock);
+    return rc;
+}

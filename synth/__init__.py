@@ -35,6 +35,11 @@ Layer inputs (the prologue and epilogue around the operator, ``gen_layer_tokens`
 * the output-gate pre-activation z ~ N(0, 1), bf16; the RMSNorm weight
   1 + 0.1 N(0, 1) fp32 [dv].
 
+General-DPLR inputs (``gen_dplr_tokens``; the baseline with independent low-rank
+vectors that KDA constrains): q, k, v and log_alpha as above (k is the write key,
+unit length); a = rate * (unit row), rate = sigmoid(N(0, 1)) per (token, head);
+b = an independent unit row; a and b rounded like q and k.
+
 bf16 tensors are returned as ``numpy.uint16`` arrays holding the bf16 bit
 patterns; fp32 tensors as ``numpy.float32``.
 """
@@ -50,7 +55,8 @@ BLOCK = 16384  # tokens per independently seeded block
 
 # tensor ids used in the spawn keys
 _TID = {"q": 0, "k": 1, "v": 2, "beta": 3, "log_alpha": 4, "init": 5, "lengths": 6, "log_alpha_head": 7,
-        "q_raw": 8, "k_raw": 9, "gate_pre": 10, "gate_pre_head": 11, "out_gate": 12, "norm_weight": 13}
+        "q_raw": 8, "k_raw": 9, "gate_pre": 10, "gate_pre_head": 11, "out_gate": 12, "norm_weight": 13,
+        "dplr_a": 14, "dplr_rate": 15, "dplr_b": 16}
 
 
 @dataclass(frozen=True)
@@ -201,6 +207,42 @@ def gen_tokens(seed: int, T: int, H: int, dk: int, dv: int, dtype: str, gate_sca
         _fill_blocks(seed, "log_alpha", T, heads, dk, afn, out["log_alpha"], threads)
     else:
         _fill_blocks(seed, "log_alpha_head", T, heads, None, afn, out["log_alpha"], threads)
+    return out
+
+
+def gen_dplr_tokens(seed: int, T: int, H: int, d: int, dtype: str, gate_scale: float, heads=None,
+                    threads=None) -> dict:
+    """General-DPLR token inputs: q, k, v, a, b [T, Hs, d] and log_alpha [T, Hs, d]
+    (q, k, v, log_alpha identical to ``gen_tokens``'s draw of the same seed)."""
+    heads = list(range(H)) if heads is None else list(heads)
+    threads = _threads() if threads is None else threads
+    out = gen_tokens(seed, T, H, d, d, dtype, gate_scale, heads=heads, threads=threads)
+    del out["beta"]
+    dt = np.uint16 if dtype == "bf16" else np.float32
+    Hs = len(heads)
+
+    def afn(r, n):
+        x = r.standard_normal((n, d))
+        x /= np.sqrt(np.sum(x * x, axis=1, keepdims=True))
+        rate = 1.0 / (1.0 + np.exp(-r.standard_normal(n)))
+        x = (x * rate[:, None]).astype(np.float32)
+        return f32_to_bf16_bits(x) if dtype == "bf16" else x
+    out["a"] = np.empty((T, Hs, d), dt)
+    out["b"] = np.empty((T, Hs, d), dt)
+    _fill_blocks(seed, "dplr_a", T, heads, d, afn, out["a"], threads)
+    unit = _unit_rows(dtype)
+    _fill_blocks(seed, "dplr_b", T, heads, d, lambda r, n: unit(r, n, d), out["b"], threads)
+    return out
+
+
+def dplr_small(seed: int, T: int, H: int, d: int, dtype: str = "f32", gate_scale: float = 0.05,
+               init_std: float | None = 0.02, batch: int = 1, lens=None) -> dict:
+    """Small general-DPLR workload (tests): q, k, v, a, b, log_alpha, cu_seqlens, init."""
+    lens = np.full(batch, T, np.int64) if lens is None else np.asarray(lens, np.int64)
+    cu = cu_from_lengths(lens)
+    out = gen_dplr_tokens(seed, int(cu[-1]), H, d, dtype, gate_scale, threads=1)
+    out["cu_seqlens"] = cu
+    out["init"] = None if init_std is None else gen_states(seed, len(lens), H, d, d, init_std)
     return out
 
 

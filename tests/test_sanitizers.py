@@ -1,7 +1,8 @@
 """CPU sanitizer runs: AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
 
 * the fp64 oracle built with -fsanitize=address,undefined (KDA_ORACLE_SANITIZE=1),
-  running every oracle, layer-oracle, parity-figure and generator pin;
+  running every oracle (KDA and general DPLR), layer-oracle, parity-figure and
+  generator pin;
 * the library with its host code (argument validation, aliasing checks, workspace
   planning) built with the same sanitizers (build.py --sanitize-host; device code
   as usual), running the C ABI tests, none of which launches a kernel.
@@ -48,6 +49,7 @@ def test_oracle_under_asan_ubsan(tmp_path):
     env, log = _san_env(tmp_path, ":".join(libs))
     env["KDA_ORACLE_SANITIZE"] = "1"
     tests = ["tests/test_oracle_pins.py", "tests/test_oracle_backward.py", "tests/test_layer_oracle.py",
+             "tests/test_oracle_dplr.py",
              "tests/test_metrics_pin.py", "tests/test_synth.py"]
     _run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", *tests], env, log)
 
