@@ -1,4 +1,5 @@
-"""MI355X (gfx950) Kimi Delta Attention operator: chunked prefill and recurrent decode.
+"""MI355X (gfx950) Kimi Delta Attention operator: chunked prefill and recurrent decode,
+and the general DPLR transition it constrains (chunked prefill).
 
 A thin binding over ``libkda.so`` (see ``include/kda.h``).  Every step of the
 computation runs in the library's HIP kernels; this module only checks
@@ -11,7 +12,7 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "dplr_chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step",
            "workspace_size", "bwd_workspace_size", "KdaError"]
 
 
@@ -74,7 +75,8 @@ def _prefill_args(q, k, v, log_alpha, beta, init_state, cu_seqlens, out, out_dty
     _check_dev(v, "v", q.dtype, (B, T, H, dv))
     gate_per_head = log_alpha.dim() == 3
     _check_dev(log_alpha, "log_alpha", torch.float32, (B, T, H) if gate_per_head else (B, T, H, dk))
-    _check_dev(beta, "beta", torch.float32, (B, T, H))
+    if beta is not None:  # the general DPLR variant has none
+        _check_dev(beta, "beta", torch.float32, (B, T, H))
     if cu_seqlens is not None:
         _check_dev(cu_seqlens, "cu_seqlens", torch.int32)
         if B != 1:
@@ -127,6 +129,35 @@ def chunk_fwd(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out
     _lib.check(st, "kda_chunk_fwd")
     return out, final_state
 
+
+
+def dplr_chunk_fwd(q, k, v, a, b, log_alpha, init_state=None, cu_seqlens=None, *, out=None, out_dtype=None,
+                   final_state=True, max_seqlen=None, workspace=None):
+    """Chunked prefill of the general DPLR transition (kda_dplr_chunk_fwd):
+    S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+
+    q, k, a, b [B,T,H,128] and v [B,T,H,128] (all fp32 or all bf16); log_alpha
+    [B,T,H,128] fp32; no beta.  init_state, cu_seqlens, out, final_state,
+    max_seqlen and workspace as for ``chunk_fwd``.  Returns (out, final_state or None).
+    """
+    torch = _torch()
+    _check_dev(a, "a", q.dtype, q.shape)
+    _check_dev(b, "b", q.dtype, q.shape)
+    if log_alpha.dim() != 4:
+        raise ValueError("the general DPLR variant takes a per-channel log_alpha [B,T,H,dk]")
+    shape, out, final_state = _prefill_args(q, k, v, log_alpha, None, init_state, cu_seqlens, out, out_dtype,
+                                            final_state, max_seqlen)
+    L = lib()
+    need = int(L.kda_dplr_chunk_fwd_workspace_size(shape))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check_dev(workspace, "workspace", torch.uint8)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = L.kda_dplr_chunk_fwd(shape, ptr(q), ptr(k), ptr(v), ptr(a), ptr(b), ptr(log_alpha), ptr(init_state),
+                              ptr(cu_seqlens), ptr(out), ptr(final_state), ptr(workspace), workspace.numel(),
+                              _stream_handle(q.device))
+    _lib.check(st, "kda_dplr_chunk_fwd")
+    return out, final_state
 
 def chunk_fwd_noalloc(q, k, v, log_alpha, beta, init_state=None, cu_seqlens=None, *, out, final_state=None,
                       max_seqlen=None):

@@ -15,7 +15,8 @@ NOALLOC_SCRATCH_BYTES = 256 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "KDA_ERR_WORKSPACE",
           4: "KDA_ERR_HIP"}
 # every symbol include/kda.h declares
-EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_decode_step",
+EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
+           "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd", "kda_decode_step",
            "kda_decode_step_head_gate",
            "kda_layer_fwd", "kda_layer_decode_step", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
            "kda_status_string")
@@ -66,6 +67,10 @@ def lib():
     L.kda_chunk_fwd.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     L.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_dplr_chunk_fwd_workspace_size.restype = sz
+    L.kda_dplr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(Shape)]
+    L.kda_dplr_chunk_fwd.restype = ctypes.c_int
+    L.kda_dplr_chunk_fwd.argtypes = [ctypes.POINTER(Shape)] + [vp] * 11 + [sz, vp]
     for name in ("kda_decode_step", "kda_decode_step_head_gate"):
         f = getattr(L, name)
         f.restype = ctypes.c_int

@@ -152,9 +152,10 @@ static size_t segment_bytes(const Plan& p, int heads, int G) {
     return align256((size_t)p.N * heads * G * p.d * p.d * sizeof(float));
 }
 
-static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) {
+static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p, bool dplr = false) {
     kda_status_t st = plan_chunk(s, p);
     if (st != KDA_OK) return st;
+    if (dplr && (p.d != 128 || s->gate_per_head != 0)) return KDA_ERR_UNSUPPORTED;
     if (varlen) {
         if (s->batch != 1 || s->num_seqs < 0) return KDA_ERR_INVALID_ARG;
         p.N = s->num_seqs;
@@ -167,9 +168,26 @@ static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p) 
     }
     if (p.N * (int64_t)s->heads > INT32_MAX / 16) return KDA_ERR_UNSUPPORTED;
     p.max_chunks = (p.max_len + CHUNK - 1) / CHUNK;
-    p.rec = kda::chunk_record_bytes(p.d, enum_code(s->in_dtype) == KDA_DTYPE_BF16);
+    p.rec = dplr ? kda::dplr_record_bytes(enum_code(s->in_dtype) == KDA_DTYPE_BF16)
+                 : kda::chunk_record_bytes(p.d, enum_code(s->in_dtype) == KDA_DTYPE_BF16);
     p.state_bytes = align256((size_t)p.N * s->heads * p.d * p.d * sizeof(float));
     return KDA_OK;
+}
+
+// Record bytes of the windowed schedule: every chunk if that fits the record
+// budget, else windows of chunks.
+static size_t window_record_bytes(const Plan& p, size_t per_chunk) {
+    const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    if ((size_t)all * per_chunk <= RECORD_BUDGET) return (size_t)all * per_chunk;
+    // two windows of half the record budget, or one of twice the size
+    int64_t wc = 2 * (int64_t)(RECORD_BUDGET / 2 / per_chunk);
+    // Many (sequence, head) pairs leave few chunks per window inside the budget,
+    // and then the per-window launch costs outweigh keeping the records in the
+    // last-level cache: windows of at least MIN_WINDOW chunks (records of at most
+    // WINDOW_CAP bytes; 512 pairs of the 1M-token batch: 5 -> 32 chunks, 1.3x).
+    const int64_t wide = std::min<int64_t>(MIN_WINDOW, (int64_t)(WINDOW_CAP / per_chunk));
+    wc = std::min<int64_t>(all, std::max<int64_t>(std::max<int64_t>(wc, wide), 1));
+    return (size_t)wc * per_chunk;
 }
 
 size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
@@ -183,17 +201,9 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     const int G = kda::chunk_segments(p.d, kda::chunk_value_slice(p.d, units), units, p.max_chunks, sc);
     if (G > 0)  // sequence-parallel state pass: every record plus three per-segment state blocks
         return p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G);
-    if ((size_t)all * per_chunk <= RECORD_BUDGET) return p.state_bytes + (size_t)all * per_chunk;
-    // two windows of half the record budget, or one of twice the size
-    int64_t wc = 2 * (int64_t)(RECORD_BUDGET / 2 / per_chunk);
-    // Many (sequence, head) pairs leave few chunks per window inside the budget,
-    // and then the per-window launch costs outweigh keeping the records in the
-    // last-level cache: windows of at least MIN_WINDOW chunks (records of at most
-    // WINDOW_CAP bytes; 512 pairs of the 1M-token batch: 5 -> 32 chunks, 1.3x).
-    const int64_t wide = std::min<int64_t>(MIN_WINDOW, (int64_t)(WINDOW_CAP / per_chunk));
-    wc = std::min<int64_t>(all, std::max<int64_t>(std::max<int64_t>(wc, wide), 1));
-    return p.state_bytes + (size_t)wc * per_chunk;
+    return p.state_bytes + window_record_bytes(p, per_chunk);
 }
+
 
 // The prefill behind kda_chunk_fwd (gate: fp32 log_alpha, layer null) and
 // kda_layer_fwd (gate: the layer's bf16 pre-activation).
@@ -339,6 +349,101 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* s, const void* q, const vo
                                    const int32_t* cu_seqlens, void* out, float* final_state, hipStream_t stream) {
     return chunk_fwd_impl(s, nullptr, q, k, v, log_alpha, beta, init_state, cu_seqlens, out, final_state, nullptr,
                           NOALLOC_SCRATCH_BYTES, stream, /*static_scratch=*/true);
+}
+
+size_t kda_dplr_chunk_fwd_workspace_size(const kda_shape_t* s) {
+    Plan p;
+    if (!s || chunk_plan_full(s, s->num_seqs > 0, p, /*dplr=*/true) != KDA_OK) return 0;
+    const size_t per_chunk = (size_t)p.N * s->heads * p.rec;
+    if (per_chunk == 0) return p.state_bytes + 256;
+    return p.state_bytes + window_record_bytes(p, per_chunk);
+}
+
+kda_status_t kda_dplr_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v, const void* a,
+                                const void* b, const float* log_alpha, const float* init_state,
+                                const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    Plan p;
+    kda_status_t st = chunk_plan_full(s, cu_seqlens != nullptr, p, /*dplr=*/true);
+    if (st != KDA_OK) return st;
+    const int H = s->heads, d = p.d;
+    const size_t in_b = dsize(enum_code(s->in_dtype)), out_b = dsize(enum_code(s->out_dtype));
+    const size_t tok_bytes = (size_t)p.tokens * H * d;
+    const size_t state_bytes = (size_t)p.N * H * d * d * 4;
+    if (p.tokens > 0) {
+        if (!q || !k || !v || !a || !b || !log_alpha || !out) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(a) || !aligned16(b) ||
+            !aligned16(log_alpha) || !aligned16(out))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARG;
+    if ((init_state && !aligned16(init_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERR_INVALID_ARG;
+    if (init_state && final_state && init_state != final_state &&
+        overlaps(init_state, state_bytes, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    const Range inputs[] = {{q, tok_bytes * in_b},
+                            {k, tok_bytes * in_b},
+                            {v, tok_bytes * in_b},
+                            {a, tok_bytes * in_b},
+                            {b, tok_bytes * in_b},
+                            {log_alpha, tok_bytes * 4},
+                            {cu_seqlens, cu_seqlens ? (size_t)(p.N + 1) * 4 : 0}};
+    const size_t out_bytes = tok_bytes * out_b;
+    if (overlaps_any(out, out_bytes, inputs) || overlaps(out, out_bytes, init_state, state_bytes) ||
+        overlaps(out, out_bytes, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if (final_state && overlaps_any(final_state, state_bytes, inputs)) return KDA_ERR_INVALID_ARG;
+    const size_t per_chunk = (size_t)p.N * H * p.rec;
+    if (p.N == 0) return KDA_OK;  // nothing to compute
+    if (!workspace || !aligned16(workspace) || workspace_bytes < p.state_bytes + per_chunk)
+        return KDA_ERR_WORKSPACE;
+    if (overlaps_any(workspace, workspace_bytes, inputs) || overlaps(workspace, workspace_bytes, out, out_bytes) ||
+        overlaps(workspace, workspace_bytes, init_state, state_bytes) ||
+        overlaps(workspace, workspace_bytes, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens) {
+        const char* chk = getenv("KDA_CHECK");
+        if (chk && chk[0] == '1') {
+            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
+            if (cs != KDA_OK) return cs;
+        }
+    }
+    // one record buffer for every chunk if it fits, else windows of chunks
+    const size_t avail = workspace_bytes - p.state_bytes;
+    const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
+    const int64_t wc_max = 65535 / p.N;  // grid rows of the chunk-local pass
+    if (wc_max < 1) return KDA_ERR_UNSUPPORTED;
+    int64_t wc = (size_t)all * per_chunk <= avail ? all : (int64_t)(avail / per_chunk);
+    if (wc > wc_max) wc = wc_max;
+    const int64_t nwin64 = p.max_chunks > 0 ? (p.max_chunks + wc - 1) / wc : 1;
+    if (nwin64 > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::ChunkArgs ca;
+    ca.q = q;
+    ca.k = k;
+    ca.v = v;
+    ca.dplr_a = a;
+    ca.dplr_b = b;
+    ca.la = log_alpha;
+    ca.beta = nullptr;
+    ca.gate_per_head = 0;
+    ca.cu = cu_seqlens;
+    ca.T = s->seqlen;
+    ca.H = H;
+    ca.N = (int)p.N;
+    ca.Wc = (int)wc;
+    ca.win = 0;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    ca.state_buf = final_state ? final_state : reinterpret_cast<float*>(ws);
+    ca.rec = ws + p.state_bytes;
+    ca.rec_bytes = p.rec;
+    ca.init = init_state;
+    ca.out = out;
+    const bool in_bf16 = enum_code(s->in_dtype) == KDA_DTYPE_BF16;
+    hipError_t e = kda::dplr_dispatch(in_bf16, enum_code(s->out_dtype) == KDA_DTYPE_BF16,
+                                      kda::dplr_value_slice(in_bf16, p.N * H), ca, (int)nwin64, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_layer_fwd(const kda_shape_t* s, const kda_layer_t* layer, const void* q, const void* k,

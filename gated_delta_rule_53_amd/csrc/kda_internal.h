@@ -11,6 +11,8 @@ struct ChunkArgs {
     const void* q;
     const void* k;
     const void* v;
+    const void* dplr_a = nullptr;  // general DPLR variant: the rank-one vectors a and b
+    const void* dplr_b = nullptr;
     const float* la;
     const float* beta;
     const int32_t* cu;  // packed sequence offsets, or null for a dense batch
@@ -102,6 +104,11 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
 // by RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
                           hipStream_t st);
+// General DPLR variant (dplr_chunk.hip): dk = dv = 128, windows of a.Wc chunks,
+// value slices of 16 or 32 columns (16 for fp32 inputs).
+size_t dplr_record_bytes(bool in_bf16);
+int dplr_value_slice(bool in_bf16, int64_t units);
+hipError_t dplr_dispatch(bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a, int nwin, hipStream_t st);
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
                            const void* k, const void* v, const float* la, const float* beta, float* state,
                            void* out, const DecodeLayer& layer, hipStream_t st);

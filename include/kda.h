@@ -155,6 +155,34 @@ kda_status_t kda_chunk_fwd_noalloc(const kda_shape_t* s, const void* q, const vo
                                    const float* log_alpha, const float* beta, const float* init_state,
                                    const int32_t* cu_seqlens, void* out, float* final_state, hipStream_t stream);
 
+/* General DPLR transition, the form KDA constrains ("Kimi Linear" page, "The
+ * constrained DPLR form and the chunkwise algorithm"): a diagonal gate plus a
+ * rank-one term whose vectors a and b are independent of the key,
+ *
+ *     S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,    o_t = S_t^T q_t,
+ *
+ * where a_t b_t^T acts on the state before the token's decay (b_t^T S_{t-1}).
+ * KDA is the case a = beta k, b = alpha (.) k with write key beta k.  Evaluated
+ * chunkwise like kda_chunk_fwd (64-token chunks, a UT transform per chunk, an
+ * fp32 state between chunks); four gated products per chunk instead of KDA's two.
+ *
+ * shape: as for kda_chunk_fwd, with dk = dv = 128 and gate_per_head = 0 only
+ *   (otherwise KDA_ERR_UNSUPPORTED).
+ * q, k, a, b: [.., H, dk] and v [.., H, dv] in shape->in_dtype; k is the write
+ *   key (any learning rate folded in); log_alpha fp32 [.., H, dk]; no beta.
+ * init_state, cu_seqlens, out, final_state, workspace, stream: as kda_chunk_fwd,
+ *   with the same alignment, aliasing and error rules (a and b count as inputs).
+ * Preconditions not checked on the device: log_alpha finite and <= 0 (any such
+ *   value; diagonal blocks whose single-anchor factors leave their range are
+ *   formed in a form with every factor at most 1); a, b and k such that the
+ *   state stays bounded; with bf16 inputs the fp16 staging bound of kda_chunk_fwd
+ *   on q, k, a, b, v, the state and the outputs. */
+size_t kda_dplr_chunk_fwd_workspace_size(const kda_shape_t* s);
+kda_status_t kda_dplr_chunk_fwd(const kda_shape_t* s, const void* q, const void* k, const void* v, const void* a,
+                                const void* b, const float* log_alpha, const float* init_state,
+                                const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* One recurrent decode step for `batch` independent sequences ("Kimi Linear"
  * page, "Why linear attention exists": decoding is a recurrent update whose
  * cost does not depend on context length; "Kimi Delta Attention" for the

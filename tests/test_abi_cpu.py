@@ -350,3 +350,35 @@ def test_noalloc_validation(L):
     F = 1 << 40
     big = _shape(1, 64, 0, 0, 4096, 128, 128, BF16, F32)
     assert L.kda_chunk_fwd_noalloc(big, F, 2 * F, 3 * F, 4 * F, 5 * F, None, None, 6 * F, None, None) == WORKSPACE
+
+
+def _dplr(L, s, q=A, k=2 * A, v=3 * A, a=4 * A, b=5 * A, la=6 * A, init=None, cu=None, out=7 * A, fin=None,
+          ws=None, wsb=0):
+    return L.kda_dplr_chunk_fwd(s, q, k, v, a, b, la, init, cu, out, fin, ws, wsb, None)
+
+
+def test_dplr_chunk_fwd_validation(L):
+    """kda_dplr_chunk_fwd: dk = dv = 128 and per-channel gates only; the kda_chunk_fwd checks
+    with a and b counted among the inputs."""
+    s = _shape(T=128, dk=128, dv=128)
+    assert L.kda_dplr_chunk_fwd_workspace_size(s) > 2 * 128 * 128 * 4
+    assert L.kda_dplr_chunk_fwd_workspace_size(_shape()) == 0                     # dk = 64
+    assert L.kda_dplr_chunk_fwd_workspace_size(_shape(T=128, dk=128, dv=128, gph=1)) == 0
+    assert _dplr(L, None) == INVALID
+    assert _dplr(L, _shape()) == UNSUPPORTED                                      # dk = 64
+    assert _dplr(L, _shape(T=128, dk=128, dv=128, gph=1)) == UNSUPPORTED          # one gate per head
+    assert _dplr(L, _shape(T=128, dk=128, dv=128, i=7)) == UNSUPPORTED
+    assert _dplr(L, s, a=None) == INVALID
+    assert _dplr(L, s, b=5 * A + 4) == INVALID                                   # misaligned
+    assert _dplr(L, s, out=4 * A + 64) == INVALID                                # out over a
+    assert _dplr(L, s, out=5 * A + 64) == INVALID                                # out over b
+    assert _dplr(L, s, fin=5 * A) == INVALID                                     # final state over b
+    assert _dplr(L, s, init=9 * A, fin=9 * A + 64) == INVALID                    # partial state overlap
+    assert _dplr(L, s, ws=None) == WORKSPACE
+    assert _dplr(L, s, ws=10 * A, wsb=1024) == WORKSPACE
+    assert _dplr(L, s, ws=4 * A, wsb=1 << 30) == INVALID                         # workspace over a
+    assert _dplr(L, s, cu=9 * A, ws=10 * A, wsb=1 << 30) == OK                   # varlen, zero sequences
+    assert _dplr(L, _shape(B=2, T=128, dk=128, dv=128), cu=9 * A) == INVALID     # varlen needs batch 1
+    # the record is larger than KDA's: the workspace of the same shape is larger at a single window
+    s1 = _shape(T=4096, H=4, dk=128, dv=128, i=BF16)
+    assert L.kda_dplr_chunk_fwd_workspace_size(s1) > L.kda_chunk_fwd_workspace_size(s1)
