@@ -216,6 +216,9 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the other prefill workloads (4K x 32, 1M varlen, one gate per head)")
     ap.add_argument("--no-varlen", action="store_true", help="skip the 1M-token varlen prefill")
+    ap.add_argument("--no-dplr", action="store_true", help="skip the KDA vs general-DPLR prefill comparison")
+    ap.add_argument("--dplr-only", action="store_true",
+                    help="only the KDA vs general-DPLR prefill comparison (profiling runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (HBM counter calibration)")
     args = ap.parse_args()
@@ -243,6 +246,11 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 10}), flush=True)
         return
 
+    if args.dplr_only:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        print(json.dumps({"dplr_vs_kda": bench_dplr(kda, torch, synth, args, flush, torch.cuda.current_stream())}),
+              flush=True)
+        return
     wp, wd = WORKLOADS[2], WORKLOADS[3]
     # ---- prefill inputs (64K tokens, 32 heads) ----
     t0 = time.time()
@@ -353,6 +361,9 @@ def main():
         del out, fin, ws
         res["prefill_configs"], d1 = bench_prefill_configs(kda, torch, synth, args, flush, stream, q, k, v, be, init)
         log("other prefill workloads timed")
+    if not (args.no_dplr or args.prefill_only or gph):
+        res["dplr_vs_kda"] = bench_dplr(kda, torch, synth, args, flush, stream)
+        log("KDA vs general DPLR timed")
     if not (args.no_backward or args.prefill_only or gph):
         res["backward"] = bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream)
         log("backward timed")
@@ -466,6 +477,40 @@ def bench_prefill_configs(kda, torch, synth, args, flush, stream, q2, k2, v2, be
         del q, k, v, la, be, init, cu, o, f, ws
     torch.cuda.empty_cache()
     return out, d1
+
+
+def bench_dplr(kda, torch, synth, args, flush, stream):
+    """KDA against the general DPLR transition it constrains, at the pages' comparison shape
+    (batch 1, 16 heads, inputs up to 64K tokens): the same synthetic q, k, v and gates; KDA with
+    beta, the DPLR kernel with independent a and b (synth's general-DPLR recipe)."""
+    H, D = 16, 128
+    res = {"heads": H, "dk": D, "dv": D, "in": "bf16", "out": "fp32", "init_state": "fp32 N(0,0.02^2)",
+           "pages": "KDA kernel close to twice the speed of a general DPLR kernel for inputs up to 64K tokens "
+                    "at batch 1 with 16 heads (hardware not stated)", "lengths": {}}
+    for T in (4096, 16384, 65536):
+        dd = synth.gen_dplr_tokens(5, T, H, D, "bf16", 0.01)
+        be = to_dev(synth.gen_tokens(5, T, H, D, D, "bf16", 0.01)["beta"], torch).unsqueeze(0)
+        q, k, v, a, b, la = (to_dev(dd[x], torch).unsqueeze(0) for x in ("q", "k", "v", "a", "b", "log_alpha"))
+        del dd
+        init = to_dev(synth.gen_states(5, 1, H, D, D, 0.02), torch)
+        o = torch.empty((1, T, H, D), dtype=torch.float32, device="cuda")
+        f = torch.empty((1, H, D, D), dtype=torch.float32, device="cuda")
+        wk = torch.empty(kda.workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32), dtype=torch.uint8,
+                         device="cuda")
+        wd = torch.empty(kda.dplr_workspace_size(1, T, H, D, D, torch.bfloat16, torch.float32), dtype=torch.uint8,
+                         device="cuda")
+        n = max(10, args.steps)
+        km, kmin = time_calls(torch, lambda: kda.chunk_fwd(q, k, v, la, be, init, None, out=o, final_state=f,
+                                                           workspace=wk), n, args.warmup, flush, stream)
+        dm, dmin = time_calls(torch, lambda: kda.dplr_chunk_fwd(q, k, v, a, b, la, init, None, out=o,
+                                                                final_state=f, workspace=wd),
+                              n, args.warmup, flush, stream)
+        res["lengths"][str(T)] = {"kda_ms": km, "dplr_ms": dm, "kda_ms_min": kmin, "dplr_ms_min": dmin,
+                                  "kda_tokens_per_s": T / (km / 1e3), "dplr_tokens_per_s": T / (dm / 1e3),
+                                  "dplr_over_kda_time": dm / km}
+        del q, k, v, a, b, la, be, init, o, f, wk, wd
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):

@@ -13,7 +13,7 @@ from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
 __all__ = ["chunk_fwd", "chunk_fwd_noalloc", "dplr_chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step",
-           "workspace_size", "bwd_workspace_size", "KdaError"]
+           "workspace_size", "dplr_workspace_size", "bwd_workspace_size", "KdaError"]
 
 
 def _torch():
@@ -54,6 +54,15 @@ def workspace_size(batch, seqlen, heads, dk, dv, in_dtype, out_dtype=None, num_s
     shape = _lib.shape(batch, seqlen, num_seqs, heads, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype),
                        max_seqlen)
     return int(lib().kda_chunk_fwd_workspace_size(shape))
+
+
+def dplr_workspace_size(batch, seqlen, heads, dk, dv, in_dtype, out_dtype=None, num_seqs=0, max_seqlen=0):
+    """Bytes of device workspace ``dplr_chunk_fwd`` needs (varlen iff num_seqs > 0)."""
+    torch = _torch()
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    shape = _lib.shape(batch, seqlen, num_seqs, heads, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype),
+                       max_seqlen)
+    return int(lib().kda_dplr_chunk_fwd_workspace_size(shape))
 
 
 def bwd_workspace_size(batch, seqlen, heads, dk, dv, in_dtype, dout_dtype=None, num_seqs=0, max_seqlen=0):
