@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -147,12 +148,48 @@ static kda_status_t check_cu_seqlens(const int32_t* cu, const Plan& p, hipStream
     return KDA_OK;
 }
 
+// Under KDA_CHECK=1 with bf16 inputs: the largest |v| and |initial state|,
+// measured on the device (synchronising `stream`).  Past F16_RANGE_SAFE the
+// call runs with fp32 matrix-core operands and records instead of fp16 ones,
+// whose range (6.5e4) values a few times larger would leave.  `scratch` is
+// 2 * RANGE_BLOCKS floats of the workspace, written before any kernel of the
+// call uses it.
+constexpr float F16_RANGE_SAFE = 1024.f;
+constexpr int RANGE_BLOCKS = 256;
+
+static kda_status_t needs_f32_operands(const void* v, size_t nv, const float* init, size_t ninit, float* scratch,
+                                       hipStream_t stream, bool& f32) {
+    f32 = false;
+    if (nv == 0 && ninit == 0) return KDA_OK;
+    if (nv && kda::max_abs_dispatch(v, nv, true, scratch, RANGE_BLOCKS, stream) != hipSuccess) return KDA_ERR_HIP;
+    if (ninit && kda::max_abs_dispatch(init, ninit, false, scratch + RANGE_BLOCKS, RANGE_BLOCKS, stream) != hipSuccess)
+        return KDA_ERR_HIP;
+    std::vector<float> h(2 * RANGE_BLOCKS, 0.f);
+    if (nv && hipMemcpyAsync(h.data(), scratch, RANGE_BLOCKS * sizeof(float), hipMemcpyDeviceToHost, stream) !=
+                  hipSuccess)
+        return KDA_ERR_HIP;
+    if (ninit && hipMemcpyAsync(h.data() + RANGE_BLOCKS, scratch + RANGE_BLOCKS, RANGE_BLOCKS * sizeof(float),
+                                hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+    float m = 0.f;
+    for (float x : h) m = x > m ? x : m;  // a NaN block maximum is +inf
+    f32 = !(m <= F16_RANGE_SAFE);
+    return KDA_OK;
+}
+
+static bool check_enabled() {
+    const char* chk = getenv("KDA_CHECK");
+    return chk && chk[0] == '1';
+}
+
 // Bytes of one per-segment state array [units, G, d, d] fp32 (256-aligned).
 static size_t segment_bytes(const Plan& p, int heads, int G) {
     return align256((size_t)p.N * heads * G * p.d * p.d * sizeof(float));
 }
 
-static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p, bool dplr = false) {
+static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p, bool dplr = false,
+                                   bool f32_operands = false) {
     kda_status_t st = plan_chunk(s, p);
     if (st != KDA_OK) return st;
     if (dplr && (p.d != 128 || s->gate_per_head != 0)) return KDA_ERR_UNSUPPORTED;
@@ -168,8 +205,8 @@ static kda_status_t chunk_plan_full(const kda_shape_t* s, bool varlen, Plan& p, 
     }
     if (p.N * (int64_t)s->heads > INT32_MAX / 16) return KDA_ERR_UNSUPPORTED;
     p.max_chunks = (p.max_len + CHUNK - 1) / CHUNK;
-    p.rec = dplr ? kda::dplr_record_bytes(enum_code(s->in_dtype) == KDA_DTYPE_BF16)
-                 : kda::chunk_record_bytes(p.d, enum_code(s->in_dtype) == KDA_DTYPE_BF16);
+    const bool bf16 = enum_code(s->in_dtype) == KDA_DTYPE_BF16;
+    p.rec = dplr ? kda::dplr_record_bytes(bf16) : kda::chunk_record_bytes(p.d, bf16 && !f32_operands);
     p.state_bytes = align256((size_t)p.N * s->heads * p.d * p.d * sizeof(float));
     return KDA_OK;
 }
@@ -199,9 +236,14 @@ size_t kda_chunk_fwd_workspace_size(const kda_shape_t* s) {
     const int64_t units = p.N * s->heads;
     int sc = 0;
     const int G = kda::chunk_segments(p.d, kda::chunk_value_slice(p.d, units), units, p.max_chunks, sc);
-    if (G > 0)  // sequence-parallel state pass: every record plus three per-segment state blocks
-        return p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G);
-    return p.state_bytes + window_record_bytes(p, per_chunk);
+    size_t need = G > 0  // sequence-parallel state pass: every record plus three per-segment state blocks
+                      ? p.state_bytes + (size_t)all * per_chunk + 3 * segment_bytes(p, s->heads, G)
+                      : p.state_bytes + window_record_bytes(p, per_chunk);
+    // bf16 inputs: room for one chunk of the fp32-operand records KDA_CHECK=1 may select
+    Plan p32;
+    if (enum_code(s->in_dtype) == KDA_DTYPE_BF16 && chunk_plan_full(s, s->num_seqs > 0, p32, false, true) == KDA_OK)
+        need = std::max(need, p32.state_bytes + (size_t)p32.N * s->heads * p32.rec);
+    return need;
 }
 
 
@@ -256,7 +298,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         return KDA_ERR_INVALID_ARG;
     if (final_state && overlaps_any(final_state, state_bytes, inputs)) return KDA_ERR_INVALID_ARG;
 
-    const size_t per_chunk = (size_t)p.N * H * p.rec;
+    size_t per_chunk = (size_t)p.N * H * p.rec;
     if (p.N == 0) return KDA_OK;  // nothing to compute
     if (static_scratch) {  // kda_chunk_fwd_noalloc: the device's static array, once arguments are valid
         if (workspace_bytes < p.state_bytes + per_chunk) return KDA_ERR_WORKSPACE;
@@ -276,6 +318,20 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         if (chk && chk[0] == '1') {
             kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
             if (cs != KDA_OK) return cs;
+        }
+    }
+    bool f32 = false;
+    if (check_enabled() && enum_code(s->in_dtype) == KDA_DTYPE_BF16) {
+        float* scratch = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.state_bytes);
+        kda_status_t rs = needs_f32_operands(v, tok_bytes, init_state, init_state ? state_bytes / 4 : 0, scratch,
+                                             stream, f32);
+        if (rs != KDA_OK) return rs;
+        // the layer's epilogue keeps o in the bf16 output buffer as fp16 until it normalises it
+        if (f32 && layer && layer->out_gate && enum_code(s->out_dtype) == KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+        if (f32) {  // the larger fp32 records
+            p.rec = kda::chunk_record_bytes(d, false);
+            per_chunk = (size_t)p.N * H * p.rec;
+            if (workspace_bytes < p.state_bytes + per_chunk) return KDA_ERR_WORKSPACE;
         }
     }
     // Few (sequence, head) pairs and a workspace for every record: the
@@ -332,7 +388,7 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         a.seg_init = reinterpret_cast<float*>(sb + 2 * segb);
     }
     hipError_t e = kda::chunk_dispatch(d, enum_code(s->in_dtype) == KDA_DTYPE_BF16, enum_code(s->out_dtype) == KDA_DTYPE_BF16,
-                                       layer && layer->qk_l2norm, bv, a, (int)nwin64, stream);
+                                       layer && layer->qk_l2norm, bv, a, (int)nwin64, stream, f32);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -545,8 +601,8 @@ struct BwdLayout {
 // its chunks in windows (KDA_BWD_WINDOW=n forces n chunks per window).
 constexpr size_t BWD_BUDGET = size_t(24) << 30;
 
-static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l) {
-    kda_status_t st = chunk_plan_full(s, varlen, p);
+static kda_status_t bwd_layout(const kda_shape_t* s, bool varlen, Plan& p, BwdLayout& l, bool f32 = false) {
+    kda_status_t st = chunk_plan_full(s, varlen, p, false, f32);
     if (st != KDA_OK) return st;
     const int64_t all = p.max_chunks > 0 ? p.max_chunks : 1;
     const size_t d = p.d, H = s->heads;
@@ -583,7 +639,11 @@ size_t kda_chunk_bwd_workspace_size(const kda_shape_t* s) {
     Plan p;
     BwdLayout l;
     if (!s || bwd_layout(s, s->num_seqs > 0, p, l) != KDA_OK) return 0;
-    return l.total;
+    size_t need = l.total;
+    // bf16 inputs: also the layout with the fp32-operand records KDA_CHECK=1 may select
+    if (enum_code(s->in_dtype) == KDA_DTYPE_BF16 && bwd_layout(s, s->num_seqs > 0, p, l, true) == KDA_OK)
+        need = std::max(need, l.total);
+    return need;
 }
 
 kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, const void* v,
@@ -641,8 +701,19 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
                              {dbeta, tb4},          {d_init_state, st_bytes}};
         if (overlaps_any(workspace, workspace_bytes, all)) return KDA_ERR_INVALID_ARG;
     }
+    bool f32 = false;
+    if (check_enabled() && enum_code(s->in_dtype) == KDA_DTYPE_BF16) {
+        float* scratch = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + l.rec);
+        kda_status_t rs = needs_f32_operands(v, tok, init_state, init_state ? st_bytes / 4 : 0, scratch, stream, f32);
+        if (rs != KDA_OK) return rs;
+        if (f32) {  // the recompute with fp32 records: their layout
+            if ((st = bwd_layout(s, cu_seqlens != nullptr, p, l, true)) != KDA_OK) return st;
+            if (workspace_bytes < l.total) return KDA_ERR_WORKSPACE;
+        }
+    }
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     kda::BwdArgs b;
+    b.f32_records = f32;
     kda::ChunkArgs& a = b.fwd;
     a.q = q;
     a.k = k;

@@ -1342,7 +1342,7 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
     const size_t units = (size_t)a.N * a.H, sb = units * D * D * sizeof(float);
     hipError_t e;
     for (int w = 0; w + 1 < nbw; ++w) {
-        if ((e = chunk_snapshot_dispatch(D, BF, a, rw, w * rpb, rpb, false, st)) != hipSuccess) return e;
+        if ((e = chunk_snapshot_dispatch(D, BF, a, rw, w * rpb, rpb, false, st, b.f32_records)) != hipSuccess) return e;
         if ((e = hipMemcpyAsync(b.ckpt + (size_t)w * units * D * D, a.state_buf, sb, hipMemcpyDeviceToDevice, st)) !=
             hipSuccess)
             return e;
@@ -1354,8 +1354,8 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
         ChunkArgs r = a;
         r.snap_wc = wb;
         r.snap_j0 = w * wb;
-        if ((e = chunk_snapshot_dispatch(D, BF, r, rw, w * rpb, std::min(rpb, nrw - w * rpb), true, st)) !=
-            hipSuccess)
+        if ((e = chunk_snapshot_dispatch(D, BF, r, rw, w * rpb, std::min(rpb, nrw - w * rpb), true, st,
+                                         b.f32_records)) != hipSuccess)
             return e;
         BwdArgs bw = b;
         bw.fwd.Wc = wb;

@@ -1324,22 +1324,56 @@ static hipError_t run_snapshots(const ChunkArgs& base, int window, int w0, int n
 }
 
 hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, int w0, int nw, bool snap,
-                                   hipStream_t st) {
-    if (d == 128)
+                                   hipStream_t st, bool f32_operands) {
+    if (d == 128) {
+        if (in_bf16 && f32_operands) return run_snapshots<128, bf16_t, float>(a, window, w0, nw, snap, st);
         return in_bf16 ? run_snapshots<128, bf16_t, _Float16>(a, window, w0, nw, snap, st)
                        : run_snapshots<128, float, float>(a, window, w0, nw, snap, st);
+    }
+    if (in_bf16 && f32_operands) return run_snapshots<64, bf16_t, float>(a, window, w0, nw, snap, st);
     return in_bf16 ? run_snapshots<64, bf16_t, _Float16>(a, window, w0, nw, snap, st)
                    : run_snapshots<64, float, float>(a, window, w0, nw, snap, st);
 }
 
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
-                          hipStream_t st) {
+                          hipStream_t st, bool f32_operands) {
     if (d == 128) {
+        if (in_bf16 && f32_operands) return run_norm<128, bf16_t, float>(a, out_bf16, qk_norm, nwin, bv, st);
         if (in_bf16) return run_norm<128, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, st);
         return run_norm<128, float, float>(a, out_bf16, qk_norm, nwin, bv, st);
     }
+    if (in_bf16 && f32_operands) return run_norm<64, bf16_t, float>(a, out_bf16, qk_norm, nwin, bv, st);
     if (in_bf16) return run_norm<64, bf16_t, _Float16>(a, out_bf16, qk_norm, nwin, bv, st);
     return run_norm<64, float, float>(a, out_bf16, qk_norm, nwin, bv, st);
+}
+
+// One partial max of |x| per block: grid-stride over the elements, then a
+// shared-memory tree over the block's 256 threads.
+template <typename T>
+__global__ void __launch_bounds__(256) max_abs_kernel(const T* x, size_t n, float* block_max) {
+    __shared__ float red[256];
+    float m = 0.f;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        const float a = fabsf(to_f32(x[i]));
+        m = a == a ? fmaxf(m, a) : __builtin_inff();
+    }
+    red[threadIdx.x] = m;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) block_max[blockIdx.x] = red[0];
+}
+
+hipError_t max_abs_dispatch(const void* x, size_t n, bool bf16, float* block_max, int nblocks, hipStream_t st) {
+    if (bf16)
+        hipLaunchKernelGGL((max_abs_kernel<bf16_t>), dim3(nblocks), dim3(256), 0, st, static_cast<const bf16_t*>(x),
+                           n, block_max);
+    else
+        hipLaunchKernelGGL((max_abs_kernel<float>), dim3(nblocks), dim3(256), 0, st, static_cast<const float*>(x), n,
+                           block_max);
+    return hipGetLastError();
 }
 
 }  // namespace kda

@@ -83,6 +83,7 @@ struct BwdArgs {
     float* dG;            // [tokens, H, D] fp32: dL/dlog_alpha per channel; null when the gate is per head
     float* dla_head;      // [tokens, H] fp32 when the gate is per head, else null
     float* dbeta;         // [tokens, H] fp32
+    bool f32_records = false;  // bf16 inputs: recompute the forward with fp32 operands and records
 };
 size_t bwd_record_bytes(int d);
 hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, hipStream_t st);
@@ -91,7 +92,7 @@ hipError_t bwd_dispatch(int d, bool in_bf16, bool dout_bf16, const BwdArgs& b, h
 // chunk a.snap_j0), for record windows w0 .. w0 + nw - 1 of `window` chunks
 // through one record buffer, carrying S through a.state_buf; no outputs.
 hipError_t chunk_snapshot_dispatch(int d, bool in_bf16, const ChunkArgs& a, int window, int w0, int nw, bool snap,
-                                   hipStream_t st);
+                                   hipStream_t st, bool f32_operands = false);
 
 size_t chunk_record_bytes(int d, bool in_bf16);
 int chunk_value_slice(int d, int64_t units);
@@ -102,8 +103,13 @@ int chunk_segments(int d, int bv, int64_t units, int64_t max_chunks, int& chunks
 // With a.out_gate set, the state pass writes o to `out` (fp16 when out_bf16,
 // else fp32) and an epilogue pass after the last window replaces it in place
 // by RMSNorm(o) * w * sigmoid(out_gate) (bf16 or fp32).
+// f32_operands: bf16 inputs with fp32 matrix-core operands and records (the
+// fp32 inputs' kernels reading bf16), for values past the fp16 operands' range.
 hipError_t chunk_dispatch(int d, bool in_bf16, bool out_bf16, bool qk_norm, int bv, const ChunkArgs& a, int nwin,
-                          hipStream_t st);
+                          hipStream_t st, bool f32_operands = false);
+// Largest |x| over n elements (bf16 or fp32; NaN counts as +inf), as one partial
+// maximum per block in block_max[0 .. nblocks), nblocks <= 1024.
+hipError_t max_abs_dispatch(const void* x, size_t n, bool bf16, float* block_max, int nblocks, hipStream_t st);
 // General DPLR variant (dplr_chunk.hip): dk = dv = 128, windows of a.Wc chunks,
 // value slices of 16 or 32 columns (16 for fp32 inputs).
 size_t dplr_record_bytes(bool in_bf16);

@@ -50,7 +50,14 @@
  *    operands are staged in fp16, so |v|, state entries and outputs must
  *    stay below 6.5e4 (larger values give non-finite results, never silent
  *    garbage); q and k are expected L2-normalised per head as in the KDA
- *    layer.
+ *    layer.  With KDA_CHECK=1 and bf16 inputs, kda_chunk_fwd,
+ *    kda_chunk_fwd_noalloc, kda_layer_fwd and kda_chunk_bwd also measure
+ *    max|v| and max|init_state| on the device (synchronising `stream`) and,
+ *    past 1024, run that call with fp32 matrix-core operands and records
+ *    (correct for any finite magnitude; the workspace sizes returned for
+ *    bf16 inputs cover it).  kda_layer_fwd with an out_gate and bf16 output
+ *    then returns KDA_ERR_UNSUPPORTED: its o passes through fp16 in the
+ *    output buffer.  The general DPLR variant has no such switch.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = default stream)
  *    and runs asynchronously; results are valid once the stream is
  *    synchronised.  Argument validation is synchronous: on any error no
