@@ -40,8 +40,9 @@ METRIC = "KDA prefill tokens/s (H32,d128,T64K) + decode-step HBM GB/s, 1 MI355X"
 # sources each traffic measurement depends on (profiles/traffic.json is ignored once they change)
 KERNEL_SOURCES = {
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_device.h"],
-    "prefill": ["gated_delta_rule_53_amd/csrc/kda_chunk.hip", "gated_delta_rule_53_amd/csrc/kda_device.h",
-                "gated_delta_rule_53_amd/csrc/kda_internal.h", "gated_delta_rule_53_amd/csrc/kda_api.hip"],
+    "prefill": ["gated_delta_rule_53_amd/csrc/kda_chunk.hip", "gated_delta_rule_53_amd/csrc/kda_chunk_common.h",
+                "gated_delta_rule_53_amd/csrc/kda_device.h", "gated_delta_rule_53_amd/csrc/kda_internal.h",
+                "gated_delta_rule_53_amd/csrc/kda_api.hip"],
 }
 
 
