@@ -241,10 +241,17 @@ def main():
         n = args.copy_probe << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
+        ms = []
         for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes": n, "launches": 10}), flush=True)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        med = float(np.median(ms[2:]))
+        print(json.dumps({"copy_probe_bytes": n, "launches": 10, "ms_median": med,
+                          "read_plus_write_tb_s": 2 * n / med / 1e9}), flush=True)
         return
 
     if args.dplr_only:
