@@ -60,7 +60,7 @@ struct DRec {
 };
 
 // LDS of the chunk-local kernel.  R_OP: the gate products of the half-blocks,
-// then the operand rows of each round of gated products (128 rows: b, q, a, k
+// then the operand rows of each set of gated products (128 rows: b, q, a, k
 // scaled for one anchor), then T (fp32), then the channel-major right-hand sides
 // B e^{Gx} and V.  R_A: Mba (fp32), later T as an fp16 operand.  R_M: Mbk stored
 // transposed, -Mqa and Mqk (later T Mbk).
@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(512) dplr_local_kernel(ChunkArgs a) {
                 sMqk[row * C::MP + col] = from_f32<OT>(x);
         }
     };
-    // rows of the operand rounds: b at 0.., q at 32.., a at 64.., k at 96..
+    // operand rows of each set of products: b at 0.., q at 32.., a at 64.., k at 96..
     auto put_left = [&](int row, int i, float fb0, float fb1, float fq0, float fq1) {
         put2<OT>(sOp + row * C::DP + ch, bb.get(i, 0) * fb0, bb.get(i, 1) * fb1);
         put2<OT>(sOp + (32 + row) * C::DP + ch, qq.get(i, 0) * fq0, qq.get(i, 1) * fq1);
@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(512) dplr_local_kernel(ChunkArgs a) {
         return acc;
     };
 
-    // ---- round 1: rows 32..63 against columns 0..31, anchor row 31 ----
+    // ---- level 32: rows 32..63 against columns 0..31, anchor row 31 ----
     if (hb >= 4) {
         const float L0 = prodH(4, hb - 1, 0), L1 = prodH(4, hb - 1, 1);
 #pragma unroll
@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(512) dplr_local_kernel(ChunkArgs a) {
     }
     lds_barrier();
 
-    // ---- round 2: rows 16..31 against 0..15 (anchor 15), 48..63 against 32..47 (anchor 47) ----
+    // ---- level 16: rows 16..31 against 0..15 (anchor 15), 48..63 against 32..47 (anchor 47) ----
     {
         const int half = hb >> 2, hq = hb & 3;
         if (hq >= 2) {
@@ -309,7 +309,7 @@ __global__ void __launch_bounds__(512) dplr_local_kernel(ChunkArgs a) {
                     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(qq.get(i, e)), fabsf(kk.get(i, e))),
                                          fmaxf(fabsf(aa.get(i, e)), fabsf(bb.get(i, e)))));
         }
-        // also the barrier after round 2's products
+        // also the barrier after the level-16 products
         wide = C::F16 ? __syncthreads_or(!(mx * fx <= DPLR_F16_OPERAND_LIMIT) || !(fx <= DPLR_F16_FACTOR_LIMIT))
                       : __syncthreads_or(!(fx <= DPLR_F32_FACTOR_LIMIT));
     }
@@ -336,7 +336,7 @@ __global__ void __launch_bounds__(512) dplr_local_kernel(ChunkArgs a) {
     } else {
         // Every factor <= 1.  Later half against earlier half: rows 8..15 carry
         // their decay since the boundary, rows 0..7 the decay after them up to it;
-        // fp32 operands, one block per round (b 0..15, q 16..31, a 32..47, k 48..63;
+        // fp32 operands, one block at a time (b 0..15, q 16..31, a 32..47, k 48..63;
         // the other half's rows are zero, so the tile holds only those pairs).
 #pragma unroll 1
         for (int db = 0; db < 4; ++db) {

@@ -41,7 +41,7 @@ _LIBS: dict = {}
 
 # KDA_ORACLE_SANITIZE=1 builds and loads the oracle with AddressSanitizer and
 # UndefinedBehaviorSanitizer (a separate library; the Python process must then
-# preload gcc's libasan and libubsan).
+# preload gcc's libasan and libubsan, as tests/test_sanitizers.py does).
 _SANITIZE = os.environ.get("KDA_ORACLE_SANITIZE") == "1"
 _SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
