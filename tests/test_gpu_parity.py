@@ -107,7 +107,8 @@ def test_chunk_small(kda, T, H, D, dtype, init, lens):
 
 
 def test_chunk_strong_decay(kda):
-    """Gates near the supported edge (log_alpha down to about -10 per token)."""
+    """Strong gates (log_alpha down to about -10 per token): diagonal sub-blocks near the
+    single-anchor form's range limit and past it."""
     d = random_small(5, 256, 2, 128, 128, dtype="bf16", gate_scale=4.0)
     assert d["log_alpha"].min() < -8
     o, S = run_chunk(kda, torch, d)
