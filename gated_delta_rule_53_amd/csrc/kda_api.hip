@@ -313,12 +313,9 @@ static kda_status_t chunk_fwd_impl(const kda_shape_t* s, const kda_layer_t* laye
         overlaps(workspace, workspace_bytes, init_state, state_bytes) ||
         overlaps(workspace, workspace_bytes, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
-    if (cu_seqlens) {
-        const char* chk = getenv("KDA_CHECK");
-        if (chk && chk[0] == '1') {
-            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
-            if (cs != KDA_OK) return cs;
-        }
+    if (cu_seqlens && check_enabled()) {
+        kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
+        if (cs != KDA_OK) return cs;
     }
     bool f32 = false;
     if (check_enabled() && enum_code(s->in_dtype) == KDA_DTYPE_BF16) {
@@ -458,12 +455,9 @@ kda_status_t kda_dplr_chunk_fwd(const kda_shape_t* s, const void* q, const void*
         overlaps(workspace, workspace_bytes, init_state, state_bytes) ||
         overlaps(workspace, workspace_bytes, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
-    if (cu_seqlens) {
-        const char* chk = getenv("KDA_CHECK");
-        if (chk && chk[0] == '1') {
-            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
-            if (cs != KDA_OK) return cs;
-        }
+    if (cu_seqlens && check_enabled()) {
+        kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
+        if (cs != KDA_OK) return cs;
     }
     // one record buffer for every chunk if it fits, else windows of chunks
     const size_t avail = workspace_bytes - p.state_bytes;
@@ -684,12 +678,9 @@ kda_status_t kda_chunk_bwd(const kda_shape_t* s, const void* q, const void* k, c
         }
     }
     if (p.N == 0) return KDA_OK;
-    if (cu_seqlens) {
-        const char* chk = getenv("KDA_CHECK");
-        if (chk && chk[0] == '1') {
-            kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
-            if (cs != KDA_OK) return cs;
-        }
+    if (cu_seqlens && check_enabled()) {
+        kda_status_t cs = check_cu_seqlens(cu_seqlens, p, stream);
+        if (cs != KDA_OK) return cs;
     }
     if (!workspace || !aligned16(workspace) || workspace_bytes < l.total) return KDA_ERR_WORKSPACE;
     {  // the workspace is written by the kernels: it must not overlap any argument

@@ -2,7 +2,7 @@
 
 S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T with independent a and b ("Kimi
 Linear" page, "The constrained DPLR form and the chunkwise algorithm").  Cases: several
-chunks with ragged tails, varlen with empty and one-token sequences, bf16 output, the
+chunks with ragged tails, a dense batch, varlen with empty and one-token sequences, bf16 output, the
 reduction to KDA, gates strong enough that the diagonal blocks take the form whose
 factors are all at most 1 (every chunk, and single chunks among ordinary ones), a
 workspace small enough for several windows, and the benchmark's shape (1 x 65,536
@@ -74,6 +74,27 @@ def test_dplr_varlen(kda, dtype):
     d = synth.dplr_small(31, 0, 2, D, dtype, lens=lens, init_std=0.05)
     o, S = run_dplr(kda, d)
     check(d, o, S, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dplr_dense_batch(kda, dtype):
+    """A dense batch of three 150-token sequences ([B, T, H, d], no cu_seqlens), against the
+    oracle run over the same rows as three sequences; the final state once returned and once
+    not requested (the output must not change)."""
+    B, T, H = 3, 150, 2
+    d = synth.dplr_small(37, T, H, D, dtype, init_std=0.02, batch=B)
+    q, k, v, a, b, la = (to_dev(d[x], torch).reshape(B, T, H, -1) for x in ("q", "k", "v", "a", "b", "log_alpha"))
+    init = to_dev(d["init"], torch)
+    out = nan_tensor(torch, (B, T, H, D), torch.float32)
+    fin = nan_tensor(torch, (B, H, D, D))
+    out, fin = kda.dplr_chunk_fwd(q, k, v, a, b, la, init, out=out, final_state=fin)
+    out2 = nan_tensor(torch, (B, T, H, D), torch.float32)
+    out2, fin2 = kda.dplr_chunk_fwd(q, k, v, a, b, la, init, out=out2, final_state=None)
+    torch.cuda.synchronize()
+    assert fin2 is None
+    o = out.reshape(B * T, H, D).cpu().numpy()
+    assert np.array_equal(o, out2.reshape(B * T, H, D).cpu().numpy())
+    check(d, o, fin.cpu().numpy(), dtype)
 
 
 def test_dplr_bf16_output(kda):
