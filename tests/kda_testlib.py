@@ -23,20 +23,24 @@ def to_dev(x, torch, device="cuda"):
     return t.to(device)
 
 
-def assert_close(name, got, ref, tol):
-    m = oracle.metrics(got, ref)
-    assert np.isfinite(np.asarray(got, np.float64)).all(), f"{name}: non-finite values"
+def _report(name, m, tol):
+    """One line per comparison (shown with pytest -s), then the bar."""
+    print(f"  {name}: max|err|/rms {m['max_over_rms']:.2e} (bar {tol:.0e}), max abs {m['max_abs']:.2e}, "
+          f"rms ref {m['rms_ref']:.2e}", flush=True)
     assert m["max_over_rms"] <= tol, (f"{name}: max|err|/rms = {m['max_over_rms']:.3e} > {tol:.1e} "
                                       f"(max abs {m['max_abs']:.3e}, rms ref {m['rms_ref']:.3e})")
     return m
+
+
+def assert_close(name, got, ref, tol):
+    m = oracle.metrics(got, ref)
+    assert np.isfinite(np.asarray(got, np.float64)).all(), f"{name}: non-finite values"
+    return _report(name, m, tol)
 
 
 def assert_metrics(name, acc, tol):
     """assert_close for a figure accumulated over pieces (oracle.Metrics)."""
-    m = acc.result()
-    assert m["max_over_rms"] <= tol, (f"{name}: max|err|/rms = {m['max_over_rms']:.3e} > {tol:.1e} "
-                                      f"(max abs {m['max_abs']:.3e}, rms ref {m['rms_ref']:.3e})")
-    return m
+    return _report(name, acc.result(), tol)
 
 
 def nan_tensor(torch, shape, dtype=None, device="cuda"):
