@@ -38,6 +38,22 @@ def assert_close(name, got, ref, tol):
     return _report(name, m, tol)
 
 
+def assert_close_bf16_storage(name, got, ref, tol):
+    """Parity of a bf16-stored output: each element may differ from the reference by the
+    rounding of its storage, up to 2^-8 of its magnitude (round to nearest even at 8
+    significant bits), on top of tol x RMS(ref).  Over many elements the largest ones reach
+    several times RMS(ref), where that rounding alone can exceed an RMS-relative bar."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.maximum(np.abs(got), np.abs(ref))
+    worst = max(float(excess.max()), 0.0) if ref.size else 0.0
+    fig = worst / rms if rms > 0 else (0.0 if worst == 0 else float("inf"))
+    print(f"  {name}: beyond bf16 storage rounding, max|err|/rms {fig:.2e} (bar {tol:.0e})", flush=True)
+    assert fig <= tol, f"{name}: {fig:.3e} beyond the bf16 storage rounding > {tol:.1e}"
+
+
 def assert_metrics(name, acc, tol):
     """assert_close for a figure accumulated over pieces (oracle.Metrics)."""
     return _report(name, acc.result(), tol)

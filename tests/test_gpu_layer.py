@@ -23,11 +23,12 @@ epilogue rather than applied to y directly:
 import numpy as np
 import pytest
 
+import oracle
 import synth
 from oracle import layer as olayer
 from synth import WORKLOADS, layer_small, random_small
 
-from kda_testlib import DECODE_TOL, TOL, assert_close, to_dev, nan_tensor
+from kda_testlib import DECODE_TOL, TOL, assert_close, assert_close_bf16_storage, assert_metrics, to_dev, nan_tensor
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -141,16 +142,60 @@ def test_layer_prefill_segments(kda, monkeypatch):
 
 
 def test_layer_prefill_workload(kda):
-    """64K tokens x 32 heads in the benchmark's launch configuration; every element of four heads."""
+    """64K tokens x 32 heads in the benchmark's launch configuration; every element of every
+    head, with fp32 y and with bf16 y (the benchmark's).  The oracle runs on 8 heads at a time
+    (heads are independent) and the figures accumulate over the four groups.
+
+    fp32 y is held to assert_y_close's checks.  A bf16 y also carries its own storage
+    rounding, up to 2^-8 of each element (round to nearest even at 8 significant bits): over
+    the 268 M outputs the largest |o| reach several times RMS(o), so that rounding alone can
+    exceed the RMS-relative bar.  Each bf16 element is therefore allowed 2^-8 of its own
+    magnitude on top of the bar; the row-RMS check is the same for both."""
     w = WORKLOADS[2]
     d = synth.make_layer_prefill(w)
-    y, S = run_layer(kda, d, out_dtype=torch.bfloat16)
-    heads = [0, 9, 20, 31]
-    sub = {x: d[x][:, heads] for x in ("q", "k", "v", "g", "beta", "out_gate")}
-    sub.update(cu_seqlens=d["cu_seqlens"], init=d["init"][:, heads], norm_weight=d["norm_weight"])
-    _, S_ref, o_ref = oracle_layer(sub)
-    assert_y_close("y", y[:, heads], o_ref, sub["out_gate"], sub["norm_weight"], TOL["bf16"], True)
-    assert_close("state", S[:, heads], S_ref, TOL["bf16"])
+    y32, S32 = run_layer(kda, d, out_dtype=torch.float32)
+    y16, S16 = run_layer(kda, d, out_dtype=torch.bfloat16)
+    acc32, acc_s, acc_s16 = oracle.Metrics(), oracle.Metrics(), oracle.Metrics()
+    sum_ref2, count, excess16, row_dev = 0.0, 0, 0.0, {"f32": 0.0, "bf16": 0.0}
+    wt = olayer.widen(d["norm_weight"])
+    for h0 in range(0, w.heads, 8):
+        heads = list(range(h0, h0 + 8))
+        print(f"  layer oracle, heads {h0}..{h0 + 7}", flush=True)
+        sub = {x: d[x][:, heads] for x in ("q", "k", "v", "g", "beta", "out_gate")}
+        sub.update(cu_seqlens=d["cu_seqlens"], init=d["init"][:, heads], norm_weight=d["norm_weight"])
+        _, S_ref, o_ref = oracle_layer(sub)
+        gate = wt * olayer.sigmoid(sub["out_gate"])
+        ms_ref = np.mean(o_ref * o_ref, axis=-1, keepdims=True)
+        r_ref = np.sqrt(ms_ref + 1e-6)
+        keep = ms_ref[..., 0] >= 1e3 * 1e-6
+        for name, y in (("f32", y32), ("bf16", y16)):
+            # y undone to o with the oracle's row RMS (as assert_y_close), and the row RMS itself
+            n = np.asarray(y[:, heads], np.float64) / gate
+            assert np.isfinite(n).all(), f"y ({name}): non-finite values"
+            o_gpu = n * r_ref
+            if name == "f32":
+                acc32.add(o_gpu, o_ref)
+            else:
+                err = np.abs(o_gpu - o_ref) - 2.0 ** -8 * np.maximum(np.abs(o_gpu), np.abs(o_ref))
+                excess16 = max(excess16, float(err.max()))
+            rows = np.sqrt(np.mean(n * n, axis=-1))[keep]
+            rows_ref = (np.sqrt(ms_ref[..., 0]) / r_ref[..., 0])[keep]
+            if rows.size:
+                row_dev[name] = max(row_dev[name], float(np.abs(rows - rows_ref).max()))
+            del n, o_gpu
+        sum_ref2 += float(np.sum(o_ref * o_ref))
+        count += o_ref.size
+        acc_s.add(S32[:, heads], S_ref)
+        acc_s16.add(S16[:, heads], S_ref)
+        del o_ref
+    assert_metrics("y fp32 (as o)", acc32, TOL["bf16"])
+    fig16 = max(excess16, 0.0) / np.sqrt(sum_ref2 / count)
+    print(f"  y bf16 (as o): beyond 2^-8 of each element, max|err|/rms {fig16:.2e} (bar {TOL['bf16']:.0e})",
+          flush=True)
+    assert fig16 <= TOL["bf16"], f"y bf16: {fig16:.3e} beyond the element rounding allowance"
+    assert row_dev["f32"] <= 1e-5 and row_dev["bf16"] <= 1e-2, f"row RMS after the epilogue off by {row_dev}"
+    assert_metrics("state", acc_s, TOL["bf16"])
+    assert_metrics("state (bf16 y run)", acc_s16, TOL["bf16"])
 
 
 def _decode_inputs(N, H, D, dtype, gate, steps, seed):
@@ -183,8 +228,8 @@ def test_layer_decode(kda, N, H, D, dtype, gate, epi):
     assert_close("state", state.cpu().numpy(), S_ref, DECODE_TOL)
 
 
-def test_layer_decode_workload_sampled(kda):
-    """256 sequences x 32 heads (the decode benchmark's shape), 4 steps, bf16 y; 4 heads checked."""
+def test_layer_decode_workload(kda):
+    """256 sequences x 32 heads (the decode benchmark's shape), 4 steps, bf16 y; every head."""
     w = WORKLOADS[3]
     S0 = synth.make_decode_state(w)
     state = to_dev(S0, torch)
@@ -197,9 +242,7 @@ def test_layer_decode_workload_sampled(kda):
                                           norm_weight=to_dev(wt, torch),
                                           out=nan_tensor(torch, a[2].shape, torch.bfloat16)).float().cpu().numpy())
     torch.cuda.synchronize()
-    heads = [0, 7, 19, 31]
-    sub = [{x: st[x][:, heads] for x in st} for st in seq]
-    ref_outs, S_ref = olayer.decode_steps(S0[:, heads], sub, wt)
-    for i in range(len(seq)):
-        assert_close(f"y{i}", outs[i][:, heads], ref_outs[i], TOL["bf16"])
-    assert_close("state", state.cpu().numpy()[:, heads], S_ref, DECODE_TOL)
+    ref_outs, S_ref = olayer.decode_steps(S0, seq, wt)
+    for i in range(len(seq)):  # decode is fp32 arithmetic: its bar once y's bf16 storage is allowed for
+        assert_close_bf16_storage(f"y{i}", outs[i], ref_outs[i], DECODE_TOL)
+    assert_close("state", state.cpu().numpy(), S_ref, DECODE_TOL)

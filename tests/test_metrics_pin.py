@@ -88,3 +88,30 @@ def test_pieces_agree_with_the_whole():
     assert part["max_abs"] == whole["max_abs"]
     for key in ("max_over_rms", "rms_err", "rms_ref"):
         assert part[key] == pytest.approx(whole[key], rel=1e-13)
+
+
+def test_bf16_storage_allowance():
+    """The bf16-output check allows each element the rounding of its own storage and no more:
+    fp32 values rounded to nearest even bf16 pass with no further tolerance, while values
+    moved two bf16 units away fail; an element's allowance does not grow with the others'."""
+    from kda_testlib import assert_close_bf16_storage
+    import synth
+
+    r = np.random.default_rng(3)
+    ref = (r.standard_normal(4096) * np.exp(r.uniform(-3, 3, 4096))).astype(np.float32)
+    rounded = synth.f32_to_bf16_bits(ref)
+    got = (rounded.astype(np.uint32) << 16).view(np.float32)
+    assert_close_bf16_storage("rounded", got, ref, 0.0)
+    # 2^-6 of its magnitude (two to four bf16 units in the last place) at one element
+    bad = got.copy()
+    i = int(np.argmax(np.abs(ref)))
+    bad[i] = np.float32(ref[i] * (1 + 2.0 ** -6))
+    with pytest.raises(AssertionError):
+        assert_close_bf16_storage("moved", bad, ref, 1e-3)
+    # a large element's allowance does not cover a small one: moving the smallest element by
+    # 2^-8 of the largest fails
+    bad = got.copy()
+    j = int(np.argmin(np.abs(ref)))
+    bad[j] = np.float32(ref[j] + 2.0 ** -8 * np.abs(ref).max())
+    with pytest.raises(AssertionError):
+        assert_close_bf16_storage("small", bad, ref, 1e-3)
