@@ -17,11 +17,11 @@
 namespace {
 
 constexpr int CHUNK = 64;
-// Record budget across the two window buffers: records written by the
-// chunk-local pass should still sit in the 256 MB last-level (MALL) cache when
-// the state pass reads them.  The chunk-local pass streams its inputs and
-// outputs with non-temporal accesses, so records of up to about 230 MB stay
-// resident; past that the state pass starts missing.
+// Record budget of one window: records written by the chunk-local pass should
+// still sit in the 256 MB last-level (MALL) cache when the state pass reads
+// them.  The chunk-local pass streams its inputs and outputs with non-temporal
+// accesses, so records of up to about 230 MB stay resident; past that the state
+// pass starts missing.
 constexpr size_t RECORD_BUDGET = size_t(220) << 20;
 constexpr int64_t MIN_WINDOW = 32;
 constexpr size_t WINDOW_CAP = size_t(4) << 30;
