@@ -98,24 +98,32 @@ def chunkwise(q, k, v, log_alpha, beta, S0, C=64, solve="substitution"):
     o = np.empty((T, dv))
     for c0 in range(0, T, C):
         c1 = min(T, c0 + C)
-        Q, K, V = q[c0:c1], k[c0:c1], v[c0:c1]
-        b = beta[c0:c1]
-        G = np.cumsum(log_alpha[c0:c1], axis=0)
-        D = np.exp(G[:, None, :] - G[None, :, :])           # [r, i, c] = exp(G_rc - G_ic)
-        kk = np.einsum("rc,ic,ric->ri", K, K, D)
-        qk = np.einsum("rc,ic,ric->ri", Q, K, D)
-        Atil = np.tril(b[:, None] * kk, -1)
-        P = np.tril(qk)
-        if solve == "substitution":
-            Tm = forward_substitution(Atil)
-        else:
-            Tm = np.linalg.inv(np.eye(len(b)) + Atil)
-        W = Tm @ (b[:, None] * (K * np.exp(G)))
-        Ut = Tm @ (b[:, None] * V)
-        U = Ut - W @ S
-        o[c0:c1] = (Q * np.exp(G)) @ S + P @ U
-        S = np.exp(G[-1])[:, None] * S + (K * np.exp(G[-1][None, :] - G)).T @ U
+        L = chunk_local(q[c0:c1], k[c0:c1], v[c0:c1], log_alpha[c0:c1], beta[c0:c1], solve)
+        U = L["Ut"] - L["W"] @ S
+        o[c0:c1] = L["Qg"] @ S + L["P"] @ U
+        S = L["gamma"][:, None] * S + L["Kh"].T @ U
     return o, S
+
+
+def chunk_local(Q, K, V, log_alpha, beta, solve="substitution"):
+    """The quantities of one chunk that do not depend on the state entering it (the
+    terms of ``chunkwise``'s docstring): G, Atil, Tm = (I + Atil)^-1, W, Util, P,
+    Qg = Q exp(G), Kh = K exp(G_last - G) and gamma = exp(G_last); fp64 dict."""
+    b = np.asarray(beta, np.float64)
+    G = np.cumsum(log_alpha, axis=0)
+    D = np.exp(G[:, None, :] - G[None, :, :])           # [r, i, c] = exp(G_rc - G_ic)
+    kk = np.einsum("rc,ic,ric->ri", K, K, D)
+    qk = np.einsum("rc,ic,ric->ri", Q, K, D)
+    Atil = np.tril(b[:, None] * kk, -1)
+    P = np.tril(qk)
+    if solve == "substitution":
+        Tm = forward_substitution(Atil)
+    else:
+        Tm = np.linalg.inv(np.eye(len(b)) + Atil)
+    W = Tm @ (b[:, None] * (K * np.exp(G)))
+    Ut = Tm @ (b[:, None] * V)
+    return {"G": G, "Atil": Atil, "Tm": Tm, "W": W, "Ut": Ut, "P": P, "Qg": Q * np.exp(G),
+            "Kh": K * np.exp(G[-1][None, :] - G), "gamma": np.exp(G[-1])}
 
 
 # ---------------------------------------------------------------------------
