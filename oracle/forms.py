@@ -180,19 +180,29 @@ def dplr_chunkwise(q, k, v, a, b, log_alpha, S0, C=64):
     o = np.empty((T, dv))
     for c0 in range(0, T, C):
         c1 = min(T, c0 + C)
-        Q, K, V, A_, B_ = q[c0:c1], k[c0:c1], v[c0:c1], a[c0:c1], b[c0:c1]
-        G = np.cumsum(log_alpha[c0:c1], axis=0)
-        Gx = G - log_alpha[c0:c1]
-        # [r, i, c]; only i < r (Dx) and i <= r (D) are used, where the exponent is <= 0
-        Dx = np.exp(np.minimum(Gx[:, None, :] - G[None, :, :], 0.0))
-        D = np.exp(np.minimum(G[:, None, :] - G[None, :, :], 0.0))
-        Mba = np.tril(np.einsum("rc,ic,ric->ri", B_, A_, Dx), -1)
-        Mbk = np.tril(np.einsum("rc,ic,ric->ri", B_, K, Dx), -1)
-        Mqa = np.tril(np.einsum("rc,ic,ric->ri", Q, A_, D))
-        Mqk = np.tril(np.einsum("rc,ic,ric->ri", Q, K, D))
-        n = c1 - c0
-        w = np.linalg.solve(np.eye(n) + Mba, (B_ * np.exp(Gx)) @ S + Mbk @ V)
-        o[c0:c1] = (Q * np.exp(G)) @ S + Mqk @ V - Mqa @ w
-        dec = np.exp(G[-1][None, :] - G)
-        S = np.exp(G[-1])[:, None] * S + (K * dec).T @ V - (A_ * dec).T @ w
+        L = dplr_chunk_local(q[c0:c1], k[c0:c1], v[c0:c1], a[c0:c1], b[c0:c1], log_alpha[c0:c1])
+        w = L["Z"] + L["Y"] @ S
+        o[c0:c1] = L["Qg"] @ S + L["Mqk"] @ v[c0:c1] - L["Mqa"] @ w
+        S = L["gamma"][:, None] * S + L["Kh"].T @ v[c0:c1] - L["Ah"].T @ w
     return o, S
+
+
+def dplr_chunk_local(Q, K, V, A_, B_, log_alpha):
+    """The state-free quantities of one chunk of ``dplr_chunkwise`` (fp64 dict): the four
+    gated products, Y = (I + Mba)^-1 B e^{Gx} and Z = (I + Mba)^-1 Mbk V (so that
+    w = Z + Y S), Qg = Q e^G, Kh = K e^{G_last - G}, Ah = A e^{G_last - G} and
+    gamma = e^{G_last}."""
+    G = np.cumsum(log_alpha, axis=0)
+    Gx = G - log_alpha
+    # [r, i, c]; only i < r (Dx) and i <= r (D) are used, where the exponent is <= 0
+    Dx = np.exp(np.minimum(Gx[:, None, :] - G[None, :, :], 0.0))
+    D = np.exp(np.minimum(G[:, None, :] - G[None, :, :], 0.0))
+    Mba = np.tril(np.einsum("rc,ic,ric->ri", B_, A_, Dx), -1)
+    Mbk = np.tril(np.einsum("rc,ic,ric->ri", B_, K, Dx), -1)
+    Mqa = np.tril(np.einsum("rc,ic,ric->ri", Q, A_, D))
+    Mqk = np.tril(np.einsum("rc,ic,ric->ri", Q, K, D))
+    I_M = np.eye(len(G)) + Mba
+    dec = np.exp(G[-1][None, :] - G)
+    return {"Mba": Mba, "Mbk": Mbk, "Mqa": Mqa, "Mqk": Mqk,
+            "Y": np.linalg.solve(I_M, B_ * np.exp(Gx)), "Z": np.linalg.solve(I_M, Mbk @ V),
+            "Qg": Q * np.exp(G), "Kh": K * dec, "Ah": A_ * dec, "gamma": np.exp(G[-1])}

@@ -1,7 +1,8 @@
 """Rows a1-a3 at their own boundary: the per-chunk record of the chunk-local pass against
 the fp64 chunk-local quantities (``oracle.forms.chunk_local``, the state-free part of the
 pinned chunkwise form; "Kimi Linear" page, "The constrained DPLR form and the chunkwise
-algorithm").  Needs an MI355X.
+algorithm"), and the same for the general DPLR variant's records
+(``oracle.forms.dplr_chunk_local``).  Needs an MI355X.
 
 A white-box test: after a prefill whose chunks all fit one window, the workspace still
 holds every chunk's record, and this file decodes it with the layout the kernels write.
@@ -159,3 +160,105 @@ def test_records_strong_gates(kda, dtype, scale):
     written by the second chunk-local kernel)."""
     d = synth.random_small(520, 200, 2, 128, 128, dtype=dtype, gate_scale=scale)
     check_records(kda, d, dtype, 128)
+
+
+# ----------------------------------------------------------------------------
+# the general DPLR variant's records (kda_dplr_chunk_fwd, d = 128): Y = T B e^{Gx} and
+# Q e^G in fragment order, K e^{G_last - G} and -A e^{G_last - G} transposed, Mqk and
+# -Mqa (64 x 64) in fragment order, Z = (T Mbk) V and V as [4 row tiles][dv][16 rows],
+# gamma fp32; against oracle.forms.dplr_chunk_local
+# ----------------------------------------------------------------------------
+
+def dplr_layout(osz, D=128):
+    tile, sq = CH * D * osz, CH * CH * osz
+    off = {"Y": 0}
+    off["QG"] = a256(off["Y"] + tile)
+    off["KHT"] = a256(off["QG"] + tile)
+    off["ANT"] = a256(off["KHT"] + tile)
+    off["MQK"] = a256(off["ANT"] + tile)
+    off["NQA"] = a256(off["MQK"] + sq)
+    off["Z"] = a256(off["NQA"] + sq)
+    off["V"] = a256(off["Z"] + tile)
+    off["GAM"] = a256(off["V"] + tile)
+    off["BYTES"] = a256(off["GAM"] + D * 4)
+    return off
+
+
+def decode_dplr(rec, osz, D=128):
+    off = dplr_layout(osz, D)
+    ke = 8 if osz == 2 else 1
+    dt = np.float16 if osz == 2 else np.float32
+    mat = lambda key, n: rec[off[key]:off[key] + n * osz].view(dt).astype(np.float64)
+    r = np.arange(CH)[:, None]
+    c = np.arange(D)[None, :]
+    tiles = ((r >> 4) * D + c) * 16 + (r & 15)
+    return {"Y": mat("Y", CH * D)[frag_index(CH, D, ke)], "Qg": mat("QG", CH * D)[frag_index(CH, D, ke)],
+            "Kh": mat("KHT", CH * D)[frag_index(D, CH, ke)].T, "Ah": -mat("ANT", CH * D)[frag_index(D, CH, ke)].T,
+            "Mqk": mat("MQK", CH * CH)[frag_index(CH, CH, ke)], "Mqa": -mat("NQA", CH * CH)[frag_index(CH, CH, ke)],
+            "Z": mat("Z", CH * D)[tiles], "V": mat("V", CH * D)[tiles],
+            "gamma": rec[off["GAM"]:off["GAM"] + 4 * D].view(np.float32).astype(np.float64)}
+
+
+def check_dplr_records(kda, d, dtype):
+    D = 128
+    cu = np.asarray(d["cu_seqlens"], np.int64)
+    N, H = len(cu) - 1, d["q"].shape[1]
+    lens = np.diff(cu)
+    chunks = int((lens.max() + CH - 1) // CH)
+    osz = 2 if dtype == "bf16" else 4
+    off = dplr_layout(osz)
+    T = int(cu[-1])
+    varlen = N > 1
+    need = kda.dplr_workspace_size(1, T, H, D, D, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                   num_seqs=N if varlen else 0, max_seqlen=int(lens.max()) if varlen else 0)
+    state = a256(N * H * D * D * 4)
+    assert need >= state + N * chunks * H * off["BYTES"], "the test needs every chunk in one window"
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dev = lambda x: (torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16) if x.dtype == np.uint16
+                     else torch.from_numpy(np.ascontiguousarray(x))).cuda().unsqueeze(0)
+    args = [dev(d[x]) for x in ("q", "k", "v", "a", "b", "log_alpha")]
+    cu_t = torch.from_numpy(cu.astype(np.int32)).cuda() if varlen else None
+    init = None if d.get("init") is None else torch.from_numpy(d["init"]).cuda()
+    kda.dplr_chunk_fwd(*args, init, cu_t, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    wsh = ws.cpu().numpy()
+    q, k, v, a, b = (synth.as_f64(d[x]) for x in ("q", "k", "v", "a", "b"))
+    la = np.asarray(d["log_alpha"], np.float64)
+    keys = ("Y", "Z", "Qg", "Kh", "Ah", "V", "Mqk", "Mqa", "gamma")
+    acc = {key: oracle.Metrics() for key in keys}
+    for s in range(N):
+        for j in range((int(lens[s]) + CH - 1) // CH):
+            t0 = int(cu[s]) + j * CH
+            n = min(CH, int(cu[s + 1]) - t0)
+            for h in range(H):
+                slot = (s * chunks + j) * H + h
+                g = decode_dplr(wsh[state + slot * off["BYTES"]: state + (slot + 1) * off["BYTES"]], osz)
+                sl = slice(t0, t0 + n)
+                ref = forms.dplr_chunk_local(q[sl, h], k[sl, h], v[sl, h], a[sl, h], b[sl, h], la[sl, h])
+                ref["V"] = v[sl, h]
+                for key in ("Y", "Z", "Qg", "Kh", "Ah", "V"):
+                    acc[key].add(g[key][:n], ref[key])
+                    assert not g[key][n:].any(), f"{key}: rows past the sequence end are not zero"
+                for key in ("Mqk", "Mqa"):
+                    acc[key].add(g[key][:n, :n], ref[key])
+                    assert not g[key][n:].any() and not g[key][:, n:].any()
+                tiny = ref["gamma"] < 2.0 ** -126
+                assert (g["gamma"][tiny] < 2.0 ** -126).all()
+                acc["gamma"].add(g["gamma"][~tiny], ref["gamma"][~tiny])
+    for key, m in acc.items():
+        r = m.result()
+        print(f"  dplr {key}: max|err|/rms {r['max_over_rms']:.2e} (bar {BAR[dtype]:.0e})", flush=True)
+        assert r["max_over_rms"] <= BAR[dtype], f"dplr {key}: {r['max_over_rms']:.3e} > {BAR[dtype]:.0e}"
+
+
+@pytest.mark.parametrize("T,H,dtype,scale", [(300, 2, "bf16", 0.05), (200, 2, "f32", 0.05),
+                                             (200, 2, "bf16", 3.0), (150, 1, "f32", 15.0)])
+def test_dplr_records(kda, T, H, dtype, scale):
+    """Ordinary gates, and gates strong enough for the form whose factors are all <= 1."""
+    d = synth.dplr_small(530 + T, T, H, 128, dtype, gate_scale=scale)
+    check_dplr_records(kda, d, dtype)
+
+
+def test_dplr_records_varlen(kda):
+    d = synth.dplr_small(540, 0, 2, 128, "bf16", lens=[130, 40, 200])
+    check_dplr_records(kda, d, "bf16")
