@@ -518,7 +518,45 @@ def bench_dplr(kda, torch, synth, args, flush, stream):
                                   "dplr_over_kda_time": dm / km}
         del q, k, v, a, b, la, be, init, o, f, wk, wd
     torch.cuda.empty_cache()
+    res["decode"] = bench_dplr_decode(kda, torch, synth, args, stream)
     return res
+
+
+def bench_dplr_decode(kda, torch, synth, args, stream):
+    """One decode step of KDA and of the general DPLR transition at the decode workload's shape
+    (256 sequences x 32 heads, d = 128, bf16 inputs, fp32 state in place, fp32 out): time per
+    step over 20 consecutive steps, each updating the same state buffer in place."""
+    N, H, D = 256, 32, 128
+    dd = synth.gen_dplr_tokens(7, N, H, D, "bf16", 0.05)
+    be = to_dev(synth.gen_tokens(7, N, H, D, D, "bf16", 0.05)["beta"], torch)
+    q, k, v, a, b, la = (to_dev(dd[x], torch) for x in ("q", "k", "v", "a", "b", "log_alpha"))
+    del dd
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    state = torch.randn((N, H, D, D), dtype=torch.float32, device="cuda", generator=gen).mul_(0.02)
+    out = torch.empty((N, H, D), dtype=torch.float32, device="cuda")
+    steps = 20
+
+    def per_step(call):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps  # us
+
+    kda_us = per_step(lambda: kda.decode_step(q, k, v, la, be, state, out=out))
+    dplr_us = per_step(lambda: kda.dplr_decode_step(q, k, v, a, b, la, state, out=out))
+    kda_b = decode_bytes(N * H, D)
+    dplr_b = N * H * (2 * D * D * 4 + 5 * D * 2 + D * 4 + D * 4)  # state twice; q, k, v, a, b; log_alpha; out
+    del q, k, v, a, b, la, be, state, out
+    torch.cuda.empty_cache()
+    return {"units": N * H, "steps": steps, "kda_us_per_step": kda_us, "dplr_us_per_step": dplr_us,
+            "kda_hbm_gbs": kda_b / (kda_us * 1e3), "dplr_hbm_gbs": dplr_b / (dplr_us * 1e3),
+            "dplr_algorithmic_bytes": dplr_b, "dplr_over_kda_time": dplr_us / kda_us}
 
 
 def bench_backward(kda, torch, wp, q, k, v, la, be, init, args, flush, stream):

@@ -12,7 +12,8 @@ from __future__ import annotations
 from . import _lib
 from ._lib import KdaError, lib, status_string  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "dplr_chunk_fwd", "chunk_bwd", "decode_step", "layer_fwd", "layer_decode_step",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "dplr_chunk_fwd", "dplr_decode_step", "chunk_bwd", "decode_step",
+           "layer_fwd", "layer_decode_step",
            "workspace_size", "dplr_workspace_size", "bwd_workspace_size", "KdaError"]
 
 
@@ -209,6 +210,30 @@ def decode_step(q, k, v, log_alpha, beta, state, *, out=None, out_dtype=None):
                               k.data_ptr(), v.data_ptr(), log_alpha.data_ptr(), beta.data_ptr(), state.data_ptr(),
                               out.data_ptr(), _stream_handle(q.device))
     _lib.check(st, name)
+    return out
+
+
+def dplr_decode_step(q, k, v, a, b, log_alpha, state, *, out=None, out_dtype=None):
+    """One recurrent step of the general DPLR transition (kda_dplr_decode_step) for N
+    sequences: S <- Diag(alpha) S - a (b^T S) + k v^T, o = S^T q; updates ``state``
+    [N,H,dk,dv] in place.  q, k, a, b [N,H,dk], v [N,H,dv] (all fp32 or all bf16),
+    log_alpha [N,H,dk] fp32.  Returns out [N,H,dv]."""
+    torch = _torch()
+    _check_dev(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for t, name in ((k, "k"), (a, "a"), (b, "b")):
+        _check_dev(t, name, q.dtype, q.shape)
+    _check_dev(v, "v", q.dtype, (N, H, dv))
+    _check_dev(log_alpha, "log_alpha", torch.float32, (N, H, dk))
+    _check_dev(state, "state", torch.float32, (N, H, dk, dv))
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=q.dtype if out_dtype is None else out_dtype, device=q.device)
+    _check_dev(out, "out", None, (N, H, dv))
+    st = lib().kda_dplr_decode_step(N, H, dk, dv, _dtype_code(q.dtype), _dtype_code(out.dtype), q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), a.data_ptr(), b.data_ptr(), log_alpha.data_ptr(),
+                                    state.data_ptr(), out.data_ptr(), _stream_handle(q.device))
+    _lib.check(st, "kda_dplr_decode_step")
     return out
 
 

@@ -17,7 +17,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED", 3: "K
 # every symbol include/kda.h declares
 EXPORTS = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc",
            "kda_dplr_chunk_fwd_workspace_size", "kda_dplr_chunk_fwd", "kda_decode_step",
-           "kda_decode_step_head_gate",
+           "kda_decode_step_head_gate", "kda_dplr_decode_step",
            "kda_layer_fwd", "kda_layer_decode_step", "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
            "kda_status_string")
 
@@ -75,6 +75,8 @@ def lib():
         f = getattr(L, name)
         f.restype = ctypes.c_int
         f.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.kda_dplr_decode_step.restype = ctypes.c_int
+    L.kda_dplr_decode_step.argtypes = [i32, i32, i32, i32, ctypes.c_int, ctypes.c_int] + [vp] * 9
     L.kda_layer_fwd.restype = ctypes.c_int
     L.kda_layer_fwd.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Layer), vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 sz, vp]

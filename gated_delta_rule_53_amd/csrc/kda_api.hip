@@ -570,6 +570,33 @@ kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk,
                        out, stream);
 }
 
+kda_status_t kda_dplr_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
+                                  kda_dtype_t out_dtype, const void* q, const void* k, const void* v, const void* a,
+                                  const void* b, const float* log_alpha, float* state_inout, void* out,
+                                  hipStream_t stream) {
+    if (batch < 0 || heads <= 0 || dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    const int in_dt = enum_code(in_dtype), out_dt = enum_code(out_dtype);
+    if ((in_dt != KDA_DTYPE_F32 && in_dt != KDA_DTYPE_BF16) || (out_dt != KDA_DTYPE_F32 && out_dt != KDA_DTYPE_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (dk != dv || (dk != 64 && dk != 128)) return KDA_ERR_UNSUPPORTED;
+    if (batch == 0) return KDA_OK;
+    const int64_t units = (int64_t)batch * heads;
+    if (units > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !a || !b || !log_alpha || !state_inout || !out) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(state_inout) || !aligned16(out)) return KDA_ERR_INVALID_ARG;
+    const size_t vec = (size_t)units * dk;
+    const size_t in_b = dsize(in_dt), out_b = dsize(out_dt);
+    const size_t st_bytes = (size_t)units * dk * dv * 4, out_bytes = vec * out_b;
+    const Range inputs[] = {{q, vec * in_b}, {k, vec * in_b}, {v, vec * in_b},
+                            {a, vec * in_b}, {b, vec * in_b}, {log_alpha, vec * 4}};
+    if (overlaps(out, out_bytes, state_inout, st_bytes) || overlaps_any(out, out_bytes, inputs) ||
+        overlaps_any(state_inout, st_bytes, inputs))
+        return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda::dplr_decode_dispatch((int)units, dk, in_dt == KDA_DTYPE_BF16, out_dt == KDA_DTYPE_BF16, q, k,
+                                             v, a, b, log_alpha, state_inout, out, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status_t kda_layer_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv, kda_dtype_t in_dtype,
                                    kda_dtype_t out_dtype, int32_t gate_per_head, const kda_layer_t* layer,
                                    const void* q, const void* k, const void* v, const float* beta,

@@ -118,5 +118,9 @@ hipError_t dplr_dispatch(bool in_bf16, bool out_bf16, int bv, const ChunkArgs& a
 hipError_t decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, bool gate_per_head, const void* q,
                            const void* k, const void* v, const float* la, const float* beta, float* state,
                            void* out, const DecodeLayer& layer, hipStream_t st);
+// One step of the general DPLR transition (kda_decode.hip), d in {64, 128}.
+hipError_t dplr_decode_dispatch(int units, int d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                                const void* v, const void* a, const void* b, const float* la, float* state,
+                                void* out, hipStream_t st);
 
 }  // namespace kda

@@ -215,6 +215,23 @@ kda_status_t kda_decode_step_head_gate(int32_t batch, int32_t heads, int32_t dk,
                                        const void* q, const void* k, const void* v, const float* log_alpha,
                                        const float* beta, float* state_inout, void* out, hipStream_t stream);
 
+/* One recurrent step of the general DPLR transition (as kda_dplr_chunk_fwd,
+ * "Kimi Linear" page, "The constrained DPLR form and the chunkwise algorithm"):
+ * per (sequence, head), with alpha = exp(log_alpha) and w = b^T S read from the
+ * state before the token's decay,
+ *     S <- Diag(alpha) S - a w^T + k v^T;   o = S^T q.
+ * It reads and writes the state once, as kda_decode_step does.
+ *   q, k, a, b  [batch, H, dk] in_dtype;   v [batch, H, dv] in_dtype
+ *   log_alpha   [batch, H, dk] fp32 (no beta: the learning rate sits in a and k)
+ *   state_inout [batch, H, dk, dv] fp32, read and overwritten in place
+ *   out         [batch, H, dv] out_dtype
+ * dk == dv in {64, 128}.  No two of state_inout, out and the inputs may overlap
+ * (KDA_ERR_INVALID_ARG).  batch = 0 does nothing and returns KDA_OK. */
+kda_status_t kda_dplr_decode_step(int32_t batch, int32_t heads, int32_t dk, int32_t dv,
+                                  kda_dtype_t in_dtype, kda_dtype_t out_dtype,
+                                  const void* q, const void* k, const void* v, const void* a, const void* b,
+                                  const float* log_alpha, float* state_inout, void* out, hipStream_t stream);
+
 /* Layer prologue and epilogue fused around the operator ("Kimi Linear" page,
  * "Kimi Delta Attention" section): before the recurrence, q and k are scaled
  * to unit L2 norm per head and the per-channel decay is formed from the

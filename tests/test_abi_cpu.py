@@ -175,6 +175,25 @@ def test_decode_validation(L):
                              None) == INVALID
 
 
+def test_dplr_decode_validation(L):
+    """kda_dplr_decode_step: the decode checks, with a and b counted among the inputs."""
+    f = L.kda_dplr_decode_step
+    assert f(0, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, A, None) == OK  # empty batch: nothing to do
+    assert f(-1, 2, 64, 64, F32, F32, A, A, A, A, A, A, A, A, None) == INVALID
+    assert f(2, 2, 96, 96, F32, F32, A, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 128, F32, F32, A, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    assert f(2, 2, 64, 64, F32, 7, A, A, A, A, A, A, A, A, None) == UNSUPPORTED
+    for i in range(8):  # each of q, k, v, a, b, log_alpha, state, out missing
+        ptrs = [j * A for j in range(1, 7)] + [8 * A, 12 * A]
+        ptrs[i] = None
+        assert f(2, 2, 64, 64, F32, F32, *ptrs, None) == INVALID
+    st, out = 8 * A, 12 * A
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, st + 4, out, None) == INVALID  # misaligned
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, st, st + 256, None) == INVALID  # out in state
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, st + 64, 5 * A, 6 * A, st, out, None) == INVALID  # a in state
+    assert f(2, 2, 64, 64, F32, F32, A, 2 * A, 3 * A, 4 * A, out + 16, 6 * A, st, out, None) == INVALID  # b in out
+
+
 def test_shape_struct_layout_matches_the_boundary():
     """kda_shape_t starts with the fields batch, seqlen, num_seqs, heads, dk, dv, in_dtype,
     out_dtype at the offsets a C compiler gives them, then max_seqlen and gate_per_head;

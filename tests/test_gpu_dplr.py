@@ -172,3 +172,56 @@ def test_dplr_bench_shape_every_head(kda):
     m = assert_close("out", o, ro, TOL["bf16"])
     ms = assert_close("final_state", S, rS, TOL["bf16"])
     print(f"dplr bench shape: out {m['max_over_rms']:.2e}, final state {ms['max_over_rms']:.2e}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# decode: one token per sequence, state in place (kda_dplr_decode_step)
+# ----------------------------------------------------------------------------
+
+DECODE_TOL = 1e-4  # fp32 arithmetic from the inputs to the state, whatever the input dtype
+
+
+def oracle_dplr_step(S, st):
+    """One step for N sequences: the oracle's DPLR recurrence over N one-token sequences."""
+    N = st["q"].shape[0]
+    return oracle.dplr_recurrent(st["q"], st["k"], st["v"], st["a"], st["b"], st["log_alpha"], S,
+                                 np.arange(N + 1, dtype=np.int64))
+
+
+@pytest.mark.parametrize("N,H,dtype,D", [(5, 3, "f32", 64), (16, 4, "bf16", 128), (7, 2, "f32", 128),
+                                         (9, 2, "bf16", 64)])
+def test_dplr_decode_steps(kda, N, H, dtype, D):
+    """Three steps from a random state, every output and the final state against the oracle."""
+    S0 = synth.gen_states(81 + N, N, H, D, D, 0.3)
+    steps = [synth.gen_dplr_tokens(82 + N + i, N, H, D, dtype, 0.05) for i in range(3)]
+    names = ("q", "k", "v", "a", "b", "log_alpha")
+    state = to_dev(S0, torch)
+    outs = [kda.dplr_decode_step(*[to_dev(st[x], torch) for x in names], state,
+                                 out=nan_tensor(torch, (N, H, D))).cpu().numpy() for st in steps]
+    torch.cuda.synchronize()
+    S = S0
+    for i, st in enumerate(steps):
+        o, S = oracle_dplr_step(S, st)
+        assert_close(f"out{i}", outs[i], o, DECODE_TOL)
+    assert_close("state", state.cpu().numpy(), S, DECODE_TOL)
+
+
+def test_dplr_decode_continues_prefill(kda):
+    """A prefill of 200 tokens (2 sequences of 120 and 80, bf16) then one decode step from its
+    final state: the oracle over the same 121 and 81 tokens at once."""
+    lens = [120, 80]
+    d = synth.dplr_small(91, 0, 2, D, "bf16", lens=lens, init_std=0.02)
+    o, S = run_dplr(kda, d)
+    st = synth.gen_dplr_tokens(92, 2, 2, D, "bf16", 0.05)
+    state = torch.from_numpy(S).cuda()
+    y = kda.dplr_decode_step(*[to_dev(st[x], torch) for x in ("q", "k", "v", "a", "b", "log_alpha")], state,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # the oracle over each sequence with its decode token appended
+    cu = np.asarray(d["cu_seqlens"], np.int64)
+    joined = {x: np.concatenate([d[x][cu[0]:cu[1]], st[x][0:1], d[x][cu[1]:cu[2]], st[x][1:2]])
+              for x in ("q", "k", "v", "a", "b", "log_alpha")}
+    cu2 = np.array([0, lens[0] + 1, lens[0] + lens[1] + 2], np.int64)
+    ro, rS = oracle.dplr_recurrent(*[joined[x] for x in ("q", "k", "v", "a", "b", "log_alpha")], d["init"], cu2)
+    assert_close("decode out", y.cpu().numpy(), ro[[cu2[1] - 1, cu2[2] - 1]], TOL["bf16"])
+    assert_close("state", state.cpu().numpy(), rS, TOL["bf16"])
