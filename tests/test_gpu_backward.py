@@ -244,6 +244,16 @@ def test_backward_workload2_every_head(kda):
         assert_metrics(gk, acc[gk], TOL["bf16"])
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_d64_long(kda, dtype):
+    """Head dimension 64 at length: 8,192 tokens x 8 heads (128-chunk reverse chain), every
+    gradient element."""
+    d = random_small(131, 8192, 8, 64, 64, dtype=dtype, init_std=0.02)
+    dO, dF = _grads(132, d)
+    g = run_bwd(kda, d, dO, dF)
+    check(g, oracle_bwd(d, dO, dF), TOL[dtype])
+
+
 @pytest.mark.parametrize("B,T,D,dtype", [(3, 130, 64, "f32"), (2, 100, 128, "bf16")])
 def test_backward_dense_batch(kda, B, T, D, dtype):
     """A dense batch [B, T, H, d] (no cu_seqlens): the same gradients as the B sequences packed."""

@@ -382,6 +382,18 @@ def test_workload4_varlen_1m(kda):
     assert_close("state", S, S_ref, TOL["bf16"])
 
 
+def test_long_d64(kda):
+    """Head dimension 64 at length: 65,536 tokens x 8 heads, bf16, long-memory gates and a
+    random initial state (1,024-step chain in 32-column value slices), every element."""
+    w = synth.Workload("kda_prefill_bf16_h8_t65536_d64", "prefill", "bf16", heads=8, dk=64, dv=64,
+                       seqlen=65536, batch=1, gate_scale=0.01, init_std=0.02, seed=6)
+    d = synth.make_prefill(w)
+    o, S = run_chunk(kda, torch, d)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["bf16"])
+    assert_close("state", S, S_ref, TOL["bf16"])
+
+
 def test_long_single_sequence_1m(kda):
     """One sequence of 1,048,576 tokens (the context length the pages give the released model)
     on 4 heads, with the long-memory gate draw (log_alpha = -0.01 softplus(N(0,1))) and a
