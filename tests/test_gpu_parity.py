@@ -505,6 +505,18 @@ def test_many_sequences_grid_rows(kda):
     assert T == 4096 + sum(lens[1:])
 
 
+
+def test_most_sequences_one_launch_holds(kda):
+    """65,535 sequences of 0 to 3 tokens (the most a launch's grid rows hold: one chunk index
+    per window), one head, d = 64, fp32: every output and final state."""
+    lens = [int(x) for x in np.random.default_rng(65535).integers(0, 4, 65535)]
+    d = random_small(77, 0, 1, 64, 64, dtype="f32", init_std=0.02, lens=lens)
+    o, S = run_chunk(kda, torch, d, max_seqlen=3)
+    o_ref, S_ref = oracle_chunk(d)
+    assert_close("out", o, o_ref, TOL["f32"])
+    assert_close("state", S, S_ref, TOL["f32"])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_beta_up_to_two(kda, dtype):
     """beta uniform in [0, 2] (the method allows any finite beta; 2 is a reflection): parity with
