@@ -112,6 +112,8 @@ def check_records(kda, d, dtype, D):
     wsh = ws.cpu().numpy()
     q, k, v = (synth.as_f64(d[x]) for x in ("q", "k", "v"))
     la = np.asarray(d["log_alpha"], np.float64)
+    if la.ndim == 2:  # one gate per (token, head): the same for every key channel
+        la = np.repeat(la[:, :, None], D, axis=2)
     beta = np.asarray(d["beta"], np.float64)
     acc = {key: oracle.Metrics() for key in ("W", "Ut", "Qg", "Kh", "P", "gamma")}
     for s in range(N):
@@ -146,6 +148,13 @@ def check_records(kda, d, dtype, D):
 def test_records_dense(kda, T, H, D, dtype):
     d = synth.random_small(500 + T, T, H, D, D, dtype=dtype)
     check_records(kda, d, dtype, D)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_records_head_gate(kda, dtype):
+    """One gate per (token, head) (the scalar gate of Gated DeltaNet) on the same kernels."""
+    d = synth.random_small(505, 230, 2, 128, 128, dtype=dtype, gate="head")
+    check_records(kda, d, dtype, 128)
 
 
 def test_records_varlen(kda):
