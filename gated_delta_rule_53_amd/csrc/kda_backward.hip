@@ -250,13 +250,23 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     using C16 = ChainRec16<D>;
     constexpr bool H16 = std::is_same<IT, bf16_t>::value;  // chain operands as fp16 fragments
     constexpr int DP = D + 1;
-    __shared__ float sK[CH * DP];
-    __shared__ float sX[CH * DP];  // q, then v
-    __shared__ float sG[CH * DP];
-    __shared__ float sA[CH * (CH + 1)];  // A0
-    __shared__ float sT[CH * (CH + 1)];
-    __shared__ float sB[CH];
     constexpr int AP = CH + 1;
+    // q and k are staged in their input type (a bf16 input is exact as bf16) with rows
+    // of an odd number of dwords; once the products that read them are done, each
+    // region holds a 64 x 64 fp32 matrix (k's: T, q's: A0).  G's region later holds
+    // Bk = beta K e^G, then Bv = beta V.  With bf16 inputs this is 67 KB of LDS, so two
+    // workgroups share a CU.
+    constexpr int KP = H16 ? D + 2 : D + 1;  // elements per staged q or k row
+    constexpr int RB = (CH * KP * (int)sizeof(IT) > CH * AP * 4 ? CH * KP * (int)sizeof(IT) : CH * AP * 4);
+    __shared__ __align__(16) float sG[CH * DP];
+    __shared__ __align__(16) unsigned char sKT[RB];
+    __shared__ __align__(16) unsigned char sQA[RB];
+    __shared__ float sB[CH];
+    __shared__ float sGL[D];  // G of the chunk's last row
+    IT* sK = reinterpret_cast<IT*>(sKT);
+    IT* sQ = reinterpret_cast<IT*>(sQA);
+    float* sT = reinterpret_cast<float*>(sKT);
+    float* sA = reinterpret_cast<float*>(sQA);
 
     // a.Wc chunks per sequence in this backward window, a.win its index
     const int h = blockIdx.x, s = blockIdx.y / a.Wc, jl = blockIdx.y % a.Wc, j = a.win * a.Wc + jl;
@@ -300,10 +310,11 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int idx = t + BW_T * i, r = idx / D, c = idx % D;
         const size_t th = (size_t)(tb + c0 + min(r, n - 1)) * H + h;
         const bool ok = r < n;
-        const float kx = ld(k, th * D + c), qx = ld(q, th * D + c), vx = ld(v, th * D + c);
+        const IT kx = k[th * D + c], qx = q[th * D + c];
+        const float vx = ld(v, th * D + c);
         const float gx = a.gate_per_head ? a.la[th] : a.la[th * D + c];
-        sK[r * DP + c] = ok ? kx : 0.f;
-        sX[r * DP + c] = ok ? qx : 0.f;
+        sK[r * KP + c] = ok ? kx : IT{};
+        sQ[r * KP + c] = ok ? qx : IT{};
         sG[r * DP + c] = ok ? gx : 0.f;
         vr[i] = ok ? vx : 0.f;
     }
@@ -315,19 +326,23 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             acc += (double)sG[r * DP + t];
             sG[r * DP + t] = (float)acc;
         }
+        sGL[t] = sG[(n - 1) * DP + t];
     }
     __syncthreads();
+    auto kf = [&](int r, int c) { return to_f32(sK[r * KP + c]); };
 
     // A0 (strict) and P (inclusive) by 16x16 blocks, anchored: row a for an
     // off-diagonal block (the later block's first row), the block's ninth row
-    // for a diagonal one
+    // for a diagonal one.  P goes to the record; this wave's A0 blocks (tasks
+    // wave and wave + BW_W below 10) stay in registers until q's region is free.
+    floatx4 a0[2] = {zero4(), zero4()};
     for (int task = wave; task < 20; task += BW_W) {
         const bool isP = task >= 10;
         const int bt = task % 10;
         const int rb = bt < 1 ? 0 : bt < 3 ? 1 : bt < 6 ? 2 : 3;
         const int cb = bt - rb * (rb + 1) / 2;
         const int an = cb < rb ? 16 * rb : 16 * rb + 8;
-        const float* X = isP ? sX : sK;
+        const IT* X = isP ? sQ : sK;
         const int rr = 16 * rb + li, ii = 16 * cb + li;
         floatx4 acc = zero4();
         // a diagonal block whose single-anchor exponents pass kWideExp (in either direction:
@@ -342,8 +357,8 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         }
         if (!wide) {
             tile_f32(acc, D, lane,
-                     [&](int c) { return X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[an * DP + c]); },
-                     [&](int c) { return sK[ii * DP + c] * fast_exp(sG[an * DP + c] - sG[ii * DP + c]); });
+                     [&](int c) { return to_f32(X[rr * KP + c]) * fast_exp(sG[rr * DP + c] - sG[an * DP + c]); },
+                     [&](int c) { return kf(ii, c) * fast_exp(sG[an * DP + c] - sG[ii * DP + c]); });
         } else {
             // level lev: pairs (r, i) in the later / earlier half of an aligned sub-block of
             // sz rows, anchored at its middle row; a last level (isP only) for the diagonal
@@ -354,14 +369,13 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
                 floatx4 lv = zero4();
                 tile_f32(lv, D, lane,
                          [&](int c) {
-                             return dg ? X[rr * DP + c]
-                                       : ((li & msk) >= hs ? X[rr * DP + c] * fast_exp(sG[rr * DP + c] - sG[ra * DP + c])
-                                                           : 0.f);
+                             const float x = to_f32(X[rr * KP + c]);
+                             return dg ? x
+                                       : ((li & msk) >= hs ? x * fast_exp(sG[rr * DP + c] - sG[ra * DP + c]) : 0.f);
                          },
                          [&](int c) {
-                             return dg ? sK[ii * DP + c]
-                                       : ((li & msk) < hs ? sK[ii * DP + c] * fast_exp(sG[ra * DP + c] - sG[ii * DP + c])
-                                                          : 0.f);
+                             const float x = kf(ii, c);
+                             return dg ? x : ((li & msk) < hs ? x * fast_exp(sG[ra * DP + c] - sG[ii * DP + c]) : 0.f);
                          });
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -378,23 +392,45 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
             const bool keep = cb < rb || (isP ? row >= col : row > col);
             const float x = keep ? acc[r] : 0.f;
             if (isP) put_p(row, col, x);
-            else sA[row * AP + col] = x;
+            else if (task < BW_W) a0[0][r] = x;
+            else a0[1][r] = x;
         }
     }
-    // zero upper blocks of A0; P's upper blocks in the record
+    // P's upper blocks in the record
     for (int idx = t; idx < CH * CH; idx += BW_T) {
         const int r = idx / CH, c = idx % CH;
-        if ((c >> 4) > (r >> 4)) {
-            sA[r * AP + c] = 0.f;
-            put_p(r, c, 0.f);
-        }
+        if ((c >> 4) > (r >> 4)) put_p(r, c, 0.f);
+    }
+    __syncthreads();
+    // Qg, Kh, G and gamma to the record; Bk = beta K e^G replaces G in LDS (each
+    // element by the thread that read it)
+    for (int idx = t; idx < CH * D; idx += BW_T) {
+        const int r = idx / D, c = idx % D;
+        const float g = sG[r * DP + c], e = fast_exp(g), kx = kf(r, c);
+        put_qg(r, c, to_f32(sQ[r * KP + c]) * e);
+        put_kh(r, c, kx * fast_exp(sGL[c] - g));
+        rec[R::G + idx] = g;
+        sG[r * DP + c] = sB[r] * kx * e;
+    }
+    __syncthreads();
+    // q and k are no longer read: A0 into q's region (this wave's blocks, then zero
+    // upper blocks), T zeroed in k's
+    for (int task = wave, i = 0; task < 10; task += BW_W, ++i) {
+        const int rb = task < 1 ? 0 : task < 3 ? 1 : task < 6 ? 2 : 3;
+        const int cb = task - rb * (rb + 1) / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sA[(16 * rb + 4 * gq + r) * AP + 16 * cb + li] = a0[i][r];
+    }
+    for (int idx = t; idx < CH * CH; idx += BW_T) {
+        const int r = idx / CH, c = idx % CH;
+        if ((c >> 4) > (r >> 4)) sA[r * AP + c] = 0.f;
+        sT[r * AP + c] = 0.f;
     }
     __syncthreads();
     for (int idx = t; idx < CH * CH; idx += BW_T) {  // A0 to the record, then Atil = diag(beta) A0 in LDS
         const int r = idx / CH, c = idx % CH;
         rec[R::A0 + idx] = sA[r * AP + c];
         sA[r * AP + c] *= sB[r];
-        sT[r * AP + c] = 0.f;
     }
     __syncthreads();
     // T = (I + Atil)^-1 (the same product form and block inversion as the forward's)
@@ -405,17 +441,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     }
     __syncthreads();
     for (int idx = t; idx < CH * CH; idx += BW_T) rec[R::T + idx] = sT[(idx / CH) * AP + idx % CH];
-    // Qg, Kh, G and gamma to the record; then Bk = beta K e^G replaces K in LDS and
-    // W = T Bk
-    const float* GL = sG + (n - 1) * DP;
-    for (int idx = t; idx < CH * D; idx += BW_T) {
-        const int r = idx / D, c = idx % D;
-        const float g = sG[r * DP + c], e = fast_exp(g), kx = sK[r * DP + c];
-        put_qg(r, c, sX[r * DP + c] * e);
-        put_kh(r, c, kx * fast_exp(GL[c] - g));
-        rec[R::G + idx] = g;
-        sK[r * DP + c] = sB[r] * kx * e;
-    }
+    const float* GL = sGL;
     for (int idx = t; idx < D * 16; idx += BW_T) {  // gamma of dS row c, for every li
         const int c = idx / 16, l = (idx % 16) + 16 * ((c & 15) >> 2);
         if constexpr (H16) rec[R::CR + C16::gam(C::wave_of(c), C::tile_of(c), l, c & 3)] = fast_exp(GL[c]);
@@ -428,7 +454,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         floatx4 acc = zero4();
         // T is lower triangular: row block mt sees columns below 16 (mt + 1)
         tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
-                 [&](int i) { return sK[i * DP + cc]; });
+                 [&](int i) { return sG[i * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
@@ -437,11 +463,11 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         }
     }
     __syncthreads();
-    // Ut = T Bv (Bv = beta V)
+    // Ut = T Bv (Bv = beta V, into G's region)
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int idx = t + BW_T * i, r = idx / D, c = idx % D;
-        sX[r * DP + c] = sB[r] * vr[i];
+        sG[r * DP + c] = sB[r] * vr[i];
     }
     __syncthreads();
     for (int task = wave; task < 4 * (D / 16); task += BW_W) {
@@ -449,7 +475,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         const int cc = 16 * nt + li;
         floatx4 acc = zero4();
         tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
-                 [&](int i) { return sX[i * DP + cc]; });
+                 [&](int i) { return sG[i * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) rec[R::UT + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
     }
