@@ -24,11 +24,12 @@
 //
 // Kernels (all fp32 arithmetic, fp32 matrix cores):
 //   chunk_local_kernel + chunk_inter_kernel (the forward's, with state
-//     snapshots): S_j for every chunk;
+//     snapshots): S_j and U_j for every chunk, U_j as the state pass forms it
+//     (the U that carried S_j to S_{j+1});
 //   bwd_prep_kernel   one 512-thread workgroup per (chunk, head): G, A0, P, T,
-//                     W, Ut, Qg, Kh, gamma -> an fp32 record (T, A0, W, Ut, G
-//                     row-major for the local pass; P^T, Kh, Qg^T, -W^T and
-//                     gamma in the chain's matrix-core order);
+//                     W, Qg, Kh, gamma -> an fp32 record (T, A0, G row-major for
+//                     the local pass; P^T, Kh, Qg^T, -W^T and gamma in the
+//                     chain's matrix-core order);
 //   bwd_chain_kernel  one 256-thread workgroup per (sequence, head, 16 value
 //                     columns): the reverse chain over chunks, writing dS_{j+1}
 //                     and dU_j, each chunk's operands loaded during the previous;
@@ -115,12 +116,12 @@ template <int D>
 struct BRec {
     static constexpr size_t T = 0;
     static constexpr size_t A0 = T + CH * CH;
-    static constexpr size_t W = A0 + CH * CH;
-    static constexpr size_t UT = W + CH * D;
-    static constexpr size_t G = UT + CH * D;
+    static constexpr size_t U = A0 + CH * CH;  // U = Ut - W S_j, stored by the recompute's state pass
+    static constexpr size_t G = U + CH * D;
     static constexpr size_t CR = G + CH * D;
     static constexpr size_t FLOATS = CR + ChainRec<D>::FLOATS;
     static_assert(ChainRec16<D>::FLOATS <= ChainRec<D>::FLOATS, "fp16 chain operands fit the chain region");
+    static_assert(U % 4 == 0 && FLOATS % 4 == 0, "the state pass stores U as 16-byte aligned float4s");
 };
 
 __device__ __forceinline__ void seq_range(const ChunkArgs& a, int s, int64_t& t0, int64_t& L) {
@@ -254,7 +255,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     // q and k are staged in their input type (a bf16 input is exact as bf16) with rows
     // of an odd number of dwords; once the products that read them are done, each
     // region holds a 64 x 64 fp32 matrix (k's: T, q's: A0).  G's region later holds
-    // Bk = beta K e^G, then Bv = beta V.  With bf16 inputs this is 67 KB of LDS, so two
+    // Bk = beta K e^G.  With bf16 inputs this is 67 KB of LDS, so two
     // workgroups share a CU.
     constexpr int KP = H16 ? D + 2 : D + 1;  // elements per staged q or k row
     constexpr int RB = (CH * KP * (int)sizeof(IT) > CH * AP * 4 ? CH * KP * (int)sizeof(IT) : CH * AP * 4);
@@ -279,7 +280,6 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, li = lane & 15, gq = lane >> 4;
     const IT* q = static_cast<const IT*>(a.q);
     const IT* k = static_cast<const IT*>(a.k);
-    const IT* v = static_cast<const IT*>(a.v);
     float* rec = brec + ((size_t)(s * a.Wc + jl) * H + h) * R::FLOATS;
     _Float16* rec16 = reinterpret_cast<_Float16*>(rec + R::CR);
     // chain operands: P[row][col] (A-row col of dU), Qg[r][c] and -W[r][c] (A-row c of
@@ -301,22 +301,18 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         else rec[R::CR + C::at(C::wave_of(c), C::qbase(c) + C::EQ + C::ks(r), (c & 15) + 16 * C::kg(r))] = x;
     };
 
-    // inputs, branch-free: rows past the sequence end clamped, then zeroed; v
-    // stays in registers until Ut
+    // inputs, branch-free: rows past the sequence end clamped, then zeroed
     constexpr int PER = CH * D / BW_T;
-    float vr[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int idx = t + BW_T * i, r = idx / D, c = idx % D;
         const size_t th = (size_t)(tb + c0 + min(r, n - 1)) * H + h;
         const bool ok = r < n;
         const IT kx = k[th * D + c], qx = q[th * D + c];
-        const float vx = ld(v, th * D + c);
         const float gx = a.gate_per_head ? a.la[th] : a.la[th * D + c];
         sK[r * KP + c] = ok ? kx : IT{};
         sQ[r * KP + c] = ok ? qx : IT{};
         sG[r * DP + c] = ok ? gx : 0.f;
-        vr[i] = ok ? vx : 0.f;
     }
     if (t < CH) sB[t] = t < n ? a.beta[(size_t)(tb + c0 + t) * H + h] : 0.f;
     __syncthreads();
@@ -456,28 +452,7 @@ __global__ void __launch_bounds__(BW_T) bwd_prep_kernel(ChunkArgs a, float* brec
         tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
                  [&](int i) { return sG[i * DP + cc]; });
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * gq + r;
-            rec[R::W + row * D + cc] = acc[r];
-            put_mw(row, cc, -acc[r]);
-        }
-    }
-    __syncthreads();
-    // Ut = T Bv (Bv = beta V, into G's region)
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int idx = t + BW_T * i, r = idx / D, c = idx % D;
-        sG[r * DP + c] = sB[r] * vr[i];
-    }
-    __syncthreads();
-    for (int task = wave; task < 4 * (D / 16); task += BW_W) {
-        const int mt = task / (D / 16), nt = task % (D / 16);
-        const int cc = 16 * nt + li;
-        floatx4 acc = zero4();
-        tile_f32(acc, 16 * (mt + 1), lane, [&](int i) { return sT[(16 * mt + li) * AP + i]; },
-                 [&](int i) { return sG[i * DP + cc]; });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rec[R::UT + (16 * mt + 4 * gq + r) * D + cc] = acc[r];
+        for (int r = 0; r < 4; ++r) put_mw(16 * mt + 4 * gq + r, cc, -acc[r]);
     }
 }
 
@@ -876,20 +851,16 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     __syncthreads();
     const float* GL = sG + (n - 1) * GD;
 
-    // U = Ut - W S_j
+    // U = Ut - W S_j, as the recompute's state pass formed it (rows past the end zeroed)
+    {
+        float4 x[V4];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int mt = mt_of(i), cc = 16 * nt_of(i) + li, rr = 16 * mt + li;
-        floatx4 acc = zero4();
-        tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(rec + R::W, (size_t)rr * D + c); },
-                      [&](int c) {
-                          const float* p = S + (size_t)c * D + cc;
-                          return make_float4(p[0], p[D], p[2 * D], p[3 * D]);
-                      });
+        for (int i = 0; i < V4; ++i) x[i] = ld4(rec + R::U, 4 * (t + BL_T * i));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * gq + r;
-            sX[row * DP + cc] = rec[R::UT + (size_t)row * D + cc] - acc[r];
+        for (int i = 0; i < V4; ++i) {
+            const int idx = 4 * (t + BL_T * i), r = idx / D, c = idx % D;
+            const float m = r < n ? 1.f : 0.f;
+            *reinterpret_cast<float4*>(sX + r * DP + c) = make_float4(m * x[i].x, m * x[i].y, m * x[i].z, m * x[i].w);
         }
     }
     stage(dO, sY, same);
@@ -1275,6 +1246,8 @@ static hipError_t bwd_run(const BwdArgs& b, hipStream_t st) {
         ChunkArgs r = a;
         r.snap_wc = wb;
         r.snap_j0 = w * wb;
+        r.snapU = b.brec + BRec<D>::U;
+        r.snapU_stride = BRec<D>::FLOATS;
         if ((e = chunk_snapshot_dispatch(D, BF, r, rw, w * rpb, std::min(rpb, nrw - w * rpb), true, st,
                                          b.f32_records)) != hipSuccess)
             return e;

@@ -787,6 +787,7 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
     __shared__ __align__(16) OT sU[2][BV * UP];
     constexpr int SNP = BV + 1;
     __shared__ float sSnap[SNAP ? D * SNP : 1];
+    __shared__ float sUsnap[SNAP ? CH * SNP : 1];
 
     constexpr int ZS = D / BV;                   // slices of the value columns
     constexpr int Z = MODE == 1 ? 2 * ZS : ZS;  // the first segment pass also carries the transition product
@@ -906,6 +907,10 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Uv[r] = f.U[ct][r] - acc[r];
                 store4<OT>(sU[cur] + (16 * ct + li) * UP + 16 * w + 4 * gq, Uv);
+                if constexpr (SNAP) {  // U_j in fp32, for the backward pass
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sUsnap[(16 * w + 4 * gq + r) * SNP + 16 * ct + li] = Uv[r];
+                }
             }
             lds_barrier();  // U_j is in sU[cur]
 #pragma unroll
@@ -941,15 +946,27 @@ __global__ void __launch_bounds__(512) chunk_inter_kernel(ChunkArgs a) {
             }
         }
     } else if constexpr (SNAP) {
-        // no outputs: between the step's two barriers, store the chain's fp32 copy of S_j
+        // no outputs: between the step's two barriers, store the chain's fp32 copy of
+        // S_j; after the second, U_j (the chain writes the next U only after the next
+        // step's first barrier)
         for (int j = jb; j < je; ++j) {
             lds_barrier();  // S_j is in sSnap
-            float* dst = a.snap + ((size_t)(s * a.snap_wc + (j - a.snap_j0)) * H + h) * D * D + col0;
-            for (int idx = t - 256; idx < D * BV; idx += 256) {
-                const int k = idx / BV, c = idx % BV;
-                dst[(size_t)k * D + c] = sSnap[k * SNP + c];
+            const size_t chh = (size_t)(s * a.snap_wc + (j - a.snap_j0)) * H + h;
+            float* dst = a.snap + chh * D * D + col0;
+            for (int idx = t - 256; idx < D * BV / 4; idx += 256) {  // 16 bytes per lane
+                const int k = idx / (BV / 4), c = 4 * (idx % (BV / 4));
+                const float* sp = sSnap + k * SNP + c;
+                *reinterpret_cast<float4*>(dst + (size_t)k * D + c) = make_float4(sp[0], sp[1], sp[2], sp[3]);
             }
-            lds_barrier();
+            lds_barrier();  // U_j is in sUsnap
+            if (a.snapU) {
+                float* du = a.snapU + chh * a.snapU_stride + col0;
+                for (int idx = t - 256; idx < CH * BV / 4; idx += 256) {
+                    const int r = idx / (BV / 4), c = 4 * (idx % (BV / 4));
+                    const float* sp = sUsnap + r * SNP + c;
+                    *reinterpret_cast<float4*>(du + (size_t)r * D + c) = make_float4(sp[0], sp[1], sp[2], sp[3]);
+                }
+            }
         }
     } else if constexpr (MODE == 1) {
         for (int j = jb; j < je; ++j) {  // no outputs in this pass; keep the barrier count

@@ -46,6 +46,10 @@ struct ChunkArgs {
     float* snap = nullptr;
     int snap_wc = 0;
     int snap_j0 = 0;  // chunk index of the snapshot array's first chunk
+    // with snap: the chunk's U = Ut - W S_j as the state pass forms it, fp32 [64][D]
+    // at snapU + (the snapshot's chunk-head index) * snapU_stride (null: not written)
+    float* snapU = nullptr;
+    size_t snapU_stride = 0;
 };
 
 // Layer prologue and epilogue of one decode step (null pointers: off).
