@@ -761,7 +761,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
     constexpr int TPW = 4 * NB / BL_W;    // tiles of such a matrix per wave
     __shared__ __align__(16) float sG[CH * GD];  // G, rows padded against bank conflicts
     __shared__ float sT[CH * AP];
-    __shared__ __align__(16) float sX[CH * DP];   // U, dW, T^T dT, q, dG
+    __shared__ __align__(16) float sX[CH * DP];   // U, dW, dU, T^T dT, q, dG
     __shared__ __align__(16) float sY[CH * DP];   // dO, Bk, Bv, k
     __shared__ float sP[CH * AP];   // dP, then column partial sums
     __shared__ float sM[CH * AP];   // dT, then diag(beta) dAtil
@@ -962,7 +962,18 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         }
     }
     __syncthreads();
-    stage(v, sY, same);
+    // dU to LDS (sX: dW's last reader, dBk, is done), beside V
+    {
+        float4 x[V4];
+#pragma unroll
+        for (int i = 0; i < V4; ++i) x[i] = ld4(dU, 4 * (t + BL_T * i));
+        stage(v, sY, same);
+#pragma unroll
+        for (int i = 0; i < V4; ++i) {
+            const int idx = 4 * (t + BL_T * i);
+            *reinterpret_cast<float4*>(sX + (idx / D) * DP + idx % D) = x[i];
+        }
+    }
     __syncthreads();
     // dT += tril(dU Bv^T) (the same tasks per wave as above, Bv = diag(beta) V);  dBv = T^T dU -> dv, dbeta
     for (int task = wave; task < 16; task += BL_W) {
@@ -970,7 +981,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         if (nt > mt) continue;
         floatx4 acc = zero4();
         const float bc = sBeta[16 * nt + li];
-        tile_f32_v<4>(acc, D, lane, [&](int c) { return ld4(dU, (size_t)(16 * mt + li) * D + c); },
+        tile_f32_v<4>(acc, D, lane, [&](int c) { return lds4(sX + (16 * mt + li) * DP + c); },
                       [&](int c) {
                           const float4 y = lds4(sY + (16 * nt + li) * DP + c);
                           return make_float4(bc * y.x, bc * y.y, bc * y.z, bc * y.w);
@@ -987,7 +998,7 @@ __global__ void __launch_bounds__(BL_T) bwd_local_kernel(BwdArgs b) {
         floatx4 acc = zero4();
         const int r0 = 16 * mt;
         tile_f32(acc, CH - r0, lane, [&](int r) { return sT[(r0 + r) * AP + ii]; },
-                 [&](int r) { return dU[(size_t)(r0 + r) * D + cc]; });
+                 [&](int r) { return sX[(r0 + r) * DP + cc]; });
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * mt + 4 * gq + r;
